@@ -1,0 +1,326 @@
+// Host side of libsla2.so: argument validation, workspace plan, launch sequence.
+// The declarations and conventions are in include/sla2.h.
+#include <atomic>
+#include <cmath>
+#include <cstdlib>
+#include <cstring>
+
+#include "../../include/sla2.h"
+#include "sla2_common.h"
+
+using namespace sla2;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+struct Plan {
+  size_t qsum, ksum, mu64, mu32, A, Bt, mask, list, cnt, qc, kc, vc, sq, sk, sv, hbf, z, hpart,
+      zpart, htot, ztot, ol, total;
+};
+
+Plan make_plan(const Geom& g) {
+  Plan p{};
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o += up(bytes);
+    return at;
+  };
+  const size_t BH = static_cast<size_t>(g.BH), N = g.N, nqb = g.nqb, nkb = g.nkb;
+  const size_t np = (nkb + kKpPerWg - 1) / kKpPerWg;
+  p.qsum = take(BH * nqb * kD * 8);
+  p.ksum = take(BH * nkb * kD * 8);
+  p.mu64 = take(BH * kD * 8);
+  p.mu32 = take(BH * kD * 4);
+  p.A = take(BH * nqb * kD * 8);
+  p.Bt = take(BH * nkb * kD * 8);
+  p.mask = take(BH * nqb * nkb);
+  p.list = take(BH * nqb * nkb * 4);
+  p.cnt = take(BH * nqb * 4);
+  p.qc = take(BH * N * kD);
+  p.kc = take(BH * N * kD);
+  p.vc = take(BH * N * kD);
+  p.sq = take(BH * nqb * 4);
+  p.sk = take(BH * nkb * 4);
+  p.sv = take(BH * nkb * 4);
+  p.hbf = take(BH * nkb * kD * kD * 2);
+  p.z = take(BH * nkb * kD * 4);
+  p.hpart = take(BH * np * kD * kD * 4);
+  p.zpart = take(BH * np * kD * 4);
+  p.htot = take(BH * kD * kD * 4);
+  p.ztot = take(BH * kD * 4);
+  p.ol = take(BH * N * kD * 4);
+  p.total = o;
+  return p;
+}
+
+template <typename T>
+T* at(void* ws, size_t off) {
+  return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+sla2_status check_shape(const sla2_shape* s, Geom* g) {
+  if (s == nullptr) return SLA2_ERR_NULL_POINTER;
+  if (s->dtype != SLA2_FP32 && s->dtype != SLA2_BF16) return SLA2_ERR_BAD_DTYPE;
+  if (s->B < 1 || s->H < 1 || s->d != kD || s->N < kBQ || s->N % kBQ != 0 || s->N > kMaxN)
+    return SLA2_ERR_BAD_SHAPE;
+  if (static_cast<int64_t>(s->B) * s->H > 65535) return SLA2_ERR_BAD_SHAPE;
+  g->B = s->B;
+  g->H = s->H;
+  g->N = s->N;
+  g->BH = s->B * s->H;
+  g->nqb = s->N / kBQ;
+  g->nkb = s->N / kBK;
+  return SLA2_OK;
+}
+
+bool keep_ok(float k) { return std::isfinite(k) && k > 0.f && k <= 1.f; }
+
+// Pointer checks: required pointers non-null; every given pointer 16-byte aligned.
+struct PtrCheck {
+  sla2_status st = SLA2_OK;
+  void req(const void* p) {
+    if (st != SLA2_OK) return;
+    if (p == nullptr) st = SLA2_ERR_NULL_POINTER;
+    else if (!aligned16(p)) st = SLA2_ERR_MISALIGNED;
+  }
+  void opt(const void* p) {
+    if (st != SLA2_OK || p == nullptr) return;
+    if (!aligned16(p)) st = SLA2_ERR_MISALIGNED;
+  }
+};
+
+sla2_status check_workspace(const Geom& g, const void* ws, size_t bytes) {
+  const size_t need = make_plan(g).total;
+  if (ws == nullptr) return SLA2_ERR_NULL_POINTER;
+  if (!aligned16(ws)) return SLA2_ERR_MISALIGNED;
+  if (bytes < need) return SLA2_ERR_WORKSPACE_TOO_SMALL;
+  return SLA2_OK;
+}
+
+std::atomic<int> g_dev_ok[64];  // 0 unknown, 1 gfx950, 2 other
+
+sla2_status check_device() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return SLA2_ERR_HIP;
+  if (dev < 0 || dev >= 64) return SLA2_ERR_UNSUPPORTED_DEVICE;
+  int st = g_dev_ok[dev].load(std::memory_order_relaxed);
+  if (st == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return SLA2_ERR_HIP;
+    st = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+    if (st == 1 && configure_router() != hipSuccess) return SLA2_ERR_HIP;
+    g_dev_ok[dev].store(st, std::memory_order_relaxed);
+  }
+  return st == 1 ? SLA2_OK : SLA2_ERR_UNSUPPORTED_DEVICE;
+}
+
+bool debug_sync() {
+  static const bool on = [] {
+    const char* e = std::getenv("SLA2_DEBUG_SYNC");
+    return e != nullptr && e[0] == '1';
+  }();
+  return on;
+}
+
+// Runs a launch; in debug mode also synchronises and checks.
+#define SLA2_LAUNCH(expr)                                                   \
+  do {                                                                      \
+    if ((expr) != hipSuccess) return SLA2_ERR_HIP;                          \
+    if (debug_sync() && hipStreamSynchronize(stream) != hipSuccess)         \
+      return SLA2_ERR_HIP;                                                  \
+  } while (0)
+
+}  // namespace
+
+extern "C" {
+
+int32_t sla2_blocks_kept(int32_t n_key_blocks, float keep_frac) {
+  if (n_key_blocks < 1 || !keep_ok(keep_frac)) return -1;
+  const double v = std::floor(static_cast<double>(keep_frac) * n_key_blocks + 1e-9);
+  int64_t kb = static_cast<int64_t>(v);
+  if (kb < 1) kb = 1;
+  if (kb > n_key_blocks) kb = n_key_blocks;
+  return static_cast<int32_t>(kb);
+}
+
+size_t sla2_workspace_bytes(const sla2_shape* shape) {
+  Geom g;
+  if (check_shape(shape, &g) != SLA2_OK) return 0;
+  return make_plan(g).total;
+}
+
+const char* sla2_status_string(sla2_status s) {
+  switch (s) {
+    case SLA2_OK: return "success";
+    case SLA2_ERR_NULL_POINTER: return "a required pointer is NULL";
+    case SLA2_ERR_BAD_SHAPE:
+      return "bad shape: need d == 128, N a positive multiple of 128 up to 262144, B, H >= 1, "
+             "B*H <= 65535";
+    case SLA2_ERR_BAD_DTYPE: return "unsupported dtype (SLA2_FP32 or SLA2_BF16)";
+    case SLA2_ERR_MISALIGNED: return "a device pointer is not 16-byte aligned";
+    case SLA2_ERR_BAD_ARGUMENT: return "bad argument (keep_frac must lie in (0, 1]; quant must be SLA2_QUANT_I8_FP8)";
+    case SLA2_ERR_WORKSPACE_TOO_SMALL: return "workspace smaller than sla2_workspace_bytes()";
+    case SLA2_ERR_UNSUPPORTED_DEVICE: return "the current HIP device is not gfx950 (MI355X)";
+    case SLA2_ERR_HIP: return "a HIP call or kernel launch failed";
+  }
+  return "unknown status";
+}
+
+sla2_status sla2_router(const sla2_shape* shape, const void* Q, const void* K,
+                        const float* proj_q, const float* proj_k, float keep_frac,
+                        uint8_t* mask, int32_t* blocks, float* scores, void* workspace,
+                        size_t workspace_bytes, void* stream_) {
+  Geom g;
+  sla2_status st = check_shape(shape, &g);
+  if (st != SLA2_OK) return st;
+  PtrCheck pc;
+  pc.req(Q); pc.req(K); pc.req(proj_q); pc.req(proj_k); pc.req(blocks);
+  pc.opt(mask); pc.opt(scores);
+  if (pc.st != SLA2_OK) return pc.st;
+  if (!keep_ok(keep_frac)) return SLA2_ERR_BAD_ARGUMENT;
+  if ((st = check_workspace(g, workspace, workspace_bytes)) != SLA2_OK) return st;
+  if ((st = check_device()) != SLA2_OK) return st;
+  hipStream_t stream = static_cast<hipStream_t>(stream_);
+  const Plan p = make_plan(g);
+  const int kb = sla2_blocks_kept(g.nkb, keep_frac);
+  const int dt = shape->dtype == SLA2_FP32 ? 0 : 1;
+  SLA2_LAUNCH(launch_pool(g, dt, Q, K, at<double>(workspace, p.qsum), at<double>(workspace, p.ksum), stream));
+  SLA2_LAUNCH(launch_colmean(g, at<double>(workspace, p.ksum), at<double>(workspace, p.mu64),
+                             at<float>(workspace, p.mu32), nullptr, stream));
+  SLA2_LAUNCH(launch_project(g, at<double>(workspace, p.qsum), at<double>(workspace, p.ksum),
+                             at<double>(workspace, p.mu64), proj_q, proj_k,
+                             at<double>(workspace, p.A), at<double>(workspace, p.Bt), stream));
+  SLA2_LAUNCH(launch_score_topk(g, at<double>(workspace, p.A), at<double>(workspace, p.Bt), kb,
+                                mask, blocks, kb, nullptr, scores, stream));
+  return SLA2_OK;
+}
+
+sla2_status sla2_linear_precompute(const sla2_shape* shape, const void* K, const void* V,
+                                   float* k_colmean, float* h, float* z, float* h_total,
+                                   float* z_total, void* workspace, size_t workspace_bytes,
+                                   void* stream_) {
+  Geom g;
+  sla2_status st = check_shape(shape, &g);
+  if (st != SLA2_OK) return st;
+  PtrCheck pc;
+  pc.req(K); pc.req(V); pc.req(k_colmean); pc.req(h_total); pc.req(z_total);
+  pc.opt(h); pc.opt(z);
+  if (pc.st != SLA2_OK) return pc.st;
+  if ((st = check_workspace(g, workspace, workspace_bytes)) != SLA2_OK) return st;
+  if ((st = check_device()) != SLA2_OK) return st;
+  hipStream_t stream = static_cast<hipStream_t>(stream_);
+  const Plan p = make_plan(g);
+  const int dt = shape->dtype == SLA2_FP32 ? 0 : 1;
+  SLA2_LAUNCH(launch_pool(g, dt, nullptr, K, at<double>(workspace, p.qsum), at<double>(workspace, p.ksum), stream));
+  SLA2_LAUNCH(launch_colmean(g, at<double>(workspace, p.ksum), at<double>(workspace, p.mu64),
+                             at<float>(workspace, p.mu32), k_colmean, stream));
+  float* zz = z ? z : at<float>(workspace, p.z);
+  SLA2_LAUNCH(launch_linear_pre(g, dt, K, V, at<float>(workspace, p.mu32), nullptr, h, zz,
+                                at<float>(workspace, p.hpart), at<float>(workspace, p.zpart), stream));
+  SLA2_LAUNCH(launch_linear_total(g, at<float>(workspace, p.hpart), at<float>(workspace, p.zpart),
+                                  h_total, z_total, stream));
+  return SLA2_OK;
+}
+
+namespace {
+
+// Everything after the block lists exist: quantise, linear branch, sparse branch + combine.
+sla2_status run_branches(const Geom& g, int dt, const void* Q, const void* K, const void* V,
+                         const float* alpha, float* O, const sla2_taps* taps, void* ws,
+                         const Plan& p, int list_stride, hipStream_t stream) {
+  const sla2_taps none{};
+  const sla2_taps& tp = taps ? *taps : none;
+  SLA2_LAUNCH(launch_quant(g, dt, Q, K, V, at<float>(ws, p.mu32), at<int8_t>(ws, p.qc),
+                           at<int8_t>(ws, p.kc), at<uint8_t>(ws, p.vc),
+                           tp.s_q ? tp.s_q : at<float>(ws, p.sq), tp.s_k ? tp.s_k : at<float>(ws, p.sk),
+                           tp.s_v ? tp.s_v : at<float>(ws, p.sv), tp.q_codes, tp.k_codes,
+                           tp.v_codes, stream));
+  const float* sq = tp.s_q ? tp.s_q : at<float>(ws, p.sq);
+  const float* sk = tp.s_k ? tp.s_k : at<float>(ws, p.sk);
+  const float* sv = tp.s_v ? tp.s_v : at<float>(ws, p.sv);
+  SLA2_LAUNCH(launch_linear_pre(g, dt, K, V, at<float>(ws, p.mu32), at<uint16_t>(ws, p.hbf),
+                                nullptr, at<float>(ws, p.z), at<float>(ws, p.hpart),
+                                at<float>(ws, p.zpart), stream));
+  SLA2_LAUNCH(launch_linear_total(g, at<float>(ws, p.hpart), at<float>(ws, p.zpart),
+                                  at<float>(ws, p.htot), at<float>(ws, p.ztot), stream));
+  float* ol = tp.O_l ? tp.O_l : at<float>(ws, p.ol);
+  SLA2_LAUNCH(launch_linear_out(g, dt, Q, at<uint16_t>(ws, p.hbf), at<float>(ws, p.z),
+                                at<float>(ws, p.htot), at<float>(ws, p.ztot),
+                                at<uint8_t>(ws, p.mask), at<int32_t>(ws, p.cnt), ol, stream));
+  SLA2_LAUNCH(launch_sparse(g, at<int8_t>(ws, p.qc), at<int8_t>(ws, p.kc), at<uint8_t>(ws, p.vc),
+                            sq, sk, sv, at<int32_t>(ws, p.list), list_stride,
+                            at<int32_t>(ws, p.cnt), alpha, ol, O, tp.O_s, stream));
+  return SLA2_OK;
+}
+
+void check_taps(PtrCheck& pc, const sla2_taps* t) {
+  if (!t) return;
+  pc.opt(t->O_s); pc.opt(t->O_l); pc.opt(t->q_codes); pc.opt(t->k_codes); pc.opt(t->v_codes);
+  pc.opt(t->s_q); pc.opt(t->s_k); pc.opt(t->s_v); pc.opt(t->k_colmean);
+}
+
+}  // namespace
+
+sla2_status sla2_forward(const sla2_shape* shape, const void* Q, const void* K, const void* V,
+                         const float* proj_q, const float* proj_k, const float* alpha,
+                         float keep_frac, sla2_quant quant, float* O, const sla2_taps* taps,
+                         void* workspace, size_t workspace_bytes, void* stream_) {
+  Geom g;
+  sla2_status st = check_shape(shape, &g);
+  if (st != SLA2_OK) return st;
+  PtrCheck pc;
+  pc.req(Q); pc.req(K); pc.req(V); pc.req(proj_q); pc.req(proj_k); pc.req(alpha); pc.req(O);
+  check_taps(pc, taps);
+  if (pc.st != SLA2_OK) return pc.st;
+  if (!keep_ok(keep_frac) || quant != SLA2_QUANT_I8_FP8) return SLA2_ERR_BAD_ARGUMENT;
+  if ((st = check_workspace(g, workspace, workspace_bytes)) != SLA2_OK) return st;
+  if ((st = check_device()) != SLA2_OK) return st;
+  hipStream_t stream = static_cast<hipStream_t>(stream_);
+  const Plan p = make_plan(g);
+  const int kb = sla2_blocks_kept(g.nkb, keep_frac);
+  const int dt = shape->dtype == SLA2_FP32 ? 0 : 1;
+  void* ws = workspace;
+  SLA2_LAUNCH(launch_pool(g, dt, Q, K, at<double>(ws, p.qsum), at<double>(ws, p.ksum), stream));
+  SLA2_LAUNCH(launch_colmean(g, at<double>(ws, p.ksum), at<double>(ws, p.mu64), at<float>(ws, p.mu32),
+                             taps ? taps->k_colmean : nullptr, stream));
+  SLA2_LAUNCH(launch_project(g, at<double>(ws, p.qsum), at<double>(ws, p.ksum), at<double>(ws, p.mu64),
+                             proj_q, proj_k, at<double>(ws, p.A), at<double>(ws, p.Bt), stream));
+  SLA2_LAUNCH(launch_score_topk(g, at<double>(ws, p.A), at<double>(ws, p.Bt), kb,
+                                at<uint8_t>(ws, p.mask), at<int32_t>(ws, p.list), kb,
+                                at<int32_t>(ws, p.cnt), nullptr, stream));
+  return run_branches(g, dt, Q, K, V, alpha, O, taps, ws, p, kb, stream);
+}
+
+sla2_status sla2_forward_with_mask(const sla2_shape* shape, const void* Q, const void* K,
+                                   const void* V, const uint8_t* mask, const float* alpha,
+                                   sla2_quant quant, float* O, const sla2_taps* taps,
+                                   void* workspace, size_t workspace_bytes, void* stream_) {
+  Geom g;
+  sla2_status st = check_shape(shape, &g);
+  if (st != SLA2_OK) return st;
+  PtrCheck pc;
+  pc.req(Q); pc.req(K); pc.req(V); pc.req(mask); pc.req(alpha); pc.req(O);
+  check_taps(pc, taps);
+  if (pc.st != SLA2_OK) return pc.st;
+  if (quant != SLA2_QUANT_I8_FP8) return SLA2_ERR_BAD_ARGUMENT;
+  if ((st = check_workspace(g, workspace, workspace_bytes)) != SLA2_OK) return st;
+  if ((st = check_device()) != SLA2_OK) return st;
+  hipStream_t stream = static_cast<hipStream_t>(stream_);
+  const Plan p = make_plan(g);
+  const int dt = shape->dtype == SLA2_FP32 ? 0 : 1;
+  void* ws = workspace;
+  SLA2_LAUNCH(launch_pool(g, dt, nullptr, K, at<double>(ws, p.qsum), at<double>(ws, p.ksum), stream));
+  SLA2_LAUNCH(launch_colmean(g, at<double>(ws, p.ksum), at<double>(ws, p.mu64), at<float>(ws, p.mu32),
+                             taps ? taps->k_colmean : nullptr, stream));
+  SLA2_LAUNCH(launch_mask_to_list(g, mask, at<uint8_t>(ws, p.mask), at<int32_t>(ws, p.list),
+                                  at<int32_t>(ws, p.cnt), stream));
+  return run_branches(g, dt, Q, K, V, alpha, O, taps, ws, p, g.nkb, stream);
+}
+
+}  // extern "C"

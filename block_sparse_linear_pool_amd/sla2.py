@@ -1,0 +1,229 @@
+"""Thin Python binding of libsla2.so (ctypes). Argument marshalling only.
+
+Every step of the SLA2 forward runs in the HIP kernels behind the C ABI
+declared in include/sla2.h; PyTorch only provides device memory and the
+stream. Importing works without a GPU (the host-only functions and the
+argument checks run on the CPU); the library must have been built
+(python -m block_sparse_linear_pool_amd.build), otherwise loading fails loudly.
+
+Function names match the C entry points.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libsla2.so")
+
+SLA2_FP32, SLA2_BF16 = 0, 1
+SLA2_QUANT_I8_FP8 = 1
+D = 128
+
+STATUS = {
+    0: "SLA2_OK", 1: "SLA2_ERR_NULL_POINTER", 2: "SLA2_ERR_BAD_SHAPE", 3: "SLA2_ERR_BAD_DTYPE",
+    4: "SLA2_ERR_MISALIGNED", 5: "SLA2_ERR_BAD_ARGUMENT", 6: "SLA2_ERR_WORKSPACE_TOO_SMALL",
+    7: "SLA2_ERR_UNSUPPORTED_DEVICE", 8: "SLA2_ERR_HIP",
+}
+
+
+class Shape(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("H", ctypes.c_int32), ("N", ctypes.c_int32),
+                ("d", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+
+
+class Taps(ctypes.Structure):
+    _fields_ = [(name, ctypes.c_void_p) for name in
+                ("O_s", "O_l", "q_codes", "k_codes", "v_codes", "s_q", "s_k", "s_v", "k_colmean")]
+
+
+class SLA2Error(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {STATUS.get(status, status)}: {sla2_status_string(status)}")
+
+
+_lib = None
+
+
+def lib():
+    """The loaded libsla2.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m block_sparse_linear_pool_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, sz, f32, i32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_float, ctypes.c_int32
+        L.sla2_blocks_kept.argtypes = [i32, f32]
+        L.sla2_blocks_kept.restype = i32
+        L.sla2_workspace_bytes.argtypes = [ctypes.POINTER(Shape)]
+        L.sla2_workspace_bytes.restype = sz
+        L.sla2_status_string.argtypes = [ctypes.c_int]
+        L.sla2_status_string.restype = ctypes.c_char_p
+        L.sla2_router.argtypes = [ctypes.POINTER(Shape), vp, vp, vp, vp, f32, vp, vp, vp, vp, sz, vp]
+        L.sla2_linear_precompute.argtypes = [ctypes.POINTER(Shape), vp, vp, vp, vp, vp, vp, vp,
+                                             vp, sz, vp]
+        L.sla2_forward.argtypes = [ctypes.POINTER(Shape), vp, vp, vp, vp, vp, vp, f32, ctypes.c_int,
+                                   vp, ctypes.POINTER(Taps), vp, sz, vp]
+        L.sla2_forward_with_mask.argtypes = [ctypes.POINTER(Shape), vp, vp, vp, vp, vp, ctypes.c_int,
+                                             vp, ctypes.POINTER(Taps), vp, sz, vp]
+        for name in ("sla2_router", "sla2_linear_precompute", "sla2_forward",
+                     "sla2_forward_with_mask"):
+            getattr(L, name).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise SLA2Error(status, where)
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def shape_of(q: torch.Tensor) -> Shape:
+    if q.dim() != 4:
+        raise ValueError("Q, K, V must be [B, H, N, d]")
+    dt = {torch.float32: SLA2_FP32, torch.bfloat16: SLA2_BF16}.get(q.dtype)
+    if dt is None:
+        raise ValueError(f"unsupported dtype {q.dtype}")
+    B, H, N, d = q.shape
+    return Shape(B, H, N, d, dt)
+
+
+def _contig(*ts):
+    for t in ts:
+        if t is not None and not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+
+
+# ------------------------------------------------------------------ host-only helpers
+def sla2_blocks_kept(n_key_blocks: int, keep_frac: float) -> int:
+    return int(lib().sla2_blocks_kept(int(n_key_blocks), float(keep_frac)))
+
+
+def sla2_workspace_bytes(B: int, H: int, N: int, dtype=torch.bfloat16, d: int = D) -> int:
+    dt = SLA2_FP32 if dtype == torch.float32 else SLA2_BF16
+    return int(lib().sla2_workspace_bytes(ctypes.byref(Shape(B, H, N, d, dt))))
+
+
+def sla2_status_string(status: int) -> str:
+    return lib().sla2_status_string(int(status)).decode()
+
+
+def workspace_for(q: torch.Tensor) -> torch.Tensor:
+    B, H, N, _ = q.shape
+    n = sla2_workspace_bytes(B, H, N, q.dtype)
+    if n == 0:
+        raise SLA2Error(2, "sla2_workspace_bytes")
+    return torch.empty(n, dtype=torch.uint8, device=q.device)
+
+
+# ------------------------------------------------------------------ entry points
+def sla2_router(q, k, proj_q, proj_k, keep_frac, want_mask=True, want_scores=False,
+                workspace=None):
+    """Returns (blocks [B,H,N/128,kb] int32, mask uint8 or None, scores fp32 or None)."""
+    _contig(q, k, proj_q, proj_k)
+    shp = shape_of(q)
+    B, H, N, _ = q.shape
+    nqb, nkb = N // 128, N // 64
+    kb = sla2_blocks_kept(nkb, keep_frac)
+    if kb < 1:
+        raise SLA2Error(5, "sla2_router")
+    dev = q.device
+    blocks = torch.empty((B, H, nqb, kb), dtype=torch.int32, device=dev)
+    mask = torch.empty((B, H, nqb, nkb), dtype=torch.uint8, device=dev) if want_mask else None
+    scores = torch.empty((B, H, nqb, nkb), dtype=torch.float32, device=dev) if want_scores else None
+    ws = workspace if workspace is not None else workspace_for(q)
+    st = lib().sla2_router(ctypes.byref(shp), _ptr(q), _ptr(k), _ptr(proj_q), _ptr(proj_k),
+                           float(keep_frac), _ptr(mask), _ptr(blocks), _ptr(scores), _ptr(ws),
+                           ws.numel(), _stream(dev))
+    _check(st, "sla2_router")
+    return blocks, mask, scores
+
+
+def sla2_linear_precompute(k, v, want_h=True, want_z=True, workspace=None):
+    """Returns dict k_colmean, h (or None), z (or None), h_total, z_total (fp32)."""
+    _contig(k, v)
+    shp = shape_of(k)
+    B, H, N, d = k.shape
+    nkb = N // 64
+    dev = k.device
+    out = {
+        "k_colmean": torch.empty((B, H, d), dtype=torch.float32, device=dev),
+        "h": torch.empty((B, H, nkb, d, d), dtype=torch.float32, device=dev) if want_h else None,
+        "z": torch.empty((B, H, nkb, d), dtype=torch.float32, device=dev) if want_z else None,
+        "h_total": torch.empty((B, H, d, d), dtype=torch.float32, device=dev),
+        "z_total": torch.empty((B, H, d), dtype=torch.float32, device=dev),
+    }
+    ws = workspace if workspace is not None else workspace_for(k)
+    st = lib().sla2_linear_precompute(ctypes.byref(shp), _ptr(k), _ptr(v), _ptr(out["k_colmean"]),
+                                      _ptr(out["h"]), _ptr(out["z"]), _ptr(out["h_total"]),
+                                      _ptr(out["z_total"]), _ptr(ws), ws.numel(), _stream(dev))
+    _check(st, "sla2_linear_precompute")
+    return out
+
+
+def _make_taps(q, want):
+    if not want:
+        return None, None
+    B, H, N, d = q.shape
+    dev = q.device
+    t = {
+        "O_s": torch.empty((B, H, N, d), dtype=torch.float32, device=dev),
+        "O_l": torch.empty((B, H, N, d), dtype=torch.float32, device=dev),
+        "q_codes": torch.empty((B, H, N, d), dtype=torch.int8, device=dev),
+        "k_codes": torch.empty((B, H, N, d), dtype=torch.int8, device=dev),
+        "v_codes": torch.empty((B, H, N, d), dtype=torch.uint8, device=dev),
+        "s_q": torch.empty((B, H, N // 128), dtype=torch.float32, device=dev),
+        "s_k": torch.empty((B, H, N // 64), dtype=torch.float32, device=dev),
+        "s_v": torch.empty((B, H, N // 64), dtype=torch.float32, device=dev),
+        "k_colmean": torch.empty((B, H, d), dtype=torch.float32, device=dev),
+    }
+    if want is not True:
+        t = {k: v for k, v in t.items() if k in want}
+    taps = Taps(**{k: (v.data_ptr() if v is not None else None) for k, v in t.items()})
+    return taps, t
+
+
+def sla2_forward(q, k, v, proj_q, proj_k, alpha, keep_frac, taps=False, out=None,
+                 workspace=None):
+    """O [B,H,N,d] fp32; with taps=True (or a collection of tap names) also a dict of taps."""
+    _contig(q, k, v, proj_q, proj_k, alpha, out)
+    shp = shape_of(q)
+    dev = q.device
+    o = out if out is not None else torch.empty(q.shape, dtype=torch.float32, device=dev)
+    ctaps, tdict = _make_taps(q, taps)
+    ws = workspace if workspace is not None else workspace_for(q)
+    st = lib().sla2_forward(ctypes.byref(shp), _ptr(q), _ptr(k), _ptr(v), _ptr(proj_q),
+                            _ptr(proj_k), _ptr(alpha), float(keep_frac), SLA2_QUANT_I8_FP8,
+                            _ptr(o), ctypes.byref(ctaps) if ctaps else None, _ptr(ws),
+                            ws.numel(), _stream(dev))
+    _check(st, "sla2_forward")
+    return (o, tdict) if taps else o
+
+
+def sla2_forward_with_mask(q, k, v, mask, alpha, taps=False, out=None, workspace=None):
+    """O [B,H,N,d] fp32 from a caller block mask [B,H,N/128,N/64] uint8."""
+    _contig(q, k, v, mask, alpha, out)
+    shp = shape_of(q)
+    dev = q.device
+    o = out if out is not None else torch.empty(q.shape, dtype=torch.float32, device=dev)
+    ctaps, tdict = _make_taps(q, taps)
+    ws = workspace if workspace is not None else workspace_for(q)
+    st = lib().sla2_forward_with_mask(ctypes.byref(shp), _ptr(q), _ptr(k), _ptr(v), _ptr(mask),
+                                      _ptr(alpha), SLA2_QUANT_I8_FP8, _ptr(o),
+                                      ctypes.byref(ctaps) if ctaps else None, _ptr(ws),
+                                      ws.numel(), _stream(dev))
+    _check(st, "sla2_forward_with_mask")
+    return (o, tdict) if taps else o

@@ -1,0 +1,146 @@
+/*
+ * sla2.h — C ABI of libsla2.so: the SLA2 inference forward on one AMD MI355X (gfx950).
+ *
+ * SLA2 is sparse-linear attention with a learned block router. The four steps
+ * follow the computation-flow paragraph (steps 1-4) of the summary page
+ * "SLA2: Sparse-Linear Attention with Learnable Routing and QAT"
+ * (paper.rainbus.top), with K smoothing and the per-key-block precompute of
+ * §7 (implementation notes 1 and 2) of "SLA2: Sparse-Linear Attention v2 for
+ * Diffusion Transformers" (zhaifeiyue.github.io):
+ *
+ *   router   pool Q (128-row blocks) and K (64-row blocks), project with
+ *            proj_q / proj_k, P_c = row softmax(A B^T / sqrt d), hard Top-k
+ *            -> block mask M_c and ascending per-row block lists (step 1)
+ *   sparse   FlashAttention-style attention over the kept block pairs with
+ *            INT8 Q, K and FP8 (OCP E4M3) P, V (step 2)
+ *   linear   phi = softmax over d; h_j = phi(K_j)^T V_j, z_j; O_l from the
+ *            dropped blocks, O_l = phi(Q) H / (phi(Q) Z) (step 3)
+ *   combine  O = alpha * O_s + (1 - alpha) * O_l, alpha per query block (step 4)
+ *
+ * Conventions shared by every entry point
+ *   Layout     Q, K, V: contiguous [B, H, N, d] in shape->dtype. proj_q, proj_k:
+ *              fp32 [H, d, d] row-major, applied as x @ W (W[in][out]), no bias.
+ *              alpha: fp32 [H, N/128], used as given (expected in [0, 1]).
+ *              Outputs O, O_s, O_l: fp32 [B, H, N, d]. Masks: uint8 0/1
+ *              [B, H, N/128, N/64]. Block lists: int32, ascending.
+ *   Shapes     d == 128; N a positive multiple of 128, N <= 262144; B, H >= 1;
+ *              B*H <= 65535. Otherwise SLA2_ERR_BAD_SHAPE.
+ *   Kept count kb = sla2_blocks_kept(N/64, keep_frac) key blocks per query
+ *              block; keep_frac must lie in (0, 1].
+ *   Pointers   Every array pointer is caller-owned DEVICE memory, 16-byte aligned
+ *              (SLA2_ERR_MISALIGNED otherwise). The library allocates nothing and
+ *              keeps no pointer after a call returns; buffers must stay alive
+ *              until the stream has executed the work.
+ *   Workspace  Caller-provided device scratch of sla2_workspace_bytes(...) bytes.
+ *   Streams    `stream` is a hipStream_t (NULL = the default stream). All work is
+ *              enqueued on it; no call synchronises or copies device -> host.
+ *   Errors     Arguments are validated on the host before anything is enqueued;
+ *              on error nothing is written. A failed launch returns SLA2_ERR_HIP.
+ *              No C++ exception crosses this interface. Calls are re-entrant;
+ *              concurrent calls must use distinct workspaces.
+ *   Debug      Environment SLA2_DEBUG_SYNC=1 synchronises and checks after every
+ *              kernel (slow; for debugging only).
+ */
+#ifndef SLA2_H
+#define SLA2_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    SLA2_OK = 0,
+    SLA2_ERR_NULL_POINTER = 1,
+    SLA2_ERR_BAD_SHAPE = 2,
+    SLA2_ERR_BAD_DTYPE = 3,
+    SLA2_ERR_MISALIGNED = 4,
+    SLA2_ERR_BAD_ARGUMENT = 5,
+    SLA2_ERR_WORKSPACE_TOO_SMALL = 6,
+    SLA2_ERR_UNSUPPORTED_DEVICE = 7,
+    SLA2_ERR_HIP = 8
+} sla2_status;
+
+/* element type of Q, K, V */
+typedef enum { SLA2_FP32 = 0, SLA2_BF16 = 1 } sla2_dtype;
+
+/* operand precision of the sparse branch (step 2). Only the low-bit form the
+ * pages describe is built: INT8 Q, K per block, OCP E4M3 P, V. */
+typedef enum { SLA2_QUANT_I8_FP8 = 1 } sla2_quant;
+
+typedef struct {
+    int32_t B, H, N, d;
+    sla2_dtype dtype;
+} sla2_shape;
+
+/* Optional debug outputs of sla2_forward / sla2_forward_with_mask; pass NULL for
+ * the struct or for any member to skip it. Layouts in standard row order. */
+typedef struct {
+    float   *O_s;       /* [B,H,N,d] sparse-branch output (0 for a query block with no kept block) */
+    float   *O_l;       /* [B,H,N,d] linear-branch output (0 for a query block with no dropped block) */
+    int8_t  *q_codes;   /* [B,H,N,d] INT8 codes of Q, one scale per 128-row block */
+    int8_t  *k_codes;   /* [B,H,N,d] INT8 codes of K_s = K - colmean(K), one scale per 64-row block */
+    uint8_t *v_codes;   /* [B,H,N,d] E4M3 codes of V, one scale per 64-row block */
+    float   *s_q;       /* [B,H,N/128] */
+    float   *s_k;       /* [B,H,N/64] */
+    float   *s_v;       /* [B,H,N/64] */
+    float   *k_colmean; /* [B,H,d] colmean(K) rounded to fp32 */
+} sla2_taps;
+
+/* Kept key blocks per query block: max(1, floor(keep_frac * n_key_blocks + 1e-9)),
+ * capped at n_key_blocks (the "top k%" of step 1). Host only; returns -1 when
+ * n_key_blocks < 1 or keep_frac is not in (0, 1]. */
+int32_t sla2_blocks_kept(int32_t n_key_blocks, float keep_frac);
+
+/* Device workspace, in bytes, that any entry point needs for this shape; the same
+ * size serves every call with this shape. Returns 0 for an invalid shape. */
+size_t sla2_workspace_bytes(const sla2_shape *shape);
+
+/* Static English text for a status code. */
+const char *sla2_status_string(sla2_status status);
+
+/* Step 1 only (the learned router).
+ *   mask   [B,H,N/128,N/64] uint8 M_c, or NULL
+ *   blocks [B,H,N/128,kb] int32 kept key-block indices, ascending (required)
+ *   scores [B,H,N/128,N/64] fp32 P_c, or NULL
+ * Ranking is by the logit in fp64; equal logits go to the lower block index. */
+sla2_status sla2_router(const sla2_shape *shape, const void *Q, const void *K,
+                        const float *proj_q, const float *proj_k, float keep_frac,
+                        uint8_t *mask, int32_t *blocks, float *scores,
+                        void *workspace, size_t workspace_bytes, void *stream);
+
+/* The linear branch's per-key-block precompute (step 3; §7 note 2) on the smoothed
+ * K_s = K - colmean(K):
+ *   k_colmean [B,H,d] fp32 (required)
+ *   h         [B,H,N/64,d,d] fp32 h_j = phi(K_s,j)^T V_j (or NULL)
+ *   z         [B,H,N/64,d] fp32 column sums of phi(K_s,j) (or NULL)
+ *   h_total   [B,H,d,d] fp32 sum over j of h_j (required)
+ *   z_total   [B,H,d] fp32 sum over j of z_j (required)
+ * phi(K_s) is rounded to bf16 for the matrix product; sums are fp32. */
+sla2_status sla2_linear_precompute(const sla2_shape *shape, const void *K, const void *V,
+                                   float *k_colmean, float *h, float *z,
+                                   float *h_total, float *z_total,
+                                   void *workspace, size_t workspace_bytes, void *stream);
+
+/* The whole forward: router, sparse branch, linear branch and combine.
+ *   O [B,H,N,d] fp32 (required); taps optional (NULL). */
+sla2_status sla2_forward(const sla2_shape *shape, const void *Q, const void *K, const void *V,
+                         const float *proj_q, const float *proj_k, const float *alpha,
+                         float keep_frac, sla2_quant quant, float *O, const sla2_taps *taps,
+                         void *workspace, size_t workspace_bytes, void *stream);
+
+/* The forward with a caller-supplied block mask instead of the router. Any 0/1
+ * pattern is accepted (any byte != 0 counts as 1): a row with no kept block gets
+ * O_s = 0, a row with no dropped block gets O_l = 0. */
+sla2_status sla2_forward_with_mask(const sla2_shape *shape, const void *Q, const void *K,
+                                   const void *V, const uint8_t *mask, const float *alpha,
+                                   sla2_quant quant, float *O, const sla2_taps *taps,
+                                   void *workspace, size_t workspace_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SLA2_H */
