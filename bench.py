@@ -1,0 +1,192 @@
+#!/usr/bin/env python3
+"""Benchmark of the SLA2 inference forward on one MI355X.
+
+One step = one sla2_forward call over the whole workload (router, quantise, linear
+branch, sparse branch, combine) with inputs resident in HBM. Prints ONE JSON line:
+value = full-attention-equivalent TFLOPS (4 B H N^2 d per call / time), ms_per_step =
+ms per call, plus the roofline of the dominant kernel (HIP events recorded by the
+library around each of its kernels) and the CPU oracle timed on a bounded sample.
+
+Default workload: Wan2.1-1.3B-480P-shaped latents, B=1 H=12 N=32768 (21x30x52 tokens
+padded) d=128, 3% of key blocks kept (97% sparsity). Inputs are seeded synthetic
+stand-ins for the model's Q/K/V (see block_sparse_linear_pool_amd/workloads.py).
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+METRIC = "SLA2 fwd ms/call + full-attn-equiv TFLOPS, N=32768 H=12 d=128 @97%"
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="wan13b_480p_N32768")
+    ap.add_argument("--keep", type=float, default=None, help="kept fraction (default: workload's)")
+    ap.add_argument("--cpu-heads", type=int, default=2, help="heads in the CPU-oracle sample")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
+    ap.add_argument("--traffic", default=None,
+                    help="JSON with measured HBM bytes per launch of the dominant kernel")
+    ap.add_argument("--quiet", action="store_true")
+    return ap.parse_args()
+
+
+def log(args, *a):
+    if not args.quiet:
+        print(*a, file=sys.stderr, flush=True)
+
+
+def cpu_baseline(args, w, q, k, v, wq, wk, alpha, keep, acc):
+    """Time the fp64 oracle (as it stands) on the first heads of batch 0."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    from oracle import sla2 as oracle
+
+    cores = min(16, len(os.sched_getaffinity(0)))
+    heads = list(range(min(args.cpu_heads, w.H)))
+    with threadpool_limits(limits=cores):
+        t0 = time.perf_counter()
+        for h in heads:
+            oracle.forward_head(q[0, h].astype(np.float64), k[0, h].astype(np.float64),
+                                v[0, h].astype(np.float64), wq[h], wk[h], alpha[h], keep,
+                                quant=True)
+        dt = time.perf_counter() - t0
+    flops = 4.0 * w.N * w.N * w.d * len(heads)
+    return {
+        "value": flops / dt / 1e12,
+        "unit": "TFLOPS (full-attention-equivalent)",
+        "cores": cores,
+        "kind": "oracle",
+        "sample": f"batch 0, heads {heads[0]}-{heads[-1]} of {w.H} ({len(heads)}/{w.B * w.H} of one "
+                  f"call), fp64 numpy oracle with quantisation, {dt:.1f} s; "
+                  f"ms/call extrapolated {dt * 1e3 * w.B * w.H / len(heads):.0f}",
+        "cpu": platform.processor() or platform.machine(),
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+              "(the forward shards by (batch, head); see the design notes)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from block_sparse_linear_pool_amd import accounting as acc
+    from block_sparse_linear_pool_amd import sla2
+    from block_sparse_linear_pool_amd import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    sla2.lib()                                   # fail loudly if the library is missing
+    w = W.WORKLOADS[args.workload]
+    keep = args.keep if args.keep is not None else w.keep_frac[-1]
+    log(args, f"[bench] generating {w.name} B={w.B} H={w.H} N={w.N} keep={keep}")
+    t0 = time.time()
+    q, k, v = W.generate(w)
+    wq, wk, alpha = W.weights(w)
+    log(args, f"[bench] inputs ready in {time.time() - t0:.1f} s")
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    dev = torch.device("cuda:0")
+    gq, gk, gv = (torch.from_numpy(a).to(dev, dt) for a in (q, k, v))
+    gwq, gwk, ga = (torch.from_numpy(a).to(dev) for a in (wq, wk, alpha))
+    out = torch.empty(gq.shape, dtype=torch.float32, device=dev)
+    ws = sla2.workspace_for(gq)
+    kb = sla2.sla2_blocks_kept(w.n_kb, keep)
+    prob = acc.Problem(w.B, w.H, w.N, kb, in_bytes=2 if dt == torch.bfloat16 else 4)
+
+    def step(events=None):
+        sla2.sla2_forward(gq, gk, gv, gwq, gwk, ga, keep, out=out, workspace=ws, events=events)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    # ---- timed region: exactly `steps` calls between synchronisations
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    ms = e0.elapsed_time(e1) / args.steps
+    log(args, f"[bench] {ms:.3f} ms/call (events), {t_wall * 1e3 / args.steps:.3f} ms/call (wall)")
+
+    # ---- per-kernel durations: the library records events around each kernel
+    names = acc.KERNELS_FORWARD
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(sla2.MAX_STAGES + 1)]
+    per = np.zeros(len(names))
+    for _ in range(args.steps):
+        step(evs)
+        torch.cuda.synchronize()
+        per += [evs[i].elapsed_time(evs[i + 1]) for i in range(len(names))]
+    per /= args.steps
+    kernels = {}
+    for n, t in zip(names, per):
+        fl, by = acc.kernel_flops(prob, n), acc.kernel_bytes(prob, n)
+        kernels[n] = {"ms": round(float(t), 5),
+                      "tflops": round(fl / (t * 1e-3) / 1e12, 2) if fl else None,
+                      "gbs": round(by / (t * 1e-3) / 1e9, 1) if by else None}
+        log(args, f"[bench]   {n:13s} {t * 1e3:9.1f} us  {kernels[n]}")
+    dom = names[int(np.argmax(per))]
+    t_dom = float(per[int(np.argmax(per))]) * 1e-3
+    if acc.kernel_bound(dom) == "mfma":
+        achieved = acc.kernel_flops(prob, dom) / t_dom / 1e12
+        peak, unit = acc.MI355X_PEAK["mfma_i8_fp8_tflops"], "TFLOP/s"
+    else:
+        achieved = acc.kernel_bytes(prob, dom) / t_dom / 1e9
+        peak, unit = acc.MI355X_PEAK["hbm_gbs"], "GB/s"
+    traffic = None
+    if args.traffic and os.path.exists(args.traffic):
+        with open(args.traffic) as f:
+            tr = json.load(f)
+        if tr.get("kernel") == dom and tr.get("workload") == w.name:
+            traffic = tr.get("bytes_per_launch")
+    roofline = {"kernel": dom, "bound": acc.kernel_bound(dom), "achieved": round(achieved, 2),
+                "peak": peak, "unit": unit, "frac": round(achieved / peak, 4),
+                "traffic": traffic, "avg_launch_ms": round(t_dom * 1e3, 5)}
+
+    full = acc.full_attention_flops(prob)
+    result = {
+        "metric": METRIC,
+        "value": round(full / (ms * 1e-3) / 1e12, 2),
+        "unit": "TFLOPS (full-attention-equivalent)",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8+fp8",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d,
+                   "input_dtype": w.dtype, "keep_frac": keep, "kb": kb, "n_key_blocks": w.n_kb,
+                   "sparsity": round(prob.sparsity, 4),
+                   "full_attn_tflop_per_call": round(full / 1e12, 3),
+                   "sparse_tflop_per_call": round(acc.sparse_flops(prob) / 1e12, 4)},
+        "roofline": roofline,
+        "kernels": kernels,
+    }
+    if not args.no_cpu:
+        log(args, f"[bench] timing the CPU oracle on {args.cpu_heads} heads")
+        result["cpu_baseline"] = cpu_baseline(args, w, q, k, v, wq, wk, alpha, keep, acc)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,111 @@
+"""FLOP and byte accounting of the SLA2 forward, per kernel of libsla2.so.
+
+Counts only: nothing here computes any part of the method. Used by bench.py for the
+full-attention-equivalent rate and the roofline fractions.
+
+Full-attention-equivalent work is 4 B H N^2 d FLOP per call (QK^T and PV of dense
+attention over the padded N, no softmax). The sparse kernel's algorithmic work is
+4 * 128 * 64 * d FLOP per kept (query block, key block) pair. Byte counts are the
+compulsory (algorithmic) HBM traffic of each kernel: every input read once, every
+output written once; gathers that a cache can serve are not counted.
+"""
+
+from __future__ import annotations
+
+import dataclasses
+
+MI355X_PEAK = {
+    "hbm_gbs": 8000.0,          # HBM3E, GB/s
+    "mfma_i8_fp8_tflops": 5000.0,  # dense INT8 / FP8 MFMA
+    "mfma_bf16_tflops": 2500.0,
+    "fp64_tflops": 78.6,
+}
+
+KERNELS_FORWARD = ("pool", "colmean", "project", "score_topk", "quant", "linear_pre",
+                   "linear_total", "linear_out", "sparse")
+KERNELS_WITH_MASK = ("pool", "colmean", "mask_to_list", "quant", "linear_pre", "linear_total",
+                     "linear_out", "sparse")
+
+
+@dataclasses.dataclass
+class Problem:
+    B: int
+    H: int
+    N: int
+    kb: int
+    d: int = 128
+    in_bytes: int = 2            # bf16 inputs
+
+    @property
+    def BH(self):
+        return self.B * self.H
+
+    @property
+    def nqb(self):
+        return self.N // 128
+
+    @property
+    def nkb(self):
+        return self.N // 64
+
+    @property
+    def E(self):                 # elements of one [B, H, N, d] tensor
+        return self.BH * self.N * self.d
+
+    @property
+    def pairs(self):             # kept (query block, key block) pairs
+        return self.BH * self.nqb * self.kb
+
+    @property
+    def sparsity(self):
+        return 1.0 - self.kb / self.nkb
+
+
+def full_attention_flops(p: Problem) -> float:
+    return 4.0 * p.BH * p.N * p.N * p.d
+
+
+def sparse_flops(p: Problem) -> float:
+    return 4.0 * 128 * 64 * p.d * p.pairs
+
+
+def linear_flops(p: Problem) -> float:
+    """phi(K)^T V per key block plus phi(Q) H per query block: 4 N d^2 per head."""
+    return 2.0 * p.BH * p.N * p.d * p.d + 2.0 * p.BH * p.N * p.d * p.d
+
+
+def kernel_bytes(p: Problem, name: str) -> float:
+    """Compulsory HBM bytes of one launch of kernel `name`."""
+    E, BH, d = p.E, p.BH, p.d
+    np_ = (p.nkb + 7) // 8
+    if name == "pool":
+        return 2 * E * p.in_bytes + BH * (p.nqb + p.nkb) * d * 8
+    if name == "quant":
+        return 3 * E * p.in_bytes + 3 * E + BH * (p.nqb + 2 * p.nkb) * 4
+    if name == "linear_pre":
+        return 2 * E * p.in_bytes + BH * p.nkb * (d * d * 2 + d * 4) + BH * np_ * (d * d + d) * 4
+    if name == "linear_total":
+        return BH * np_ * (d * d + d) * 4 + BH * (d * d + d) * 4
+    if name == "linear_out":
+        return E * p.in_bytes + E * 4 + BH * p.nkb * (d * d * 2 + d * 4) + BH * (d * d + d) * 4
+    if name == "sparse":
+        return E + 2 * E + E * 4 + E * 4        # Qhat, Khat + Vhat once, O_l read, O write
+    return 0.0
+
+
+def kernel_flops(p: Problem, name: str) -> float:
+    if name == "sparse":
+        return sparse_flops(p)
+    if name == "score_topk":
+        return 2.0 * p.BH * p.nqb * p.nkb * p.d
+    if name == "project":
+        return 2.0 * p.BH * (p.nqb + p.nkb) * p.d * p.d
+    if name == "linear_pre":
+        return 2.0 * p.BH * p.N * p.d * p.d
+    if name == "linear_out":
+        return 2.0 * p.BH * p.N * p.d * p.d * 2        # H split into bf16 hi + lo
+    return 0.0
+
+
+def kernel_bound(name: str) -> str:
+    return "mfma" if name == "sparse" else "hbm"

@@ -128,10 +128,22 @@ bool debug_sync() {
   return on;
 }
 
-// Runs a launch; in debug mode also synchronises and checks.
+// Optional caller events recorded around every kernel (see sla2_taps.stage_events).
+struct Rec {
+  void** ev;
+  int n;
+  explicit Rec(const sla2_taps* t) : ev(t ? t->stage_events : nullptr), n(0) {}
+  hipError_t mark(hipStream_t s) {
+    if (ev == nullptr || n > SLA2_MAX_STAGES) return hipSuccess;
+    return hipEventRecord(static_cast<hipEvent_t>(ev[n++]), s);
+  }
+};
+
+// Runs a launch; records the caller's stage event; in debug mode also synchronises.
 #define SLA2_LAUNCH(expr)                                                   \
   do {                                                                      \
     if ((expr) != hipSuccess) return SLA2_ERR_HIP;                          \
+    if (rec.mark(stream) != hipSuccess) return SLA2_ERR_HIP;                \
     if (debug_sync() && hipStreamSynchronize(stream) != hipSuccess)         \
       return SLA2_ERR_HIP;                                                  \
   } while (0)
@@ -190,6 +202,7 @@ sla2_status sla2_router(const sla2_shape* shape, const void* Q, const void* K,
   const Plan p = make_plan(g);
   const int kb = sla2_blocks_kept(g.nkb, keep_frac);
   const int dt = shape->dtype == SLA2_FP32 ? 0 : 1;
+  Rec rec(nullptr);
   SLA2_LAUNCH(launch_pool(g, dt, Q, K, at<double>(workspace, p.qsum), at<double>(workspace, p.ksum), stream));
   SLA2_LAUNCH(launch_colmean(g, at<double>(workspace, p.ksum), at<double>(workspace, p.mu64),
                              at<float>(workspace, p.mu32), nullptr, stream));
@@ -217,6 +230,7 @@ sla2_status sla2_linear_precompute(const sla2_shape* shape, const void* K, const
   hipStream_t stream = static_cast<hipStream_t>(stream_);
   const Plan p = make_plan(g);
   const int dt = shape->dtype == SLA2_FP32 ? 0 : 1;
+  Rec rec(nullptr);
   SLA2_LAUNCH(launch_pool(g, dt, nullptr, K, at<double>(workspace, p.qsum), at<double>(workspace, p.ksum), stream));
   SLA2_LAUNCH(launch_colmean(g, at<double>(workspace, p.ksum), at<double>(workspace, p.mu64),
                              at<float>(workspace, p.mu32), k_colmean, stream));
@@ -233,7 +247,7 @@ namespace {
 // Everything after the block lists exist: quantise, linear branch, sparse branch + combine.
 sla2_status run_branches(const Geom& g, int dt, const void* Q, const void* K, const void* V,
                          const float* alpha, float* O, const sla2_taps* taps, void* ws,
-                         const Plan& p, int list_stride, hipStream_t stream) {
+                         const Plan& p, int list_stride, Rec& rec, hipStream_t stream) {
   const sla2_taps none{};
   const sla2_taps& tp = taps ? *taps : none;
   SLA2_LAUNCH(launch_quant(g, dt, Q, K, V, at<float>(ws, p.mu32), at<int8_t>(ws, p.qc),
@@ -286,6 +300,8 @@ sla2_status sla2_forward(const sla2_shape* shape, const void* Q, const void* K, 
   const int kb = sla2_blocks_kept(g.nkb, keep_frac);
   const int dt = shape->dtype == SLA2_FP32 ? 0 : 1;
   void* ws = workspace;
+  Rec rec(taps);
+  if (rec.mark(stream) != hipSuccess) return SLA2_ERR_HIP;
   SLA2_LAUNCH(launch_pool(g, dt, Q, K, at<double>(ws, p.qsum), at<double>(ws, p.ksum), stream));
   SLA2_LAUNCH(launch_colmean(g, at<double>(ws, p.ksum), at<double>(ws, p.mu64), at<float>(ws, p.mu32),
                              taps ? taps->k_colmean : nullptr, stream));
@@ -294,7 +310,7 @@ sla2_status sla2_forward(const sla2_shape* shape, const void* Q, const void* K, 
   SLA2_LAUNCH(launch_score_topk(g, at<double>(ws, p.A), at<double>(ws, p.Bt), kb,
                                 at<uint8_t>(ws, p.mask), at<int32_t>(ws, p.list), kb,
                                 at<int32_t>(ws, p.cnt), nullptr, stream));
-  return run_branches(g, dt, Q, K, V, alpha, O, taps, ws, p, kb, stream);
+  return run_branches(g, dt, Q, K, V, alpha, O, taps, ws, p, kb, rec, stream);
 }
 
 sla2_status sla2_forward_with_mask(const sla2_shape* shape, const void* Q, const void* K,
@@ -315,12 +331,14 @@ sla2_status sla2_forward_with_mask(const sla2_shape* shape, const void* Q, const
   const Plan p = make_plan(g);
   const int dt = shape->dtype == SLA2_FP32 ? 0 : 1;
   void* ws = workspace;
+  Rec rec(taps);
+  if (rec.mark(stream) != hipSuccess) return SLA2_ERR_HIP;
   SLA2_LAUNCH(launch_pool(g, dt, nullptr, K, at<double>(ws, p.qsum), at<double>(ws, p.ksum), stream));
   SLA2_LAUNCH(launch_colmean(g, at<double>(ws, p.ksum), at<double>(ws, p.mu64), at<float>(ws, p.mu32),
                              taps ? taps->k_colmean : nullptr, stream));
   SLA2_LAUNCH(launch_mask_to_list(g, mask, at<uint8_t>(ws, p.mask), at<int32_t>(ws, p.list),
                                   at<int32_t>(ws, p.cnt), stream));
-  return run_branches(g, dt, Q, K, V, alpha, O, taps, ws, p, g.nkb, stream);
+  return run_branches(g, dt, Q, K, V, alpha, O, taps, ws, p, g.nkb, rec, stream);
 }
 
 }  // extern "C"

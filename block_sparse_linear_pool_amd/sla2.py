@@ -35,9 +35,22 @@ class Shape(ctypes.Structure):
                 ("d", ctypes.c_int32), ("dtype", ctypes.c_int32)]
 
 
+TAP_NAMES = ("O_s", "O_l", "q_codes", "k_codes", "v_codes", "s_q", "s_k", "s_v", "k_colmean")
+MAX_STAGES = 9   # SLA2_MAX_STAGES
+
+
 class Taps(ctypes.Structure):
-    _fields_ = [(name, ctypes.c_void_p) for name in
-                ("O_s", "O_l", "q_codes", "k_codes", "v_codes", "s_q", "s_k", "s_v", "k_colmean")]
+    _fields_ = [(name, ctypes.c_void_p) for name in TAP_NAMES] + [("stage_events", ctypes.c_void_p)]
+
+
+def event_array(events):
+    """ctypes array of raw hipEvent_t handles of torch.cuda.Event objects (created if needed)."""
+    if len(events) != MAX_STAGES + 1:
+        raise ValueError(f"need {MAX_STAGES + 1} events")
+    for e in events:
+        if e.cuda_event == 0:
+            e.record()                         # torch creates the event on first record
+    return (ctypes.c_void_p * len(events))(*[e.cuda_event for e in events])
 
 
 class SLA2Error(RuntimeError):
@@ -174,9 +187,14 @@ def sla2_linear_precompute(k, v, want_h=True, want_z=True, workspace=None):
     return out
 
 
-def _make_taps(q, want):
+def _make_taps(q, want, events=None):
     if not want:
-        return None, None
+        if events is None:
+            return None, None
+        taps = Taps()
+        taps._events = event_array(events)
+        taps.stage_events = ctypes.cast(taps._events, ctypes.c_void_p)
+        return taps, None
     B, H, N, d = q.shape
     dev = q.device
     t = {
@@ -193,17 +211,23 @@ def _make_taps(q, want):
     if want is not True:
         t = {k: v for k, v in t.items() if k in want}
     taps = Taps(**{k: (v.data_ptr() if v is not None else None) for k, v in t.items()})
+    if events is not None:
+        taps._events = event_array(events)
+        taps.stage_events = ctypes.cast(taps._events, ctypes.c_void_p)
     return taps, t
 
 
 def sla2_forward(q, k, v, proj_q, proj_k, alpha, keep_frac, taps=False, out=None,
-                 workspace=None):
-    """O [B,H,N,d] fp32; with taps=True (or a collection of tap names) also a dict of taps."""
+                 workspace=None, events=None):
+    """O [B,H,N,d] fp32; with taps=True (or a collection of tap names) also a dict of taps.
+
+    `events`: optional list of 10 torch.cuda.Event(enable_timing=True); the library records
+    them before the first and after every kernel on the current stream."""
     _contig(q, k, v, proj_q, proj_k, alpha, out)
     shp = shape_of(q)
     dev = q.device
     o = out if out is not None else torch.empty(q.shape, dtype=torch.float32, device=dev)
-    ctaps, tdict = _make_taps(q, taps)
+    ctaps, tdict = _make_taps(q, taps, events)
     ws = workspace if workspace is not None else workspace_for(q)
     st = lib().sla2_forward(ctypes.byref(shp), _ptr(q), _ptr(k), _ptr(v), _ptr(proj_q),
                             _ptr(proj_k), _ptr(alpha), float(keep_frac), SLA2_QUANT_I8_FP8,
@@ -213,13 +237,14 @@ def sla2_forward(q, k, v, proj_q, proj_k, alpha, keep_frac, taps=False, out=None
     return (o, tdict) if taps else o
 
 
-def sla2_forward_with_mask(q, k, v, mask, alpha, taps=False, out=None, workspace=None):
+def sla2_forward_with_mask(q, k, v, mask, alpha, taps=False, out=None, workspace=None,
+                           events=None):
     """O [B,H,N,d] fp32 from a caller block mask [B,H,N/128,N/64] uint8."""
     _contig(q, k, v, mask, alpha, out)
     shp = shape_of(q)
     dev = q.device
     o = out if out is not None else torch.empty(q.shape, dtype=torch.float32, device=dev)
-    ctaps, tdict = _make_taps(q, taps)
+    ctaps, tdict = _make_taps(q, taps, events)
     ws = workspace if workspace is not None else workspace_for(q)
     st = lib().sla2_forward_with_mask(ctypes.byref(shp), _ptr(q), _ptr(k), _ptr(v), _ptr(mask),
                                       _ptr(alpha), SLA2_QUANT_I8_FP8, _ptr(o),

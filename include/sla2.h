@@ -87,7 +87,16 @@ typedef struct {
     float   *s_k;       /* [B,H,N/64] */
     float   *s_v;       /* [B,H,N/64] */
     float   *k_colmean; /* [B,H,d] colmean(K) rounded to fp32 */
+    /* NULL, or SLA2_MAX_STAGES + 1 caller-created hipEvent_t handles: element 0 is
+     * recorded on the stream before the first kernel and element s + 1 after kernel s,
+     * so consecutive pairs time each kernel. Kernel order of sla2_forward: pool,
+     * colmean, project, score_topk, quant, linear_pre, linear_total, linear_out,
+     * sparse; of sla2_forward_with_mask: pool, colmean, mask_to_list, quant,
+     * linear_pre, linear_total, linear_out, sparse. */
+    void   **stage_events;
 } sla2_taps;
+
+#define SLA2_MAX_STAGES 9
 
 /* Kept key blocks per query block: max(1, floor(keep_frac * n_key_blocks + 1e-9)),
  * capped at n_key_blocks (the "top k%" of step 1). Host only; returns -1 when
