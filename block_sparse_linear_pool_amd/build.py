@@ -21,6 +21,8 @@ FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
     # never emit packed fp32 VALU ops
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # keep MFMA accumulators in arch VGPRs: the online-softmax rescale is VALU work on them
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
 ]
 
 

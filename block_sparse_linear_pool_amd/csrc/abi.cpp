@@ -238,7 +238,7 @@ sla2_status sla2_linear_precompute(const sla2_shape* shape, const void* K, const
   SLA2_LAUNCH(launch_linear_pre(g, dt, K, V, at<float>(workspace, p.mu32), nullptr, h, zz,
                                 at<float>(workspace, p.hpart), at<float>(workspace, p.zpart), stream));
   SLA2_LAUNCH(launch_linear_total(g, at<float>(workspace, p.hpart), at<float>(workspace, p.zpart),
-                                  h_total, z_total, stream));
+                                  h_total, z_total, 1, stream));
   return SLA2_OK;
 }
 
@@ -262,11 +262,12 @@ sla2_status run_branches(const Geom& g, int dt, const void* Q, const void* K, co
                                 nullptr, at<float>(ws, p.z), at<float>(ws, p.hpart),
                                 at<float>(ws, p.zpart), stream));
   SLA2_LAUNCH(launch_linear_total(g, at<float>(ws, p.hpart), at<float>(ws, p.zpart),
-                                  at<float>(ws, p.htot), at<float>(ws, p.ztot), stream));
+                                  at<float>(ws, p.htot), at<float>(ws, p.ztot), 0, stream));
   float* ol = tp.O_l ? tp.O_l : at<float>(ws, p.ol);
   SLA2_LAUNCH(launch_linear_out(g, dt, Q, at<uint16_t>(ws, p.hbf), at<float>(ws, p.z),
                                 at<float>(ws, p.htot), at<float>(ws, p.ztot),
-                                at<uint8_t>(ws, p.mask), at<int32_t>(ws, p.cnt), ol, stream));
+                                at<uint8_t>(ws, p.mask), at<int32_t>(ws, p.list), list_stride,
+                                at<int32_t>(ws, p.cnt), ol, stream));
   SLA2_LAUNCH(launch_sparse(g, at<int8_t>(ws, p.qc), at<int8_t>(ws, p.kc), at<uint8_t>(ws, p.vc),
                             sq, sk, sv, at<int32_t>(ws, p.list), list_stride,
                             at<int32_t>(ws, p.cnt), alpha, ol, O, tp.O_s, stream));

@@ -4,20 +4,27 @@
 // Diffusion Transformers"; phi = softmax over the head dim per its §4 symbol table).
 //
 //   linear_pre    per key block j: phi(K_s,j) (softmax of each row over d), rounded to
-//                 bf16; z_j = column sums of those values; h_j = phi^T V_j by bf16 MFMA
-//                 with fp32 accumulation. Also fp32 partial sums over 8 key blocks.
+//                 bf16; z_j = column sums of those values; h_j^T = V_j^T phi by bf16 MFMA
+//                 with fp32 accumulation, stored transposed ([d_v][d_phi]) in bf16 for
+//                 the output kernel. Also fp32 partial sums over 8 key blocks.
 //   linear_total  H_tot = sum_j h_j and Z_tot = sum_j z_j from the partials (fixed order).
 //   linear_out    per query block i: H_i, Z_i over the dropped blocks — as the total
 //                 minus the kept blocks when those are fewer, else as a direct sum over
 //                 the dropped blocks (bounds the cancellation) — then
 //                 O_l = phi(Q_i) H_i / (phi(Q_i) . Z_i), with H_i split into bf16 hi + lo
 //                 parts for the MFMA. A query block with no dropped block gets O_l = 0.
+//
+// In linear_out every wavefront owns 32 rows (d_v) of H_i^T for all 128 queries, so it
+// gathers exactly the A-operand fragments of its MFMA into registers: no LDS staging of H.
+// The MFMA k slots are assigned so that lane group g holds d_phi = 64 g + 8 s + [0, 8) at
+// step s: each lane then reads one contiguous 128-byte run of a transposed h_j row. The
+// phi(Q) B operand uses the same assignment.
 #include "sla2_common.h"
 
 namespace sla2 {
 
 constexpr int kPadKP = 72;    // bf16 row stride of the transposed 128 x 64 tiles (bank spread)
-constexpr int kPadH = 136;    // bf16 row stride of the transposed 128 x 128 H tiles
+constexpr int kPadQ = 136;    // bf16 row stride of the phi(Q) tile
 
 __device__ inline bf16x8 lds_bf16x8(const uint16_t* p) {
   return *reinterpret_cast<const bf16x8*>(p);
@@ -28,7 +35,7 @@ __device__ inline bf16x8 lds_bf16x8(const uint16_t* p) {
 template <typename T>
 __global__ __launch_bounds__(256) void linear_pre_kernel(
     const T* __restrict__ K, const T* __restrict__ V, const float* __restrict__ mu32,
-    uint16_t* __restrict__ h_bf16, float* __restrict__ h_f32, float* __restrict__ z,
+    uint16_t* __restrict__ ht_bf16, float* __restrict__ h_f32, float* __restrict__ z,
     float* __restrict__ hpart, float* __restrict__ zpart, int N) {
   __shared__ __attribute__((aligned(16))) uint16_t phit[kD][kPadKP];  // phi^T [d][row]
   __shared__ __attribute__((aligned(16))) uint16_t vt[kD][kPadKP];    // V^T   [d][row]
@@ -80,99 +87,115 @@ __global__ __launch_bounds__(256) void linear_pre_kernel(
       z[(static_cast<size_t>(bh) * nkb + j) * kD + t] = s;
       zs += s;
     }
-    // h_j tiles: rows d_a = 32w + ..., columns d_b = 32tb + ...
+    // h_j^T tiles: rows d_v = 32 tb + ..., columns d_phi = 32 w + ...
     f32x16 acc[4];
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb) acc[tb] = f32x16{};
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      const bf16x8 a = lds_bf16x8(&phit[32 * w + l32][16 * s + 8 * g]);
+      const bf16x8 b = lds_bf16x8(&phit[32 * w + l32][16 * s + 8 * g]);
 #pragma unroll
       for (int tb = 0; tb < 4; ++tb) {
-        const bf16x8 b = lds_bf16x8(&vt[32 * tb + l32][16 * s + 8 * g]);
+        const bf16x8 a = lds_bf16x8(&vt[32 * tb + l32][16 * s + 8 * g]);
         acc[tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[tb], 0, 0, 0);
       }
     }
     const size_t hbase = (static_cast<size_t>(bh) * nkb + j) * (kD * kD);
+    const int dphi = 32 * w + l32;
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const int da = 32 * w + 8 * (i >> 2) + 4 * g + (i & 3);
-        const int db = 32 * tb + l32;
+        const int dv = 32 * tb + 8 * (i >> 2) + 4 * g + (i & 3);
         const float hv = acc[tb][i];
-        if (h_bf16) h_bf16[hbase + da * kD + db] = f32_to_bf16_rne(hv);
-        if (h_f32) h_f32[hbase + da * kD + db] = hv;
+        if (ht_bf16) ht_bf16[hbase + dv * kD + dphi] = f32_to_bf16_rne(hv);
+        if (h_f32) h_f32[hbase + dphi * kD + dv] = hv;
         hsum[tb][i] += hv;
       }
     }
   }
   const size_t pbase = (static_cast<size_t>(bh) * np + p) * (kD * kD);
+  const int dphi = 32 * w + l32;
 #pragma unroll
   for (int tb = 0; tb < 4; ++tb) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const int da = 32 * w + 8 * (i >> 2) + 4 * g + (i & 3);
-      hpart[pbase + da * kD + 32 * tb + l32] = hsum[tb][i];
+      const int dv = 32 * tb + 8 * (i >> 2) + 4 * g + (i & 3);
+      hpart[pbase + dv * kD + dphi] = hsum[tb][i];
     }
   }
   if (t < kD) zpart[(static_cast<size_t>(bh) * np + p) * kD + t] = zs;
 }
 
 hipError_t launch_linear_pre(const Geom& g, int dtype, const void* K, const void* V,
-                             const float* mu32, uint16_t* h_bf16, float* h_f32, float* z,
+                             const float* mu32, uint16_t* ht_bf16, float* h_f32, float* z,
                              float* hpart, float* zpart, hipStream_t s) {
   dim3 grid((g.nkb + kKpPerWg - 1) / kKpPerWg, g.BH);
   if (dtype == 0)
     hipLaunchKernelGGL(linear_pre_kernel<float>, grid, dim3(256), 0, s,
-                       static_cast<const float*>(K), static_cast<const float*>(V), mu32, h_bf16,
+                       static_cast<const float*>(K), static_cast<const float*>(V), mu32, ht_bf16,
                        h_f32, z, hpart, zpart, g.N);
   else
     hipLaunchKernelGGL(linear_pre_kernel<uint16_t>, grid, dim3(256), 0, s,
                        static_cast<const uint16_t*>(K), static_cast<const uint16_t*>(V), mu32,
-                       h_bf16, h_f32, z, hpart, zpart, g.N);
+                       ht_bf16, h_f32, z, hpart, zpart, g.N);
   return hipGetLastError();
 }
 
 // ---------------------------------------------------------------- linear_total
-// grid (64, BH), 256 threads: element e = 256 * blockIdx.x + t of H_tot; block 0 also Z_tot.
+// grid (64, BH), 256 threads: element e = 256 * blockIdx.x + t of H_tot^T (partials are
+// transposed); with `standard` set the result is written as H_tot ([d_phi][d_v]).
+// Block 0 also sums Z_tot.
 __global__ __launch_bounds__(256) void linear_total_kernel(const float* __restrict__ hpart,
                                                            const float* __restrict__ zpart,
                                                            float* __restrict__ htot,
-                                                           float* __restrict__ ztot, int np) {
+                                                           float* __restrict__ ztot, int np,
+                                                           int standard) {
   const int bh = blockIdx.y, t = threadIdx.x;
   const int e = 256 * blockIdx.x + t;
-  float s = 0.f;
-  for (int p = 0; p < np; ++p) s += hpart[(static_cast<size_t>(bh) * np + p) * (kD * kD) + e];
-  htot[static_cast<size_t>(bh) * (kD * kD) + e] = s;
+  const float* hp = hpart + static_cast<size_t>(bh) * np * (kD * kD) + e;
+  float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;   // fixed interleaved order: deterministic
+  int p = 0;
+  for (; p + 4 <= np; p += 4) {
+    s0 += hp[static_cast<size_t>(p) * (kD * kD)];
+    s1 += hp[static_cast<size_t>(p + 1) * (kD * kD)];
+    s2 += hp[static_cast<size_t>(p + 2) * (kD * kD)];
+    s3 += hp[static_cast<size_t>(p + 3) * (kD * kD)];
+  }
+  for (; p < np; ++p) s0 += hp[static_cast<size_t>(p) * (kD * kD)];
+  const int out = standard ? (e & (kD - 1)) * kD + (e >> 7) : e;
+  htot[static_cast<size_t>(bh) * (kD * kD) + out] = (s0 + s1) + (s2 + s3);
   if (blockIdx.x == 0 && t < kD) {
     float zz = 0.f;
-    for (int p = 0; p < np; ++p) zz += zpart[(static_cast<size_t>(bh) * np + p) * kD + t];
+    for (int q = 0; q < np; ++q) zz += zpart[(static_cast<size_t>(bh) * np + q) * kD + t];
     ztot[static_cast<size_t>(bh) * kD + t] = zz;
   }
 }
 
 hipError_t launch_linear_total(const Geom& g, const float* hpart, const float* zpart,
-                               float* htot, float* ztot, hipStream_t s) {
+                               float* htot, float* ztot, int standard, hipStream_t s) {
   const int np = (g.nkb + kKpPerWg - 1) / kKpPerWg;
   hipLaunchKernelGGL(linear_total_kernel, dim3(kD * kD / 256, g.BH), dim3(256), 0, s, hpart,
-                     zpart, htot, ztot, np);
+                     zpart, htot, ztot, np, standard);
   return hipGetLastError();
 }
 
 // ---------------------------------------------------------------- linear_out
-// grid (nqb, BH), 256 threads (4 wavefronts x 32 queries).
+// grid (nqb, BH), 256 threads. Wavefront w: rows d_v = 32 w + (lane % 32) of H_i^T, all 128
+// queries (4 query tiles of 32).
 template <typename T>
-__global__ __launch_bounds__(256) void linear_out_kernel(
-    const T* __restrict__ Q, const uint16_t* __restrict__ h_bf16, const float* __restrict__ z,
-    const float* __restrict__ htot, const float* __restrict__ ztot,
-    const uint8_t* __restrict__ mask, const int32_t* __restrict__ cnt, float* __restrict__ O_l,
-    int N) {
-  __shared__ __attribute__((aligned(16))) uint16_t hhi[kD][kPadH];  // H^T hi [d_out][d_in]
-  __shared__ __attribute__((aligned(16))) uint16_t hlo[kD][kPadH];  // H^T lo
+__global__ __launch_bounds__(256, 2) void linear_out_kernel(
+    const T* __restrict__ Q, const uint16_t* __restrict__ ht_bf16, const float* __restrict__ z,
+    const float* __restrict__ htot_t, const float* __restrict__ ztot,
+    const uint8_t* __restrict__ mask, const int32_t* __restrict__ list, int list_stride,
+    const int32_t* __restrict__ cnt, float* __restrict__ O_l, int N) {
+  __shared__ __attribute__((aligned(16))) uint16_t phq[kBQ][kPadQ];   // phi(Q_i), bf16
   __shared__ float zsh[kD];
-  __shared__ int lst[kMaxN / kBK];
-  const int i = blockIdx.x, bh = blockIdx.y, t = threadIdx.x;
+  __shared__ float den[kBQ];
+  __shared__ uint16_t lst[kMaxN / kBK];
+  const int t = threadIdx.x;
+  int i, bh;
+  xcd_block(N / kBQ, static_cast<int>(gridDim.y), &i, &bh);
   const int lane = t & 63, w = t >> 6, g = lane >> 5, l32 = lane & 31;
   const int nqb = N / kBQ, nkb = N / kBK;
   const size_t row = static_cast<size_t>(bh) * nqb + i;
@@ -186,27 +209,59 @@ __global__ __launch_bounds__(256) void linear_out_kernel(
   }
   const bool sub = nsel <= nuns;  // total minus kept, else direct sum over dropped
   const int nl = sub ? nsel : nuns;
-  if (w == 0) {
+  if (sub) {
+    for (int n = t; n < nsel; n += 256) lst[n] = static_cast<uint16_t>(list[row * list_stride + n]);
+  } else if (w == 0) {
     int before = 0;
     for (int j0 = 0; j0 < nkb; j0 += 64) {
       const int j = j0 + lane;
-      const bool kept = j < nkb && mask[row * nkb + j] != 0;
-      const bool take = j < nkb && (kept == sub);
+      const bool take = j < nkb && mask[row * nkb + j] == 0;
       const uint64_t m = __ballot(take);
       if (take)
         lst[before + __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m >> 32),
-                                               __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0))] = j;
+                                               __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0))] =
+            static_cast<uint16_t>(j);
       before += __popcll(m);
     }
   }
-  __syncthreads();
-  // ---- gather H (thread t owns elements 64t .. 64t+63 of the row-major [d_in][d_out])
+  // ---- phi(Q_i) into LDS: thread t -> query t/2, d = 64 (t%2) .. +64
+  {
+    const int q = t >> 1, d0 = 64 * (t & 1);
+    const T* qrow = Q + (static_cast<size_t>(bh) * N + static_cast<size_t>(i) * kBQ + q) * kD + d0;
+    float x[64];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) load8<T>(qrow + 8 * u, x + 8 * u);
+    float mx = -INFINITY;
+#pragma unroll
+    for (int e = 0; e < 64; ++e) mx = fmaxf(mx, x[e]);
+    mx = fmaxf(mx, __shfl_xor(mx, 1));
+    float sum = 0.f;
+#pragma unroll
+    for (int e = 0; e < 64; ++e) {
+      x[e] = __expf(x[e] - mx);
+      sum += x[e];
+    }
+    sum += __shfl_xor(sum, 1);
+    const float inv = 1.0f / sum;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      i32x4 pk;
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        pk[k] = static_cast<int>(static_cast<uint32_t>(f32_to_bf16_rne(x[8 * u + 2 * k] * inv)) |
+                                 (static_cast<uint32_t>(f32_to_bf16_rne(x[8 * u + 2 * k + 1] * inv)) << 16));
+      *reinterpret_cast<i32x4*>(&phq[q][d0 + 8 * u]) = pk;
+    }
+  }
+  __syncthreads();   // list and phi(Q) ready
+  // ---- gather this lane's part of H_i^T: row dv, d_phi = 64 g + [0, 64)
+  const int dv = 32 * w + l32;
   float hacc[64];
-  const size_t hoff = static_cast<size_t>(bh) * (kD * kD) + 64 * t;
   if (sub) {
+    const float* hp = htot_t + static_cast<size_t>(bh) * (kD * kD) + dv * kD + 64 * g;
 #pragma unroll
     for (int u = 0; u < 16; ++u) {
-      const f32x4 v = *reinterpret_cast<const f32x4*>(htot + hoff + 4 * u);
+      const f32x4 v = *reinterpret_cast<const f32x4*>(hp + 4 * u);
       hacc[4 * u] = v[0]; hacc[4 * u + 1] = v[1]; hacc[4 * u + 2] = v[2]; hacc[4 * u + 3] = v[3];
     }
   } else {
@@ -216,9 +271,11 @@ __global__ __launch_bounds__(256) void linear_out_kernel(
   float zacc = 0.f;
   if (t < kD) zacc = sub ? ztot[static_cast<size_t>(bh) * kD + t] : 0.f;
   const float sgn = sub ? -1.f : 1.f;
+  const uint16_t* hbase = ht_bf16 + static_cast<size_t>(bh) * nkb * (kD * kD) + dv * kD + 64 * g;
+  const float* zbase = z + static_cast<size_t>(bh) * nkb * kD + t;
   for (int n = 0; n < nl; ++n) {
     const int j = lst[n];
-    const uint16_t* hp = h_bf16 + (static_cast<size_t>(bh) * nkb + j) * (kD * kD) + 64 * t;
+    const uint16_t* hp = hbase + static_cast<size_t>(j) * (kD * kD);
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const i32x4 v = *reinterpret_cast<const i32x4*>(hp + 8 * u);
@@ -229,64 +286,46 @@ __global__ __launch_bounds__(256) void linear_out_kernel(
         hacc[8 * u + 2 * k + 1] = fmaf(sgn, __uint_as_float(wd & 0xFFFF0000u), hacc[8 * u + 2 * k + 1]);
       }
     }
-    if (t < kD) zacc += sgn * z[(static_cast<size_t>(bh) * nkb + j) * kD + t];
+    if (t < kD) zacc = fmaf(sgn, zbase[static_cast<size_t>(j) * kD], zacc);
   }
-  // ---- H^T into LDS as bf16 hi + lo
-  {
-    const int din = t >> 1, dout0 = 64 * (t & 1);
-#pragma unroll
-    for (int e = 0; e < 64; ++e) {
-      const uint16_t hi = f32_to_bf16_rne(hacc[e]);
-      const float rem = hacc[e] - bf16_to_f32(hi);
-      hhi[dout0 + e][din] = hi;
-      hlo[dout0 + e][din] = f32_to_bf16_rne(rem);
-    }
-    if (t < kD) zsh[t] = zacc;
-  }
-  __syncthreads();
-  // ---- phi(Q) for query q = 32w + l32: this lane holds d_in = 16s + 8g + [0, 8)
-  const int q = 32 * w + l32;
-  const T* qrow = Q + (static_cast<size_t>(bh) * N + static_cast<size_t>(i) * kBQ + q) * kD;
-  float x[64];
-#pragma unroll
-  for (int s = 0; s < 8; ++s) load8<T>(qrow + 16 * s + 8 * g, x + 8 * s);
-  float mx = -INFINITY;
-#pragma unroll
-  for (int e = 0; e < 64; ++e) mx = fmaxf(mx, x[e]);
-  mx = fmaxf(mx, __shfl_xor(mx, 32));
-  float sum = 0.f;
-#pragma unroll
-  for (int e = 0; e < 64; ++e) {
-    x[e] = __expf(x[e] - mx);
-    sum += x[e];
-  }
-  sum += __shfl_xor(sum, 32);
-  const float inv = 1.0f / sum;
-  bf16x8 bq[8];
-  float den = 0.f;
+  if (t < kD) zsh[t] = zacc;
+  // ---- bf16 hi + lo A operands (k slot: step s, element b -> d_phi = 64 g + 8 s + b)
+  bf16x8 ahi[8], alo[8];
 #pragma unroll
   for (int s = 0; s < 8; ++s) {
 #pragma unroll
     for (int b = 0; b < 8; ++b) {
-      const uint16_t pb = f32_to_bf16_rne(x[8 * s + b] * inv);
-      bq[s][b] = __builtin_bit_cast(__bf16, pb);
-      den = fmaf(bf16_to_f32(pb), zsh[16 * s + 8 * g + b], den);
+      const float hv = hacc[8 * s + b];
+      const uint16_t hi = f32_to_bf16_rne(hv);
+      ahi[s][b] = __builtin_bit_cast(__bf16, hi);
+      alo[s][b] = __builtin_bit_cast(__bf16, f32_to_bf16_rne(hv - bf16_to_f32(hi)));
     }
   }
-  den += __shfl_xor(den, 32);
-  const float rden = 1.0f / den;
+  __syncthreads();   // Z ready
+  // ---- den[q] = phi(q) . Z_i with the bf16 phi values the MFMA uses
+  {
+    const int q = t >> 1, d0 = 64 * (t & 1);
+    float dsum = 0.f;
 #pragma unroll
-  for (int td = 0; td < 4; ++td) {
+    for (int e = 0; e < 64; ++e) dsum = fmaf(bf16_to_f32(phq[q][d0 + e]), zsh[d0 + e], dsum);
+    dsum += __shfl_xor(dsum, 1);
+    if ((t & 1) == 0) den[q] = dsum;
+  }
+  __syncthreads();
+  // ---- O_l^T[dv][q] = sum_dphi H^T[dv][dphi] phi(q)[dphi], 4 query tiles
+#pragma unroll
+  for (int qt = 0; qt < 4; ++qt) {
     f32x16 acc = f32x16{};
+    const int q = 32 * qt + l32;
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
-      const bf16x8 ahi = lds_bf16x8(&hhi[32 * td + l32][16 * s + 8 * g]);
-      const bf16x8 alo = lds_bf16x8(&hlo[32 * td + l32][16 * s + 8 * g]);
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahi, bq[s], acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(alo, bq[s], acc, 0, 0, 0);
+      const bf16x8 b = lds_bf16x8(&phq[q][64 * g + 8 * s]);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahi[s], b, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(alo[s], b, acc, 0, 0, 0);
     }
-    // lane holds O_l^T[d_out = 32td + 8(i/4) + 4g + (i%4)][q]
-    float* orow = out + static_cast<size_t>(q) * kD + 32 * td + 4 * g;
+    // lane holds O_l^T[32 w + 8 (ii/4) + 4 g + (ii%4)][q]
+    const float rden = 1.0f / den[q];
+    float* orow = out + static_cast<size_t>(q) * kD + 32 * w + 4 * g;
 #pragma unroll
     for (int ib = 0; ib < 4; ++ib)
       *reinterpret_cast<f32x4*>(orow + 8 * ib) =
@@ -295,18 +334,19 @@ __global__ __launch_bounds__(256) void linear_out_kernel(
   }
 }
 
-hipError_t launch_linear_out(const Geom& g, int dtype, const void* Q, const uint16_t* h_bf16,
-                             const float* z, const float* htot, const float* ztot,
-                             const uint8_t* mask, const int32_t* cnt, float* O_l,
-                             hipStream_t s) {
+hipError_t launch_linear_out(const Geom& g, int dtype, const void* Q, const uint16_t* ht_bf16,
+                             const float* z, const float* htot_t, const float* ztot,
+                             const uint8_t* mask, const int32_t* list, int list_stride,
+                             const int32_t* cnt, float* O_l, hipStream_t s) {
   dim3 grid(g.nqb, g.BH);
   if (dtype == 0)
     hipLaunchKernelGGL(linear_out_kernel<float>, grid, dim3(256), 0, s,
-                       static_cast<const float*>(Q), h_bf16, z, htot, ztot, mask, cnt, O_l, g.N);
+                       static_cast<const float*>(Q), ht_bf16, z, htot_t, ztot, mask, list,
+                       list_stride, cnt, O_l, g.N);
   else
     hipLaunchKernelGGL(linear_out_kernel<uint16_t>, grid, dim3(256), 0, s,
-                       static_cast<const uint16_t*>(Q), h_bf16, z, htot, ztot, mask, cnt, O_l,
-                       g.N);
+                       static_cast<const uint16_t*>(Q), ht_bf16, z, htot_t, ztot, mask, list,
+                       list_stride, cnt, O_l, g.N);
   return hipGetLastError();
 }
 

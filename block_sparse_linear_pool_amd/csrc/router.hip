@@ -85,101 +85,111 @@ hipError_t launch_pool(const Geom& g, int dtype, const void* Q, const void* K, d
 }
 
 // ---------------------------------------------------------------- colmean
-// grid BH, 128 threads (one per column). Eight interleaved fp64 partial sums.
-__global__ __launch_bounds__(128) void colmean_kernel(const double* __restrict__ ksum,
-                                                      double* __restrict__ mu64,
-                                                      float* __restrict__ mu32,
-                                                      float* __restrict__ mu32_tap, int nkb,
-                                                      int N) {
-  const int bh = blockIdx.x, c = threadIdx.x;
+// grid BH, 1024 threads: column c = t % 128, part = t / 128 sums key blocks part, part + 8,
+// ...; the 8 parts are combined in a fixed order (deterministic).
+__global__ __launch_bounds__(1024) void colmean_kernel(const double* __restrict__ ksum,
+                                                       double* __restrict__ mu64,
+                                                       float* __restrict__ mu32,
+                                                       float* __restrict__ mu32_tap, int nkb,
+                                                       int N) {
+  __shared__ double part[8][kD];
+  const int bh = blockIdx.x, t = threadIdx.x, c = t & 127, pr = t >> 7;
   const double* p = ksum + static_cast<size_t>(bh) * nkb * kD + c;
-  double part[8] = {};
-  int j = 0;
-  for (; j + 8 <= nkb; j += 8) {
-#pragma unroll
-    for (int u = 0; u < 8; ++u) part[u] += p[static_cast<size_t>(j + u) * kD];
+  double a0 = 0.0, a1 = 0.0, a2 = 0.0, a3 = 0.0;
+  int j = pr;
+  for (; j + 24 < nkb; j += 32) {
+    a0 += p[static_cast<size_t>(j) * kD];
+    a1 += p[static_cast<size_t>(j + 8) * kD];
+    a2 += p[static_cast<size_t>(j + 16) * kD];
+    a3 += p[static_cast<size_t>(j + 24) * kD];
   }
-  for (; j < nkb; ++j) part[0] += p[static_cast<size_t>(j) * kD];
-  double s = ((part[0] + part[1]) + (part[2] + part[3])) + ((part[4] + part[5]) + (part[6] + part[7]));
-  const double mu = s / static_cast<double>(N);
-  mu64[bh * kD + c] = mu;
-  mu32[bh * kD + c] = static_cast<float>(mu);
-  if (mu32_tap) mu32_tap[bh * kD + c] = static_cast<float>(mu);
+  for (; j < nkb; j += 8) a0 += p[static_cast<size_t>(j) * kD];
+  part[pr][c] = (a0 + a1) + (a2 + a3);
+  __syncthreads();
+  if (t < kD) {
+    double s = 0.0;
+    for (int q = 0; q < 8; ++q) s += part[q][t];
+    const double mu = s / static_cast<double>(N);
+    mu64[bh * kD + t] = mu;
+    mu32[bh * kD + t] = static_cast<float>(mu);
+    if (mu32_tap) mu32_tap[bh * kD + t] = static_cast<float>(mu);
+  }
 }
 
 hipError_t launch_colmean(const Geom& g, const double* ksum, double* mu64, float* mu32,
                           float* mu32_tap, hipStream_t s) {
-  hipLaunchKernelGGL(colmean_kernel, dim3(g.BH), dim3(128), 0, s, ksum, mu64, mu32, mu32_tap,
+  hipLaunchKernelGGL(colmean_kernel, dim3(g.BH), dim3(1024), 0, s, ksum, mu64, mu32, mu32_tap,
                      g.nkb, g.N);
   return hipGetLastError();
 }
 
+// fp64 MFMA 16x16x4 operand/result layout (gfx950): lane l supplies A[l % 16][l / 16] and
+// B[l / 16][l % 16]; result register i of lane l is D[l / 16 + 4 i][l % 16].
+__device__ inline f64x4 mfma_f64(double a, double b, f64x4 c) {
+  return __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, c, 0, 0, 0);
+}
+
 // ---------------------------------------------------------------- project
-// grid (ceil((nqb + nkb) / 16), BH), 128 threads (one per output column).
-// Rows [0, nqb) are query blocks, [nqb, nqb + nkb) key blocks.
-constexpr int kProjRows = 16;
-__global__ __launch_bounds__(128) void project_kernel(
+// grid (ceil(nqb/64) + ceil(nkb/64), BH), 256 threads. A workgroup takes 64 rows of either
+// Qbar (W = proj_q) or Kbar - mu (W = proj_k); wavefront w the 16-row tile 16w..16w+15,
+// all 128 output columns as eight 16x16 fp64 MFMA tiles.
+constexpr int kXPad = kD + 1;
+__global__ __launch_bounds__(256) void project_kernel(
     const double* __restrict__ qsum, const double* __restrict__ ksum,
     const double* __restrict__ mu64, const float* __restrict__ wq, const float* __restrict__ wk,
     double* __restrict__ A, double* __restrict__ Bt, int nqb, int nkb, int H) {
-  __shared__ double x[kProjRows][kD];
-  const int bh = blockIdx.y, h = bh % H, c = threadIdx.x;
-  const int r0 = blockIdx.x * kProjRows;
-  const int total = nqb + nkb;
-  const double mu = mu64[bh * kD + c];
-  for (int r = 0; r < kProjRows; ++r) {
-    const int rr = r0 + r;
+  __shared__ double xs[64][kXPad];
+  const int bh = blockIdx.y, h = bh % H, t = threadIdx.x;
+  const int lane = t & 63, w = t >> 6;
+  const int qwg = (nqb + 63) / 64;
+  const bool is_q = static_cast<int>(blockIdx.x) < qwg;
+  const int r0 = 64 * (is_q ? blockIdx.x : blockIdx.x - qwg);
+  const int nrows = is_q ? nqb : nkb;
+  const double* src = is_q ? qsum + static_cast<size_t>(bh) * nqb * kD
+                           : ksum + static_cast<size_t>(bh) * nkb * kD;
+  const double scale = is_q ? 1.0 / kBQ : 1.0 / kBK;
+  for (int e = t; e < 64 * kD; e += 256) {
+    const int r = e >> 7, c = e & 127;
     double v = 0.0;
-    if (rr < nqb) v = qsum[(static_cast<size_t>(bh) * nqb + rr) * kD + c] * (1.0 / kBQ);
-    else if (rr < total)
-      v = ksum[(static_cast<size_t>(bh) * nkb + (rr - nqb)) * kD + c] * (1.0 / kBK) - mu;
-    x[r][c] = v;
+    if (r0 + r < nrows) {
+      v = src[static_cast<size_t>(r0 + r) * kD + c] * scale;
+      if (!is_q) v -= mu64[bh * kD + c];
+    }
+    xs[r][c] = v;
   }
   __syncthreads();
-  // Two passes when the chunk straddles query and key rows: W differs.
-  double acc[kProjRows];
+  const float* W = (is_q ? wq : wk) + static_cast<size_t>(h) * kD * kD;
+  const int ra = 16 * w + (lane & 15), kq = lane >> 4;
+#pragma unroll 1
+  for (int ct = 0; ct < 8; ++ct) {
+    float wv[32];
 #pragma unroll
-  for (int r = 0; r < kProjRows; ++r) acc[r] = 0.0;
-  const bool any_q = r0 < nqb;
-  const bool any_k = r0 + kProjRows > nqb && r0 < total;
-  for (int pass = 0; pass < 2; ++pass) {
-    if ((pass == 0 && !any_q) || (pass == 1 && !any_k)) continue;
-    const float* W = (pass == 0 ? wq : wk) + static_cast<size_t>(h) * kD * kD + c;
-    double a2[kProjRows];
+    for (int s = 0; s < 32; ++s) wv[s] = W[(4 * s + kq) * kD + 16 * ct + (lane & 15)];
+    f64x4 acc = f64x4{0.0, 0.0, 0.0, 0.0};
 #pragma unroll
-    for (int r = 0; r < kProjRows; ++r) a2[r] = 0.0;
-    for (int k = 0; k < kD; ++k) {
-      const double w = static_cast<double>(W[k * kD]);
+    for (int s = 0; s < 32; ++s)
+      acc = mfma_f64(xs[ra][4 * s + kq], static_cast<double>(wv[s]), acc);
+    const int col = 16 * ct + (lane & 15);
 #pragma unroll
-      for (int r = 0; r < kProjRows; ++r) a2[r] = fma(x[r][k], w, a2[r]);
+    for (int i = 0; i < 4; ++i) {
+      const int r = r0 + 16 * w + kq + 4 * i;
+      if (r >= nrows) continue;
+      if (is_q) A[(static_cast<size_t>(bh) * nqb + r) * kD + col] = acc[i];
+      else Bt[(static_cast<size_t>(bh) * kD + col) * nkb + r] = acc[i];
     }
-#pragma unroll
-    for (int r = 0; r < kProjRows; ++r) {
-      const int rr = r0 + r;
-      const bool is_q = rr < nqb;
-      if ((pass == 0) == is_q) acc[r] = a2[r];
-    }
-  }
-#pragma unroll
-  for (int r = 0; r < kProjRows; ++r) {
-    const int rr = r0 + r;
-    if (rr < nqb) A[(static_cast<size_t>(bh) * nqb + rr) * kD + c] = acc[r];
-    else if (rr < total) Bt[(static_cast<size_t>(bh) * kD + c) * nkb + (rr - nqb)] = acc[r];
   }
 }
 
 hipError_t launch_project(const Geom& g, const double* qsum, const double* ksum,
                           const double* mu64, const float* wq, const float* wk, double* A,
                           double* Bt, hipStream_t s) {
-  dim3 grid((g.nqb + g.nkb + kProjRows - 1) / kProjRows, g.BH);
-  hipLaunchKernelGGL(project_kernel, grid, dim3(128), 0, s, qsum, ksum, mu64, wq, wk, A, Bt,
+  dim3 grid((g.nqb + 63) / 64 + (g.nkb + 63) / 64, g.BH);
+  hipLaunchKernelGGL(project_kernel, grid, dim3(256), 0, s, qsum, ksum, mu64, wq, wk, A, Bt,
                      g.nqb, g.nkb, g.H);
   return hipGetLastError();
 }
 
 // ---------------------------------------------------------------- score + top-k
-constexpr int kScoreRows = 4;  // query blocks per workgroup, one per wavefront
-
 __device__ inline uint64_t order_key(double g) {
   // monotone map from finite doubles to unsigned integers (larger g -> larger key)
   const uint64_t b = static_cast<uint64_t>(__double_as_longlong(g));
@@ -191,109 +201,153 @@ __device__ inline int count_below_lane(uint64_t m) {
                                    __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0));
 }
 
-// grid (ceil(nqb / 4), BH), 256 threads; dynamic LDS kScoreRows * nkb doubles.
-__global__ __launch_bounds__(256) void score_topk_kernel(
-    const double* __restrict__ A, const double* __restrict__ Bt, int nqb, int nkb, int kb,
-    uint8_t* __restrict__ mask, int32_t* __restrict__ list, int list_stride,
-    int32_t* __restrict__ cnt, float* __restrict__ scores) {
-  extern __shared__ double smem[];
-  __shared__ double arow[kScoreRows][kD];
-  double* G = smem;  // [kScoreRows][nkb]
-  const int bh = blockIdx.y, t = threadIdx.x;
-  const int i0 = blockIdx.x * kScoreRows;
-  for (int e = t; e < kScoreRows * kD; e += 256) {
-    const int r = e / kD, k = e % kD;
-    const int i = i0 + r;
-    arow[r][k] = i < nqb ? A[(static_cast<size_t>(bh) * nqb + i) * kD + k] : 0.0;
-  }
-  __syncthreads();
-  const double inv_sqrt_d = 0.088388347648318440550;  // 1/sqrt(128)
-  const double* bt = Bt + static_cast<size_t>(bh) * kD * nkb;
-  for (int j = t; j < nkb; j += 256) {
-    double acc[kScoreRows] = {};
-    for (int k = 0; k < kD; ++k) {
-      const double b = bt[static_cast<size_t>(k) * nkb + j];
-#pragma unroll
-      for (int r = 0; r < kScoreRows; ++r) acc[r] = fma(arow[r][k], b, acc[r]);
-    }
-#pragma unroll
-    for (int r = 0; r < kScoreRows; ++r) G[r * nkb + j] = acc[r] * inv_sqrt_d + 0.0;
-  }
-  __syncthreads();
+// Rows of logits one workgroup keeps in LDS (fp64), by key-block count.
+__host__ __device__ inline int score_rows(int nkb) { return nkb <= 1024 ? 16 : (nkb <= 2048 ? 8 : 4); }
 
-  const int w = t >> 6, lane = t & 63;
-  const int i = i0 + w;
-  if (i >= nqb) return;
-  const double* g = G + w * nkb;
-  const int E = (nkb + 63) >> 6;
-  // kb-th largest key by bitwise construction: largest T with #{key >= T} >= kb
+// Kept set of one row, exact (ties to the lower index), by one wavefront. The row's keys
+// sit in registers, E per lane (key j = lane + 64 e). T = the kb-th largest key, built bit by
+// bit from the top: the largest T with #{key >= T} >= kb, each count a sum of ballot
+// popcounts. Then every key > T is kept, plus the lowest-index keys equal to T up to kb.
+template <int E>
+__device__ void select_row(const double* g, int nkb, int kb, int lane, size_t row,
+                           int32_t* __restrict__ list, int list_stride,
+                           uint8_t* __restrict__ mask) {
+  uint64_t key[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int j = lane + 64 * e;
+    key[e] = j < nkb ? order_key(g[j]) : 0ull;   // finite keys are >= 1
+  }
   uint64_t T = 0;
   for (int bit = 63; bit >= 0; --bit) {
     const uint64_t cand = T | (1ull << bit);
     int c = 0;
-    for (int e = 0; e < E; ++e) {
-      const int j = lane + 64 * e;
-      const uint64_t key = j < nkb ? order_key(g[j]) : 0ull;
-      c += __popcll(__ballot(key >= cand));
-    }
+#pragma unroll
+    for (int e = 0; e < E; ++e) c += __popcll(__ballot(key[e] >= cand));
     if (c >= kb) T = cand;
   }
   int gt = 0;
-  for (int e = 0; e < E; ++e) {
-    const int j = lane + 64 * e;
-    const uint64_t key = j < nkb ? order_key(g[j]) : 0ull;
-    gt += __popcll(__ballot(key > T));
-  }
-  const int need = kb - gt;  // equal keys to take, lowest indices first
-  const size_t row = static_cast<size_t>(bh) * nqb + i;
+#pragma unroll
+  for (int e = 0; e < E; ++e) gt += __popcll(__ballot(key[e] > T));
+  const int need = kb - gt;   // >= 1: equal keys to keep, lowest indices first
   int eq_before = 0, sel_before = 0;
+#pragma unroll
   for (int e = 0; e < E; ++e) {
     const int j = lane + 64 * e;
-    const uint64_t key = j < nkb ? order_key(g[j]) : 0ull;
-    const uint64_t eqm = __ballot(j < nkb && key == T);
-    const bool is_eq = j < nkb && key == T;
+    const bool valid = j < nkb;
+    const bool is_eq = valid && key[e] == T;
+    const uint64_t eqm = __ballot(is_eq);
     const int eq_rank = eq_before + count_below_lane(eqm);
-    const bool sel = j < nkb && (key > T || (is_eq && eq_rank < need));
+    const bool sel = valid && (key[e] > T || (is_eq && eq_rank < need));
     const uint64_t selm = __ballot(sel);
     if (sel) list[row * list_stride + sel_before + count_below_lane(selm)] = j;
-    if (j < nkb && mask) mask[row * nkb + j] = sel ? 1 : 0;
+    if (valid && mask) mask[row * nkb + j] = sel ? 1 : 0;
     eq_before += __popcll(eqm);
     sel_before += __popcll(selm);
   }
-  if (lane == 0 && cnt) cnt[row] = kb;
-  if (scores) {
-    double mx = -1.0e300;
-    for (int e = 0; e < E; ++e) {
-      const int j = lane + 64 * e;
-      if (j < nkb) mx = fmax(mx, g[j]);
+}
+
+// grid (ceil(nqb / RT), BH), 256 threads, RT = score_rows(nkb); dynamic LDS RT * nkb doubles.
+// E = keys per lane held in registers (nkb <= 64 E).
+template <int E>
+__global__ __launch_bounds__(256) void score_topk_kernel(
+    const double* __restrict__ A, const double* __restrict__ Bt, int nqb, int nkb, int kb,
+    uint8_t* __restrict__ mask, int32_t* __restrict__ list, int list_stride,
+    int32_t* __restrict__ cnt, float* __restrict__ scores) {
+  extern __shared__ double G[];                 // [RT][nkb]
+  __shared__ double as[16][kXPad];
+  const int RT = score_rows(nkb);
+  const int bh = blockIdx.y, t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int i0 = blockIdx.x * RT;
+  for (int e = t; e < 16 * kD; e += 256) {
+    const int r = e >> 7, k = e & 127;
+    const int i = i0 + r;
+    as[r][k] = (r < RT && i < nqb) ? A[(static_cast<size_t>(bh) * nqb + i) * kD + k] : 0.0;
+  }
+  __syncthreads();
+  // logits: 16-column fp64 MFMA tiles, round-robin over the wavefronts
+  const double inv_sqrt_d = 0.088388347648318440550;  // 1/sqrt(128)
+  const double* bt = Bt + static_cast<size_t>(bh) * kD * nkb;
+  const int ntile = (nkb + 15) >> 4, ra = lane & 15, kq = lane >> 4;
+  for (int ct = w; ct < ntile; ct += 4) {
+    const int col = 16 * ct + ra;
+    const bool ok = col < nkb;
+    const double* bc = bt + min(col, nkb - 1);   // unconditional loads, masked below
+    double b[32];
+#pragma unroll
+    for (int s = 0; s < 32; ++s) b[s] = bc[static_cast<size_t>(4 * s + kq) * nkb];
+    f64x4 acc = f64x4{0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+    for (int s = 0; s < 32; ++s) acc = mfma_f64(as[ra][4 * s + kq], ok ? b[s] : 0.0, acc);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = kq + 4 * i;
+      if (ok && r < RT) G[r * nkb + col] = acc[i] * inv_sqrt_d + 0.0;  // +0.0: no -0
     }
-    for (int o = 32; o >= 1; o >>= 1) mx = fmax(mx, __shfl_xor(mx, o));
-    double sum = 0.0;
-    for (int e = 0; e < E; ++e) {
-      const int j = lane + 64 * e;
-      if (j < nkb) sum += exp(g[j] - mx);
-    }
-    for (int o = 32; o >= 1; o >>= 1) sum += __shfl_xor(sum, o);
-    for (int e = 0; e < E; ++e) {
-      const int j = lane + 64 * e;
-      if (j < nkb) scores[row * nkb + j] = static_cast<float>(exp(g[j] - mx) / sum);
+  }
+  __syncthreads();
+  const int nE = (nkb + 63) >> 6;
+  for (int r = w; r < RT; r += 4) {
+    const int i = i0 + r;
+    if (i >= nqb) break;
+    const double* g = G + r * nkb;
+    const size_t row = static_cast<size_t>(bh) * nqb + i;
+    select_row<E>(g, nkb, kb, lane, row, list, list_stride, mask);
+    if (lane == 0 && cnt) cnt[row] = kb;
+    if (scores) {
+      double mx = -1.0e300;
+      for (int e = 0; e < nE; ++e) {
+        const int j = lane + 64 * e;
+        if (j < nkb) mx = fmax(mx, g[j]);
+      }
+      for (int o = 32; o >= 1; o >>= 1) mx = fmax(mx, __shfl_xor(mx, o));
+      double sum = 0.0;
+      for (int e = 0; e < nE; ++e) {
+        const int j = lane + 64 * e;
+        if (j < nkb) sum += exp(g[j] - mx);
+      }
+      for (int o = 32; o >= 1; o >>= 1) sum += __shfl_xor(sum, o);
+      for (int e = 0; e < nE; ++e) {
+        const int j = lane + 64 * e;
+        if (j < nkb) scores[row * nkb + j] = static_cast<float>(exp(g[j] - mx) / sum);
+      }
     }
   }
 }
 
 hipError_t configure_router() {
-  return hipFuncSetAttribute(reinterpret_cast<const void*>(&score_topk_kernel),
-                             hipFuncAttributeMaxDynamicSharedMemorySize,
-                             kScoreRows * (kMaxN / kBK) * static_cast<int>(sizeof(double)));
+  // largest dynamic LDS: RT * nkb doubles = 128 KB at the top of every RT class
+  const void* fns[] = {reinterpret_cast<const void*>(&score_topk_kernel<8>),
+                       reinterpret_cast<const void*>(&score_topk_kernel<16>),
+                       reinterpret_cast<const void*>(&score_topk_kernel<32>),
+                       reinterpret_cast<const void*>(&score_topk_kernel<64>)};
+  for (const void* f : fns) {
+    const hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                             16 * 1024 * 8);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 hipError_t launch_score_topk(const Geom& g, const double* A, const double* Bt, int kb,
                              uint8_t* mask, int32_t* list, int list_stride, int32_t* cnt,
                              float* scores, hipStream_t s) {
-  dim3 grid((g.nqb + kScoreRows - 1) / kScoreRows, g.BH);
-  const size_t lds = static_cast<size_t>(kScoreRows) * g.nkb * sizeof(double);
-  hipLaunchKernelGGL(score_topk_kernel, grid, dim3(256), lds, s, A, Bt, g.nqb, g.nkb, kb, mask,
-                     list, list_stride, cnt, scores);
+  const int RT = score_rows(g.nkb);
+  dim3 grid((g.nqb + RT - 1) / RT, g.BH);
+  const size_t lds = static_cast<size_t>(RT) * g.nkb * sizeof(double);
+  const int E = (g.nkb + 63) / 64;
+  if (E <= 8)
+    hipLaunchKernelGGL(score_topk_kernel<8>, grid, dim3(256), lds, s, A, Bt, g.nqb, g.nkb, kb,
+                       mask, list, list_stride, cnt, scores);
+  else if (E <= 16)
+    hipLaunchKernelGGL(score_topk_kernel<16>, grid, dim3(256), lds, s, A, Bt, g.nqb, g.nkb, kb,
+                       mask, list, list_stride, cnt, scores);
+  else if (E <= 32)
+    hipLaunchKernelGGL(score_topk_kernel<32>, grid, dim3(256), lds, s, A, Bt, g.nqb, g.nkb, kb,
+                       mask, list, list_stride, cnt, scores);
+  else
+    hipLaunchKernelGGL(score_topk_kernel<64>, grid, dim3(256), lds, s, A, Bt, g.nqb, g.nkb, kb,
+                       mask, list, list_stride, cnt, scores);
   return hipGetLastError();
 }
 

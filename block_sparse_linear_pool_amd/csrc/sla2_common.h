@@ -81,6 +81,19 @@ __device__ inline void load8<uint16_t>(const uint16_t* p, float* out) {
   }
 }
 
+// ---------------------------------------------------------------- XCD-aware block order
+// The dispatcher hands workgroups to the 8 XCDs round-robin by linear block id. For a
+// (query block, batch*head) grid this maps XCD x to the contiguous logical range
+// [x * total / 8, (x + 1) * total / 8) of (bh, i) in row-major order, so query blocks of one
+// head that run together share that XCD's L2 (their key tiles and h_j gathers).
+__device__ inline void xcd_block(int nqb, int BH, int* i, int* bh) {
+  const int total = nqb * BH;
+  int L = blockIdx.x + gridDim.x * blockIdx.y;
+  if ((total & 7) == 0) L = (L & 7) * (total >> 3) + (L >> 3);
+  *i = L % nqb;
+  *bh = L / nqb;
+}
+
 // ---------------------------------------------------------------- wave helpers
 __device__ inline float wave_max(float v) {
 #pragma unroll
@@ -113,15 +126,18 @@ hipError_t launch_quant(const Geom& g, int dtype, const void* Q, const void* K, 
                         const float* mu32, int8_t* qc, int8_t* kc, uint8_t* vc, float* sq,
                         float* sk, float* sv, int8_t* q_tap, int8_t* k_tap, uint8_t* v_tap,
                         hipStream_t s);
+// h_j is kept transposed ([d_v][d_phi]) in bf16 for linear_out; h_f32 (optional) is the
+// standard orientation [d_phi][d_v].
 hipError_t launch_linear_pre(const Geom& g, int dtype, const void* K, const void* V,
-                             const float* mu32, uint16_t* h_bf16, float* h_f32, float* z,
+                             const float* mu32, uint16_t* ht_bf16, float* h_f32, float* z,
                              float* hpart, float* zpart, hipStream_t s);
+// standard = 0: H_tot^T (for linear_out); 1: H_tot.
 hipError_t launch_linear_total(const Geom& g, const float* hpart, const float* zpart,
-                               float* htot, float* ztot, hipStream_t s);
-hipError_t launch_linear_out(const Geom& g, int dtype, const void* Q, const uint16_t* h_bf16,
-                             const float* z, const float* htot, const float* ztot,
-                             const uint8_t* mask, const int32_t* cnt, float* O_l,
-                             hipStream_t s);
+                               float* htot, float* ztot, int standard, hipStream_t s);
+hipError_t launch_linear_out(const Geom& g, int dtype, const void* Q, const uint16_t* ht_bf16,
+                             const float* z, const float* htot_t, const float* ztot,
+                             const uint8_t* mask, const int32_t* list, int list_stride,
+                             const int32_t* cnt, float* O_l, hipStream_t s);
 hipError_t launch_sparse(const Geom& g, const int8_t* qc, const int8_t* kc, const uint8_t* vc,
                          const float* sq, const float* sk, const float* sv, const int32_t* list,
                          int list_stride, const int32_t* cnt, const float* alpha,

@@ -52,7 +52,9 @@ __global__ __launch_bounds__(256) void sparse_kernel(
     const float* __restrict__ alpha, const float* __restrict__ O_l, float* __restrict__ O,
     float* __restrict__ O_s_tap, int N, int H) {
   __shared__ __attribute__((aligned(16))) int8_t stage[2][2 * kBK * kD];  // [K 8 KB | V^T 8 KB]
-  const int i = blockIdx.x, bh = blockIdx.y, t = threadIdx.x;
+  const int t = threadIdx.x;
+  int i, bh;
+  xcd_block(N / kBQ, static_cast<int>(gridDim.y), &i, &bh);
   const int lane = t & 63, w = t >> 6, g = lane >> 5, l32 = lane & 31;
   const int nqb = N / kBQ, nkb = N / kBK;
   const size_t row = static_cast<size_t>(bh) * nqb + i;
@@ -126,25 +128,19 @@ __global__ __launch_bounds__(256) void sparse_kernel(
     }
     lsum = fmaf(lsum, f, psum);
     m2 = m2new;
-    // ---- acc' <- acc' * (f * s_v,prev / s_v,j) + Phat Vhat_j
+    // ---- acc' <- acc' * (f * s_v,prev / s_v,j) + Phat Vhat_j. A block with s_v = 0 has
+    // all-zero codes, adds nothing and keeps the current units (factor f alone).
     const float svj = sv[tile0 + j];
-    if (svj > 0.f) {
-      const float r = svcur > 0.f ? f * (svcur / svj) : 0.f;
+    const float r = svj > 0.f ? (svcur > 0.f ? f * (svcur / svj) : 0.f) : f;
+    svcur = svj > 0.f ? svj : svcur;
 #pragma unroll
-      for (int td = 0; td < 4; ++td) acc[td] *= r;
-#pragma unroll
-      for (int td = 0; td < 4; ++td) {
-        const int d = 32 * td + l32;
-        const i32x4 v0 = *reinterpret_cast<const i32x4*>(vt + d * kBK + 16 * vchunk_swz(d, 2 * g));
-        const i32x4 v1 = *reinterpret_cast<const i32x4*>(vt + d * kBK + 16 * vchunk_swz(d, 2 * g + 1));
-        const i32x8 a = i32x8{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
-        acc[td] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, pk, acc[td], 0, 0, 0, 127,
-                                                                  0, 127);
-      }
-      svcur = svj;
-    } else {
-#pragma unroll
-      for (int td = 0; td < 4; ++td) acc[td] *= f;
+    for (int td = 0; td < 4; ++td) {
+      const int d = 32 * td + l32;
+      const i32x4 v0 = *reinterpret_cast<const i32x4*>(vt + d * kBK + 16 * vchunk_swz(d, 2 * g));
+      const i32x4 v1 = *reinterpret_cast<const i32x4*>(vt + d * kBK + 16 * vchunk_swz(d, 2 * g + 1));
+      const i32x8 a = i32x8{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+      acc[td] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, pk, acc[td] * r, 0, 0, 0, 127,
+                                                                0, 127);
     }
   }
   // ---- epilogue: O_s = acc' s_v,last / l;  O = alpha O_s + (1 - alpha) O_l
