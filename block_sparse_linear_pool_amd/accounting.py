@@ -22,9 +22,9 @@ MI355X_PEAK = {
 }
 
 KERNELS_FORWARD = ("pool", "colmean", "project", "score_topk", "quant", "linear_pre",
-                   "linear_total", "linear_out", "sparse")
+                   "linear_total", "attn")
 KERNELS_WITH_MASK = ("pool", "colmean", "mask_to_list", "quant", "linear_pre", "linear_total",
-                     "linear_out", "sparse")
+                     "attn")
 
 
 @dataclasses.dataclass
@@ -86,15 +86,17 @@ def kernel_bytes(p: Problem, name: str) -> float:
         return 2 * E * p.in_bytes + BH * p.nkb * (d * d * 2 + d * 4) + BH * np_ * (d * d + d) * 4
     if name == "linear_total":
         return BH * np_ * (d * d + d) * 4 + BH * (d * d + d) * 4
-    if name == "linear_out":
-        return E * p.in_bytes + E * 4 + BH * p.nkb * (d * d * 2 + d * 4) + BH * (d * d + d) * 4
-    if name == "sparse":
-        return E + 2 * E + E * 4 + E * 4        # Qhat, Khat + Vhat once, O_l read, O write
+    if name == "attn":
+        # Qhat, Khat + Vhat once, Q (phi), h_j^T + z_j once, H_tot/Z_tot, O written
+        return (E + 2 * E + E * p.in_bytes + BH * p.nkb * (d * d * 2 + d * 4)
+                + BH * (d * d + d) * 4 + E * 4)
     return 0.0
 
 
 def kernel_flops(p: Problem, name: str) -> float:
-    if name == "sparse":
+    if name == "attn":
+        # INT8/FP8 sparse-branch work only: the linear branch's bf16 phi(Q) H product
+        # (4 N d^2 per head) is reported separately by linear_flops()
         return sparse_flops(p)
     if name == "score_topk":
         return 2.0 * p.BH * p.nqb * p.nkb * p.d
@@ -102,10 +104,8 @@ def kernel_flops(p: Problem, name: str) -> float:
         return 2.0 * p.BH * (p.nqb + p.nkb) * p.d * p.d
     if name == "linear_pre":
         return 2.0 * p.BH * p.N * p.d * p.d
-    if name == "linear_out":
-        return 2.0 * p.BH * p.N * p.d * p.d * 2        # H split into bf16 hi + lo
     return 0.0
 
 
 def kernel_bound(name: str) -> str:
-    return "mfma" if name == "sparse" else "hbm"
+    return "mfma" if name == "attn" else "hbm"

@@ -18,7 +18,7 @@ size_t up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 struct Plan {
   size_t qsum, ksum, mu64, mu32, A, Bt, mask, list, cnt, qc, kc, vc, sq, sk, sv, hbf, z, hpart,
-      zpart, htot, ztot, ol, total;
+      zpart, htot, ztot, total;
 };
 
 Plan make_plan(const Geom& g) {
@@ -52,7 +52,6 @@ Plan make_plan(const Geom& g) {
   p.zpart = take(BH * np * kD * 4);
   p.htot = take(BH * kD * kD * 4);
   p.ztot = take(BH * kD * 4);
-  p.ol = take(BH * N * kD * 4);
   p.total = o;
   return p;
 }
@@ -263,14 +262,26 @@ sla2_status run_branches(const Geom& g, int dt, const void* Q, const void* K, co
                                 at<float>(ws, p.zpart), stream));
   SLA2_LAUNCH(launch_linear_total(g, at<float>(ws, p.hpart), at<float>(ws, p.zpart),
                                   at<float>(ws, p.htot), at<float>(ws, p.ztot), 0, stream));
-  float* ol = tp.O_l ? tp.O_l : at<float>(ws, p.ol);
-  SLA2_LAUNCH(launch_linear_out(g, dt, Q, at<uint16_t>(ws, p.hbf), at<float>(ws, p.z),
-                                at<float>(ws, p.htot), at<float>(ws, p.ztot),
-                                at<uint8_t>(ws, p.mask), at<int32_t>(ws, p.list), list_stride,
-                                at<int32_t>(ws, p.cnt), ol, stream));
-  SLA2_LAUNCH(launch_sparse(g, at<int8_t>(ws, p.qc), at<int8_t>(ws, p.kc), at<uint8_t>(ws, p.vc),
-                            sq, sk, sv, at<int32_t>(ws, p.list), list_stride,
-                            at<int32_t>(ws, p.cnt), alpha, ol, O, tp.O_s, stream));
+  AttnArgs x{};
+  x.qc = at<int8_t>(ws, p.qc);
+  x.kc = at<int8_t>(ws, p.kc);
+  x.vc = at<uint8_t>(ws, p.vc);
+  x.sq = sq;
+  x.sk = sk;
+  x.sv = sv;
+  x.ht_bf16 = at<uint16_t>(ws, p.hbf);
+  x.z = at<float>(ws, p.z);
+  x.htot_t = at<float>(ws, p.htot);
+  x.ztot = at<float>(ws, p.ztot);
+  x.mask = at<uint8_t>(ws, p.mask);
+  x.list = at<int32_t>(ws, p.list);
+  x.list_stride = list_stride;
+  x.cnt = at<int32_t>(ws, p.cnt);
+  x.alpha = alpha;
+  x.O = O;
+  x.O_s_tap = tp.O_s;
+  x.O_l_tap = tp.O_l;
+  SLA2_LAUNCH(launch_attn(g, dt, Q, x, stream));
   return SLA2_OK;
 }
 

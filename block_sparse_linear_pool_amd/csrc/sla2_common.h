@@ -134,13 +134,26 @@ hipError_t launch_linear_pre(const Geom& g, int dtype, const void* K, const void
 // standard = 0: H_tot^T (for linear_out); 1: H_tot.
 hipError_t launch_linear_total(const Geom& g, const float* hpart, const float* zpart,
                                float* htot, float* ztot, int standard, hipStream_t s);
-hipError_t launch_linear_out(const Geom& g, int dtype, const void* Q, const uint16_t* ht_bf16,
-                             const float* z, const float* htot_t, const float* ztot,
-                             const uint8_t* mask, const int32_t* list, int list_stride,
-                             const int32_t* cnt, float* O_l, hipStream_t s);
-hipError_t launch_sparse(const Geom& g, const int8_t* qc, const int8_t* kc, const uint8_t* vc,
-                         const float* sq, const float* sk, const float* sv, const int32_t* list,
-                         int list_stride, const int32_t* cnt, const float* alpha,
-                         const float* O_l, float* O, float* O_s_tap, hipStream_t s);
+// Operands of the fused attention kernel (sparse branch, linear branch, combine).
+struct AttnArgs {
+  const int8_t* qc;            // INT8 Q, row-major
+  const int8_t* kc;            // INT8 K_s tiles
+  const uint8_t* vc;           // E4M3 V^T tiles
+  const float *sq, *sk, *sv;   // scales
+  const uint16_t* ht_bf16;     // h_j^T, bf16
+  const float* z;              // z_j
+  const float* htot_t;         // H_tot^T, fp32
+  const float* ztot;           // Z_tot
+  const uint8_t* mask;         // 0/1 block mask
+  const int32_t* list;         // kept lists
+  int list_stride;
+  const int32_t* cnt;          // kept count per query block
+  const float* alpha;
+  float* O;
+  float* O_s_tap;              // optional
+  float* O_l_tap;              // optional
+};
+hipError_t launch_attn(const Geom& g, int dtype, const void* Q, const AttnArgs& x,
+                       hipStream_t s);
 
 }  // namespace sla2
