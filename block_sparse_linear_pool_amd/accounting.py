@@ -21,10 +21,8 @@ MI355X_PEAK = {
     "fp64_tflops": 78.6,
 }
 
-KERNELS_FORWARD = ("pool", "colmean", "project", "score_topk", "quant", "linear_pre",
-                   "linear_total", "attn")
-KERNELS_WITH_MASK = ("pool", "colmean", "mask_to_list", "quant", "linear_pre", "linear_total",
-                     "attn")
+KERNELS_FORWARD = ("pool", "colmean", "project", "score_topk", "kv_prep", "linear_total", "attn")
+KERNELS_WITH_MASK = ("pool", "colmean", "mask_to_list", "kv_prep", "linear_total", "attn")
 
 
 @dataclasses.dataclass
@@ -79,11 +77,12 @@ def kernel_bytes(p: Problem, name: str) -> float:
     E, BH, d = p.E, p.BH, p.d
     np_ = (p.nkb + 7) // 8
     if name == "pool":
-        return 2 * E * p.in_bytes + BH * (p.nqb + p.nkb) * d * 8
-    if name == "quant":
-        return 3 * E * p.in_bytes + 3 * E + BH * (p.nqb + 2 * p.nkb) * 4
-    if name == "linear_pre":
-        return 2 * E * p.in_bytes + BH * p.nkb * (d * d * 2 + d * 4) + BH * np_ * (d * d + d) * 4
+        # Q, K read; fp64 block sums, INT8 Q codes and scales written
+        return 2 * E * p.in_bytes + BH * (p.nqb + p.nkb) * d * 8 + E + BH * p.nqb * 4
+    if name == "kv_prep":
+        # K, V read; INT8 K_s and E4M3 V codes + scales, bf16 h_j^T, z_j, partials written
+        return (2 * E * p.in_bytes + 2 * E + BH * p.nkb * 8 + BH * p.nkb * (d * d * 2 + d * 4)
+                + BH * np_ * (d * d + d) * 4)
     if name == "linear_total":
         return BH * np_ * (d * d + d) * 4 + BH * (d * d + d) * 4
     if name == "attn":
@@ -102,7 +101,7 @@ def kernel_flops(p: Problem, name: str) -> float:
         return 2.0 * p.BH * p.nqb * p.nkb * p.d
     if name == "project":
         return 2.0 * p.BH * (p.nqb + p.nkb) * p.d * p.d
-    if name == "linear_pre":
+    if name == "kv_prep":
         return 2.0 * p.BH * p.N * p.d * p.d
     return 0.0
 

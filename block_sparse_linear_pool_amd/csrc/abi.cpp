@@ -202,7 +202,8 @@ sla2_status sla2_router(const sla2_shape* shape, const void* Q, const void* K,
   const int kb = sla2_blocks_kept(g.nkb, keep_frac);
   const int dt = shape->dtype == SLA2_FP32 ? 0 : 1;
   Rec rec(nullptr);
-  SLA2_LAUNCH(launch_pool(g, dt, Q, K, at<double>(workspace, p.qsum), at<double>(workspace, p.ksum), stream));
+  SLA2_LAUNCH(launch_pool(g, dt, Q, K, at<double>(workspace, p.qsum), at<double>(workspace, p.ksum),
+                          nullptr, nullptr, nullptr, stream));
   SLA2_LAUNCH(launch_colmean(g, at<double>(workspace, p.ksum), at<double>(workspace, p.mu64),
                              at<float>(workspace, p.mu32), nullptr, stream));
   SLA2_LAUNCH(launch_project(g, at<double>(workspace, p.qsum), at<double>(workspace, p.ksum),
@@ -230,12 +231,17 @@ sla2_status sla2_linear_precompute(const sla2_shape* shape, const void* K, const
   const Plan p = make_plan(g);
   const int dt = shape->dtype == SLA2_FP32 ? 0 : 1;
   Rec rec(nullptr);
-  SLA2_LAUNCH(launch_pool(g, dt, nullptr, K, at<double>(workspace, p.qsum), at<double>(workspace, p.ksum), stream));
+  SLA2_LAUNCH(launch_pool(g, dt, nullptr, K, at<double>(workspace, p.qsum),
+                          at<double>(workspace, p.ksum), nullptr, nullptr, nullptr, stream));
   SLA2_LAUNCH(launch_colmean(g, at<double>(workspace, p.ksum), at<double>(workspace, p.mu64),
                              at<float>(workspace, p.mu32), k_colmean, stream));
-  float* zz = z ? z : at<float>(workspace, p.z);
-  SLA2_LAUNCH(launch_linear_pre(g, dt, K, V, at<float>(workspace, p.mu32), nullptr, h, zz,
-                                at<float>(workspace, p.hpart), at<float>(workspace, p.zpart), stream));
+  KvArgs kv{};
+  kv.mu32 = at<float>(workspace, p.mu32);
+  kv.h_f32 = h;
+  kv.z = z ? z : at<float>(workspace, p.z);
+  kv.hpart = at<float>(workspace, p.hpart);
+  kv.zpart = at<float>(workspace, p.zpart);
+  SLA2_LAUNCH(launch_kv_prep(g, dt, K, V, kv, stream));
   SLA2_LAUNCH(launch_linear_total(g, at<float>(workspace, p.hpart), at<float>(workspace, p.zpart),
                                   h_total, z_total, 1, stream));
   return SLA2_OK;
@@ -243,23 +249,29 @@ sla2_status sla2_linear_precompute(const sla2_shape* shape, const void* K, const
 
 namespace {
 
-// Everything after the block lists exist: quantise, linear branch, sparse branch + combine.
+// Everything after the block lists exist: K, V operands and the linear precompute, H_tot,
+// then the fused sparse branch + linear branch + combine. Q codes come from the pool pass.
 sla2_status run_branches(const Geom& g, int dt, const void* Q, const void* K, const void* V,
                          const float* alpha, float* O, const sla2_taps* taps, void* ws,
                          const Plan& p, int list_stride, Rec& rec, hipStream_t stream) {
   const sla2_taps none{};
   const sla2_taps& tp = taps ? *taps : none;
-  SLA2_LAUNCH(launch_quant(g, dt, Q, K, V, at<float>(ws, p.mu32), at<int8_t>(ws, p.qc),
-                           at<int8_t>(ws, p.kc), at<uint8_t>(ws, p.vc),
-                           tp.s_q ? tp.s_q : at<float>(ws, p.sq), tp.s_k ? tp.s_k : at<float>(ws, p.sk),
-                           tp.s_v ? tp.s_v : at<float>(ws, p.sv), tp.q_codes, tp.k_codes,
-                           tp.v_codes, stream));
   const float* sq = tp.s_q ? tp.s_q : at<float>(ws, p.sq);
-  const float* sk = tp.s_k ? tp.s_k : at<float>(ws, p.sk);
-  const float* sv = tp.s_v ? tp.s_v : at<float>(ws, p.sv);
-  SLA2_LAUNCH(launch_linear_pre(g, dt, K, V, at<float>(ws, p.mu32), at<uint16_t>(ws, p.hbf),
-                                nullptr, at<float>(ws, p.z), at<float>(ws, p.hpart),
-                                at<float>(ws, p.zpart), stream));
+  float* sk = tp.s_k ? tp.s_k : at<float>(ws, p.sk);
+  float* sv = tp.s_v ? tp.s_v : at<float>(ws, p.sv);
+  KvArgs kv{};
+  kv.mu32 = at<float>(ws, p.mu32);
+  kv.kc = at<int8_t>(ws, p.kc);
+  kv.vc = at<uint8_t>(ws, p.vc);
+  kv.sk = sk;
+  kv.sv = sv;
+  kv.k_tap = tp.k_codes;
+  kv.v_tap = tp.v_codes;
+  kv.ht_bf16 = at<uint16_t>(ws, p.hbf);
+  kv.z = at<float>(ws, p.z);
+  kv.hpart = at<float>(ws, p.hpart);
+  kv.zpart = at<float>(ws, p.zpart);
+  SLA2_LAUNCH(launch_kv_prep(g, dt, K, V, kv, stream));
   SLA2_LAUNCH(launch_linear_total(g, at<float>(ws, p.hpart), at<float>(ws, p.zpart),
                                   at<float>(ws, p.htot), at<float>(ws, p.ztot), 0, stream));
   AttnArgs x{};
@@ -314,7 +326,9 @@ sla2_status sla2_forward(const sla2_shape* shape, const void* Q, const void* K, 
   void* ws = workspace;
   Rec rec(taps);
   if (rec.mark(stream) != hipSuccess) return SLA2_ERR_HIP;
-  SLA2_LAUNCH(launch_pool(g, dt, Q, K, at<double>(ws, p.qsum), at<double>(ws, p.ksum), stream));
+  SLA2_LAUNCH(launch_pool(g, dt, Q, K, at<double>(ws, p.qsum), at<double>(ws, p.ksum),
+                          at<int8_t>(ws, p.qc), taps && taps->s_q ? taps->s_q : at<float>(ws, p.sq),
+                          taps ? taps->q_codes : nullptr, stream));
   SLA2_LAUNCH(launch_colmean(g, at<double>(ws, p.ksum), at<double>(ws, p.mu64), at<float>(ws, p.mu32),
                              taps ? taps->k_colmean : nullptr, stream));
   SLA2_LAUNCH(launch_project(g, at<double>(ws, p.qsum), at<double>(ws, p.ksum), at<double>(ws, p.mu64),
@@ -345,7 +359,9 @@ sla2_status sla2_forward_with_mask(const sla2_shape* shape, const void* Q, const
   void* ws = workspace;
   Rec rec(taps);
   if (rec.mark(stream) != hipSuccess) return SLA2_ERR_HIP;
-  SLA2_LAUNCH(launch_pool(g, dt, nullptr, K, at<double>(ws, p.qsum), at<double>(ws, p.ksum), stream));
+  SLA2_LAUNCH(launch_pool(g, dt, Q, K, at<double>(ws, p.qsum), at<double>(ws, p.ksum),
+                          at<int8_t>(ws, p.qc), taps && taps->s_q ? taps->s_q : at<float>(ws, p.sq),
+                          taps ? taps->q_codes : nullptr, stream));
   SLA2_LAUNCH(launch_colmean(g, at<double>(ws, p.ksum), at<double>(ws, p.mu64), at<float>(ws, p.mu32),
                              taps ? taps->k_colmean : nullptr, stream));
   SLA2_LAUNCH(launch_mask_to_list(g, mask, at<uint8_t>(ws, p.mask), at<int32_t>(ws, p.list),

@@ -5,7 +5,8 @@
 // score every block pair, keep the top kb key blocks of every query block.
 //
 // Kernels, in launch order:
-//   pool        one pass over Q and K (HBM-bound): fp64 block sums of Q and K.
+//   pool        one pass over Q and K (HBM-bound): fp64 block sums of Q and K, and (in
+//               the forward) the INT8 codes of Q for the sparse branch.
 //   colmean     mu = colmean(K) from the key-block sums (all blocks have 64 rows), the
 //               K smoothing of §7 note 1 of the second page.
 //   project     A = Qbar Wq, B = (Kbar - mu) Wk in fp64 (Kbar - mu is the mean of K_s).
@@ -19,31 +20,47 @@ namespace sla2 {
 
 // ---------------------------------------------------------------- pool
 // grid (nqb, BH), 256 threads. Thread t: 8 columns starting at 8*(t%16), rows t/16 + 16m.
+// With qc given, the same pass also quantises the 128-row Q block to INT8 (step 2 operands,
+// §2 Q2 of the second page): inv = fl32(127 / amax), code = clamp(rne(fl32(x inv)), +-127),
+// s_q = fl32(amax / 127); an all-zero block gets scale 0 and zero codes.
 template <typename T>
 __global__ __launch_bounds__(256) void pool_kernel(const T* __restrict__ Q,
                                                    const T* __restrict__ K,
                                                    double* __restrict__ qsum,
-                                                   double* __restrict__ ksum, int N) {
+                                                   double* __restrict__ ksum,
+                                                   int8_t* __restrict__ qc,
+                                                   float* __restrict__ sq,
+                                                   int8_t* __restrict__ q_tap, int N) {
   __shared__ double red[3][16][kD + 2];
+  __shared__ float amax_w[4];
   const int i = blockIdx.x, bh = blockIdx.y, t = threadIdx.x;
   const int cg = t & 15, rl = t >> 4;
   const size_t base = (static_cast<size_t>(bh) * N + static_cast<size_t>(i) * kBQ) * kD;
   double aq[8] = {}, ak0[8] = {}, ak1[8] = {};
+  float qv[8][8];
+  float am = 0.f;
 #pragma unroll
   for (int m = 0; m < 8; ++m) {
     const size_t off = base + static_cast<size_t>(rl + 16 * m) * kD + 8 * cg;
-    float v[8];
     if (Q != nullptr) {
-      load8<T>(Q + off, v);
+      load8<T>(Q + off, qv[m]);
 #pragma unroll
-      for (int c = 0; c < 8; ++c) aq[c] += static_cast<double>(v[c]);
+      for (int c = 0; c < 8; ++c) {
+        aq[c] += static_cast<double>(qv[m][c]);
+        am = fmaxf(am, fabsf(qv[m][c]));
+      }
     }
+    float v[8];
     load8<T>(K + off, v);
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
       if (m < 4) ak0[c] += static_cast<double>(v[c]);
       else ak1[c] += static_cast<double>(v[c]);
     }
+  }
+  if (qc != nullptr) {
+    am = wave_max(am);
+    if ((t & 63) == 0) amax_w[t >> 6] = am;
   }
 #pragma unroll
   for (int c = 0; c < 8; ++c) {
@@ -52,6 +69,19 @@ __global__ __launch_bounds__(256) void pool_kernel(const T* __restrict__ Q,
     red[2][rl][8 * cg + c] = ak1[c];
   }
   __syncthreads();
+  if (qc != nullptr) {
+    const float amb = fmaxf(fmaxf(amax_w[0], amax_w[1]), fmaxf(amax_w[2], amax_w[3]));
+    const float inv = amb > 0.f ? 127.0f / amb : 0.f;
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      const size_t off = base + static_cast<size_t>(rl + 16 * m) * kD + 8 * cg;
+      const uint2 w = make_uint2(i8_pack4(qv[m][0], qv[m][1], qv[m][2], qv[m][3], inv),
+                                 i8_pack4(qv[m][4], qv[m][5], qv[m][6], qv[m][7], inv));
+      *reinterpret_cast<uint2*>(qc + off) = w;
+      if (q_tap != nullptr) *reinterpret_cast<uint2*>(q_tap + off) = w;
+    }
+    if (t == 0) sq[static_cast<size_t>(bh) * (N / kBQ) + i] = amb / 127.0f;
+  }
   // threads 0..127: Q column t; 128..255: first key block column t-128; then second.
   {
     const int which = t >> 7, c = t & 127;
@@ -71,16 +101,16 @@ __global__ __launch_bounds__(256) void pool_kernel(const T* __restrict__ Q,
 }
 
 hipError_t launch_pool(const Geom& g, int dtype, const void* Q, const void* K, double* qsum,
-                       double* ksum, hipStream_t s) {
+                       double* ksum, int8_t* qc, float* sq, int8_t* q_tap, hipStream_t s) {
   dim3 grid(g.nqb, g.BH);
   if (dtype == 0)
     hipLaunchKernelGGL(pool_kernel<float>, grid, dim3(256), 0, s,
-                       static_cast<const float*>(Q), static_cast<const float*>(K), qsum, ksum,
-                       g.N);
+                       static_cast<const float*>(Q), static_cast<const float*>(K), qsum, ksum, qc,
+                       sq, q_tap, g.N);
   else
     hipLaunchKernelGGL(pool_kernel<uint16_t>, grid, dim3(256), 0, s,
                        static_cast<const uint16_t*>(Q), static_cast<const uint16_t*>(K), qsum,
-                       ksum, g.N);
+                       ksum, qc, sq, q_tap, g.N);
   return hipGetLastError();
 }
 

@@ -51,6 +51,16 @@ __host__ __device__ inline int vkey_pos(int key) {
   return 32 * g + b;
 }
 
+// bf16 by the native conversion (round to nearest even)
+__device__ inline uint32_t pack_bf16x2(float lo, float hi) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  bf16x2_t v;
+  v[0] = static_cast<__bf16>(lo);
+  v[1] = static_cast<__bf16>(hi);
+  return __builtin_bit_cast(uint32_t, v);
+}
+__device__ inline __bf16 to_bf16(float x) { return static_cast<__bf16>(x); }
+
 __device__ inline float bf16_to_f32(uint16_t b) {
   return __uint_as_float(static_cast<uint32_t>(b) << 16);
 }
@@ -105,11 +115,106 @@ __device__ inline float wave_sum(float v) {
   for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
   return v;
 }
+// Reductions over the 16 lanes of one DPP row (lanes 16r .. 16r + 15); every lane of the
+// row gets the result. Steps: swap neighbours, swap pairs (quad permutes), mirror each half
+// row, mirror the row. Each lane combines the same two operands, so all lanes agree bitwise.
+template <int kCtrl>
+__device__ inline float dpp_mov(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
+                                                               kCtrl, 0xF, 0xF, false));
+}
+__device__ inline float row16_max(float v) {
+  v = fmaxf(v, dpp_mov<0xB1>(v));    // quad_perm [1,0,3,2]
+  v = fmaxf(v, dpp_mov<0x4E>(v));    // quad_perm [2,3,0,1]
+  v = fmaxf(v, dpp_mov<0x141>(v));   // row_half_mirror
+  v = fmaxf(v, dpp_mov<0x140>(v));   // row_mirror
+  return v;
+}
+__device__ inline float row16_sum(float v) {
+  v += dpp_mov<0xB1>(v);
+  v += dpp_mov<0x4E>(v);
+  v += dpp_mov<0x141>(v);
+  v += dpp_mov<0x140>(v);
+  return v;
+}
+
+// ---------------------------------------------------------------- quantisation steps
+// INT8: code = clamp(rne(fl32(x * inv)), -127, 127), inv = fl32(127 / amax) (0 if amax = 0)
+__device__ inline uint32_t i8_code(float x, float inv) {
+  const float y = fminf(fmaxf(rintf(x * inv), -127.f), 127.f);
+  return static_cast<uint32_t>(static_cast<int>(y)) & 0xFFu;
+}
+__device__ inline uint32_t i8_pack4(float a, float b, float c, float d, float inv) {
+  return i8_code(a, inv) | (i8_code(b, inv) << 8) | (i8_code(c, inv) << 16) | (i8_code(d, inv) << 24);
+}
+// OCP E4M3 (round to nearest even) of fl32(x * inv) saturated to +-448, four codes per word
+__device__ inline uint32_t e4m3_pack4(float a, float b, float c, float d, float inv) {
+  const float ya = fminf(fmaxf(a * inv, -448.f), 448.f);
+  const float yb = fminf(fmaxf(b * inv, -448.f), 448.f);
+  const float yc = fminf(fmaxf(c * inv, -448.f), 448.f);
+  const float yd = fminf(fmaxf(d * inv, -448.f), 448.f);
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(ya, yb, 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(yc, yd, w, true);
+  return static_cast<uint32_t>(w);
+}
+
+// Eight consecutive input elements as raw 16-byte words (1 for bf16, 2 for fp32), so a load
+// can be issued early and converted later.
+template <typename T>
+struct Raw8 {
+  i32x4 v[sizeof(T) / 2];
+};
+template <typename T>
+__device__ inline Raw8<T> load_raw8(const T* p) {
+  Raw8<T> r;
+#pragma unroll
+  for (int u = 0; u < static_cast<int>(sizeof(T) / 2); ++u)
+    r.v[u] = *reinterpret_cast<const i32x4*>(p + u * (16 / sizeof(T)));
+  return r;
+}
+// element e (a compile-time constant after unrolling) as fp32
+// (bit casts go through a scalar copy: __builtin_bit_cast of a vector-element lvalue reads
+// element 0 with this compiler)
+__device__ inline float raw8_at(const Raw8<float>& r, int e) {
+  const int i = r.v[e >> 2][e & 3];
+  return __int_as_float(i);
+}
+__device__ inline float raw8_at(const Raw8<uint16_t>& r, int e) {
+  const uint32_t w = static_cast<uint32_t>(r.v[0][e >> 1]);
+  return (e & 1) ? __uint_as_float(w & 0xFFFF0000u) : __uint_as_float(w << 16);
+}
+// bf16 of element e of rows a (low half) and b (high half); bf16 input is moved bit-exactly
+__device__ inline uint32_t raw8_bf16_pair(const Raw8<float>& a, const Raw8<float>& b, int e) {
+  return pack_bf16x2(raw8_at(a, e), raw8_at(b, e));
+}
+__device__ inline uint32_t raw8_bf16_pair(const Raw8<uint16_t>& a, const Raw8<uint16_t>& b, int e) {
+  return __builtin_amdgcn_perm(static_cast<uint32_t>(b.v[0][e >> 1]),
+                               static_cast<uint32_t>(a.v[0][e >> 1]),
+                               (e & 1) ? 0x07060302u : 0x05040100u);
+}
+__device__ inline void raw8_to_f32(const Raw8<float>& r, float* out) {
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int i0 = r.v[0][k], i1 = r.v[1][k];
+    out[k] = __int_as_float(i0);
+    out[4 + k] = __int_as_float(i1);
+  }
+}
+__device__ inline void raw8_to_f32(const Raw8<uint16_t>& r, float* out) {
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const uint32_t w = static_cast<uint32_t>(r.v[0][k]);
+    out[2 * k] = __uint_as_float(w << 16);
+    out[2 * k + 1] = __uint_as_float(w & 0xFFFF0000u);
+  }
+}
 
 // ---------------------------------------------------------------- launchers
 // Each returns hipGetLastError() after enqueueing on `s`.
+// Block sums of Q (128 rows, if Q is given) and K (64 rows) in fp64; with qc given also the
+// INT8 codes of Q (row-major) and their per-block scales sq (q_tap: optional copy of codes).
 hipError_t launch_pool(const Geom& g, int dtype, const void* Q, const void* K, double* qsum,
-                       double* ksum, hipStream_t s);
+                       double* ksum, int8_t* qc, float* sq, int8_t* q_tap, hipStream_t s);
 // one-time per-device set-up (dynamic LDS limit of the scoring kernel)
 hipError_t configure_router();
 hipError_t launch_colmean(const Geom& g, const double* ksum, double* mu64, float* mu32,
@@ -122,16 +227,25 @@ hipError_t launch_score_topk(const Geom& g, const double* A, const double* Bt, i
                              float* scores, hipStream_t s);
 hipError_t launch_mask_to_list(const Geom& g, const uint8_t* mask_in, uint8_t* mask_out,
                                int32_t* list, int32_t* cnt, hipStream_t s);
-hipError_t launch_quant(const Geom& g, int dtype, const void* Q, const void* K, const void* V,
-                        const float* mu32, int8_t* qc, int8_t* kc, uint8_t* vc, float* sq,
-                        float* sk, float* sv, int8_t* q_tap, int8_t* k_tap, uint8_t* v_tap,
-                        hipStream_t s);
-// h_j is kept transposed ([d_v][d_phi]) in bf16 for linear_out; h_f32 (optional) is the
-// standard orientation [d_phi][d_v].
-hipError_t launch_linear_pre(const Geom& g, int dtype, const void* K, const void* V,
-                             const float* mu32, uint16_t* ht_bf16, float* h_f32, float* z,
-                             float* hpart, float* zpart, hipStream_t s);
-// standard = 0: H_tot^T (for linear_out); 1: H_tot.
+// Per key block: INT8 K_s tiles + sk and E4M3 V^T tiles + sv (skipped when kc is null;
+// k_tap / v_tap optional row-major copies of the codes), z_j, h_j^T in bf16 ([d_v][d_phi],
+// optional), h_j in fp32 (standard orientation [d_phi][d_v], optional), and fp32 partial
+// sums of h_j^T and z_j over kKpPerWg blocks.
+struct KvArgs {
+  const float* mu32;
+  int8_t* kc;
+  uint8_t* vc;
+  float *sk, *sv;
+  int8_t* k_tap;
+  uint8_t* v_tap;
+  uint16_t* ht_bf16;
+  float* h_f32;
+  float* z;
+  float *hpart, *zpart;
+};
+hipError_t launch_kv_prep(const Geom& g, int dtype, const void* K, const void* V,
+                          const KvArgs& x, hipStream_t s);
+// standard = 0: H_tot^T (for the attention kernel); 1: H_tot.
 hipError_t launch_linear_total(const Geom& g, const float* hpart, const float* zpart,
                                float* htot, float* ztot, int standard, hipStream_t s);
 // Operands of the fused attention kernel (sparse branch, linear branch, combine).

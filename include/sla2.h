@@ -89,11 +89,11 @@ typedef struct {
     float   *k_colmean; /* [B,H,d] colmean(K) rounded to fp32 */
     /* NULL, or SLA2_MAX_STAGES + 1 caller-created hipEvent_t handles: element 0 is
      * recorded on the stream before the first kernel and element s + 1 after kernel s,
-     * so consecutive pairs time each kernel. Kernel order of sla2_forward: pool,
-     * colmean, project, score_topk, quant, linear_pre, linear_total, attn (sparse
-     * branch, linear branch and combine); of sla2_forward_with_mask: pool, colmean,
-     * mask_to_list, quant, linear_pre, linear_total, attn. Unused trailing events
-     * are not recorded. */
+     * so consecutive pairs time each kernel. Kernel order of sla2_forward: pool
+     * (block sums, INT8 Q), colmean, project, score_topk, kv_prep (INT8 K_s, E4M3 V,
+     * phi(K_s), z_j, h_j), linear_total, attn (sparse branch, linear branch and
+     * combine); of sla2_forward_with_mask: pool, colmean, mask_to_list, kv_prep,
+     * linear_total, attn. Unused trailing events are not recorded. */
     void   **stage_events;
 } sla2_taps;
 
