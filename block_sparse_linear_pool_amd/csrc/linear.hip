@@ -27,6 +27,7 @@ namespace sla2 {
 // 8-byte transposed writes (4 keys of one d per thread) and the 16-byte MFMA operand reads
 // (8 keys of 16 consecutive d) then both spread over all LDS banks.
 constexpr int kRowT = 72;
+constexpr int kRowH = 136;   // bf16 row stride of the staged h_j^T tile
 __device__ inline int tslot(int d, int c) { return d * kRowT + 8 * (c ^ ((d >> 4) & 7)); }
 
 __device__ inline bf16x8 lds_bf16x8(const uint16_t* p) {
@@ -42,24 +43,33 @@ __device__ inline uint32_t lane_off(uint32_t v) {
 }
 
 // ---------------------------------------------------------------- kv_prep
-// grid (ceil(nkb / kKpPerWg), BH), 256 threads. Element work: thread t takes rows
-// 4 (t/16) .. +3 and columns 8 (t%16) .. +7 of the block; a row's 16 threads share one DPP
-// row, so row maxima and sums are DPP reductions. MFMA: wavefront w computes the rows
-// d_phi = 32 w .. 32 w + 31 of h_j for all 128 d_v. The next block's K and V are loaded while
-// the current one is processed.
-template <typename T>
-__global__ __launch_bounds__(256) void kv_prep_kernel(const T* __restrict__ K,
-                                                      const T* __restrict__ V, KvArgs x,
-                                                      int N) {
+// grid (ceil(nkb / kKpPerWg), BH), 512 threads (8 wavefronts, two per SIMD: latency hiding
+// within one workgroup, and the fp32 running sum of h_j is 32 registers per lane).
+// Element work: thread t takes rows 2 (t/16), +1 and columns 8 (t%16) .. +7 of the block; a
+// row's 16 threads share one DPP row, so row maxima and sums are DPP reductions. MFMA:
+// wavefront w computes rows d_phi = 32 (w%4) .. +31, columns d_v = 64 (w/4) .. +63 of h_j.
+// The next block's K and V are loaded while the current one is processed.
+// kMode: 0 forward (codes, scales, h_j^T bf16, z_j, partials), 1 forward with the optional
+// row-major code taps, 2 linear precompute only (z_j, partials, optional fp32 h_j). In mode 0
+// every store is unconditional (single-writer outputs are written by several lanes with the
+// same value), so the wait for the prefetched block at the loop end need not wait for this
+// block's stores as well.
+constexpr int kKvThreads = 512;
+template <typename T, int kMode>
+__global__ __launch_bounds__(kKvThreads) void kv_prep_kernel(const T* __restrict__ K,
+                                                             const T* __restrict__ V, KvArgs x,
+                                                             int N) {
+  constexpr bool quant = kMode != 2;
   __shared__ __attribute__((aligned(16))) uint16_t phit[kD * kRowT];
   __shared__ __attribute__((aligned(16))) uint16_t vtt[kD * kRowT];
-  __shared__ __attribute__((aligned(16))) uint32_t vq[kD * 16];   // E4M3 V^T rows, 16 words each
-  __shared__ float red[2][4];
+  __shared__ __attribute__((aligned(16))) uint16_t vq[kD * 32];   // E4M3 V^T rows of 64 B
+  // h_j^T staged in bf16 for row-contiguous stores ([d_v][d_phi], row stride 272 B)
+  __shared__ __attribute__((aligned(16))) uint16_t hst[kMode != 2 ? kD * kRowH : 8];
+  __shared__ float red[2][8];
   const int p = blockIdx.x, bh = blockIdx.y, t = threadIdx.x;
   const int lane = t & 63, w = t >> 6, g = lane >> 5, l32 = lane & 31;
   const int rg = t >> 4, cg = t & 15;
   const int nkb = N / kBK, np = (nkb + kKpPerWg - 1) / kKpPerWg;
-  const bool quant = x.kc != nullptr;
   float mu[8];
   {
     const f32x4* mp = reinterpret_cast<const f32x4*>(x.mu32 + static_cast<size_t>(bh) * kD + 8 * cg);
@@ -70,36 +80,42 @@ __global__ __launch_bounds__(256) void kv_prep_kernel(const T* __restrict__ K,
       mu[4 + k] = m1[k];
     }
   }
-  f32x16 hsum[4];
-#pragma unroll
-  for (int tb = 0; tb < 4; ++tb) hsum[tb] = f32x16{};
+  const int ta = w & 3, tv = 2 * (w >> 2);   // MFMA tiles: d_phi tile ta, d_v tiles tv, tv + 1
+  f32x16 hsum[2];
+  hsum[0] = f32x16{};
+  hsum[1] = f32x16{};
   float zs = 0.f;
   const int j0 = p * kKpPerWg, j_end = min(nkb, j0 + kKpPerWg);
   const size_t head = static_cast<size_t>(bh) * N;
-  // word of keys 4 rg .. 4 rg + 3 inside a V^T row (key order vkey_at)
-  const int vw = 8 * (rg & 1) + 4 * (rg >> 3) + ((rg >> 1) & 3);
 
   // per-lane offsets are 32-bit against block-uniform base pointers (scalar-base addressing)
-  const uint32_t eoff = static_cast<uint32_t>(4 * rg * kD + 8 * cg);   // element (4 rg, 8 cg)
-  Raw8<T> rk[4], rv[4];
+  const uint32_t eoff = static_cast<uint32_t>(2 * rg * kD + 8 * cg);   // element (2 rg, 8 cg)
+  Raw8<T> rk[2], rv[2];
   {
     const T* kb = K + (head + static_cast<size_t>(j0) * kBK) * kD;
     const T* vb = V + (head + static_cast<size_t>(j0) * kBK) * kD;
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
+    for (int m = 0; m < 2; ++m) {
       rk[m] = load_raw8<T>(kb + (eoff + m * kD));
       rv[m] = load_raw8<T>(vb + (eoff + m * kD));
     }
   }
-  // thread-invariant LDS offsets: for d = 8 cg + e the chunk swizzle (d >> 4) & 7 and the V^T
-  // word swizzle (d >> 3) & 3 do not depend on e, so row e is base + e * row stride
-  const int tw_off = tslot(8 * cg, rg >> 1) + 4 * (rg & 1);
-  uint32_t* vq_row = vq + 8 * cg * 16 + 4 * ((vw >> 2) ^ (cg & 3)) + (vw & 3);
+  // Thread-invariant LDS offsets. For d = 8 cg + e the chunk swizzles (d >> 4) & 7 of the bf16
+  // tiles and (d >> 3) & 3 of the E4M3 tile do not depend on e: row e is base + e * stride.
+  // Keys 2 rg, 2 rg + 1 are chunk rg / 4, elements 2 (rg % 4), +1 of the bf16 rows, and
+  // byte positions vkey_pos(2 rg), +1 of the E4M3 V^T row.
+  const int tw_off = tslot(8 * cg, rg >> 2) + 2 * (rg & 3);
+  const int vpos = vkey_pos(2 * rg);
+  uint16_t* vq_row = vq + 8 * cg * 32 + 8 * ((vpos >> 4) ^ (cg & 3)) + ((vpos & 15) >> 1);
+  // Drain the prologue loads (mu, first block) here: otherwise the wait for mu, which the
+  // loop's first iteration needs, is placed inside the loop as a wait for every outstanding
+  // load, including the prefetch of the next block.
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
   for (int j = j0; j < j_end; ++j) {
-    float xk[4][8];
-    Raw8<T> cv[4];
+    float xk[2][8];
+    Raw8<T> cv[2];
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
+    for (int m = 0; m < 2; ++m) {
       raw8_to_f32(rk[m], xk[m]);
       cv[m] = rv[m];
     }
@@ -107,16 +123,16 @@ __global__ __launch_bounds__(256) void kv_prep_kernel(const T* __restrict__ K,
       const T* kb = K + (head + static_cast<size_t>(j + 1) * kBK) * kD;
       const T* vb = V + (head + static_cast<size_t>(j + 1) * kBK) * kD;
 #pragma unroll
-      for (int m = 0; m < 4; ++m) {
+      for (int m = 0; m < 2; ++m) {
         rk[m] = load_raw8<T>(kb + (eoff + m * kD));
         rv[m] = load_raw8<T>(vb + (eoff + m * kD));
       }
     }
     const size_t blk = static_cast<size_t>(bh) * nkb + j;
     // ---- K_s, block maxima of |K_s| and |V|, row maxima of K_s
-    float ak = 0.f, av = 0.f, rmax[4];
+    float ak = 0.f, av = 0.f, rmax[2];
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
+    for (int m = 0; m < 2; ++m) {
       float mx = -INFINITY;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
@@ -137,43 +153,44 @@ __global__ __launch_bounds__(256) void kv_prep_kernel(const T* __restrict__ K,
     }
     __syncthreads();   // block maxima visible; the previous block's LDS tiles are consumed
     if (quant) {
-      const float akb = fmaxf(fmaxf(red[0][0], red[0][1]), fmaxf(red[0][2], red[0][3]));
-      const float avb = fmaxf(fmaxf(red[1][0], red[1][1]), fmaxf(red[1][2], red[1][3]));
+      float akb = red[0][0], avb = red[1][0];
+#pragma unroll
+      for (int u = 1; u < 8; ++u) {
+        akb = fmaxf(akb, red[0][u]);
+        avb = fmaxf(avb, red[1][u]);
+      }
       const float ik = akb > 0.f ? 127.0f / akb : 0.f;
       int8_t* tile = x.kc + blk * (kBK * kD);
       int8_t* ktap = x.k_tap + (head + static_cast<size_t>(j) * kBK) * kD;
 #pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const int r = 4 * rg + m;
+      for (int m = 0; m < 2; ++m) {
+        const int r = 2 * rg + m;
         const uint2 cw = make_uint2(i8_pack4(xk[m][0], xk[m][1], xk[m][2], xk[m][3], ik),
                                     i8_pack4(xk[m][4], xk[m][5], xk[m][6], xk[m][7], ik));
         *reinterpret_cast<uint2*>(
             tile + lane_off(static_cast<uint32_t>(r * kD + 16 * kchunk_swz(r, cg >> 1) + 8 * (cg & 1)))) = cw;
-        if (x.k_tap) *reinterpret_cast<uint2*>(ktap + lane_off(eoff + m * kD)) = cw;
+        if (kMode == 1 && x.k_tap) *reinterpret_cast<uint2*>(ktap + lane_off(eoff + m * kD)) = cw;
       }
       const float iv = avb > 0.f ? 448.0f / avb : 0.f;
 #pragma unroll
       for (int e = 0; e < 8; ++e)
-        vq_row[16 * e] = e4m3_pack4(raw8_at(cv[0], e), raw8_at(cv[1], e), raw8_at(cv[2], e),
-                                    raw8_at(cv[3], e), iv);
-      if (x.v_tap) {
+        vq_row[32 * e] = static_cast<uint16_t>(e4m3_pack4(raw8_at(cv[0], e), raw8_at(cv[1], e), 0.f, 0.f, iv));
+      if (kMode == 1 && x.v_tap) {
         uint8_t* vtap = x.v_tap + (head + static_cast<size_t>(j) * kBK) * kD;
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
+        for (int m = 0; m < 2; ++m) {
           const uint2 cw = make_uint2(
               e4m3_pack4(raw8_at(cv[m], 0), raw8_at(cv[m], 1), raw8_at(cv[m], 2), raw8_at(cv[m], 3), iv),
               e4m3_pack4(raw8_at(cv[m], 4), raw8_at(cv[m], 5), raw8_at(cv[m], 6), raw8_at(cv[m], 7), iv));
           *reinterpret_cast<uint2*>(vtap + lane_off(eoff + m * kD)) = cw;
         }
       }
-      if (t == 0) {
-        x.sk[blk] = akb / 127.0f;
-        x.sv[blk] = avb / 448.0f;
-      }
+      x.sk[blk] = akb / 127.0f;   // every lane, same value
+      x.sv[blk] = avb / 448.0f;
     }
     // ---- phi(K_s) = softmax over d of every row
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
+    for (int m = 0; m < 2; ++m) {
       float s = 0.f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
@@ -187,19 +204,17 @@ __global__ __launch_bounds__(256) void kv_prep_kernel(const T* __restrict__ K,
     // ---- bf16 phi^T and V^T tiles
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      *reinterpret_cast<uint2*>(phit + tw_off + e * kRowT) =
-          make_uint2(pack_bf16x2(xk[0][e], xk[1][e]), pack_bf16x2(xk[2][e], xk[3][e]));
-      *reinterpret_cast<uint2*>(vtt + tw_off + e * kRowT) =
-          make_uint2(raw8_bf16_pair(cv[0], cv[1], e), raw8_bf16_pair(cv[2], cv[3], e));
+      *reinterpret_cast<uint32_t*>(phit + tw_off + e * kRowT) = pack_bf16x2(xk[0][e], xk[1][e]);
+      *reinterpret_cast<uint32_t*>(vtt + tw_off + e * kRowT) = raw8_bf16_pair(cv[0], cv[1], e);
     }
     __syncthreads();
-    // ---- z_j: thread pair (2 d, 2 d + 1) sums keys 0-31 and 32-63 of phi^T row d
+    // ---- z_j: four threads per d, 16 keys each
     {
-      const int d = t >> 1, hf = t & 1;
+      const int d = t >> 2, qq = t & 3;
       float s = 0.f;
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const i32x4 v = *reinterpret_cast<const i32x4*>(phit + tslot(d, 4 * hf + c));
+      for (int c = 0; c < 2; ++c) {
+        const i32x4 v = *reinterpret_cast<const i32x4*>(phit + tslot(d, 2 * qq + c));
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
           const uint32_t wd = static_cast<uint32_t>(v[k]);
@@ -208,73 +223,91 @@ __global__ __launch_bounds__(256) void kv_prep_kernel(const T* __restrict__ K,
         }
       }
       s += __shfl_xor(s, 1);
-      if (hf == 0) {
-        x.z[blk * kD + lane_off(static_cast<uint32_t>(d))] = s;
-        zs += s;
-      }
+      s += __shfl_xor(s, 2);   // the four lanes of d now hold the same value
+      x.z[blk * kD + lane_off(static_cast<uint32_t>(d))] = s;
+      zs += s;
     }
-    // ---- E4M3 V^T tile to HBM
+    // ---- E4M3 V^T tile to HBM: one 16-byte chunk per thread
     if (quant) {
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int q = t + 256 * u;
-        const int d = q >> 2, ch = q & 3;
-        const i32x4 val = *reinterpret_cast<const i32x4*>(vq + d * 16 + 4 * (ch ^ ((d >> 3) & 3)));
-        *reinterpret_cast<i32x4*>(x.vc + blk * (kBK * kD) +
-                                  lane_off(static_cast<uint32_t>(d * kBK + 16 * vchunk_swz(d, ch)))) = val;
-      }
+      const int d = t >> 2, ch = t & 3;
+      const i32x4 val = *reinterpret_cast<const i32x4*>(vq + d * 32 + 8 * (ch ^ ((d >> 3) & 3)));
+      *reinterpret_cast<i32x4*>(x.vc + blk * (kBK * kD) +
+                                lane_off(static_cast<uint32_t>(d * kBK + 16 * vchunk_swz(d, ch)))) = val;
     }
-    // ---- h_j = phi^T V_j, one 32 x 32 tile at a time: rows d_phi = 32 w + ..., columns
-    // d_v = 32 tb + ...; lane: d_v = 32 tb + l32, register i: d_phi = 32 w + 8 (i/4) + 4 g + i%4
-    uint16_t* htb = x.ht_bf16 + blk * (kD * kD);
+    // ---- h_j = phi^T V_j, one 32 x 32 tile at a time; lane: d_v = 32 tb + l32,
+    // register i: d_phi = 32 ta + 8 (i/4) + 4 g + i%4
     float* hfb = x.h_f32 + blk * (kD * kD);
 #pragma unroll
-    for (int tb = 0; tb < 4; ++tb) {
+    for (int u = 0; u < 2; ++u) {
+      const int tb = tv + u;
       f32x16 acc = f32x16{};
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
         const int c = 2 * s + g;
-        const bf16x8 a = lds_bf16x8(phit + tslot(32 * w + l32, c));
+        const bf16x8 a = lds_bf16x8(phit + tslot(32 * ta + l32, c));
         const bf16x8 b = lds_bf16x8(vtt + tslot(32 * tb + l32, c));
         acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0);
       }
       const int dv = 32 * tb + l32;
 #pragma unroll
       for (int k4 = 0; k4 < 4; ++k4) {
-        const int dphi = 32 * w + 8 * k4 + 4 * g;
-        if (x.ht_bf16)
-          *reinterpret_cast<uint2*>(htb + lane_off(static_cast<uint32_t>(dv * kD + dphi))) =
+        const int dphi = 32 * ta + 8 * k4 + 4 * g;
+        if (kMode != 2)
+          *reinterpret_cast<uint2*>(hst + dv * kRowH + dphi) =
               make_uint2(pack_bf16x2(acc[4 * k4], acc[4 * k4 + 1]),
                          pack_bf16x2(acc[4 * k4 + 2], acc[4 * k4 + 3]));
-        if (x.h_f32) {
+        if (kMode == 2 && x.h_f32) {
 #pragma unroll
           for (int k = 0; k < 4; ++k) hfb[static_cast<uint32_t>((dphi + k) * kD + dv)] = acc[4 * k4 + k];
         }
       }
-      hsum[tb] += acc;
+      hsum[u] += acc;
+    }
+    if (kMode != 2) {
+      // ---- h_j^T to HBM: 2048 chunks of 16 B, a wavefront stores 1 KB contiguous
+      __syncthreads();
+      uint16_t* htb = x.ht_bf16 + blk * (kD * kD);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int q = t + kKvThreads * u;
+        const int row = q >> 4, c16 = q & 15;
+        const i32x4 val = *reinterpret_cast<const i32x4*>(hst + row * kRowH + 8 * c16);
+        *reinterpret_cast<i32x4*>(htb + lane_off(static_cast<uint32_t>(8 * q))) = val;
+      }
     }
   }
   const size_t pbase = (static_cast<size_t>(bh) * np + p) * (kD * kD);
 #pragma unroll
-  for (int tb = 0; tb < 4; ++tb) {
-    const int dv = 32 * tb + l32;
+  for (int u = 0; u < 2; ++u) {
+    const int dv = 32 * (tv + u) + l32;
 #pragma unroll
     for (int k4 = 0; k4 < 4; ++k4)
-      *reinterpret_cast<f32x4*>(x.hpart + pbase + dv * kD + 32 * w + 8 * k4 + 4 * g) =
-          f32x4{hsum[tb][4 * k4], hsum[tb][4 * k4 + 1], hsum[tb][4 * k4 + 2], hsum[tb][4 * k4 + 3]};
+      *reinterpret_cast<f32x4*>(x.hpart + pbase + dv * kD + 32 * ta + 8 * k4 + 4 * g) =
+          f32x4{hsum[u][4 * k4], hsum[u][4 * k4 + 1], hsum[u][4 * k4 + 2], hsum[u][4 * k4 + 3]};
   }
-  if ((t & 1) == 0) x.zpart[(static_cast<size_t>(bh) * np + p) * kD + (t >> 1)] = zs;
+  x.zpart[(static_cast<size_t>(bh) * np + p) * kD + (t >> 2)] = zs;   // four lanes, same value
+}
+
+template <typename T>
+static void launch_kv_prep_t(dim3 grid, const T* K, const T* V, const KvArgs& x, int N,
+                             hipStream_t s) {
+  if (x.kc == nullptr)
+    hipLaunchKernelGGL((kv_prep_kernel<T, 2>), grid, dim3(kKvThreads), 0, s, K, V, x, N);
+  else if (x.k_tap != nullptr || x.v_tap != nullptr)
+    hipLaunchKernelGGL((kv_prep_kernel<T, 1>), grid, dim3(kKvThreads), 0, s, K, V, x, N);
+  else
+    hipLaunchKernelGGL((kv_prep_kernel<T, 0>), grid, dim3(kKvThreads), 0, s, K, V, x, N);
 }
 
 hipError_t launch_kv_prep(const Geom& g, int dtype, const void* K, const void* V,
                           const KvArgs& x, hipStream_t s) {
   dim3 grid((g.nkb + kKpPerWg - 1) / kKpPerWg, g.BH);
   if (dtype == 0)
-    hipLaunchKernelGGL(kv_prep_kernel<float>, grid, dim3(256), 0, s,
-                       static_cast<const float*>(K), static_cast<const float*>(V), x, g.N);
+    launch_kv_prep_t<float>(grid, static_cast<const float*>(K), static_cast<const float*>(V), x,
+                            g.N, s);
   else
-    hipLaunchKernelGGL(kv_prep_kernel<uint16_t>, grid, dim3(256), 0, s,
-                       static_cast<const uint16_t*>(K), static_cast<const uint16_t*>(V), x, g.N);
+    launch_kv_prep_t<uint16_t>(grid, static_cast<const uint16_t*>(K),
+                               static_cast<const uint16_t*>(V), x, g.N, s);
   return hipGetLastError();
 }
 
@@ -282,7 +315,7 @@ hipError_t launch_kv_prep(const Geom& g, int dtype, const void* K, const void* V
 // grid (64, BH), 256 threads: element e = 256 * blockIdx.x + t of H_tot^T (partials are
 // transposed); with `standard` set the result is written as H_tot ([d_phi][d_v]).
 // Eight interleaved accumulators in a fixed order (deterministic), sixteen loads in flight.
-// Block 0 also sums Z_tot.
+// Block 0 also sums Z_tot the same way.
 __global__ __launch_bounds__(256) void linear_total_kernel(const float* __restrict__ hpart,
                                                            const float* __restrict__ zpart,
                                                            float* __restrict__ htot,
@@ -303,9 +336,17 @@ __global__ __launch_bounds__(256) void linear_total_kernel(const float* __restri
   htot[static_cast<size_t>(bh) * (kD * kD) + out] =
       ((s[0] + s[1]) + (s[2] + s[3])) + ((s[4] + s[5]) + (s[6] + s[7]));
   if (blockIdx.x == 0 && t < kD) {
-    float zz = 0.f;
-    for (int q = 0; q < np; ++q) zz += zpart[(static_cast<size_t>(bh) * np + q) * kD + t];
-    ztot[static_cast<size_t>(bh) * kD + t] = zz;
+    const float* zp = zpart + static_cast<size_t>(bh) * np * kD + t;
+    float z8[8] = {};
+    int q = 0;
+#pragma unroll 2
+    for (; q + 8 <= np; q += 8) {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) z8[k] += zp[static_cast<size_t>(q + k) * kD];
+    }
+    for (; q < np; ++q) z8[0] += zp[static_cast<size_t>(q) * kD];
+    ztot[static_cast<size_t>(bh) * kD + t] =
+        ((z8[0] + z8[1]) + (z8[2] + z8[3])) + ((z8[4] + z8[5]) + (z8[6] + z8[7]));
   }
 }
 
