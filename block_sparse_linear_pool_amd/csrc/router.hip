@@ -116,7 +116,8 @@ hipError_t launch_pool(const Geom& g, int dtype, const void* Q, const void* K, d
 
 // ---------------------------------------------------------------- colmean
 // grid BH, 1024 threads: column c = t % 128, part = t / 128 sums key blocks part, part + 8,
-// ...; the 8 parts are combined in a fixed order (deterministic).
+// ...; sixteen accumulators keep sixteen loads in flight; the accumulators and the 8 parts
+// are combined in a fixed order (deterministic).
 __global__ __launch_bounds__(1024) void colmean_kernel(const double* __restrict__ ksum,
                                                        double* __restrict__ mu64,
                                                        float* __restrict__ mu32,
@@ -125,16 +126,20 @@ __global__ __launch_bounds__(1024) void colmean_kernel(const double* __restrict_
   __shared__ double part[8][kD];
   const int bh = blockIdx.x, t = threadIdx.x, c = t & 127, pr = t >> 7;
   const double* p = ksum + static_cast<size_t>(bh) * nkb * kD + c;
-  double a0 = 0.0, a1 = 0.0, a2 = 0.0, a3 = 0.0;
+  double a[16];
+#pragma unroll
+  for (int k = 0; k < 16; ++k) a[k] = 0.0;
   int j = pr;
-  for (; j + 24 < nkb; j += 32) {
-    a0 += p[static_cast<size_t>(j) * kD];
-    a1 += p[static_cast<size_t>(j + 8) * kD];
-    a2 += p[static_cast<size_t>(j + 16) * kD];
-    a3 += p[static_cast<size_t>(j + 24) * kD];
+  for (; j + 8 * 15 < nkb; j += 8 * 16) {
+#pragma unroll
+    for (int k = 0; k < 16; ++k) a[k] += p[static_cast<size_t>(j + 8 * k) * kD];
   }
-  for (; j < nkb; j += 8) a0 += p[static_cast<size_t>(j) * kD];
-  part[pr][c] = (a0 + a1) + (a2 + a3);
+  for (; j < nkb; j += 8) a[0] += p[static_cast<size_t>(j) * kD];
+#pragma unroll
+  for (int w = 8; w >= 1; w >>= 1)
+#pragma unroll
+    for (int k = 0; k < w; ++k) a[k] += a[k + w];
+  part[pr][c] = a[0];
   __syncthreads();
   if (t < kD) {
     double s = 0.0;
@@ -160,25 +165,26 @@ __device__ inline f64x4 mfma_f64(double a, double b, f64x4 c) {
 }
 
 // ---------------------------------------------------------------- project
-// grid (ceil(nqb/64) + ceil(nkb/64), BH), 256 threads. A workgroup takes 64 rows of either
-// Qbar (W = proj_q) or Kbar - mu (W = proj_k); wavefront w the 16-row tile 16w..16w+15,
-// all 128 output columns as eight 16x16 fp64 MFMA tiles.
+// grid (ceil(nqb/16) + ceil(nkb/16), BH), 256 threads. A workgroup takes 16 rows of either
+// Qbar (W = proj_q) or Kbar - mu (W = proj_k); wavefront w the 16x16 fp64 MFMA output tiles
+// of columns 32 w .. 32 w + 31, the two K = 128 chains interleaved, all W values of both
+// tiles loaded up front.
 constexpr int kXPad = kD + 1;
 __global__ __launch_bounds__(256) void project_kernel(
     const double* __restrict__ qsum, const double* __restrict__ ksum,
     const double* __restrict__ mu64, const float* __restrict__ wq, const float* __restrict__ wk,
     double* __restrict__ A, double* __restrict__ Bt, int nqb, int nkb, int H) {
-  __shared__ double xs[64][kXPad];
+  __shared__ double xs[16][kXPad];
   const int bh = blockIdx.y, h = bh % H, t = threadIdx.x;
   const int lane = t & 63, w = t >> 6;
-  const int qwg = (nqb + 63) / 64;
+  const int qwg = (nqb + 15) / 16;
   const bool is_q = static_cast<int>(blockIdx.x) < qwg;
-  const int r0 = 64 * (is_q ? blockIdx.x : blockIdx.x - qwg);
+  const int r0 = 16 * (is_q ? blockIdx.x : blockIdx.x - qwg);
   const int nrows = is_q ? nqb : nkb;
   const double* src = is_q ? qsum + static_cast<size_t>(bh) * nqb * kD
                            : ksum + static_cast<size_t>(bh) * nkb * kD;
   const double scale = is_q ? 1.0 / kBQ : 1.0 / kBK;
-  for (int e = t; e < 64 * kD; e += 256) {
+  for (int e = t; e < 16 * kD; e += 256) {
     const int r = e >> 7, c = e & 127;
     double v = 0.0;
     if (r0 + r < nrows) {
@@ -187,25 +193,30 @@ __global__ __launch_bounds__(256) void project_kernel(
     }
     xs[r][c] = v;
   }
-  __syncthreads();
   const float* W = (is_q ? wq : wk) + static_cast<size_t>(h) * kD * kD;
-  const int ra = 16 * w + (lane & 15), kq = lane >> 4;
-#pragma unroll 1
-  for (int ct = 0; ct < 8; ++ct) {
-    float wv[32];
+  const int ra = lane & 15, kq = lane >> 4;
+  float wv[2][32];
 #pragma unroll
-    for (int s = 0; s < 32; ++s) wv[s] = W[(4 * s + kq) * kD + 16 * ct + (lane & 15)];
-    f64x4 acc = f64x4{0.0, 0.0, 0.0, 0.0};
+  for (int u = 0; u < 2; ++u)
 #pragma unroll
-    for (int s = 0; s < 32; ++s)
-      acc = mfma_f64(xs[ra][4 * s + kq], static_cast<double>(wv[s]), acc);
-    const int col = 16 * ct + (lane & 15);
+    for (int s = 0; s < 32; ++s) wv[u][s] = W[(4 * s + kq) * kD + 32 * w + 16 * u + ra];
+  __syncthreads();
+  f64x4 acc[2] = {f64x4{0.0, 0.0, 0.0, 0.0}, f64x4{0.0, 0.0, 0.0, 0.0}};
+#pragma unroll
+  for (int s = 0; s < 32; ++s) {
+    const double x = xs[ra][4 * s + kq];
+    acc[0] = mfma_f64(x, static_cast<double>(wv[0][s]), acc[0]);
+    acc[1] = mfma_f64(x, static_cast<double>(wv[1][s]), acc[1]);
+  }
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int col = 32 * w + 16 * u + ra;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int r = r0 + 16 * w + kq + 4 * i;
+      const int r = r0 + kq + 4 * i;
       if (r >= nrows) continue;
-      if (is_q) A[(static_cast<size_t>(bh) * nqb + r) * kD + col] = acc[i];
-      else Bt[(static_cast<size_t>(bh) * kD + col) * nkb + r] = acc[i];
+      if (is_q) A[(static_cast<size_t>(bh) * nqb + r) * kD + col] = acc[u][i];
+      else Bt[(static_cast<size_t>(bh) * kD + col) * nkb + r] = acc[u][i];
     }
   }
 }
@@ -213,7 +224,7 @@ __global__ __launch_bounds__(256) void project_kernel(
 hipError_t launch_project(const Geom& g, const double* qsum, const double* ksum,
                           const double* mu64, const float* wq, const float* wk, double* A,
                           double* Bt, hipStream_t s) {
-  dim3 grid((g.nqb + 63) / 64 + (g.nkb + 63) / 64, g.BH);
+  dim3 grid((g.nqb + 15) / 16 + (g.nkb + 15) / 16, g.BH);
   hipLaunchKernelGGL(project_kernel, grid, dim3(256), 0, s, qsum, ksum, mu64, wq, wk, A, Bt,
                      g.nqb, g.nkb, g.H);
   return hipGetLastError();
@@ -235,9 +246,10 @@ __device__ inline int count_below_lane(uint64_t m) {
 __host__ __device__ inline int score_rows(int nkb) { return nkb <= 1024 ? 16 : (nkb <= 2048 ? 8 : 4); }
 
 // Kept set of one row, exact (ties to the lower index), by one wavefront. The row's keys
-// sit in registers, E per lane (key j = lane + 64 e). T = the kb-th largest key, built bit by
-// bit from the top: the largest T with #{key >= T} >= kb, each count a sum of ballot
-// popcounts. Then every key > T is kept, plus the lowest-index keys equal to T up to kb.
+// sit in registers, E per lane (key j = lane + 64 e). T is built bit by bit from the top as
+// the largest T with #{key >= T} >= kb (the kb-th largest key), each count a sum of ballot
+// popcounts, stopping early once #{key >= T} is exactly kb. Then every key > T is kept, plus
+// the lowest-index keys equal to T up to kb.
 template <int E>
 __device__ void select_row(const double* g, int nkb, int kb, int lane, size_t row,
                            int32_t* __restrict__ list, int list_stride,
@@ -254,7 +266,12 @@ __device__ void select_row(const double* g, int nkb, int kb, int lane, size_t ro
     int c = 0;
 #pragma unroll
     for (int e = 0; e < E; ++e) c += __popcll(__ballot(key[e] >= cand));
-    if (c >= kb) T = cand;
+    if (c >= kb) {
+      T = cand;
+      // exactly kb keys >= T: they are the kept set (no key equal to the boundary is left
+      // out), and the code below keeps exactly the keys >= T
+      if (c == kb) break;
+    }
   }
   int gt = 0;
 #pragma unroll
@@ -299,20 +316,39 @@ __global__ __launch_bounds__(256) void score_topk_kernel(
   const double inv_sqrt_d = 0.088388347648318440550;  // 1/sqrt(128)
   const double* bt = Bt + static_cast<size_t>(bh) * kD * nkb;
   const int ntile = (nkb + 15) >> 4, ra = lane & 15, kq = lane >> 4;
-  for (int ct = w; ct < ntile; ct += 4) {
-    const int col = 16 * ct + ra;
-    const bool ok = col < nkb;
-    const double* bc = bt + min(col, nkb - 1);   // unconditional loads, masked below
-    double b[32];
+  // This wavefront's column tiles ct = w, w + 4, ...; step q = tile q / 2, k half q % 2. The B
+  // values of step q + 1 load while step q multiplies (two register buffers); loads are
+  // unconditional at clamped addresses and masked in the product.
+  const int nsteps = 2 * ((ntile - w + 3) / 4);
+  auto bload = [&](double (&dst)[16], int q) {
+    const int qc = min(q, nsteps - 1);
+    const int col = min(16 * (w + 4 * (qc >> 1)) + ra, nkb - 1);
+    const double* bc = bt + col + static_cast<size_t>(64 * (qc & 1) + kq) * nkb;
 #pragma unroll
-    for (int s = 0; s < 32; ++s) b[s] = bc[static_cast<size_t>(4 * s + kq) * nkb];
+    for (int s = 0; s < 16; ++s) dst[s] = bc[static_cast<size_t>(4 * s) * nkb];
+  };
+  if (nsteps > 0) {
+    double bb[2][16];
+    bload(bb[0], 0);
     f64x4 acc = f64x4{0.0, 0.0, 0.0, 0.0};
+    for (int q0 = 0; q0 < nsteps; q0 += 2) {
 #pragma unroll
-    for (int s = 0; s < 32; ++s) acc = mfma_f64(as[ra][4 * s + kq], ok ? b[s] : 0.0, acc);
+      for (int u = 0; u < 2; ++u) {   // u = k half of step q0 + u
+        bload(bb[u ^ 1], q0 + u + 1);
+        const int col = 16 * (w + 4 * (q0 >> 1)) + ra;
+        const bool ok = col < nkb;
+        if (u == 0) acc = f64x4{0.0, 0.0, 0.0, 0.0};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = kq + 4 * i;
-      if (ok && r < RT) G[r * nkb + col] = acc[i] * inv_sqrt_d + 0.0;  // +0.0: no -0
+        for (int s = 0; s < 16; ++s)
+          acc = mfma_f64(as[ra][4 * (16 * u + s) + kq], ok ? bb[u][s] : 0.0, acc);
+        if (u == 1) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int r = kq + 4 * i;
+            if (ok && r < RT) G[r * nkb + col] = acc[i] * inv_sqrt_d + 0.0;  // +0.0: no -0
+          }
+        }
+      }
     }
   }
   __syncthreads();
