@@ -34,9 +34,41 @@ def parse():
     ap.add_argument("--cpu-heads", type=int, default=2, help="heads in the CPU-oracle sample")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--traffic", default=None,
-                    help="JSON with measured HBM bytes per launch of the dominant kernel")
+                    help="JSON with the measured HBM bytes per launch of the dominant kernel "
+                         "(default: profiles/<kernel>_traffic_<workload>.json when present)")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="only run plain device copies of a known size (the calibration "
+                         "workload for the FETCH_SIZE / WRITE_SIZE counters), then exit")
     ap.add_argument("--quiet", action="store_true")
     return ap.parse_args()
+
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+COPY_PROBE_BYTES = 256 * 1024 * 1024
+
+
+def kernel_source_hash(kernel):
+    """sha256 of the sources a kernel is built from: a stored traffic figure is void once
+    they change."""
+    import hashlib
+    files = {"attn": ["sparse.hip"], "kv_prep": ["linear.hip"], "linear_total": ["linear.hip"]}
+    files = files.get(kernel, ["router.hip"]) + ["sla2_common.h"]
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(HERE, "block_sparse_linear_pool_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def copy_probe():
+    """Ten device-to-device copies of COPY_PROBE_BYTES (read that many, write that many)."""
+    import torch
+    src = torch.ones(COPY_PROBE_BYTES // 4, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(10):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": COPY_PROBE_BYTES, "copies": 10}), flush=True)
 
 
 def log(args, *a):
@@ -75,6 +107,9 @@ def cpu_baseline(args, w, q, k, v, wq, wk, alpha, keep, acc):
 
 def main():
     args = parse()
+    if args.copy_probe:
+        copy_probe()
+        return
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
               "(the forward shards by (batch, head); see the design notes)", file=sys.stderr)
@@ -151,10 +186,12 @@ def main():
         achieved = acc.kernel_bytes(prob, dom) / t_dom / 1e9
         peak, unit = acc.MI355X_PEAK["hbm_gbs"], "GB/s"
     traffic = None
-    if args.traffic and os.path.exists(args.traffic):
-        with open(args.traffic) as f:
+    tpath = args.traffic or os.path.join(HERE, "profiles", f"{dom}_traffic_{w.name}.json")
+    if os.path.exists(tpath):
+        with open(tpath) as f:
             tr = json.load(f)
-        if tr.get("kernel") == dom and tr.get("workload") == w.name:
+        if (tr.get("kernel") == dom and tr.get("workload") == w.name and tr.get("keep_frac") == keep
+                and tr.get("source_sha256") == kernel_source_hash(dom)):
             traffic = tr.get("bytes_per_launch")
     roofline = {"kernel": dom, "bound": acc.kernel_bound(dom), "achieved": round(achieved, 2),
                 "peak": peak, "unit": unit, "frac": round(achieved / peak, 4),

@@ -115,46 +115,42 @@ hipError_t launch_pool(const Geom& g, int dtype, const void* Q, const void* K, d
 }
 
 // ---------------------------------------------------------------- colmean
-// grid BH, 1024 threads: column c = t % 128, part = t / 128 sums key blocks part, part + 8,
-// ...; sixteen accumulators keep sixteen loads in flight; the accumulators and the 8 parts
-// are combined in a fixed order (deterministic).
-__global__ __launch_bounds__(1024) void colmean_kernel(const double* __restrict__ ksum,
-                                                       double* __restrict__ mu64,
-                                                       float* __restrict__ mu32,
-                                                       float* __restrict__ mu32_tap, int nkb,
-                                                       int N) {
-  __shared__ double part[8][kD];
-  const int bh = blockIdx.x, t = threadIdx.x, c = t & 127, pr = t >> 7;
+// grid (8, BH), 256 threads: workgroup x takes columns 16 x .. 16 x + 15 of head bh; thread t
+// sums column 16 x + t % 16 over key blocks t / 16, t / 16 + 16, ... with four accumulators
+// (four loads in flight); the 16 partial sums are combined in a fixed order (deterministic).
+__global__ __launch_bounds__(256) void colmean_kernel(const double* __restrict__ ksum,
+                                                      double* __restrict__ mu64,
+                                                      float* __restrict__ mu32,
+                                                      float* __restrict__ mu32_tap, int nkb,
+                                                      int N) {
+  __shared__ double part[16][17];
+  const int bh = blockIdx.y, t = threadIdx.x, c = 16 * blockIdx.x + (t & 15), sl = t >> 4;
   const double* p = ksum + static_cast<size_t>(bh) * nkb * kD + c;
-  double a[16];
-#pragma unroll
-  for (int k = 0; k < 16; ++k) a[k] = 0.0;
-  int j = pr;
-  for (; j + 8 * 15 < nkb; j += 8 * 16) {
-#pragma unroll
-    for (int k = 0; k < 16; ++k) a[k] += p[static_cast<size_t>(j + 8 * k) * kD];
+  double a0 = 0.0, a1 = 0.0, a2 = 0.0, a3 = 0.0;
+  int j = sl;
+  for (; j + 48 < nkb; j += 64) {
+    a0 += p[static_cast<size_t>(j) * kD];
+    a1 += p[static_cast<size_t>(j + 16) * kD];
+    a2 += p[static_cast<size_t>(j + 32) * kD];
+    a3 += p[static_cast<size_t>(j + 48) * kD];
   }
-  for (; j < nkb; j += 8) a[0] += p[static_cast<size_t>(j) * kD];
-#pragma unroll
-  for (int w = 8; w >= 1; w >>= 1)
-#pragma unroll
-    for (int k = 0; k < w; ++k) a[k] += a[k + w];
-  part[pr][c] = a[0];
+  for (; j < nkb; j += 16) a0 += p[static_cast<size_t>(j) * kD];
+  part[sl][t & 15] = (a0 + a1) + (a2 + a3);
   __syncthreads();
-  if (t < kD) {
+  if (t < 16) {
     double s = 0.0;
-    for (int q = 0; q < 8; ++q) s += part[q][t];
+    for (int q = 0; q < 16; ++q) s += part[q][t];
     const double mu = s / static_cast<double>(N);
-    mu64[bh * kD + t] = mu;
-    mu32[bh * kD + t] = static_cast<float>(mu);
-    if (mu32_tap) mu32_tap[bh * kD + t] = static_cast<float>(mu);
+    mu64[bh * kD + c] = mu;
+    mu32[bh * kD + c] = static_cast<float>(mu);
+    if (mu32_tap) mu32_tap[bh * kD + c] = static_cast<float>(mu);
   }
 }
 
 hipError_t launch_colmean(const Geom& g, const double* ksum, double* mu64, float* mu32,
                           float* mu32_tap, hipStream_t s) {
-  hipLaunchKernelGGL(colmean_kernel, dim3(g.BH), dim3(1024), 0, s, ksum, mu64, mu32, mu32_tap,
-                     g.nkb, g.N);
+  hipLaunchKernelGGL(colmean_kernel, dim3(kD / 16, g.BH), dim3(256), 0, s, ksum, mu64, mu32,
+                     mu32_tap, g.nkb, g.N);
   return hipGetLastError();
 }
 
