@@ -48,7 +48,11 @@ __device__ inline uint32_t lane_off(uint32_t v) {
 // Element work: thread t takes rows 2 (t/16), +1 and columns 8 (t%16) .. +7 of the block; a
 // row's 16 threads share one DPP row, so row maxima and sums are DPP reductions. MFMA:
 // wavefront w computes rows d_phi = 32 (w%4) .. +31, columns d_v = 64 (w/4) .. +63 of h_j.
-// The next block's K and V are loaded while the current one is processed.
+// The next block's K and V are loaded while the current one is processed. Every LDS staging
+// area is double-buffered by block parity, so one barrier per block suffices: before it,
+// block j's block maxima, phi^T and V^T tiles are written; after it, the codes that need the
+// maxima, z_j and h_j of block j are computed, and the E4M3 V^T and bf16 h_j^T tiles of block
+// j - 1 (staged in the other buffers) are copied to HBM.
 // kMode: 0 forward (codes, scales, h_j^T bf16, z_j, partials), 1 forward with the optional
 // row-major code taps, 2 linear precompute only (z_j, partials, optional fp32 h_j). In mode 0
 // every store is unconditional (single-writer outputs are written by several lanes with the
@@ -60,12 +64,13 @@ __global__ __launch_bounds__(kKvThreads) void kv_prep_kernel(const T* __restrict
                                                              const T* __restrict__ V, KvArgs x,
                                                              int N) {
   constexpr bool quant = kMode != 2;
-  __shared__ __attribute__((aligned(16))) uint16_t phit[kD * kRowT];
-  __shared__ __attribute__((aligned(16))) uint16_t vtt[kD * kRowT];
-  __shared__ __attribute__((aligned(16))) uint16_t vq[kD * 32];   // E4M3 V^T rows of 64 B
+  constexpr int kNb = 2;   // staging buffers
+  __shared__ __attribute__((aligned(16))) uint16_t phit[kNb][kD * kRowT];
+  __shared__ __attribute__((aligned(16))) uint16_t vtt[kNb][kD * kRowT];
+  __shared__ __attribute__((aligned(16))) uint16_t vq[quant ? kNb : 1][quant ? kD * 32 : 8];  // E4M3 V^T rows
   // h_j^T staged in bf16 for row-contiguous stores ([d_v][d_phi], row stride 272 B)
-  __shared__ __attribute__((aligned(16))) uint16_t hst[kMode != 2 ? kD * kRowH : 8];
-  __shared__ float red[2][8];
+  __shared__ __attribute__((aligned(16))) uint16_t hst[quant ? kNb : 1][quant ? kD * kRowH : 8];
+  __shared__ float red[kNb][2][8];
   const int p = blockIdx.x, bh = blockIdx.y, t = threadIdx.x;
   const int lane = t & 63, w = t >> 6, g = lane >> 5, l32 = lane & 31;
   const int rg = t >> 4, cg = t & 15;
@@ -106,17 +111,36 @@ __global__ __launch_bounds__(kKvThreads) void kv_prep_kernel(const T* __restrict
   // byte positions vkey_pos(2 rg), +1 of the E4M3 V^T row.
   const int tw_off = tslot(8 * cg, rg >> 2) + 2 * (rg & 3);
   const int vpos = vkey_pos(2 * rg);
-  uint16_t* vq_row = vq + 8 * cg * 32 + 8 * ((vpos >> 4) ^ (cg & 3)) + ((vpos & 15) >> 1);
+  const int vq_off = 8 * cg * 32 + 8 * ((vpos >> 4) ^ (cg & 3)) + ((vpos & 15) >> 1);
+  // copy of the staged E4M3 V^T and bf16 h_j^T tiles of block jb (buffer b) to HBM
+  auto copy_out = [&](int jb, int b) {
+    const size_t blk = static_cast<size_t>(bh) * nkb + jb;
+    {
+      const int d = t >> 2, ch = t & 3;
+      const i32x4 val = *reinterpret_cast<const i32x4*>(&vq[b][d * 32 + 8 * (ch ^ ((d >> 3) & 3))]);
+      *reinterpret_cast<i32x4*>(x.vc + blk * (kBK * kD) +
+                                lane_off(static_cast<uint32_t>(d * kBK + 16 * vchunk_swz(d, ch)))) = val;
+    }
+    uint16_t* htb = x.ht_bf16 + blk * (kD * kD);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int q = t + kKvThreads * u;
+      const int row = q >> 4, c16 = q & 15;
+      const i32x4 val = *reinterpret_cast<const i32x4*>(&hst[b][row * kRowH + 8 * c16]);
+      *reinterpret_cast<i32x4*>(htb + lane_off(static_cast<uint32_t>(8 * q))) = val;
+    }
+  };
   // Drain the prologue loads (mu, first block) here: otherwise the wait for mu, which the
   // loop's first iteration needs, is placed inside the loop as a wait for every outstanding
   // load, including the prefetch of the next block.
   __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
   for (int j = j0; j < j_end; ++j) {
-    float xk[2][8];
+    const int b = (j - j0) & 1;
+    float ks[2][8];
     Raw8<T> cv[2];
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
-      raw8_to_f32(rk[m], xk[m]);
+      raw8_to_f32(rk[m], ks[m]);
       cv[m] = rv[m];
     }
     if (j + 1 < j_end) {
@@ -136,10 +160,10 @@ __global__ __launch_bounds__(kKvThreads) void kv_prep_kernel(const T* __restrict
       float mx = -INFINITY;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        xk[m][e] = xk[m][e] - mu[e];
-        ak = fmaxf(ak, fabsf(xk[m][e]));
+        ks[m][e] = ks[m][e] - mu[e];
+        ak = fmaxf(ak, fabsf(ks[m][e]));
         av = fmaxf(av, fabsf(raw8_at(cv[m], e)));
-        mx = fmaxf(mx, xk[m][e]);
+        mx = fmaxf(mx, ks[m][e]);
       }
       rmax[m] = row16_max(mx);
     }
@@ -147,17 +171,38 @@ __global__ __launch_bounds__(kKvThreads) void kv_prep_kernel(const T* __restrict
       ak = wave_max(ak);
       av = wave_max(av);
       if (lane == 0) {
-        red[0][w] = ak;
-        red[1][w] = av;
+        red[b][0][w] = ak;
+        red[b][1][w] = av;
       }
     }
-    __syncthreads();   // block maxima visible; the previous block's LDS tiles are consumed
+    // ---- phi(K_s) = softmax over d of every row, to the bf16 phi^T tile; V^T tile
+    {
+      float ex[2][8];
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        float sm = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          ex[m][e] = __expf(ks[m][e] - rmax[m]);
+          sm += ex[m][e];
+        }
+        const float inv = 1.0f / row16_sum(sm);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ex[m][e] *= inv;
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        *reinterpret_cast<uint32_t*>(&phit[b][tw_off + e * kRowT]) = pack_bf16x2(ex[0][e], ex[1][e]);
+        *reinterpret_cast<uint32_t*>(&vtt[b][tw_off + e * kRowT]) = raw8_bf16_pair(cv[0], cv[1], e);
+      }
+    }
+    __syncthreads();   // block j's maxima and tiles visible; block j - 1's staging complete
     if (quant) {
-      float akb = red[0][0], avb = red[1][0];
+      float akb = red[b][0][0], avb = red[b][1][0];
 #pragma unroll
       for (int u = 1; u < 8; ++u) {
-        akb = fmaxf(akb, red[0][u]);
-        avb = fmaxf(avb, red[1][u]);
+        akb = fmaxf(akb, red[b][0][u]);
+        avb = fmaxf(avb, red[b][1][u]);
       }
       const float ik = akb > 0.f ? 127.0f / akb : 0.f;
       int8_t* tile = x.kc + blk * (kBK * kD);
@@ -165,8 +210,8 @@ __global__ __launch_bounds__(kKvThreads) void kv_prep_kernel(const T* __restrict
 #pragma unroll
       for (int m = 0; m < 2; ++m) {
         const int r = 2 * rg + m;
-        const uint2 cw = make_uint2(i8_pack4(xk[m][0], xk[m][1], xk[m][2], xk[m][3], ik),
-                                    i8_pack4(xk[m][4], xk[m][5], xk[m][6], xk[m][7], ik));
+        const uint2 cw = make_uint2(i8_pack4(ks[m][0], ks[m][1], ks[m][2], ks[m][3], ik),
+                                    i8_pack4(ks[m][4], ks[m][5], ks[m][6], ks[m][7], ik));
         *reinterpret_cast<uint2*>(
             tile + lane_off(static_cast<uint32_t>(r * kD + 16 * kchunk_swz(r, cg >> 1) + 8 * (cg & 1)))) = cw;
         if (kMode == 1 && x.k_tap) *reinterpret_cast<uint2*>(ktap + lane_off(eoff + m * kD)) = cw;
@@ -174,7 +219,8 @@ __global__ __launch_bounds__(kKvThreads) void kv_prep_kernel(const T* __restrict
       const float iv = avb > 0.f ? 448.0f / avb : 0.f;
 #pragma unroll
       for (int e = 0; e < 8; ++e)
-        vq_row[32 * e] = static_cast<uint16_t>(e4m3_pack4(raw8_at(cv[0], e), raw8_at(cv[1], e), 0.f, 0.f, iv));
+        vq[b][vq_off + 32 * e] =
+            static_cast<uint16_t>(e4m3_pack4(raw8_at(cv[0], e), raw8_at(cv[1], e), 0.f, 0.f, iv));
       if (kMode == 1 && x.v_tap) {
         uint8_t* vtap = x.v_tap + (head + static_cast<size_t>(j) * kBK) * kD;
 #pragma unroll
@@ -187,52 +233,26 @@ __global__ __launch_bounds__(kKvThreads) void kv_prep_kernel(const T* __restrict
       }
       x.sk[blk] = akb / 127.0f;   // every lane, same value
       x.sv[blk] = avb / 448.0f;
+      if (j > j0) copy_out(j - 1, b ^ 1);
     }
-    // ---- phi(K_s) = softmax over d of every row
-#pragma unroll
-    for (int m = 0; m < 2; ++m) {
-      float s = 0.f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        xk[m][e] = __expf(xk[m][e] - rmax[m]);
-        s += xk[m][e];
-      }
-      const float inv = 1.0f / row16_sum(s);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) xk[m][e] *= inv;
-    }
-    // ---- bf16 phi^T and V^T tiles
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      *reinterpret_cast<uint32_t*>(phit + tw_off + e * kRowT) = pack_bf16x2(xk[0][e], xk[1][e]);
-      *reinterpret_cast<uint32_t*>(vtt + tw_off + e * kRowT) = raw8_bf16_pair(cv[0], cv[1], e);
-    }
-    __syncthreads();
     // ---- z_j: four threads per d, 16 keys each
     {
       const int d = t >> 2, qq = t & 3;
-      float s = 0.f;
+      float sz = 0.f;
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
-        const i32x4 v = *reinterpret_cast<const i32x4*>(phit + tslot(d, 2 * qq + c));
+        const i32x4 v = *reinterpret_cast<const i32x4*>(&phit[b][tslot(d, 2 * qq + c)]);
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
           const uint32_t wd = static_cast<uint32_t>(v[k]);
-          s += __uint_as_float(wd << 16);
-          s += __uint_as_float(wd & 0xFFFF0000u);
+          sz += __uint_as_float(wd << 16);
+          sz += __uint_as_float(wd & 0xFFFF0000u);
         }
       }
-      s += __shfl_xor(s, 1);
-      s += __shfl_xor(s, 2);   // the four lanes of d now hold the same value
-      x.z[blk * kD + lane_off(static_cast<uint32_t>(d))] = s;
-      zs += s;
-    }
-    // ---- E4M3 V^T tile to HBM: one 16-byte chunk per thread
-    if (quant) {
-      const int d = t >> 2, ch = t & 3;
-      const i32x4 val = *reinterpret_cast<const i32x4*>(vq + d * 32 + 8 * (ch ^ ((d >> 3) & 3)));
-      *reinterpret_cast<i32x4*>(x.vc + blk * (kBK * kD) +
-                                lane_off(static_cast<uint32_t>(d * kBK + 16 * vchunk_swz(d, ch)))) = val;
+      sz += __shfl_xor(sz, 1);
+      sz += __shfl_xor(sz, 2);   // the four lanes of d now hold the same value
+      x.z[blk * kD + lane_off(static_cast<uint32_t>(d))] = sz;
+      zs += sz;
     }
     // ---- h_j = phi^T V_j, one 32 x 32 tile at a time; lane: d_v = 32 tb + l32,
     // register i: d_phi = 32 ta + 8 (i/4) + 4 g + i%4
@@ -244,16 +264,16 @@ __global__ __launch_bounds__(kKvThreads) void kv_prep_kernel(const T* __restrict
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
         const int c = 2 * s + g;
-        const bf16x8 a = lds_bf16x8(phit + tslot(32 * ta + l32, c));
-        const bf16x8 b = lds_bf16x8(vtt + tslot(32 * tb + l32, c));
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0);
+        const bf16x8 a = lds_bf16x8(&phit[b][tslot(32 * ta + l32, c)]);
+        const bf16x8 bb = lds_bf16x8(&vtt[b][tslot(32 * tb + l32, c)]);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bb, acc, 0, 0, 0);
       }
       const int dv = 32 * tb + l32;
 #pragma unroll
       for (int k4 = 0; k4 < 4; ++k4) {
         const int dphi = 32 * ta + 8 * k4 + 4 * g;
         if (kMode != 2)
-          *reinterpret_cast<uint2*>(hst + dv * kRowH + dphi) =
+          *reinterpret_cast<uint2*>(&hst[b][dv * kRowH + dphi]) =
               make_uint2(pack_bf16x2(acc[4 * k4], acc[4 * k4 + 1]),
                          pack_bf16x2(acc[4 * k4 + 2], acc[4 * k4 + 3]));
         if (kMode == 2 && x.h_f32) {
@@ -263,18 +283,10 @@ __global__ __launch_bounds__(kKvThreads) void kv_prep_kernel(const T* __restrict
       }
       hsum[u] += acc;
     }
-    if (kMode != 2) {
-      // ---- h_j^T to HBM: 2048 chunks of 16 B, a wavefront stores 1 KB contiguous
-      __syncthreads();
-      uint16_t* htb = x.ht_bf16 + blk * (kD * kD);
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int q = t + kKvThreads * u;
-        const int row = q >> 4, c16 = q & 15;
-        const i32x4 val = *reinterpret_cast<const i32x4*>(hst + row * kRowH + 8 * c16);
-        *reinterpret_cast<i32x4*>(htb + lane_off(static_cast<uint32_t>(8 * q))) = val;
-      }
-    }
+  }
+  if (quant && j_end > j0) {
+    __syncthreads();   // the last block's staging complete
+    copy_out(j_end - 1, (j_end - 1 - j0) & 1);
   }
   const size_t pbase = (static_cast<size_t>(bh) * np + p) * (kD * kD);
 #pragma unroll
