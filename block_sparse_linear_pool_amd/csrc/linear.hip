@@ -324,48 +324,46 @@ hipError_t launch_kv_prep(const Geom& g, int dtype, const void* K, const void* V
 }
 
 // ---------------------------------------------------------------- linear_total
-// grid (64, BH), 256 threads: element e = 256 * blockIdx.x + t of H_tot^T (partials are
-// transposed); with `standard` set the result is written as H_tot ([d_phi][d_v]).
-// Eight interleaved accumulators in a fixed order (deterministic), sixteen loads in flight.
-// Block 0 also sums Z_tot the same way.
+// grid (kD * kD / 64 + 2, BH), 256 threads. Workgroup x < 256 reduces elements 64 x .. 64 x + 63
+// of H_tot^T (partials are transposed; with `standard` set the result is written as H_tot,
+// [d_phi][d_v]); workgroups 256, 257 reduce Z_tot columns 0-63, 64-127. Wavefront w sums
+// partials w, w + 4, ... (four accumulators, all loads in flight); the four wavefront sums
+// are combined in a fixed order (deterministic).
 __global__ __launch_bounds__(256) void linear_total_kernel(const float* __restrict__ hpart,
                                                            const float* __restrict__ zpart,
                                                            float* __restrict__ htot,
                                                            float* __restrict__ ztot, int np,
                                                            int standard) {
-  const int bh = blockIdx.y, t = threadIdx.x;
-  const int e = 256 * blockIdx.x + t;
-  const float* hp = hpart + static_cast<size_t>(bh) * np * (kD * kD) + e;
-  float s[8] = {};
-  int p = 0;
-#pragma unroll 2
-  for (; p + 8 <= np; p += 8) {
+  __shared__ float red[4][64];
+  const int bh = blockIdx.y, t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const bool is_z = blockIdx.x >= kD * kD / 64;
+  const int e = is_z ? 64 * (blockIdx.x - kD * kD / 64) + lane : 64 * blockIdx.x + lane;
+  const int stride = is_z ? kD : kD * kD;
+  const float* src = (is_z ? zpart : hpart) + static_cast<size_t>(bh) * np * stride + e;
+  float a[4] = {0.f, 0.f, 0.f, 0.f};
+  int p = w;
+  for (; p + 12 < np; p += 16) {
 #pragma unroll
-    for (int k = 0; k < 8; ++k) s[k] += hp[static_cast<size_t>(p + k) * (kD * kD)];
+    for (int k = 0; k < 4; ++k) a[k] += src[static_cast<size_t>(p + 4 * k) * stride];
   }
-  for (; p < np; ++p) s[0] += hp[static_cast<size_t>(p) * (kD * kD)];
-  const int out = standard ? (e & (kD - 1)) * kD + (e >> 7) : e;
-  htot[static_cast<size_t>(bh) * (kD * kD) + out] =
-      ((s[0] + s[1]) + (s[2] + s[3])) + ((s[4] + s[5]) + (s[6] + s[7]));
-  if (blockIdx.x == 0 && t < kD) {
-    const float* zp = zpart + static_cast<size_t>(bh) * np * kD + t;
-    float z8[8] = {};
-    int q = 0;
-#pragma unroll 2
-    for (; q + 8 <= np; q += 8) {
-#pragma unroll
-      for (int k = 0; k < 8; ++k) z8[k] += zp[static_cast<size_t>(q + k) * kD];
+  for (; p < np; p += 4) a[0] += src[static_cast<size_t>(p) * stride];
+  red[w][lane] = (a[0] + a[1]) + (a[2] + a[3]);
+  __syncthreads();
+  if (w == 0) {
+    const float v = (red[0][lane] + red[1][lane]) + (red[2][lane] + red[3][lane]);
+    if (is_z) {
+      ztot[static_cast<size_t>(bh) * kD + e] = v;
+    } else {
+      const int out = standard ? (e & (kD - 1)) * kD + (e >> 7) : e;
+      htot[static_cast<size_t>(bh) * (kD * kD) + out] = v;
     }
-    for (; q < np; ++q) z8[0] += zp[static_cast<size_t>(q) * kD];
-    ztot[static_cast<size_t>(bh) * kD + t] =
-        ((z8[0] + z8[1]) + (z8[2] + z8[3])) + ((z8[4] + z8[5]) + (z8[6] + z8[7]));
   }
 }
 
 hipError_t launch_linear_total(const Geom& g, const float* hpart, const float* zpart,
                                float* htot, float* ztot, int standard, hipStream_t s) {
   const int np = (g.nkb + kKpPerWg - 1) / kKpPerWg;
-  hipLaunchKernelGGL(linear_total_kernel, dim3(kD * kD / 256, g.BH), dim3(256), 0, s, hpart,
+  hipLaunchKernelGGL(linear_total_kernel, dim3(kD * kD / 64 + 2, g.BH), dim3(256), 0, s, hpart,
                      zpart, htot, ztot, np, standard);
   return hipGetLastError();
 }

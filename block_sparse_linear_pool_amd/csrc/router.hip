@@ -239,7 +239,9 @@ __device__ inline int count_below_lane(uint64_t m) {
 }
 
 // Rows of logits one workgroup keeps in LDS (fp64), by key-block count.
-__host__ __device__ inline int score_rows(int nkb) { return nkb <= 1024 ? 16 : (nkb <= 2048 ? 8 : 4); }
+// Eight rows (two per wavefront in the selection) keep enough workgroups in flight; the logit
+// tiles are 16 rows tall, the other 8 zero.
+__host__ __device__ inline int score_rows(int nkb) { return nkb <= 2048 ? 8 : 4; }
 
 // Kept set of one row, exact (ties to the lower index), by one wavefront. The row's keys
 // sit in registers, E per lane (key j = lane + 64 e). T is built bit by bit from the top as
