@@ -145,17 +145,18 @@ __global__ __launch_bounds__(256) void attn_kernel(
         issue_tile(smem + kOffK + ((p + 2) % 3) * kTile, smem + kOffV + ((p + 2) & 3) * kTile,
                    kc + o, vc + o, w, lane);
       }
-      i32x16 s0 = i32x16{}, s1 = i32x16{};
+      i32x16 s0, s1;   // written (and read) only when p < n
       if (p < n) {
-        // ---- S^T for key tiles T = 0 (keys 0-31) and T = 1 (keys 32-63)
+        // ---- S^T for key tiles T = 0 (keys 0-31) and T = 1 (keys 32-63); the first step takes
+        // a literal zero accumulator (the MFMA's inline constant, no register fill)
         const int8_t* kt = smem + kOffK + (p % 3) * kTile;
 #pragma unroll
         for (int tt = 0; tt < 4; ++tt) {
           const int r0 = l32, r1 = 32 + l32;
           const i32x4 a0 = *reinterpret_cast<const i32x4*>(kt + r0 * kD + 16 * kchunk_swz(r0, 2 * tt + g));
           const i32x4 a1 = *reinterpret_cast<const i32x4*>(kt + r1 * kD + 16 * kchunk_swz(r1, 2 * tt + g));
-          s0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a0, qf[tt], s0, 0, 0, 0);
-          s1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a1, qf[tt], s1, 0, 0, 0);
+          s0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a0, qf[tt], tt == 0 ? i32x16{} : s0, 0, 0, 0);
+          s1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a1, qf[tt], tt == 0 ? i32x16{} : s1, 0, 0, 0);
         }
       }
       if (p >= 1) {
