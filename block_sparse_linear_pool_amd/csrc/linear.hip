@@ -17,6 +17,8 @@
 //                   stored as h_j^T ([d_v][d_phi]) in bf16 for the attention kernel's
 //                   gathers; fp32 partial sums of h_j^T and z_j over kKpPerWg blocks.
 //   linear_total  H_tot = sum_j h_j and Z_tot = sum_j z_j from the partials (fixed order).
+// The bf16 h_j^T and fp32 H_tot^T for the attention kernel are stored in fragment order
+// (htot_frag_index): each of its wavefront loads is then one contiguous run.
 
 #include "sla2_common.h"
 
@@ -121,11 +123,13 @@ __global__ __launch_bounds__(kKvThreads) void kv_prep_kernel(const T* __restrict
       *reinterpret_cast<i32x4*>(x.vc + blk * (kBK * kD) +
                                 lane_off(static_cast<uint32_t>(d * kBK + 16 * vchunk_swz(d, ch)))) = val;
     }
+    // h_j^T in fragment order: chunk q holds row d_v = 32 (q / 512) + q % 32, elements
+    // 8 c .. 8 c + 7 with c = (q / 32) % 16
     uint16_t* htb = x.ht_bf16 + blk * (kD * kD);
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int q = t + kKvThreads * u;
-      const int row = q >> 4, c16 = q & 15;
+      const int row = 32 * (q >> 9) + (q & 31), c16 = (q >> 5) & 15;
       const i32x4 val = *reinterpret_cast<const i32x4*>(&hst[b][row * kRowH + 8 * c16]);
       *reinterpret_cast<i32x4*>(htb + lane_off(static_cast<uint32_t>(8 * q))) = val;
     }
@@ -325,8 +329,8 @@ hipError_t launch_kv_prep(const Geom& g, int dtype, const void* K, const void* V
 
 // ---------------------------------------------------------------- linear_total
 // grid (kD * kD / 64 + 2, BH), 256 threads. Workgroup x < 256 reduces elements 64 x .. 64 x + 63
-// of H_tot^T (partials are transposed; with `standard` set the result is written as H_tot,
-// [d_phi][d_v]); workgroups 256, 257 reduce Z_tot columns 0-63, 64-127. Wavefront w sums
+// of H_tot^T (partials are transposed; written in fragment order, or with `standard` set as
+// H_tot, [d_phi][d_v]); workgroups 256, 257 reduce Z_tot columns 0-63, 64-127. Wavefront w sums
 // partials w, w + 4, ... (four accumulators, all loads in flight); the four wavefront sums
 // are combined in a fixed order (deterministic).
 __global__ __launch_bounds__(256) void linear_total_kernel(const float* __restrict__ hpart,
@@ -354,7 +358,8 @@ __global__ __launch_bounds__(256) void linear_total_kernel(const float* __restri
     if (is_z) {
       ztot[static_cast<size_t>(bh) * kD + e] = v;
     } else {
-      const int out = standard ? (e & (kD - 1)) * kD + (e >> 7) : e;
+      const int dv = e >> 7, dphi = e & (kD - 1);
+      const int out = standard ? dphi * kD + dv : htot_frag_index(dv, dphi);
       htot[static_cast<size_t>(bh) * (kD * kD) + out] = v;
     }
   }

@@ -227,10 +227,19 @@ hipError_t launch_score_topk(const Geom& g, const double* A, const double* Bt, i
                              float* scores, hipStream_t s);
 hipError_t launch_mask_to_list(const Geom& g, const uint8_t* mask_in, uint8_t* mask_out,
                                int32_t* list, int32_t* cnt, hipStream_t s);
+// Fragment order of the d x d linear-branch matrices read by the attention kernel. Its
+// wavefront w reads rows d_v = 32 w .. +31 of h_j^T and H_tot^T, lane (g = lane / 32,
+// l = lane % 32) taking d_v = 32 w + l; storing the matrices in that read order makes each
+// wavefront load one contiguous 1 KB run instead of 32-byte pieces of 32 rows.
+//   h_j^T, bf16:   16-byte chunk (w * 8 + f) * 64 + lane holds d_phi = 16 f + 8 g .. +7
+//   H_tot^T, fp32: 16-byte chunk (w * 16 + c) * 64 + lane holds d_phi = 8 c + 4 g .. +3
+__host__ __device__ inline int htot_frag_index(int dv, int dphi) {
+  return (((dv >> 5) * 16 + (dphi >> 3)) * 64 + 32 * ((dphi >> 2) & 1) + (dv & 31)) * 4 + (dphi & 3);
+}
 // Per key block: INT8 K_s tiles + sk and E4M3 V^T tiles + sv (skipped when kc is null;
-// k_tap / v_tap optional row-major copies of the codes), z_j, h_j^T in bf16 ([d_v][d_phi],
+// k_tap / v_tap optional row-major copies of the codes), z_j, h_j^T in bf16 (fragment order,
 // optional), h_j in fp32 (standard orientation [d_phi][d_v], optional), and fp32 partial
-// sums of h_j^T and z_j over kKpPerWg blocks.
+// sums of h_j^T ([d_v][d_phi]) and z_j over kKpPerWg blocks.
 struct KvArgs {
   const float* mu32;
   int8_t* kc;
@@ -245,7 +254,7 @@ struct KvArgs {
 };
 hipError_t launch_kv_prep(const Geom& g, int dtype, const void* K, const void* V,
                           const KvArgs& x, hipStream_t s);
-// standard = 0: H_tot^T (for the attention kernel); 1: H_tot.
+// standard = 0: H_tot^T in fragment order (for the attention kernel); 1: H_tot.
 hipError_t launch_linear_total(const Geom& g, const float* hpart, const float* zpart,
                                float* htot, float* ztot, int standard, hipStream_t s);
 // Operands of the fused attention kernel (sparse branch, linear branch, combine).
@@ -254,9 +263,9 @@ struct AttnArgs {
   const int8_t* kc;            // INT8 K_s tiles
   const uint8_t* vc;           // E4M3 V^T tiles
   const float *sq, *sk, *sv;   // scales
-  const uint16_t* ht_bf16;     // h_j^T, bf16
+  const uint16_t* ht_bf16;     // h_j^T, bf16, fragment order
   const float* z;              // z_j
-  const float* htot_t;         // H_tot^T, fp32
+  const float* htot_t;         // H_tot^T, fp32, fragment order
   const float* ztot;           // Z_tot
   const uint8_t* mask;         // 0/1 block mask
   const int32_t* list;         // kept lists

@@ -361,16 +361,17 @@ __global__ __launch_bounds__(256) void attn_kernel(
 #pragma unroll
     for (int qt = 0; qt < 4; ++qt) acc[qt] *= os_scale[qt] * a * den[qt] / (1.f - a);
   }
-  // ---- H tiles of this wavefront's d_v rows: hacc[tl] rows d_phi = 32 tl + 8 (i/4) + 4 g + i%4
+  // ---- H tiles of this wavefront's d_v rows: hacc[tl] rows d_phi = 32 tl + 8 (i/4) + 4 g + i%4,
+  // column d_v = dvr = 32 w + l32
   f32x16 hacc[4];
-  const int dvr = 32 * w + l32;          // d_v of this lane's accumulator column
   if (sub) {
-    const float* hp = htot_t + static_cast<size_t>(bh) * (kD * kD) + dvr * kD + 4 * g;
+    // fragment order: chunk (16 w + 4 tl + k4) * 64 + lane holds d_phi = 32 tl + 8 k4 + 4 g .. +3
+    const float* hp = htot_t + static_cast<size_t>(bh) * (kD * kD) + (1024 * w + lane) * 4;
 #pragma unroll
     for (int tl = 0; tl < 4; ++tl)
 #pragma unroll
       for (int k4 = 0; k4 < 4; ++k4) {
-        const f32x4 v = *reinterpret_cast<const f32x4*>(hp + 32 * tl + 8 * k4);
+        const f32x4 v = *reinterpret_cast<const f32x4*>(hp + 256 * (4 * tl + k4));
         hacc[tl][4 * k4] = v[0]; hacc[tl][4 * k4 + 1] = v[1];
         hacc[tl][4 * k4 + 2] = v[2]; hacc[tl][4 * k4 + 3] = v[3];
       }
@@ -384,21 +385,22 @@ __global__ __launch_bounds__(256) void attn_kernel(
   for (int m = 0; m < 2; ++m)
 #pragma unroll
     for (int b = 0; b < 8; ++b) idf[m][b] = to_bf16(l32 == 16 * m + 8 * g + b ? sgn : 0.f);
-  // B fragment (tl, m) of block j: row d_v = dvr of h_j^T, d_phi = 32 tl + 16 m + 8 g .. +7
-  const uint16_t* hb = ht_bf16 + tile0 * (kD * kD) + dvr * kD + 8 * g;
+  // B fragment f = 2 tl + m of block j: row d_v = dvr of h_j^T, d_phi = 32 tl + 16 m + 8 g .. +7,
+  // which in fragment order is chunk (8 w + f) * 64 + lane
+  const uint16_t* hb = ht_bf16 + tile0 * (kD * kD) + (512 * w + lane) * 8;
   if (nl > 0) {
     i32x4 cur[8];
     {
       const uint16_t* hp = hb + static_cast<size_t>(sub ? L[0] : lst[0]) * (kD * kD);
 #pragma unroll
-      for (int f = 0; f < 8; ++f) cur[f] = *reinterpret_cast<const i32x4*>(hp + 16 * f);
+      for (int f = 0; f < 8; ++f) cur[f] = *reinterpret_cast<const i32x4*>(hp + 512 * f);
     }
     for (int nn = 0; nn < nl; ++nn) {
       i32x4 nxt[8];
       if (nn + 1 < nl) {
         const uint16_t* hp = hb + static_cast<size_t>(sub ? L[nn + 1] : lst[nn + 1]) * (kD * kD);
 #pragma unroll
-        for (int f = 0; f < 8; ++f) nxt[f] = *reinterpret_cast<const i32x4*>(hp + 16 * f);
+        for (int f = 0; f < 8; ++f) nxt[f] = *reinterpret_cast<const i32x4*>(hp + 512 * f);
       }
 #pragma unroll
       for (int f = 0; f < 8; ++f)   // f = 2 tl + m
