@@ -16,6 +16,7 @@ constexpr int kKpPerWg = 8;  // key blocks per workgroup in the linear precomput
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef int i32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef double f64x4 __attribute__((ext_vector_type(4)));
@@ -102,6 +103,16 @@ __device__ inline void xcd_block(int nqb, int BH, int* i, int* bh) {
   if ((total & 7) == 0) L = (L & 7) * (total >> 3) + (L >> 3);
   *i = L % nqb;
   *bh = L / nqb;
+}
+
+// Workgroup barrier for exchanges through LDS only: waits for this wavefront's LDS (and
+// scalar) memory operations, lgkmcnt(0), then meets the other wavefronts. Unlike
+// __syncthreads() it does not wait for outstanding global loads (vmcnt), so prefetches stay in
+// flight across it; data loaded into LDS by global_load_lds must be waited for explicitly
+// before it. The memory clobber keeps the compiler from moving memory accesses across it.
+__device__ inline void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+  asm volatile("s_barrier" ::: "memory");
 }
 
 // ---------------------------------------------------------------- wave helpers
