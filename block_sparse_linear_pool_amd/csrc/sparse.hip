@@ -161,16 +161,25 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(
   const bool linear_role = t >= 256;
   const int nqb = N / kBQ, nkb = N / kBK;
   const size_t row = static_cast<size_t>(bh) * nqb + i;
-  const int n = cnt[row];
-  const int32_t* L = list + row * list_stride;
-  const size_t qblk = static_cast<size_t>(bh) * N + static_cast<size_t>(i) * kBQ;  // first query
-  const float a = alpha[static_cast<size_t>(bh % H) * nqb + i];
-  const size_t tile0 = static_cast<size_t>(bh) * nkb;
-  const int nuns = nkb - n;
-  const bool do_lin = nuns > 0 && (kTaps || a != 1.f);
-  float* dsh = reinterpret_cast<float*>(smem + kOffDen);
+  // counters first: the barrier then waits for no memory read
   if (t < 8) ctr[t] = 0;
   lds_barrier();   // counters set
+  const int32_t* L = list + row * list_stride;
+  const size_t qblk = static_cast<size_t>(bh) * N + static_cast<size_t>(i) * kBQ;  // first query
+  const size_t tile0 = static_cast<size_t>(bh) * nkb;
+  // kept count and alpha of the row: read by each group where it first needs them (scalar
+  // reads share one wait counter, so an early read would hold up the first loads)
+  int n = 0, nuns = 0;
+  float a = 0.f;
+  bool do_lin = false;
+  auto read_row = [&]() {
+    asm volatile("" ::: "memory");
+    n = cnt[row];
+    a = alpha[static_cast<size_t>(bh % H) * nqb + i];
+    nuns = nkb - n;
+    do_lin = nuns > 0 && (kTaps || a != 1.f);
+  };
+  float* dsh = reinterpret_cast<float*>(smem + kOffDen);
   // N_l hand-over slot (d_v tile dt, query tile qt, k4) of this lane: 4 floats, lane-contiguous
   auto nl_slot = [&](int dt, int qt, int k4) {
     return reinterpret_cast<float*>(smem + kOffNl) + (((dt * 4 + qt) * 4 + k4) * 64 + lane) * 4;
@@ -186,17 +195,21 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(
     float lsum = 0.f, svcur = 0.f;
     {
       // block index, s_k and s_v of kept blocks 0 .. 127, one per lane (later ones are read
-      // from memory when needed)
+      // from memory when needed). The list row is read without waiting for the count n:
+      // entries past n are never used, and clamping keeps their reads in range.
+      // Order: list row and Q codes first (one round trip), then the first tiles, then the
+      // scales of the kept blocks.
       int lj[2];
-      float lsk[2], lsv[2];
 #pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        const int k = 64 * c + lane;
-        const int jj = k < n ? L[k] : 0;
-        lj[c] = jj;
-        lsk[c] = sk[tile0 + jj];
-        lsv[c] = sv[tile0 + jj];
-      }
+      for (int c = 0; c < 2; ++c) lj[c] = L[min(64 * c + lane, list_stride - 1)];
+      i32x4 qf[4];
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt)
+        qf[tt] = *reinterpret_cast<const i32x4*>(qc + (qblk + qo) * kD + 32 * tt + 16 * g);
+      read_row();
+#pragma unroll
+      for (int c = 0; c < 2; ++c) lj[c] = min(max(lj[c], 0), nkb - 1);
+      float lsk[2], lsv[2];
       // value of kept block k < 128 from the lanes, without a branch (both reads, one select)
       auto pick = [&](const auto (&v)[2], int k) {
         const auto a0 = lane_value(v[0], k & 63), a1 = lane_value(v[1], k & 63);
@@ -216,10 +229,6 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(
         if constexpr (decltype(small)::value) return pick(lsv, k);
         else return k < 128 ? pick(lsv, k) : sv[tile0 + L[k]];
       };
-      i32x4 qf[4];
-#pragma unroll
-      for (int tt = 0; tt < 4; ++tt)
-        qf[tt] = *reinterpret_cast<const i32x4*>(qc + (qblk + qo) * kD + 32 * tt + 16 * g);
       const float cq = sq[row] * (kLog2e * kInvSqrtD);
       float m2 = -INFINITY;
       auto issue = [&](int k, auto small) {
@@ -253,6 +262,11 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(
         }
       };
       for (int k = 0; k < kAhead && k < n; ++k) issue(k, std::true_type{});
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        lsk[c] = sk[tile0 + lj[c]];
+        lsv[c] = sv[tile0 + lj[c]];
+      }
       // Arrival 0: this wavefront's parts of tiles 0 .. kAhead - 1 (and the Q codes and
       // per-block values) have landed. Arrival e + 1 ends step e: its part of tile
       // e + kAhead - 1 has landed and its LDS reads of the step are done. Step e >= 1 waits
@@ -444,6 +458,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(
   }
 
   // =========================================================== linear branch
+  read_row();
   if (!do_lin) {
     lds_barrier();
     lds_barrier();
