@@ -44,6 +44,7 @@
 // Combine — the linear wavefronts leave N_l^T in LDS over the idle rings; the sparse
 // wavefronts form O = alpha O_s + (1 - alpha) N_l / den. alpha = 1 or no dropped block skips
 // the linear branch (O_l = 0).
+#include <algorithm>
 #include <type_traits>
 
 #include "sla2_common.h"
@@ -64,8 +65,10 @@ constexpr int kPadPhi = 136;               // bf16 row stride of phi(Q_i)
 constexpr int kOffPhi = 2 * kRing * kTile; // 98304
 constexpr int kOffLst = kOffPhi + 128 * kPadPhi * 2;
 constexpr int kOffZ = kOffLst + 4096;
-constexpr int kOffDen = kOffZ + 512;
-constexpr int kLdsBytes = kOffDen + 512;   // 138240
+constexpr int kOffDen = kOffZ + 512;       // 2 x 128 floats (by row parity)
+constexpr int kOstPad = 36;                // float row stride of the output staging tiles
+constexpr int kOffOst = kOffDen + 1024;    // 4 wavefronts x 32 rows x kOstPad floats
+constexpr int kLdsBytes = kOffOst + 4 * 32 * kOstPad * 4;   // 157184
 constexpr int kOffNl = 0;
 static_assert(kOffNl + 4 * 4 * 4 * 64 * 16 <= kOffPhi, "N_l hand-over exceeds the rings");
 constexpr int kAttnThreads = 512;
@@ -78,8 +81,8 @@ __device__ inline void issue_tile(int8_t* kdst, int8_t* vdst, const int8_t* kt, 
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     const int c0 = ((u & 1) * 4 + w) * 64;     // chunk of this wavefront within the tile
-    const void* src = u < 2 ? static_cast<const void*>(kt + 16 * (c0 + lane))
-                            : static_cast<const void*>(vt + 16 * (c0 + lane));
+    const unsigned off = 16u * static_cast<unsigned>(c0 + lane);
+    const void* src = u < 2 ? static_cast<const void*>(kt + off) : static_cast<const void*>(vt + off);
     int8_t* dst = (u < 2 ? kdst : vdst) + 16 * c0;
     __builtin_amdgcn_global_load_lds(src, reinterpret_cast<__attribute__((address_space(3))) void*>(
                                               reinterpret_cast<uintptr_t>(dst)),
@@ -125,6 +128,13 @@ __device__ inline void group_wait(uint32_t group, uint32_t target) {
 }
 
 __device__ inline int lane_value(int v, int k) { return __builtin_amdgcn_readlane(v, k); }
+// A per-lane value the compiler may not hoist out of the row loop: offsets derived from it
+// are recomputed per row (hoisted, they would stay live across the rows and, with all
+// registers in use, be spilled; reloading a spill waits for every store in flight)
+__device__ inline unsigned lane_off(unsigned x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
 // max / sum of a value and its copy in lane ^ 32 (one VALU swap of the two lane halves); the
 // two lanes get the same result (the operation is commutative)
 __device__ inline int pair_max(int v) {
@@ -139,8 +149,17 @@ __device__ inline float lane_value(float v, int k) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), k));
 }
 
-// grid (nqb, BH) (remapped per XCD), kAttnThreads threads. kTaps: also write O_s and O_l (debug
-// taps).
+// Values of one row (query block) for the sparse group, staged in LDS by the linear group.
+struct RowStage {
+  int n;
+  float a, sq;
+  int pad;
+  int lj[128];
+  float lsk[128], lsv[128];
+};
+
+// Persistent grid: gridDim.x workgroups (one per CU), each taking rows blockIdx.x + gridDim.x k
+// (remapped per XCD); kAttnThreads threads. kTaps: also write O_s and O_l (debug taps).
 template <typename T, bool kTaps>
 __global__ __launch_bounds__(kAttnThreads) void attn_kernel(
     const T* __restrict__ Q, const int8_t* __restrict__ qc, const int8_t* __restrict__ kc,
@@ -150,66 +169,108 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(
     const float* __restrict__ ztot, const uint8_t* __restrict__ mask,
     const int32_t* __restrict__ list, int list_stride, const int32_t* __restrict__ cnt,
     const float* __restrict__ alpha, float* __restrict__ O, float* __restrict__ O_s_tap,
-    float* __restrict__ O_l_tap, int N, int H) {
+    float* __restrict__ O_l_tap, int N, int H, int BH) {
   __shared__ __attribute__((aligned(16))) int8_t smem[kLdsBytes];
   // arrival counters of the sparse (0-3) and linear (4-7) wavefronts: an object of their own
   __shared__ __attribute__((aligned(16))) uint32_t ctr[8];
+  // the next row's values for the sparse group, staged by the linear group (by row parity)
+  __shared__ RowStage stage[2];
   const int t = threadIdx.x;
-  int i, bh;
-  xcd_block(N / kBQ, static_cast<int>(gridDim.y), &i, &bh);
-  const int lane = t & 63, w = (t >> 6) & 3, g = lane >> 5, l32 = lane & 31;
+  // w is wave-uniform (a scalar): addresses are formed as a uniform row base plus a 32-bit
+  // lane offset, so no 64-bit per-lane address stays live across rows
+  const int lane = t & 63, w = __builtin_amdgcn_readfirstlane((t >> 6) & 3), g = lane >> 5,
+            l32 = lane & 31;
   const bool linear_role = t >= 256;
-  const int nqb = N / kBQ, nkb = N / kBK;
-  const size_t row = static_cast<size_t>(bh) * nqb + i;
+  const int nqb = N / kBQ, nkb = N / kBK, total = nqb * BH;
   // counters first: the barrier then waits for no memory read
   if (t < 8) ctr[t] = 0;
   lds_barrier();   // counters set
-  const int32_t* L = list + row * list_stride;
-  const size_t qblk = static_cast<size_t>(bh) * N + static_cast<size_t>(i) * kBQ;  // first query
-  const size_t tile0 = static_cast<size_t>(bh) * nkb;
-  // kept count and alpha of the row: read by each group where it first needs them (scalar
-  // reads share one wait counter, so an early read would hold up the first loads)
-  int n = 0, nuns = 0;
-  float a = 0.f;
-  bool do_lin = false;
-  auto read_row = [&]() {
-    asm volatile("" ::: "memory");
-    n = cnt[row];
-    a = alpha[static_cast<size_t>(bh % H) * nqb + i];
-    nuns = nkb - n;
-    do_lin = nuns > 0 && (kTaps || a != 1.f);
+  // Row (query block) k of this workgroup: rows blockIdx.x + gridDim.x k, remapped so that
+  // consecutive rows of one head stay on one XCD (workgroups are dealt to the 8 XCDs in turn)
+  struct Row {
+    int i, bh;
+    size_t row, qblk, tile0;
+    const int32_t* L;
   };
-  float* dsh = reinterpret_cast<float*>(smem + kOffDen);
+  auto row_at = [&](int k, Row& r) -> bool {
+    int lr = static_cast<int>(blockIdx.x) + static_cast<int>(gridDim.x) * k;
+    if (lr >= total) return false;
+    if ((total & 7) == 0 && (gridDim.x & 7) == 0) lr = (lr & 7) * (total >> 3) + (lr >> 3);
+    r.i = lr % nqb;
+    r.bh = lr / nqb;
+    r.row = static_cast<size_t>(r.bh) * nqb + r.i;
+    r.qblk = static_cast<size_t>(r.bh) * N + static_cast<size_t>(r.i) * kBQ;   // first query
+    r.tile0 = static_cast<size_t>(r.bh) * nkb;
+    r.L = list + r.row * list_stride;
+    return true;
+  };
   // N_l hand-over slot (d_v tile dt, query tile qt, k4) of this lane: 4 floats, lane-contiguous
-  auto nl_slot = [&](int dt, int qt, int k4) {
-    return reinterpret_cast<float*>(smem + kOffNl) + (((dt * 4 + qt) * 4 + k4) * 64 + lane) * 4;
+  auto nl_slot = [&](int dt, int qt, int k4, unsigned ln) {
+    return reinterpret_cast<float*>(smem + kOffNl) + (((dt * 4 + qt) * 4 + k4) * 64 + ln) * 4;
   };
 
   if (!linear_role) {
     // =========================================================== sparse branch
     const uint32_t cs = lds_addr(&ctr[0]);   // arrivals: per wavefront, see the prologue
     const int qo = 32 * w + l32;              // the query this lane scores
+    uint32_t narr = 0;                        // this wavefront's arrivals so far (all alike)
+    for (int kr = 0;; ++kr) {
+    Row rw;
+    if (!row_at(kr, rw)) break;
+    const size_t row = rw.row, qblk = rw.qblk, tile0 = rw.tile0;
+    const int32_t* L = rw.L;
     f32x16 acc[4];
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) acc[dt] = f32x16{};
     float lsum = 0.f, svcur = 0.f;
+    int n, nuns;
+    float a;
+    bool do_lin;
     {
       // block index, s_k and s_v of kept blocks 0 .. 127, one per lane (later ones are read
-      // from memory when needed). The list row is read without waiting for the count n:
-      // entries past n are never used, and clamping keeps their reads in range.
-      // Order: list row and Q codes first (one round trip), then the first tiles, then the
-      // scales of the kept blocks.
+      // from memory when needed). The first row reads them itself: the list row without
+      // waiting for the count n (entries past n are never used, and clamping keeps their
+      // reads in range) together with the Q codes, then the first tiles, then the scales. For
+      // later rows the linear group has staged them in LDS.
       int lj[2];
-#pragma unroll
-      for (int c = 0; c < 2; ++c) lj[c] = L[min(64 * c + lane, list_stride - 1)];
+      float lsk[2], lsv[2], sqv;
       i32x4 qf[4];
+      const int8_t* qrow = qc + qblk * kD;   // Q codes of the row's first query
+      const unsigned ln = lane_off(static_cast<unsigned>(lane));
+      const unsigned qoff = (32u * w + (ln & 31u)) * kD + 16u * (ln >> 5);   // this lane's
+      if (kr == 0) {
 #pragma unroll
-      for (int tt = 0; tt < 4; ++tt)
-        qf[tt] = *reinterpret_cast<const i32x4*>(qc + (qblk + qo) * kD + 32 * tt + 16 * g);
-      read_row();
+        for (int c = 0; c < 2; ++c) lj[c] = L[static_cast<unsigned>(min(64 * c + lane, list_stride - 1))];
 #pragma unroll
-      for (int c = 0; c < 2; ++c) lj[c] = min(max(lj[c], 0), nkb - 1);
-      float lsk[2], lsv[2];
+        for (int tt = 0; tt < 4; ++tt)
+          qf[tt] = *reinterpret_cast<const i32x4*>(qrow + static_cast<unsigned>(qo * kD + 32 * tt + 16 * g));
+        asm volatile("" ::: "memory");
+        n = cnt[row];
+        a = alpha[static_cast<size_t>(rw.bh % H) * nqb + rw.i];
+        sqv = sq[row];
+#pragma unroll
+        for (int c = 0; c < 2; ++c) lj[c] = min(max(lj[c], 0), nkb - 1);
+      } else {
+        // every sparse wavefront has read the previous row's hand-over (over the rings)
+        group_arrive(cs, w);
+        ++narr;
+        group_wait(cs, narr);
+        const RowStage& st = stage[kr & 1];
+        n = st.n;
+        a = st.a;
+        sqv = st.sq;
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          lj[c] = st.lj[64 * c + lane];
+          lsk[c] = st.lsk[64 * c + lane];
+          lsv[c] = st.lsv[64 * c + lane];
+        }
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt)
+          qf[tt] = *reinterpret_cast<const i32x4*>(qrow + (qoff + 32u * tt));
+      }
+      nuns = nkb - n;
+      do_lin = nuns > 0 && (kTaps || a != 1.f);
       // value of kept block k < 128 from the lanes, without a branch (both reads, one select)
       auto pick = [&](const auto (&v)[2], int k) {
         const auto a0 = lane_value(v[0], k & 63), a1 = lane_value(v[1], k & 63);
@@ -229,7 +290,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(
         if constexpr (decltype(small)::value) return pick(lsv, k);
         else return k < 128 ? pick(lsv, k) : sv[tile0 + L[k]];
       };
-      const float cq = sq[row] * (kLog2e * kInvSqrtD);
+      const float cq = sqv * (kLog2e * kInvSqrtD);
       float m2 = -INFINITY;
       auto issue = [&](int k, auto small) {
         const size_t o = (tile0 + blk_of(k, small)) * kTile;
@@ -252,7 +313,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
           const int c0 = ((u & 1) * 4 + w) * 64;
-          const int src_off = real ? 16 * (c0 + lane) : 0;
+          const unsigned src_off = real ? 16u * static_cast<unsigned>(c0 + lane) : 0u;
           const void* src = u < 2 ? static_cast<const void*>(ks + src_off)
                                   : static_cast<const void*>(vs + src_off);
           int8_t* dst = (u < 2 ? kdst : vdst) + 16 * c0;
@@ -261,11 +322,13 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(
                                            16, 0, 0);
         }
       };
-      for (int k = 0; k < kAhead && k < n; ++k) issue(k, std::true_type{});
+      for (int kk = 0; kk < kAhead && kk < n; ++kk) issue(kk, std::true_type{});
+      if (kr == 0) {
 #pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        lsk[c] = sk[tile0 + lj[c]];
-        lsv[c] = sv[tile0 + lj[c]];
+        for (int c = 0; c < 2; ++c) {
+          lsk[c] = (sk + tile0)[static_cast<unsigned>(lj[c])];
+          lsv[c] = (sv + tile0)[static_cast<unsigned>(lj[c])];
+        }
       }
       // Arrival 0: this wavefront's parts of tiles 0 .. kAhead - 1 (and the Q codes and
       // per-block values) have landed. Arrival e + 1 ends step e: its part of tile
@@ -274,7 +337,9 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(
       // product, and the slot of tile e - 2 is free for tile e + kAhead.
       __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
       group_arrive(cs, w);
-      group_wait(cs, 1);
+      ++narr;
+      const uint32_t base = narr;   // arrivals after the prologue's
+      group_wait(cs, base);
       // S^T of block k into (s0, s1): key tiles 0-31 and 32-63; the first product takes a
       // literal zero accumulator (the MFMA's inline constant, no register fill)
       auto qk = [&](int k, i32x16& s0, i32x16& s1) {
@@ -294,7 +359,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(
       // with the softmax arithmetic and the P V products with the rescale.
       auto step = [&](int e, const i32x16& c0, const i32x16& c1, i32x16& n0, i32x16& n1,
                       auto small) {
-        if (e >= 1) group_wait(cs, e);
+        if (e >= 1) group_wait(cs, base - 1 + e);
         refill(e, small);
         const float c = cq * sk_of(e, small);
         const float svj = sv_of(e, small);
@@ -404,6 +469,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(
       };
       if (n <= 128) run(std::true_type{});
       else run(std::false_type{});
+      narr = base + n;
       __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): the last refills have landed
     }
     lsum = pair_sum(lsum);
@@ -412,18 +478,42 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(
     lds_barrier();   // N_l and den handed over
     // lane's output rows: query qo, d_v = 32 dt + 8 k4 + 4 g + (0..3)
     auto out_ptr = [&](float* base, int dt, int k4) {
-      return base + (qblk + qo) * kD + 32 * dt + 8 * k4 + 4 * g;
+      return base + qblk * kD + static_cast<unsigned>(qo * kD + 32 * dt + 8 * k4 + 4 * g);
+    };
+    // O rows of this wavefront (queries 32 w .. +31: 16 KB, contiguous) leave through LDS one
+    // d_v tile at a time: the lane's four groups of 4 go in at row l32, and each store
+    // instruction then writes 8 rows x 128 B, whole lines (the registers alone would give
+    // 32-byte pieces of 32 rows per instruction). The staging tile is this wavefront's own.
+    float* ost = reinterpret_cast<float*>(smem + kOffOst) + w * (32 * kOstPad);
+    float* orow = O + (qblk + 32 * w) * kD;   // the wavefront's first output row
+    const unsigned ln = lane_off(static_cast<unsigned>(lane));
+    auto store_tile = [&](int dt, const f32x4 (&v)[4]) {
+#pragma unroll
+      for (int k4 = 0; k4 < 4; ++k4)
+        *reinterpret_cast<f32x4*>(ost + l32 * kOstPad + 8 * k4 + 4 * g) = v[k4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const unsigned r = 8u * u + (ln >> 3), c = 4u * (ln & 7u);
+        *reinterpret_cast<f32x4*>(orow + (r * kD + 32u * dt + c)) =
+            *reinterpret_cast<const f32x4*>(ost + r * kOstPad + c);
+      }
     };
     if (!do_lin) {
       // no dropped block (O_l = 0) or alpha = 1: O = alpha O_s
       const float coef = (nuns == 0 ? a : 1.f) * os_scale;
 #pragma unroll
+      for (int dt = 0; dt < 4; ++dt) {
+        f32x4 v[4];
+#pragma unroll
+        for (int k4 = 0; k4 < 4; ++k4)
+          v[k4] = f32x4{acc[dt][4 * k4] * coef, acc[dt][4 * k4 + 1] * coef,
+                        acc[dt][4 * k4 + 2] * coef, acc[dt][4 * k4 + 3] * coef};
+        store_tile(dt, v);
+      }
+#pragma unroll
       for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
         for (int k4 = 0; k4 < 4; ++k4) {
-          *reinterpret_cast<f32x4*>(out_ptr(O, dt, k4)) =
-              f32x4{acc[dt][4 * k4] * coef, acc[dt][4 * k4 + 1] * coef,
-                    acc[dt][4 * k4 + 2] * coef, acc[dt][4 * k4 + 3] * coef};
           if (kTaps) {
             if (O_s_tap)
               *reinterpret_cast<f32x4*>(out_ptr(O_s_tap, dt, k4)) =
@@ -432,46 +522,58 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(
             if (O_l_tap) *reinterpret_cast<f32x4*>(out_ptr(O_l_tap, dt, k4)) = f32x4{0.f, 0.f, 0.f, 0.f};
           }
         }
-      return;
+      continue;
     }
     // O = alpha O_s + (1 - alpha) O_l with O_s = acc os_scale, O_l = N_l / den
-    const float rden = 1.0f / dsh[qo];
+    const float rden =
+        1.0f / (reinterpret_cast<const float*>(smem + kOffDen) + 128 * (kr & 1))[32u * w + (ln & 31u)];
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
+    for (int dt = 0; dt < 4; ++dt) {
+      f32x4 o[4];
 #pragma unroll
       for (int k4 = 0; k4 < 4; ++k4) {
-        const f32x4 nlv = *reinterpret_cast<const f32x4*>(nl_slot(dt, w, k4));
-        f32x4 os, ol, o;
+        const f32x4 nlv = *reinterpret_cast<const f32x4*>(nl_slot(dt, w, k4, ln));
+        f32x4 os, ol;
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
           os[k] = acc[dt][4 * k4 + k] * os_scale;
           ol[k] = nlv[k] * rden;
-          o[k] = fmaf(a, os[k], (1.f - a) * ol[k]);
+          o[k4][k] = fmaf(a, os[k], (1.f - a) * ol[k]);
         }
-        *reinterpret_cast<f32x4*>(out_ptr(O, dt, k4)) = o;
         if (kTaps) {
           if (O_s_tap) *reinterpret_cast<f32x4*>(out_ptr(O_s_tap, dt, k4)) = os;
           if (O_l_tap) *reinterpret_cast<f32x4*>(out_ptr(O_l_tap, dt, k4)) = ol;
         }
       }
+      store_tile(dt, o);
+    }
+    }
     return;
   }
 
   // =========================================================== linear branch
-  read_row();
-  if (!do_lin) {
-    lds_barrier();
-    lds_barrier();
-    return;
-  }
   const uint32_t cl = lds_addr(&ctr[4]);
   const int tl = t - 256;
-  const bool sub = n <= nuns;   // total minus kept, else direct sum over dropped
-  const int nl = sub ? n : nuns;
-  const float sgn = sub ? -1.f : 1.f;
+  uint32_t larr = 0;   // this wavefront's arrivals so far (all alike)
   uint16_t* phs = reinterpret_cast<uint16_t*>(smem + kOffPhi);
   uint16_t* lst = reinterpret_cast<uint16_t*>(smem + kOffLst);
   float* zsh = reinterpret_cast<float*>(smem + kOffZ);
+  for (int kr = 0;; ++kr) {
+  Row rw;
+  if (!row_at(kr, rw)) break;
+  const size_t row = rw.row, qblk = rw.qblk, tile0 = rw.tile0;
+  const int32_t* L = rw.L;
+  const int bh = rw.bh;
+  const int n = cnt[row];
+  const float a = alpha[static_cast<size_t>(rw.bh % H) * nqb + rw.i];
+  const int nuns = nkb - n;
+  const bool do_lin = nuns > 0 && (kTaps || a != 1.f);
+  float* dsh = reinterpret_cast<float*>(smem + kOffDen) + 128 * (kr & 1);
+  f32x16 accl[4];
+  if (do_lin) {
+  const bool sub = n <= nuns;   // total minus kept, else direct sum over dropped
+  const int nl = sub ? n : nuns;
+  const float sgn = sub ? -1.f : 1.f;
   // ---- block list in LDS: the kept list (total minus kept) or the dropped blocks
   if (w == 0) {
     if (sub) {
@@ -480,7 +582,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(
       int before = 0;
       for (int j0 = 0; j0 < nkb; j0 += 64) {
         const int j = j0 + lane;
-        const bool take = j < nkb && mask[row * nkb + j] == 0;
+        const bool take = j < nkb && (mask + row * nkb)[static_cast<unsigned>(j)] == 0;
         const uint64_t m = __ballot(take);
         if (take)
           lst[before + __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m >> 32),
@@ -495,7 +597,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(
   // (16 w + 4 tl4 + k4) * 64 + lane holds d_phi = 32 tl4 + 8 k4 + 4 g .. +3) or zero
   f32x16 hacc[4];
   if (sub) {
-    const float* hp = htot_t + static_cast<size_t>(bh) * (kD * kD) + (1024 * w + lane) * 4;
+    const float* hp = htot_t + static_cast<size_t>(bh) * (kD * kD) + static_cast<unsigned>((1024 * w + lane) * 4);
 #pragma unroll
     for (int tl4 = 0; tl4 < 4; ++tl4)
 #pragma unroll
@@ -515,7 +617,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(
   uint16_t* prow = phs + pq * kPadPhi + 64 * ph;
   {
     uint32_t phw[32];   // bf16 pairs, d = 64 ph + 2 e, +1
-    const T* qp = Q + (qblk + pq) * kD + 64 * ph;
+    const T* qp = Q + qblk * kD + static_cast<unsigned>(pq * kD + 64 * ph);
     float x[64];
 #pragma unroll
     for (int u = 0; u < 8; ++u) load8<T>(qp + 8 * u, x + 8 * u);
@@ -545,7 +647,8 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(
     }
   }
   group_arrive(cl, w);
-  group_wait(cl, 1);   // block list and phi(Q_i) visible
+  ++larr;
+  group_wait(cl, larr);   // block list and phi(Q_i) visible
   // ---- gathers. A = sgn I: fragment m has lane row l32 = 16 m + 8 g + b set at element b; B
   // fragment f = 2 tl4 + m of block j: row d_v = 32 w + l32 of h_j^T, d_phi = 32 tl4 + 16 m +
   // 8 g .. +7, which in fragment order is chunk (8 w + f) * 64 + lane. Each lane also sums
@@ -555,8 +658,9 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(
   for (int m = 0; m < 2; ++m)
 #pragma unroll
     for (int b = 0; b < 8; ++b) idf[m][b] = to_bf16(l32 == 16 * m + 8 * g + b ? sgn : 0.f);
-  const uint16_t* hb = ht_bf16 + tile0 * (kD * kD) + (512 * w + lane) * 8;
-  const float* zb = z + tile0 * kD + 2 * lane;
+  // block j of the head: h_j^T at ht_bf16 + (tile0 + j) d^2 (this lane's chunks at hoff +
+  // 512 f), z_j at z + (tile0 + j) d (this lane's pair at 2 lane)
+  const unsigned hoff = static_cast<unsigned>((512 * w + lane) * 8);
   float zs0 = 0.f, zs1 = 0.f;
   struct Blk {
     i32x4 h[8];
@@ -566,11 +670,11 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(
   // added. The loads are unconditional (the index is clamped; the extra loads at the end are
   // cache hits), so the wait before each use is an exact count.
   auto gload = [&](Blk& dst, int nn) {
-    const int j = lst[min(nn, nl - 1)];
-    const uint16_t* hp = hb + static_cast<size_t>(j) * (kD * kD);
+    const int j = __builtin_amdgcn_readfirstlane(lst[min(nn, nl - 1)]);   // the same in every lane
+    const uint16_t* hp = ht_bf16 + (tile0 + j) * (kD * kD);
 #pragma unroll
-    for (int f = 0; f < 8; ++f) dst.h[f] = *reinterpret_cast<const i32x4*>(hp + 512 * f);
-    dst.z = *reinterpret_cast<const f32x2*>(zb + static_cast<size_t>(j) * kD);
+    for (int f = 0; f < 8; ++f) dst.h[f] = *reinterpret_cast<const i32x4*>(hp + (hoff + 512u * f));
+    dst.z = *reinterpret_cast<const f32x2*>(z + (tile0 + j) * kD + static_cast<unsigned>(2 * lane));
     asm volatile("" ::: "memory");   // keeps the loads here (not moved down to their use)
   };
   auto gadd = [&](const Blk& src) {
@@ -598,13 +702,14 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(
     }
   }
   if (w == 0) {
-    const f32x2 zt = sub ? *reinterpret_cast<const f32x2*>(ztot + static_cast<size_t>(bh) * kD + 2 * lane)
+    const f32x2 zt = sub ? *reinterpret_cast<const f32x2*>(ztot + static_cast<size_t>(bh) * kD + static_cast<unsigned>(2 * lane))
                          : f32x2{0.f, 0.f};
     zsh[2 * lane] = fmaf(sgn, zs0, zt[0]);
     zsh[2 * lane + 1] = fmaf(sgn, zs1, zt[1]);
   }
   group_arrive(cl, w);
-  group_wait(cl, 2);   // Z_i visible
+  ++larr;
+  group_wait(cl, larr);   // Z_i visible
   {
     // den = phi(q) . Z_i from the half row of phi in LDS (read by the sparse wavefronts after
     // the hand-over). Chunk c of group G holds d = 16 G + 8 (b / 4) + 4 c + b % 4 at element b.
@@ -627,7 +732,6 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(
   // ---- N_l^T = H_i^T phi(Q_i)^T: K step ks = 2 tl4 + u takes registers 8 u .. 8 u + 7 of
   // hacc[tl4] (d_phi = 32 tl4 + 16 u + 8 (b/4) + 4 g + b%4), split into bf16 hi + lo; accl[qt]
   // holds rows d_v = 32 w + 8 (i/4) + 4 g + i%4 of query 32 qt + l32
-  f32x16 accl[4];
 #pragma unroll
   for (int qt = 0; qt < 4; ++qt) accl[qt] = f32x16{};
 #pragma unroll
@@ -647,30 +751,73 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(
       accl[qt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(alo, bph, accl[qt], 0, 0, 0);
     }
   }
+  }   // do_lin
+  // ---- the next row's values for the sparse group (its count, alpha, s_q and the block
+  // index, s_k, s_v of kept blocks 0 .. 127, entries past the count clamped and unused)
+  {
+    Row nx;
+    if (w == 0 && row_at(kr + 1, nx)) {
+      RowStage& st = stage[(kr + 1) & 1];
+      int lj[2];
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+        lj[c] = min(max(nx.L[static_cast<unsigned>(min(64 * c + lane, list_stride - 1))], 0), nkb - 1);
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        st.lj[64 * c + lane] = lj[c];
+        st.lsk[64 * c + lane] = (sk + nx.tile0)[static_cast<unsigned>(lj[c])];
+        st.lsv[64 * c + lane] = (sv + nx.tile0)[static_cast<unsigned>(lj[c])];
+      }
+      if (lane == 0) {
+        st.n = cnt[nx.row];
+        st.a = alpha[static_cast<size_t>(nx.bh % H) * nqb + nx.i];
+        st.sq = sq[nx.row];
+      }
+    }
+  }
   lds_barrier();   // rings idle
+  if (do_lin) {
+    const unsigned ln = lane_off(static_cast<unsigned>(lane));
 #pragma unroll
-  for (int qt = 0; qt < 4; ++qt)
+    for (int qt = 0; qt < 4; ++qt)
 #pragma unroll
-    for (int k4 = 0; k4 < 4; ++k4)
-      *reinterpret_cast<f32x4*>(nl_slot(w, qt, k4)) =
-          f32x4{accl[qt][4 * k4], accl[qt][4 * k4 + 1], accl[qt][4 * k4 + 2], accl[qt][4 * k4 + 3]};
+      for (int k4 = 0; k4 < 4; ++k4)
+        *reinterpret_cast<f32x4*>(nl_slot(w, qt, k4, ln)) =
+            f32x4{accl[qt][4 * k4], accl[qt][4 * k4 + 1], accl[qt][4 * k4 + 2], accl[qt][4 * k4 + 3]};
+  }
   lds_barrier();   // N_l handed over
+  }   // rows
+}
+
+// compute units of the current device (cached per device): the persistent grid's size
+static int cu_count() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cache[dev] == 0) {
+    int ncu = 0;
+    if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        ncu <= 0)
+      ncu = 256;
+    cache[dev] = ncu;
+  }
+  return cache[dev];
 }
 
 template <typename T>
 static void launch_attn_t(const Geom& g, const void* Q, const AttnArgs& x, bool taps,
                           hipStream_t s) {
-  dim3 grid(g.nqb, g.BH);
+  dim3 grid(std::min(g.nqb * g.BH, cu_count()));
   if (taps)
     hipLaunchKernelGGL((attn_kernel<T, true>), grid, dim3(kAttnThreads), 0, s, static_cast<const T*>(Q),
                        x.qc, x.kc, x.vc, x.sq, x.sk, x.sv, x.ht_bf16, x.z, x.htot_t, x.ztot,
                        x.mask, x.list, x.list_stride, x.cnt, x.alpha, x.O, x.O_s_tap, x.O_l_tap,
-                       g.N, g.H);
+                       g.N, g.H, g.BH);
   else
     hipLaunchKernelGGL((attn_kernel<T, false>), grid, dim3(kAttnThreads), 0, s, static_cast<const T*>(Q),
                        x.qc, x.kc, x.vc, x.sq, x.sk, x.sv, x.ht_bf16, x.z, x.htot_t, x.ztot,
                        x.mask, x.list, x.list_stride, x.cnt, x.alpha, x.O, x.O_s_tap, x.O_l_tap,
-                       g.N, g.H);
+                       g.N, g.H, g.BH);
 }
 
 hipError_t launch_attn(const Geom& g, int dtype, const void* Q, const AttnArgs& x,

@@ -258,3 +258,33 @@ def test_error_status_on_bad_arguments():
                           torch.zeros((1, 128, 128), device="cuda:0"),
                           torch.zeros((1, 2), device="cuda:0"), 0.5, workspace=torch.empty(16, dtype=torch.uint8, device="cuda:0"))
     assert e.value.status == 2
+
+
+# ------------------------------------------------------------------ the benchmark's own size
+def test_benchmark_size_sampled_heads():
+    """The Wan2.1-1.3B 480P-shaped workload (B=1, H=12, N=32768, 97% sparsity) run exactly as
+    bench.py runs it (all heads in one call, 3072 query-block rows: more rows than compute
+    units, so each attention workgroup takes several rows); two heads checked in full."""
+    w = W.WORKLOADS["wan13b_480p_N32768"]
+    keep = w.keep_frac[-1]
+    say("bench-size", w.name, keep)
+    q, k, v = W.generate(w)
+    wq, wk, alpha = W.weights(w)
+    g = to_gpu(w, q, k, v, wq, wk, alpha)
+    O = sla2.sla2_forward(*g, keep, out=torch.empty(g[0].shape, dtype=torch.float32,
+                                                    device="cuda:0"),
+                          workspace=sla2.workspace_for(g[0]))
+    blocks, mask, _ = sla2.sla2_router(g[0], g[1], g[3], g[4], keep)
+    torch.cuda.synchronize()
+    O, mask = host(O), host(mask)
+    assert np.isfinite(O).all()
+    for h in (0, 7):
+        r = oracle.forward_head(q[0, h], k[0, h], v[0, h], wq[h], wk[h], alpha[h], keep)
+        if not np.array_equal(mask[0, h], r["mask"]):
+            differ = check_mask_band(r["P_c"], r["kb"], mask[0, h])
+            say(f"  h{h}: {differ} rows differ from the oracle's kept set (inside the band)")
+            r = oracle.forward_head(q[0, h], k[0, h], v[0, h], wq[h], wk[h], alpha[h], keep,
+                                    mask=mask[0, h])
+        e, m = rel_l2(O[0, h], r["O"]), max_abs(O[0, h], r["O"])
+        say(f"  h{h}: O relL2 {e:.2e} maxabs {m:.2e}")
+        assert e <= REL_L2_TOL and m <= MAX_ABS_TOL
