@@ -20,10 +20,12 @@ namespace sla2 {
 
 // ---------------------------------------------------------------- pool
 // grid (nqb, BH), 256 threads. Thread t: 8 columns starting at 8*(t%16), rows t/16 + 16m.
-// With qc given, the same pass also quantises the 128-row Q block to INT8 (step 2 operands,
+// kMode 0: K only; 1: Q and K; 2: also quantise the 128-row Q block to INT8 (step 2 operands,
 // §2 Q2 of the second page): inv = fl32(127 / amax), code = clamp(rne(fl32(x inv)), +-127),
-// s_q = fl32(amax / 127); an all-zero block gets scale 0 and zero codes.
-template <typename T>
+// s_q = fl32(amax / 127); an all-zero block gets scale 0 and zero codes. Every load of the
+// thread is issued before the first use (the mode is a template argument: a run-time test
+// around the Q loads made the compiler wait for each one in turn).
+template <typename T, int kMode>
 __global__ __launch_bounds__(256) void pool_kernel(const T* __restrict__ Q,
                                                    const T* __restrict__ K,
                                                    double* __restrict__ qsum,
@@ -31,34 +33,36 @@ __global__ __launch_bounds__(256) void pool_kernel(const T* __restrict__ Q,
                                                    int8_t* __restrict__ qc,
                                                    float* __restrict__ sq,
                                                    int8_t* __restrict__ q_tap, int N) {
+  constexpr bool kQ = kMode >= 1, kCodes = kMode == 2;
   __shared__ double red[3][16][kD + 2];
   __shared__ float amax_w[4];
   const int i = blockIdx.x, bh = blockIdx.y, t = threadIdx.x;
   const int cg = t & 15, rl = t >> 4;
   const size_t base = (static_cast<size_t>(bh) * N + static_cast<size_t>(i) * kBQ) * kD;
+  auto off_of = [&](int m) { return base + static_cast<size_t>(rl + 16 * m) * kD + 8 * cg; };
+  Raw8<T> rq[8], rk[8];
+#pragma unroll
+  for (int m = 0; m < 8; ++m) {
+    if constexpr (kQ) rq[m] = load_raw8<T>(Q + off_of(m));
+    rk[m] = load_raw8<T>(K + off_of(m));
+  }
   double aq[8] = {}, ak0[8] = {}, ak1[8] = {};
-  float qv[8][8];
   float am = 0.f;
 #pragma unroll
   for (int m = 0; m < 8; ++m) {
-    const size_t off = base + static_cast<size_t>(rl + 16 * m) * kD + 8 * cg;
-    if (Q != nullptr) {
-      load8<T>(Q + off, qv[m]);
-#pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        aq[c] += static_cast<double>(qv[m][c]);
-        am = fmaxf(am, fabsf(qv[m][c]));
-      }
-    }
-    float v[8];
-    load8<T>(K + off, v);
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
-      if (m < 4) ak0[c] += static_cast<double>(v[c]);
-      else ak1[c] += static_cast<double>(v[c]);
+      if constexpr (kQ) {
+        const float x = raw8_at(rq[m], c);
+        aq[c] += static_cast<double>(x);
+        am = fmaxf(am, fabsf(x));
+      }
+      const double y = static_cast<double>(raw8_at(rk[m], c));
+      if (m < 4) ak0[c] += y;
+      else ak1[c] += y;
     }
   }
-  if (qc != nullptr) {
+  if constexpr (kCodes) {
     am = wave_max(am);
     if ((t & 63) == 0) amax_w[t >> 6] = am;
   }
@@ -69,16 +73,16 @@ __global__ __launch_bounds__(256) void pool_kernel(const T* __restrict__ Q,
     red[2][rl][8 * cg + c] = ak1[c];
   }
   __syncthreads();
-  if (qc != nullptr) {
+  if constexpr (kCodes) {
     const float amb = fmaxf(fmaxf(amax_w[0], amax_w[1]), fmaxf(amax_w[2], amax_w[3]));
     const float inv = amb > 0.f ? 127.0f / amb : 0.f;
 #pragma unroll
     for (int m = 0; m < 8; ++m) {
-      const size_t off = base + static_cast<size_t>(rl + 16 * m) * kD + 8 * cg;
-      const uint2 w = make_uint2(i8_pack4(qv[m][0], qv[m][1], qv[m][2], qv[m][3], inv),
-                                 i8_pack4(qv[m][4], qv[m][5], qv[m][6], qv[m][7], inv));
-      *reinterpret_cast<uint2*>(qc + off) = w;
-      if (q_tap != nullptr) *reinterpret_cast<uint2*>(q_tap + off) = w;
+      const uint2 w = make_uint2(
+          i8_pack4(raw8_at(rq[m], 0), raw8_at(rq[m], 1), raw8_at(rq[m], 2), raw8_at(rq[m], 3), inv),
+          i8_pack4(raw8_at(rq[m], 4), raw8_at(rq[m], 5), raw8_at(rq[m], 6), raw8_at(rq[m], 7), inv));
+      *reinterpret_cast<uint2*>(qc + off_of(m)) = w;
+      if (q_tap != nullptr) *reinterpret_cast<uint2*>(q_tap + off_of(m)) = w;
     }
     if (t == 0) sq[static_cast<size_t>(bh) * (N / kBQ) + i] = amb / 127.0f;
   }
@@ -88,7 +92,7 @@ __global__ __launch_bounds__(256) void pool_kernel(const T* __restrict__ Q,
     double s = 0.0;
     for (int r = 0; r < 16; ++r) s += red[which][r][c];
     if (which == 0) {
-      if (Q != nullptr) qsum[(static_cast<size_t>(bh) * (N / kBQ) + i) * kD + c] = s;
+      if constexpr (kQ) qsum[(static_cast<size_t>(bh) * (N / kBQ) + i) * kD + c] = s;
     } else {
       ksum[(static_cast<size_t>(bh) * (N / kBK) + 2 * i) * kD + c] = s;
     }
@@ -100,17 +104,29 @@ __global__ __launch_bounds__(256) void pool_kernel(const T* __restrict__ Q,
   }
 }
 
+template <typename T>
+static void launch_pool_t(const Geom& g, const T* Q, const T* K, double* qsum, double* ksum,
+                          int8_t* qc, float* sq, int8_t* q_tap, hipStream_t s) {
+  dim3 grid(g.nqb, g.BH);
+  if (Q == nullptr)
+    hipLaunchKernelGGL((pool_kernel<T, 0>), grid, dim3(256), 0, s, Q, K, qsum, ksum, qc, sq,
+                       q_tap, g.N);
+  else if (qc == nullptr)
+    hipLaunchKernelGGL((pool_kernel<T, 1>), grid, dim3(256), 0, s, Q, K, qsum, ksum, qc, sq,
+                       q_tap, g.N);
+  else
+    hipLaunchKernelGGL((pool_kernel<T, 2>), grid, dim3(256), 0, s, Q, K, qsum, ksum, qc, sq,
+                       q_tap, g.N);
+}
+
 hipError_t launch_pool(const Geom& g, int dtype, const void* Q, const void* K, double* qsum,
                        double* ksum, int8_t* qc, float* sq, int8_t* q_tap, hipStream_t s) {
-  dim3 grid(g.nqb, g.BH);
   if (dtype == 0)
-    hipLaunchKernelGGL(pool_kernel<float>, grid, dim3(256), 0, s,
-                       static_cast<const float*>(Q), static_cast<const float*>(K), qsum, ksum, qc,
-                       sq, q_tap, g.N);
+    launch_pool_t<float>(g, static_cast<const float*>(Q), static_cast<const float*>(K), qsum,
+                         ksum, qc, sq, q_tap, s);
   else
-    hipLaunchKernelGGL(pool_kernel<uint16_t>, grid, dim3(256), 0, s,
-                       static_cast<const uint16_t*>(Q), static_cast<const uint16_t*>(K), qsum,
-                       ksum, qc, sq, q_tap, g.N);
+    launch_pool_t<uint16_t>(g, static_cast<const uint16_t*>(Q), static_cast<const uint16_t*>(K),
+                            qsum, ksum, qc, sq, q_tap, s);
   return hipGetLastError();
 }
 
