@@ -4,6 +4,7 @@
 #include <cmath>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/sla2.h"
 #include "sla2_common.h"
@@ -102,6 +103,30 @@ sla2_status check_workspace(const Geom& g, const void* ws, size_t bytes) {
   return SLA2_OK;
 }
 
+// A helper stream and two events per device (created with the device check on the first
+// call, before any graph capture; default priority; kept until the process ends). sla2_forward runs the router's projection and scoring on the
+// helper stream while the key-block precompute runs on the caller's stream: after colmean the
+// two chains are independent (the first is latency-bound, the second bandwidth-bound), and
+// the attention kernel needs both. `ready` forks the helper stream after colmean, `done`
+// joins it before attn. The mutex keeps one call's record/wait pairs together when several
+// host threads share a device.
+struct Fork {
+  hipStream_t side = nullptr;
+  hipEvent_t ready = nullptr, done = nullptr;
+};
+std::mutex g_fork_mu;
+Fork g_fork[64];
+hipError_t make_fork(int dev) {   // caller holds g_fork_mu
+  Fork& f = g_fork[dev];
+  if (f.side == nullptr) {
+    hipError_t e = hipStreamCreateWithFlags(&f.side, hipStreamNonBlocking);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&f.ready, hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&f.done, hipEventDisableTiming);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
 std::atomic<int> g_dev_ok[64];  // 0 unknown, 1 gfx950, 2 other
 
 sla2_status check_device() {
@@ -114,6 +139,10 @@ sla2_status check_device() {
     if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return SLA2_ERR_HIP;
     st = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
     if (st == 1 && configure_router() != hipSuccess) return SLA2_ERR_HIP;
+    if (st == 1) {
+      std::lock_guard<std::mutex> lock(g_fork_mu);
+      if (make_fork(dev) != hipSuccess) return SLA2_ERR_HIP;
+    }
     g_dev_ok[dev].store(st, std::memory_order_relaxed);
   }
   return st == 1 ? SLA2_OK : SLA2_ERR_UNSUPPORTED_DEVICE;
@@ -253,7 +282,8 @@ namespace {
 // then the fused sparse branch + linear branch + combine. Q codes come from the pool pass.
 sla2_status run_branches(const Geom& g, int dt, const void* Q, const void* K, const void* V,
                          const float* alpha, float* O, const sla2_taps* taps, void* ws,
-                         const Plan& p, int list_stride, Rec& rec, hipStream_t stream) {
+                         const Plan& p, int list_stride, Rec& rec, hipStream_t stream,
+                         hipEvent_t join = nullptr) {
   const sla2_taps none{};
   const sla2_taps& tp = taps ? *taps : none;
   const float* sq = tp.s_q ? tp.s_q : at<float>(ws, p.sq);
@@ -293,6 +323,7 @@ sla2_status run_branches(const Geom& g, int dt, const void* Q, const void* K, co
   x.O = O;
   x.O_s_tap = tp.O_s;
   x.O_l_tap = tp.O_l;
+  if (join != nullptr && hipStreamWaitEvent(stream, join, 0) != hipSuccess) return SLA2_ERR_HIP;
   SLA2_LAUNCH(launch_attn(g, dt, Q, x, stream));
   return SLA2_OK;
 }
@@ -331,12 +362,31 @@ sla2_status sla2_forward(const sla2_shape* shape, const void* Q, const void* K, 
                           taps ? taps->q_codes : nullptr, stream));
   SLA2_LAUNCH(launch_colmean(g, at<double>(ws, p.ksum), at<double>(ws, p.mu64), at<float>(ws, p.mu32),
                              taps ? taps->k_colmean : nullptr, stream));
-  SLA2_LAUNCH(launch_project(g, at<double>(ws, p.qsum), at<double>(ws, p.ksum), at<double>(ws, p.mu64),
-                             proj_q, proj_k, at<double>(ws, p.A), at<double>(ws, p.Bt), stream));
-  SLA2_LAUNCH(launch_score_topk(g, at<double>(ws, p.A), at<double>(ws, p.Bt), kb,
-                                at<uint8_t>(ws, p.mask), at<int32_t>(ws, p.list), kb,
-                                at<int32_t>(ws, p.cnt), nullptr, stream));
-  return run_branches(g, dt, Q, K, V, alpha, O, taps, ws, p, kb, rec, stream);
+  auto router_tail = [&](hipStream_t s) -> bool {
+    return launch_project(g, at<double>(ws, p.qsum), at<double>(ws, p.ksum), at<double>(ws, p.mu64),
+                          proj_q, proj_k, at<double>(ws, p.A), at<double>(ws, p.Bt), s) == hipSuccess &&
+           launch_score_topk(g, at<double>(ws, p.A), at<double>(ws, p.Bt), kb,
+                             at<uint8_t>(ws, p.mask), at<int32_t>(ws, p.list), kb,
+                             at<int32_t>(ws, p.cnt), nullptr, s) == hipSuccess;
+  };
+  if (rec.ev != nullptr || debug_sync()) {
+    // per-kernel events or debugging: every kernel in order on the caller's stream
+    SLA2_LAUNCH(launch_project(g, at<double>(ws, p.qsum), at<double>(ws, p.ksum), at<double>(ws, p.mu64),
+                               proj_q, proj_k, at<double>(ws, p.A), at<double>(ws, p.Bt), stream));
+    SLA2_LAUNCH(launch_score_topk(g, at<double>(ws, p.A), at<double>(ws, p.Bt), kb,
+                                  at<uint8_t>(ws, p.mask), at<int32_t>(ws, p.list), kb,
+                                  at<int32_t>(ws, p.cnt), nullptr, stream));
+    return run_branches(g, dt, Q, K, V, alpha, O, taps, ws, p, kb, rec, stream);
+  }
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return SLA2_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_fork_mu);
+  const Fork* f = &g_fork[dev];
+  if (hipEventRecord(f->ready, stream) != hipSuccess ||
+      hipStreamWaitEvent(f->side, f->ready, 0) != hipSuccess || !router_tail(f->side) ||
+      hipEventRecord(f->done, f->side) != hipSuccess)
+    return SLA2_ERR_HIP;
+  return run_branches(g, dt, Q, K, V, alpha, O, taps, ws, p, kb, rec, stream, f->done);
 }
 
 sla2_status sla2_forward_with_mask(const sla2_shape* shape, const void* Q, const void* K,

@@ -28,12 +28,16 @@
  *   Kept count kb = sla2_blocks_kept(N/64, keep_frac) key blocks per query
  *              block; keep_frac must lie in (0, 1].
  *   Pointers   Every array pointer is caller-owned DEVICE memory, 16-byte aligned
- *              (SLA2_ERR_MISALIGNED otherwise). The library allocates nothing and
- *              keeps no pointer after a call returns; buffers must stay alive
+ *              (SLA2_ERR_MISALIGNED otherwise). The library allocates no device
+ *              memory and keeps no pointer after a call returns; buffers must stay alive
  *              until the stream has executed the work.
  *   Workspace  Caller-provided device scratch of sla2_workspace_bytes(...) bytes.
  *   Streams    `stream` is a hipStream_t (NULL = the default stream). All work is
- *              enqueued on it; no call synchronises or copies device -> host.
+ *              ordered on it; no call synchronises or copies device -> host.
+ *              sla2_forward (without stage_events) runs the router's projection
+ *              and scoring on a helper stream that the library creates once per
+ *              device (default priority, with two events): forked from `stream`
+ *              after the column mean, joined back before the attention kernel.
  *   Errors     Arguments are validated on the host before anything is enqueued;
  *              on error nothing is written. A failed launch returns SLA2_ERR_HIP.
  *              No C++ exception crosses this interface. Calls are re-entrant;
