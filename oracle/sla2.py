@@ -21,6 +21,8 @@ Sparse-Linear Attention v2 for Diffusion Transformers" (zhaifeiyue.github.io;
      O_l = phi(Q_i) H_i / (phi(Q_i) Z_i) with H_i, Z_i summed over the dropped
      key blocks of query block i (step 3; §7 note 2).
   4. O = alpha * O_s + (1 - alpha) * O_l with one alpha per query block (step 4).
+  Training-time router (soft_topk): sigma(P_c / tau + lambda_i) with lambda_i set by
+     bisection so that each row sums to kb (§4 Eq. 17 of the second page).
 
 Readings where the pages are silent (each is listed with its reason in the
 design notes of the repository):
@@ -124,6 +126,45 @@ def topk_blocks(P: np.ndarray, kb: int):
         lists[i] = chosen
         mask[i, chosen] = 1
     return mask, lists
+
+
+def soft_topk(P: np.ndarray, kb: int, tau: float = 0.1, iters: int = 200):
+    """SoftTop-k of the router (training time): soft mask sigma(P_ij / tau + lambda_i), with
+    lambda_i the root of sum_j sigma(P_ij / tau + lambda_i) = kb found by bisection
+    ("SLA2: Sparse-Linear Attention v2 for Diffusion Transformers", §4 Eq. 17 and the
+    six-checks item 3; summary page, step 1).
+
+    Reading: the row sum is kb, the kept count of the hard rule (kept_blocks), so that the
+    soft mask tends to the hard Top-k mask as tau -> 0. The root lies in the bracket
+    [L - max_j x_j, L - min_j x_j] with x = P / tau and L = log(kb / (n_kb - kb)): there
+    every term is at most (resp. at least) kb / n_kb. Bisection halves the bracket until it
+    stops shrinking in fp64 (or `iters` steps). kb = n_kb gives a mask of ones and
+    lambda = +inf.
+
+    Returns (soft mask [n_qb, n_kb] fp64, lambda [n_qb] fp64).
+    """
+    P = np.asarray(P, np.float64)
+    n_qb, n_kb = P.shape
+    if kb >= n_kb:
+        return np.ones_like(P), np.full(n_qb, np.inf)
+    x = P / float(tau)
+    L = math.log(kb / (n_kb - kb))
+    lam = np.empty(n_qb)
+    for i in range(n_qb):
+        lo, hi = L - x[i].max(), L - x[i].min()
+        with np.errstate(over="ignore"):   # exp overflow -> a term of exactly 0
+            for _ in range(iters):
+                mid = 0.5 * (lo + hi)
+                if mid <= lo or mid >= hi:
+                    break
+                if (1.0 / (1.0 + np.exp(-(x[i] + mid)))).sum() < kb:
+                    lo = mid
+                else:
+                    hi = mid
+        lam[i] = 0.5 * (lo + hi)
+    with np.errstate(over="ignore"):
+        soft = 1.0 / (1.0 + np.exp(-(x + lam[:, None])))
+    return soft, lam
 
 
 def mask_to_lists(mask: np.ndarray):
