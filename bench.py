@@ -39,6 +39,10 @@ def parse():
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run plain device copies of a known size (the calibration "
                          "workload for the FETCH_SIZE / WRITE_SIZE counters), then exit")
+    ap.add_argument("--op", choices=("forward", "router_soft"), default="forward",
+                    help="forward (default): the inference forward; router_soft: the SoftTop-k "
+                         "router (training-time step 1) on the same workload, its own JSON line")
+    ap.add_argument("--tau", type=float, default=0.1, help="SoftTop-k temperature (router_soft)")
     ap.add_argument("--quiet", action="store_true")
     return ap.parse_args()
 
@@ -105,6 +109,100 @@ def cpu_baseline(args, w, q, k, v, wq, wk, alpha, keep, acc):
     }
 
 
+def run_router_soft(args, w, q, k, wq, wk, keep):
+    """Times sla2_router_soft (SoftTop-k router) like the forward: W warm-up calls, K timed
+    back-to-back calls, then K calls with the library's events around its four kernels."""
+    import numpy as np
+    import torch
+
+    from block_sparse_linear_pool_amd import accounting as acc
+    from block_sparse_linear_pool_amd import sla2
+
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    dev = torch.device("cuda:0")
+    gq, gk = (torch.from_numpy(a).to(dev, dt) for a in (q, k))
+    gwq, gwk = (torch.from_numpy(a).to(dev) for a in (wq, wk))
+    soft = torch.empty((w.B, w.H, w.n_qb, w.n_kb), dtype=torch.float32, device=dev)
+    ws = sla2.workspace_for(gq)
+    kb = sla2.sla2_blocks_kept(w.n_kb, keep)
+    prob = acc.Problem(w.B, w.H, w.N, kb, in_bytes=2 if dt == torch.bfloat16 else 4)
+
+    def step(events=None):
+        sla2.sla2_router_soft(gq, gk, gwq, gwk, keep, args.tau, workspace=ws, out=soft,
+                              events=events)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    names = acc.KERNELS_SOFT_ROUTER
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
+    per = np.zeros(len(names))
+    for _ in range(args.steps):
+        step(evs)
+        torch.cuda.synchronize()
+        per += [evs[i].elapsed_time(evs[i + 1]) for i in range(len(names))]
+    per /= args.steps
+    kernels = {}
+    for n, t in zip(names, per):
+        fl, by = acc.kernel_flops(prob, n), acc.kernel_bytes(prob, n)
+        kernels[n] = {"ms": round(float(t), 5),
+                      "tflops": round(fl / (t * 1e-3) / 1e12, 2) if fl else None,
+                      "gbs": round(by / (t * 1e-3) / 1e9, 1) if by else None}
+        log(args, f"[bench]   {n:11s} {t * 1e3:9.1f} us  {kernels[n]}")
+    dom = names[int(np.argmax(per))]
+    t_dom = float(np.max(per)) * 1e-3
+    if acc.kernel_bound(dom) == "mfma_fp64":
+        achieved = acc.kernel_flops(prob, dom) / t_dom / 1e12
+        peak, unit, bound = acc.MI355X_PEAK["fp64_tflops"], "TFLOP/s", "mfma"
+    else:
+        achieved = acc.kernel_bytes(prob, dom) / t_dom / 1e9
+        peak, unit, bound = acc.MI355X_PEAK["hbm_gbs"], "GB/s", "hbm"
+    rows = w.B * w.H * w.n_qb
+    result = {
+        "metric": "SLA2 SoftTop-k router rows/s (training-time step 1), N=32768 H=12 d=128 @97%",
+        "value": round(rows / (ms * 1e-3), 1),
+        "unit": "query-block rows/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f64+f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d,
+                   "input_dtype": w.dtype, "keep_frac": keep, "kb": kb, "tau": args.tau},
+        "roofline": {"kernel": dom, "bound": bound, "achieved": round(achieved, 2), "peak": peak,
+                     "unit": unit, "frac": round(achieved / peak, 4), "traffic": None,
+                     "avg_launch_ms": round(t_dom * 1e3, 5)},
+        "kernels": kernels,
+    }
+    if not args.no_cpu:
+        from threadpoolctl import threadpool_limits
+
+        from oracle import sla2 as oracle
+        cores = min(16, len(os.sched_getaffinity(0)))
+        heads = list(range(min(args.cpu_heads, w.H)))
+        with threadpool_limits(limits=cores):
+            t0 = time.perf_counter()
+            for h in heads:
+                K = k[0, h].astype(np.float64)
+                mu, mu32 = oracle.colmean(K)
+                _, P = oracle.router_scores(oracle.block_mean(q[0, h].astype(np.float64), 128),
+                                            oracle.block_mean(oracle.smooth_k(K, mu32), 64),
+                                            wq[h], wk[h])
+                oracle.soft_topk(P, kb, args.tau)
+            dt_cpu = time.perf_counter() - t0
+        result["cpu_baseline"] = {
+            "value": round(len(heads) * w.n_qb / dt_cpu, 1), "unit": "query-block rows/s",
+            "cores": cores, "kind": "oracle",
+            "sample": f"batch 0, heads {heads[0]}-{heads[-1]} of {w.H}: the oracle's router up to "
+                      f"P_c and its fp64-bisection SoftTop-k, {dt_cpu:.2f} s"}
+    print(json.dumps(result), flush=True)
+
+
 def main():
     args = parse()
     if args.copy_probe:
@@ -141,6 +239,10 @@ def main():
     ws = sla2.workspace_for(gq)
     kb = sla2.sla2_blocks_kept(w.n_kb, keep)
     prob = acc.Problem(w.B, w.H, w.N, kb, in_bytes=2 if dt == torch.bfloat16 else 4)
+    if args.op == "router_soft":
+        del gv, out
+        run_router_soft(args, w, q, k, wq, wk, keep)
+        return
 
     def step(events=None):
         sla2.sla2_forward(gq, gk, gv, gwq, gwk, ga, keep, out=out, workspace=ws, events=events)

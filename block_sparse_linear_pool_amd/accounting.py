@@ -23,6 +23,8 @@ MI355X_PEAK = {
 
 KERNELS_FORWARD = ("pool", "colmean", "project", "score_topk", "kv_prep", "linear_total", "attn")
 KERNELS_WITH_MASK = ("pool", "colmean", "mask_to_list", "kv_prep", "linear_total", "attn")
+# sla2_router_soft: pool here writes block sums only (no Q codes)
+KERNELS_SOFT_ROUTER = ("pool_sums", "colmean", "project", "score_soft")
 
 
 @dataclasses.dataclass
@@ -79,6 +81,12 @@ def kernel_bytes(p: Problem, name: str) -> float:
     if name == "pool":
         # Q, K read; fp64 block sums, INT8 Q codes and scales written
         return 2 * E * p.in_bytes + BH * (p.nqb + p.nkb) * d * 8 + E + BH * p.nqb * 4
+    if name == "pool_sums":
+        # Q, K read; fp64 block sums written
+        return 2 * E * p.in_bytes + BH * (p.nqb + p.nkb) * d * 8
+    if name == "score_soft":
+        # A, B^T (fp64) read; the fp32 soft mask and lambda written
+        return BH * (p.nqb + p.nkb) * d * 8 + BH * p.nqb * p.nkb * 4 + BH * p.nqb * 4
     if name == "kv_prep":
         # K, V read; INT8 K_s and E4M3 V codes + scales, bf16 h_j^T, z_j, partials written
         return (2 * E * p.in_bytes + 2 * E + BH * p.nkb * 8 + BH * p.nkb * (d * d * 2 + d * 4)
@@ -97,7 +105,7 @@ def kernel_flops(p: Problem, name: str) -> float:
         # INT8/FP8 sparse-branch work only: the linear branch's bf16 phi(Q) H product
         # (4 N d^2 per head) is reported separately by linear_flops()
         return sparse_flops(p)
-    if name == "score_topk":
+    if name in ("score_topk", "score_soft"):
         return 2.0 * p.BH * p.nqb * p.nkb * p.d
     if name == "project":
         return 2.0 * p.BH * (p.nqb + p.nkb) * p.d * p.d
@@ -107,4 +115,10 @@ def kernel_flops(p: Problem, name: str) -> float:
 
 
 def kernel_bound(name: str) -> str:
-    return "mfma" if name == "attn" else "hbm"
+    """Roofline a kernel is priced against: attn on the INT8/FP8 matrix peak, the fp64
+    logits kernels on the fp64 matrix peak, everything else on HBM bandwidth."""
+    if name == "attn":
+        return "mfma"
+    if name in ("score_topk", "score_soft", "project"):
+        return "mfma_fp64"
+    return "hbm"

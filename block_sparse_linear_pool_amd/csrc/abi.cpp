@@ -161,6 +161,7 @@ struct Rec {
   void** ev;
   int n;
   explicit Rec(const sla2_taps* t) : ev(t ? t->stage_events : nullptr), n(0) {}
+  explicit Rec(void** events) : ev(events), n(0) {}
   hipError_t mark(hipStream_t s) {
     if (ev == nullptr || n > SLA2_MAX_STAGES) return hipSuccess;
     return hipEventRecord(static_cast<hipEvent_t>(ev[n++]), s);
@@ -230,7 +231,7 @@ sla2_status sla2_router(const sla2_shape* shape, const void* Q, const void* K,
   const Plan p = make_plan(g);
   const int kb = sla2_blocks_kept(g.nkb, keep_frac);
   const int dt = shape->dtype == SLA2_FP32 ? 0 : 1;
-  Rec rec(nullptr);
+  Rec rec(static_cast<void**>(nullptr));
   SLA2_LAUNCH(launch_pool(g, dt, Q, K, at<double>(workspace, p.qsum), at<double>(workspace, p.ksum),
                           nullptr, nullptr, nullptr, stream));
   SLA2_LAUNCH(launch_colmean(g, at<double>(workspace, p.ksum), at<double>(workspace, p.mu64),
@@ -240,6 +241,39 @@ sla2_status sla2_router(const sla2_shape* shape, const void* Q, const void* K,
                              at<double>(workspace, p.A), at<double>(workspace, p.Bt), stream));
   SLA2_LAUNCH(launch_score_topk(g, at<double>(workspace, p.A), at<double>(workspace, p.Bt), kb,
                                 mask, blocks, kb, nullptr, scores, stream));
+  return SLA2_OK;
+}
+
+sla2_status sla2_router_soft(const sla2_shape* shape, const void* Q, const void* K,
+                             const float* proj_q, const float* proj_k, float keep_frac, float tau,
+                             float* soft_mask, float* lambda, void** stage_events,
+                             void* workspace, size_t workspace_bytes, void* stream_) {
+  Geom g;
+  sla2_status st = check_shape(shape, &g);
+  if (st != SLA2_OK) return st;
+  PtrCheck pc;
+  pc.req(Q); pc.req(K); pc.req(proj_q); pc.req(proj_k); pc.req(soft_mask);
+  pc.opt(lambda);
+  if (pc.st != SLA2_OK) return pc.st;
+  if (!keep_ok(keep_frac) || !std::isfinite(tau) || !(tau > 0.f) || !std::isfinite(1.0f / tau))
+    return SLA2_ERR_BAD_ARGUMENT;
+  if ((st = check_workspace(g, workspace, workspace_bytes)) != SLA2_OK) return st;
+  if ((st = check_device()) != SLA2_OK) return st;
+  hipStream_t stream = static_cast<hipStream_t>(stream_);
+  const Plan p = make_plan(g);
+  const int kb = sla2_blocks_kept(g.nkb, keep_frac);
+  const int dt = shape->dtype == SLA2_FP32 ? 0 : 1;
+  Rec rec(stage_events);
+  if (rec.mark(stream) != hipSuccess) return SLA2_ERR_HIP;
+  SLA2_LAUNCH(launch_pool(g, dt, Q, K, at<double>(workspace, p.qsum), at<double>(workspace, p.ksum),
+                          nullptr, nullptr, nullptr, stream));
+  SLA2_LAUNCH(launch_colmean(g, at<double>(workspace, p.ksum), at<double>(workspace, p.mu64),
+                             at<float>(workspace, p.mu32), nullptr, stream));
+  SLA2_LAUNCH(launch_project(g, at<double>(workspace, p.qsum), at<double>(workspace, p.ksum),
+                             at<double>(workspace, p.mu64), proj_q, proj_k,
+                             at<double>(workspace, p.A), at<double>(workspace, p.Bt), stream));
+  SLA2_LAUNCH(launch_score_soft(g, at<double>(workspace, p.A), at<double>(workspace, p.Bt), kb,
+                                1.0f / tau, soft_mask, lambda, stream));
   return SLA2_OK;
 }
 
@@ -259,7 +293,7 @@ sla2_status sla2_linear_precompute(const sla2_shape* shape, const void* K, const
   hipStream_t stream = static_cast<hipStream_t>(stream_);
   const Plan p = make_plan(g);
   const int dt = shape->dtype == SLA2_FP32 ? 0 : 1;
-  Rec rec(nullptr);
+  Rec rec(static_cast<void**>(nullptr));
   SLA2_LAUNCH(launch_pool(g, dt, nullptr, K, at<double>(workspace, p.qsum),
                           at<double>(workspace, p.ksum), nullptr, nullptr, nullptr, stream));
   SLA2_LAUNCH(launch_colmean(g, at<double>(workspace, p.ksum), at<double>(workspace, p.mu64),

@@ -308,13 +308,82 @@ __device__ void select_row(const double* g, int nkb, int kb, int lane, size_t ro
   }
 }
 
-// grid (ceil(nqb / RT), BH), 256 threads, RT = score_rows(nkb); dynamic LDS RT * nkb doubles.
-// E = keys per lane held in registers (nkb <= 64 E).
+// SoftTop-k of one row (training-time router, §4 Eq. 17 of the second page), by one wavefront:
+// P_c = softmax(g) in fp64, x = P_c / tau in fp32, then lambda with sum_j sigma(x_j + lambda)
+// = kb by bisection over [L - max x, L - min x], L = log(kb / (nkb - kb)) (every term is at
+// most, resp. at least, kb / nkb at the ends), 40 halvings in fp32; the row sums are
+// butterfly reductions (every lane holds the same value, fixed order: deterministic). kb =
+// nkb gives ones and lambda = +inf. Writes soft[row][j] = sigma(x_j + lambda), lam[row].
 template <int E>
+__device__ void soft_row(const double* g, int nkb, int kb, float inv_tau, int lane, size_t row,
+                         float* __restrict__ soft, float* __restrict__ lam) {
+  double ex[E];
+  double mx = -1.0e300;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int j = lane + 64 * e;
+    if (j < nkb) mx = fmax(mx, g[j]);
+  }
+  for (int o = 32; o >= 1; o >>= 1) mx = fmax(mx, __shfl_xor(mx, o));
+  double sum = 0.0;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int j = lane + 64 * e;
+    ex[e] = j < nkb ? exp(g[min(j, nkb - 1)] - mx) : 0.0;
+    sum += ex[e];
+  }
+  for (int o = 32; o >= 1; o >>= 1) sum += __shfl_xor(sum, o);
+  float x[E];
+  float xmax = -INFINITY, xmin = INFINITY;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int j = lane + 64 * e;
+    x[e] = static_cast<float>(ex[e] / sum * static_cast<double>(inv_tau));
+    if (j < nkb) {
+      xmax = fmaxf(xmax, x[e]);
+      xmin = fminf(xmin, x[e]);
+    }
+  }
+  for (int o = 32; o >= 1; o >>= 1) {
+    xmax = fmaxf(xmax, __shfl_xor(xmax, o));
+    xmin = fminf(xmin, __shfl_xor(xmin, o));
+  }
+  float l = INFINITY;
+  if (kb < nkb) {
+    const float L = logf(static_cast<float>(kb) / static_cast<float>(nkb - kb));
+    float lo = L - xmax, hi = L - xmin;
+    for (int it = 0; it < 40; ++it) {
+      const float mid = 0.5f * (lo + hi);
+      float sr = 0.f;
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const int j = lane + 64 * e;
+        if (j < nkb) sr += 1.0f / (1.0f + __expf(-(x[e] + mid)));
+      }
+      for (int o = 32; o >= 1; o >>= 1) sr += __shfl_xor(sr, o);
+      sr = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(sr)));   // uniform
+      if (sr < static_cast<float>(kb)) lo = mid;
+      else hi = mid;
+    }
+    l = 0.5f * (lo + hi);
+  }
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int j = lane + 64 * e;
+    if (j < nkb) soft[row * nkb + j] = kb < nkb ? 1.0f / (1.0f + __expf(-(x[e] + l))) : 1.0f;
+  }
+  if (lane == 0 && lam) lam[row] = l;
+}
+
+// grid (ceil(nqb / RT), BH), 256 threads, RT = score_rows(nkb); dynamic LDS RT * nkb doubles.
+// E = keys per lane held in registers (nkb <= 64 E). kSoft: the SoftTop-k mask and lambda
+// (soft, lam, inv_tau) instead of the hard selection.
+template <int E, bool kSoft>
 __global__ __launch_bounds__(256) void score_topk_kernel(
     const double* __restrict__ A, const double* __restrict__ Bt, int nqb, int nkb, int kb,
     uint8_t* __restrict__ mask, int32_t* __restrict__ list, int list_stride,
-    int32_t* __restrict__ cnt, float* __restrict__ scores) {
+    int32_t* __restrict__ cnt, float* __restrict__ scores, float inv_tau,
+    float* __restrict__ soft, float* __restrict__ lam) {
   extern __shared__ double G[];                 // [RT][nkb]
   __shared__ double as[16][kXPad];
   const int RT = score_rows(nkb);
@@ -372,6 +441,10 @@ __global__ __launch_bounds__(256) void score_topk_kernel(
     if (i >= nqb) break;
     const double* g = G + r * nkb;
     const size_t row = static_cast<size_t>(bh) * nqb + i;
+    if constexpr (kSoft) {
+      soft_row<E>(g, nkb, kb, inv_tau, lane, row, soft, lam);
+      continue;
+    }
     select_row<E>(g, nkb, kb, lane, row, list, list_stride, mask);
     if (lane == 0 && cnt) cnt[row] = kb;
     if (scores) {
@@ -397,10 +470,14 @@ __global__ __launch_bounds__(256) void score_topk_kernel(
 
 hipError_t configure_router() {
   // largest dynamic LDS: RT * nkb doubles = 128 KB at the top of every RT class
-  const void* fns[] = {reinterpret_cast<const void*>(&score_topk_kernel<8>),
-                       reinterpret_cast<const void*>(&score_topk_kernel<16>),
-                       reinterpret_cast<const void*>(&score_topk_kernel<32>),
-                       reinterpret_cast<const void*>(&score_topk_kernel<64>)};
+  const void* fns[] = {reinterpret_cast<const void*>(&score_topk_kernel<8, false>),
+                       reinterpret_cast<const void*>(&score_topk_kernel<16, false>),
+                       reinterpret_cast<const void*>(&score_topk_kernel<32, false>),
+                       reinterpret_cast<const void*>(&score_topk_kernel<64, false>),
+                       reinterpret_cast<const void*>(&score_topk_kernel<8, true>),
+                       reinterpret_cast<const void*>(&score_topk_kernel<16, true>),
+                       reinterpret_cast<const void*>(&score_topk_kernel<32, true>),
+                       reinterpret_cast<const void*>(&score_topk_kernel<64, true>)};
   for (const void* f : fns) {
     const hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize,
                                              16 * 1024 * 8);
@@ -409,25 +486,40 @@ hipError_t configure_router() {
   return hipSuccess;
 }
 
-hipError_t launch_score_topk(const Geom& g, const double* A, const double* Bt, int kb,
-                             uint8_t* mask, int32_t* list, int list_stride, int32_t* cnt,
-                             float* scores, hipStream_t s) {
+template <bool kSoft>
+static void launch_score_t(const Geom& g, const double* A, const double* Bt, int kb, uint8_t* mask,
+                           int32_t* list, int list_stride, int32_t* cnt, float* scores,
+                           float inv_tau, float* soft, float* lam, hipStream_t s) {
   const int RT = score_rows(g.nkb);
   dim3 grid((g.nqb + RT - 1) / RT, g.BH);
   const size_t lds = static_cast<size_t>(RT) * g.nkb * sizeof(double);
   const int E = (g.nkb + 63) / 64;
   if (E <= 8)
-    hipLaunchKernelGGL(score_topk_kernel<8>, grid, dim3(256), lds, s, A, Bt, g.nqb, g.nkb, kb,
-                       mask, list, list_stride, cnt, scores);
+    hipLaunchKernelGGL((score_topk_kernel<8, kSoft>), grid, dim3(256), lds, s, A, Bt, g.nqb, g.nkb,
+                       kb, mask, list, list_stride, cnt, scores, inv_tau, soft, lam);
   else if (E <= 16)
-    hipLaunchKernelGGL(score_topk_kernel<16>, grid, dim3(256), lds, s, A, Bt, g.nqb, g.nkb, kb,
-                       mask, list, list_stride, cnt, scores);
+    hipLaunchKernelGGL((score_topk_kernel<16, kSoft>), grid, dim3(256), lds, s, A, Bt, g.nqb,
+                       g.nkb, kb, mask, list, list_stride, cnt, scores, inv_tau, soft, lam);
   else if (E <= 32)
-    hipLaunchKernelGGL(score_topk_kernel<32>, grid, dim3(256), lds, s, A, Bt, g.nqb, g.nkb, kb,
-                       mask, list, list_stride, cnt, scores);
+    hipLaunchKernelGGL((score_topk_kernel<32, kSoft>), grid, dim3(256), lds, s, A, Bt, g.nqb,
+                       g.nkb, kb, mask, list, list_stride, cnt, scores, inv_tau, soft, lam);
   else
-    hipLaunchKernelGGL(score_topk_kernel<64>, grid, dim3(256), lds, s, A, Bt, g.nqb, g.nkb, kb,
-                       mask, list, list_stride, cnt, scores);
+    hipLaunchKernelGGL((score_topk_kernel<64, kSoft>), grid, dim3(256), lds, s, A, Bt, g.nqb,
+                       g.nkb, kb, mask, list, list_stride, cnt, scores, inv_tau, soft, lam);
+}
+
+hipError_t launch_score_topk(const Geom& g, const double* A, const double* Bt, int kb,
+                             uint8_t* mask, int32_t* list, int list_stride, int32_t* cnt,
+                             float* scores, hipStream_t s) {
+  launch_score_t<false>(g, A, Bt, kb, mask, list, list_stride, cnt, scores, 0.f, nullptr,
+                        nullptr, s);
+  return hipGetLastError();
+}
+
+hipError_t launch_score_soft(const Geom& g, const double* A, const double* Bt, int kb,
+                             float inv_tau, float* soft, float* lam, hipStream_t s) {
+  launch_score_t<true>(g, A, Bt, kb, nullptr, nullptr, 0, nullptr, nullptr, inv_tau, soft, lam,
+                       s);
   return hipGetLastError();
 }
 

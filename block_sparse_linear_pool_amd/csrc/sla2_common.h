@@ -236,6 +236,9 @@ hipError_t launch_project(const Geom& g, const double* qsum, const double* ksum,
 hipError_t launch_score_topk(const Geom& g, const double* A, const double* Bt, int kb,
                              uint8_t* mask, int32_t* list, int list_stride, int32_t* cnt,
                              float* scores, hipStream_t s);
+// SoftTop-k (training-time router): soft [BH, nqb, nkb] fp32, lam [BH, nqb] fp32 (or null)
+hipError_t launch_score_soft(const Geom& g, const double* A, const double* Bt, int kb,
+                             float inv_tau, float* soft, float* lam, hipStream_t s);
 hipError_t launch_mask_to_list(const Geom& g, const uint8_t* mask_in, uint8_t* mask_out,
                                int32_t* list, int32_t* cnt, hipStream_t s);
 // Fragment order of the d x d linear-branch matrices read by the attention kernel. Its

@@ -78,13 +78,15 @@ def lib():
         L.sla2_status_string.argtypes = [ctypes.c_int]
         L.sla2_status_string.restype = ctypes.c_char_p
         L.sla2_router.argtypes = [ctypes.POINTER(Shape), vp, vp, vp, vp, f32, vp, vp, vp, vp, sz, vp]
+        L.sla2_router_soft.argtypes = [ctypes.POINTER(Shape), vp, vp, vp, vp, f32, f32, vp, vp,
+                                       ctypes.POINTER(vp), vp, sz, vp]
         L.sla2_linear_precompute.argtypes = [ctypes.POINTER(Shape), vp, vp, vp, vp, vp, vp, vp,
                                              vp, sz, vp]
         L.sla2_forward.argtypes = [ctypes.POINTER(Shape), vp, vp, vp, vp, vp, vp, f32, ctypes.c_int,
                                    vp, ctypes.POINTER(Taps), vp, sz, vp]
         L.sla2_forward_with_mask.argtypes = [ctypes.POINTER(Shape), vp, vp, vp, vp, vp, ctypes.c_int,
                                              vp, ctypes.POINTER(Taps), vp, sz, vp]
-        for name in ("sla2_router", "sla2_linear_precompute", "sla2_forward",
+        for name in ("sla2_router", "sla2_router_soft", "sla2_linear_precompute", "sla2_forward",
                      "sla2_forward_with_mask"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
@@ -163,6 +165,35 @@ def sla2_router(q, k, proj_q, proj_k, keep_frac, want_mask=True, want_scores=Fal
                            ws.numel(), _stream(dev))
     _check(st, "sla2_router")
     return blocks, mask, scores
+
+
+def sla2_router_soft(q, k, proj_q, proj_k, keep_frac, tau=0.1, want_lambda=True,
+                     workspace=None, out=None, events=None):
+    """SoftTop-k router: returns (soft mask [B,H,N/128,N/64] fp32, lambda [B,H,N/128] fp32 or None).
+
+    `events`: optional list of 5 torch.cuda.Event(enable_timing=True), recorded before the
+    first and after each of the four kernels on the current stream."""
+    _contig(q, k, proj_q, proj_k, out)
+    shp = shape_of(q)
+    B, H, N, _ = q.shape
+    nqb, nkb = N // 128, N // 64
+    dev = q.device
+    soft = out if out is not None else torch.empty((B, H, nqb, nkb), dtype=torch.float32, device=dev)
+    lam = torch.empty((B, H, nqb), dtype=torch.float32, device=dev) if want_lambda else None
+    ws = workspace if workspace is not None else workspace_for(q)
+    evs = None
+    if events is not None:
+        if len(events) < 5:
+            raise ValueError("sla2_router_soft needs 5 events")
+        for e in events[:5]:
+            if e.cuda_event == 0:
+                e.record()                     # torch creates the event on first record
+        evs = (ctypes.c_void_p * 5)(*[e.cuda_event for e in events[:5]])
+    st = lib().sla2_router_soft(ctypes.byref(shp), _ptr(q), _ptr(k), _ptr(proj_q), _ptr(proj_k),
+                                float(keep_frac), float(tau), _ptr(soft), _ptr(lam), evs, _ptr(ws),
+                                ws.numel(), _stream(dev))
+    _check(st, "sla2_router_soft")
+    return soft, lam
 
 
 def sla2_linear_precompute(k, v, want_h=True, want_z=True, workspace=None):

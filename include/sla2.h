@@ -125,6 +125,23 @@ sla2_status sla2_router(const sla2_shape *shape, const void *Q, const void *K,
                         uint8_t *mask, int32_t *blocks, float *scores,
                         void *workspace, size_t workspace_bytes, void *stream);
 
+/* Step 1 with SoftTop-k, the training-time router ("SLA2: Sparse-Linear Attention v2 for
+ * Diffusion Transformers", §4 Eq. 17 and its six-checks item 3; summary page, step 1):
+ *   soft_mask [B,H,N/128,N/64] fp32 sigma(P_c / tau + lambda_i) (required)
+ *   lambda    [B,H,N/128] fp32 lambda_i (or NULL)
+ *   stage_events  NULL, or 5 caller-created hipEvent_t handles recorded on the stream
+ *             before the first kernel and after each of pool, colmean, project and
+ *             score_soft (the SoftTop-k pass), so consecutive pairs time each kernel
+ * P_c as in sla2_router (fp64 logits and softmax). lambda_i makes every row sum to kb =
+ * sla2_blocks_kept(N/64, keep_frac), so the mask tends to the hard Top-k mask as tau -> 0;
+ * it is found by bisection in fp32 (40 halvings of [L - max x, L - min x], x = P_c / tau,
+ * L = log(kb / (N/64 - kb))). kb = N/64 gives a mask of ones and lambda = +inf. tau must be
+ * finite and > 0 with 1/tau finite (SLA2_ERR_BAD_ARGUMENT otherwise). */
+sla2_status sla2_router_soft(const sla2_shape *shape, const void *Q, const void *K,
+                             const float *proj_q, const float *proj_k, float keep_frac,
+                             float tau, float *soft_mask, float *lambda, void **stage_events,
+                             void *workspace, size_t workspace_bytes, void *stream);
+
 /* The linear branch's per-key-block precompute (step 3; §7 note 2) on the smoothed
  * K_s = K - colmean(K):
  *   k_colmean [B,H,d] fp32 (required)

@@ -27,8 +27,8 @@ def test_library_exports_every_declared_symbol():
     L = sla2.lib()
     names = declared_functions()
     assert set(names) == {"sla2_blocks_kept", "sla2_workspace_bytes", "sla2_status_string",
-                          "sla2_router", "sla2_linear_precompute", "sla2_forward",
-                          "sla2_forward_with_mask"}
+                          "sla2_router", "sla2_router_soft", "sla2_linear_precompute",
+                          "sla2_forward", "sla2_forward_with_mask"}
     for n in names:
         assert hasattr(L, n), n
 
@@ -106,6 +106,14 @@ def test_other_entry_points_validate():
     assert r == ARG
     r = L.sla2_router(ctypes.byref(s), A, A, A, A, 0.25, MIS, A, None, A, need, None)
     assert r == MISAL
+    soft = L.sla2_router_soft
+    assert soft(ctypes.byref(s), A, A, A, A, 0.25, 0.1, None, None, None, A, need, None) == NULL
+    assert soft(ctypes.byref(s), A, A, A, A, 0.25, 0.0, A, None, None, A, need, None) == ARG   # tau > 0
+    assert soft(ctypes.byref(s), A, A, A, A, 0.25, float("nan"), A, None, None, A, need, None) == ARG
+    assert soft(ctypes.byref(s), A, A, A, A, 0.25, 1e-45, A, None, None, A, need, None) == ARG  # 1/tau inf
+    assert soft(ctypes.byref(s), A, A, A, A, 1.5, 0.1, A, None, None, A, need, None) == ARG
+    assert soft(ctypes.byref(s), A, A, A, A, 0.25, 0.1, A, MIS, None, A, need, None) == MISAL
+    assert soft(ctypes.byref(s), A, A, A, A, 0.25, 0.1, A, None, None, A, need - 1, None) == WS
     r = L.sla2_linear_precompute(ctypes.byref(s), A, A, None, None, None, A, A, A, need, None)
     assert r == NULL                                            # k_colmean required
     r = L.sla2_linear_precompute(ctypes.byref(s), A, A, A, MIS, None, A, A, A, need, None)
