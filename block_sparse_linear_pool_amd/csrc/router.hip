@@ -308,71 +308,108 @@ __device__ void select_row(const double* g, int nkb, int kb, int lane, size_t ro
   }
 }
 
-// SoftTop-k of one row (training-time router, §4 Eq. 17 of the second page), by one wavefront:
-// P_c = softmax(g) in fp64, x = P_c / tau in fp32, then lambda with sum_j sigma(x_j + lambda)
-// = kb by bisection over [L - max x, L - min x], L = log(kb / (nkb - kb)) (every term is at
-// most, resp. at least, kb / nkb at the ends), 40 halvings in fp32; the row sums are
-// butterfly reductions (every lane holds the same value, fixed order: deterministic). kb =
-// nkb gives ones and lambda = +inf. Writes soft[row][j] = sigma(x_j + lambda), lam[row].
+// SoftTop-k of rows (training-time router, §4 Eq. 17 of the second page), two rows per
+// wavefront at once (their reductions overlap): P_c = softmax(g) in fp64, x = P_c / tau in
+// fp32, then lambda with f(lambda) = sum_j sigma(x_j + lambda) = kb. The root lies in the
+// bracket [L - max x, L - min x], L = log(kb / (nkb - kb)) (every term is at most, resp. at
+// least, kb / nkb at its ends). Safeguarded Newton in fp32, 16 steps from the uniform-row
+// root L - 1 / (tau nkb): each step evaluates f and f' = sum sigma (1 - sigma), narrows the
+// bracket at the current point, and takes the Newton step, or the bracket midpoint when that
+// step leaves the bracket. Row sums are butterfly reductions (every lane holds the same
+// value, fixed order: deterministic). kb = nkb gives ones and lambda = +inf. Writes
+// soft[row][j] = sigma(x_j + lambda) and lam[row]; `valid[q]` false skips row q's writes.
 template <int E>
-__device__ void soft_row(const double* g, int nkb, int kb, float inv_tau, int lane, size_t row,
-                         float* __restrict__ soft, float* __restrict__ lam) {
-  double ex[E];
-  double mx = -1.0e300;
+__device__ void soft_rows(const double* const (&g)[2], const bool (&valid)[2], int nkb, int kb,
+                          float inv_tau, int lane, const size_t (&row)[2],
+                          float* __restrict__ soft, float* __restrict__ lam) {
+  float x[2][E];
 #pragma unroll
-  for (int e = 0; e < E; ++e) {
-    const int j = lane + 64 * e;
-    if (j < nkb) mx = fmax(mx, g[j]);
-  }
-  for (int o = 32; o >= 1; o >>= 1) mx = fmax(mx, __shfl_xor(mx, o));
-  double sum = 0.0;
+  for (int q = 0; q < 2; ++q) {
+    double ex[E];
+    double mx = -1.0e300;
 #pragma unroll
-  for (int e = 0; e < E; ++e) {
-    const int j = lane + 64 * e;
-    ex[e] = j < nkb ? exp(g[min(j, nkb - 1)] - mx) : 0.0;
-    sum += ex[e];
-  }
-  for (int o = 32; o >= 1; o >>= 1) sum += __shfl_xor(sum, o);
-  float x[E];
-  float xmax = -INFINITY, xmin = INFINITY;
-#pragma unroll
-  for (int e = 0; e < E; ++e) {
-    const int j = lane + 64 * e;
-    x[e] = static_cast<float>(ex[e] / sum * static_cast<double>(inv_tau));
-    if (j < nkb) {
-      xmax = fmaxf(xmax, x[e]);
-      xmin = fminf(xmin, x[e]);
+    for (int e = 0; e < E; ++e) {
+      const int j = lane + 64 * e;
+      if (j < nkb) mx = fmax(mx, g[q][j]);
     }
+    for (int o = 32; o >= 1; o >>= 1) mx = fmax(mx, __shfl_xor(mx, o));
+    double sum = 0.0;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const int j = lane + 64 * e;
+      ex[e] = j < nkb ? exp(g[q][min(j, nkb - 1)] - mx) : 0.0;
+      sum += ex[e];
+    }
+    for (int o = 32; o >= 1; o >>= 1) sum += __shfl_xor(sum, o);
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+      x[q][e] = static_cast<float>(ex[e] / sum * static_cast<double>(inv_tau));
   }
-  for (int o = 32; o >= 1; o >>= 1) {
-    xmax = fmaxf(xmax, __shfl_xor(xmax, o));
-    xmin = fminf(xmin, __shfl_xor(xmin, o));
-  }
-  float l = INFINITY;
+  float lv[2] = {INFINITY, INFINITY};
   if (kb < nkb) {
+    float lo[2], hi[2];
     const float L = logf(static_cast<float>(kb) / static_cast<float>(nkb - kb));
-    float lo = L - xmax, hi = L - xmin;
-    for (int it = 0; it < 40; ++it) {
-      const float mid = 0.5f * (lo + hi);
-      float sr = 0.f;
 #pragma unroll
-      for (int e = 0; e < E; ++e) {
-        const int j = lane + 64 * e;
-        if (j < nkb) sr += 1.0f / (1.0f + __expf(-(x[e] + mid)));
+    for (int q = 0; q < 2; ++q) {
+      float xmax = -INFINITY, xmin = INFINITY;
+#pragma unroll
+      for (int e = 0; e < E; ++e)
+        if (lane + 64 * e < nkb) {
+          xmax = fmaxf(xmax, x[q][e]);
+          xmin = fminf(xmin, x[q][e]);
+        }
+      for (int o = 32; o >= 1; o >>= 1) {
+        xmax = fmaxf(xmax, __shfl_xor(xmax, o));
+        xmin = fminf(xmin, __shfl_xor(xmin, o));
       }
-      for (int o = 32; o >= 1; o >>= 1) sr += __shfl_xor(sr, o);
-      sr = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(sr)));   // uniform
-      if (sr < static_cast<float>(kb)) lo = mid;
-      else hi = mid;
+      lo[q] = L - xmax;
+      hi[q] = L - xmin;
+      lv[q] = fminf(fmaxf(L - inv_tau / static_cast<float>(nkb), lo[q]), hi[q]);
     }
-    l = 0.5f * (lo + hi);
+    const float kbf = static_cast<float>(kb);
+    for (int it = 0; it < 16; ++it) {
+      float f[2], df[2];
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        f[q] = 0.f;
+        df[q] = 0.f;
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+          if (lane + 64 * e < nkb) {
+            const float sg = 1.0f / (1.0f + __expf(-(x[q][e] + lv[q])));
+            f[q] += sg;
+            df[q] = fmaf(sg, 1.0f - sg, df[q]);
+          }
+      }
+      for (int o = 32; o >= 1; o >>= 1) {
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          f[q] += __shfl_xor(f[q], o);
+          df[q] += __shfl_xor(df[q], o);
+        }
+      }
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const float fq = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(f[q])));
+        const float dq = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(df[q])));
+        if (fq < kbf) lo[q] = lv[q];
+        else hi[q] = lv[q];
+        const float nt = lv[q] - (fq - kbf) / dq;
+        lv[q] = (nt > lo[q] && nt < hi[q]) ? nt : 0.5f * (lo[q] + hi[q]);
+      }
+    }
   }
 #pragma unroll
-  for (int e = 0; e < E; ++e) {
-    const int j = lane + 64 * e;
-    if (j < nkb) soft[row * nkb + j] = kb < nkb ? 1.0f / (1.0f + __expf(-(x[e] + l))) : 1.0f;
+  for (int q = 0; q < 2; ++q) {
+    if (!valid[q]) continue;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const int j = lane + 64 * e;
+      if (j < nkb)
+        soft[row[q] * nkb + j] = kb < nkb ? 1.0f / (1.0f + __expf(-(x[q][e] + lv[q]))) : 1.0f;
+    }
+    if (lane == 0 && lam) lam[row[q]] = lv[q];
   }
-  if (lane == 0 && lam) lam[row] = l;
 }
 
 // grid (ceil(nqb / RT), BH), 256 threads, RT = score_rows(nkb); dynamic LDS RT * nkb doubles.
@@ -442,7 +479,14 @@ __global__ __launch_bounds__(256) void score_topk_kernel(
     const double* g = G + r * nkb;
     const size_t row = static_cast<size_t>(bh) * nqb + i;
     if constexpr (kSoft) {
-      soft_row<E>(g, nkb, kb, inv_tau, lane, row, soft, lam);
+      // rows r and r + 4 together (the second only when it exists)
+      const int r2 = r + 4;
+      const bool v2 = r2 < RT && i0 + r2 < nqb;
+      const double* const gq[2] = {g, G + (v2 ? r2 : r) * nkb};
+      const bool vq[2] = {true, v2};
+      const size_t rq[2] = {row, row + (v2 ? 4 : 0)};
+      soft_rows<E>(gq, vq, nkb, kb, inv_tau, lane, rq, soft, lam);
+      if (RT > 4) break;   // this wavefront's rows are done (RT <= 8)
       continue;
     }
     select_row<E>(g, nkb, kb, lane, row, list, list_stride, mask);
