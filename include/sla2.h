@@ -134,8 +134,10 @@ sla2_status sla2_router(const sla2_shape *shape, const void *Q, const void *K,
  *             score_soft (the SoftTop-k pass), so consecutive pairs time each kernel
  * P_c as in sla2_router (fp64 logits and softmax). lambda_i makes every row sum to kb =
  * sla2_blocks_kept(N/64, keep_frac), so the mask tends to the hard Top-k mask as tau -> 0;
- * it is found by bisection in fp32 (40 halvings of [L - max x, L - min x], x = P_c / tau,
- * L = log(kb / (N/64 - kb))). kb = N/64 gives a mask of ones and lambda = +inf. tau must be
+ * it is found in fp32 by 16 safeguarded Newton steps inside the bracket [L - max x,
+ * L - min x], x = P_c / tau, L = log(kb / (N/64 - kb)) (the pages' binary search, with
+ * Newton steps where they stay in the bracket). kb = N/64 gives a mask of ones and
+ * lambda = +inf. Deterministic (fixed-order reductions). tau must be
  * finite and > 0 with 1/tau finite (SLA2_ERR_BAD_ARGUMENT otherwise). */
 sla2_status sla2_router_soft(const sla2_shape *shape, const void *Q, const void *K,
                              const float *proj_q, const float *proj_k, float keep_frac,
