@@ -1,0 +1,70 @@
+"""Parity at the full sizes of the two larger workloads (GPU, through the C ABI).
+
+Each test runs sla2_forward on the whole workload, every batch and head in one call (the
+library's normal launch for that shape), and compares sampled (batch, head) slices with the
+oracle: the kept sets must agree outside the 1e-5 near-tie band of P_c, and O must be within
+rel L2 3e-3 / max-abs 2e-2 of the oracle run with the GPU's mask. The oracle takes tens of
+seconds per slice at these sizes, hence the longer per-test timeouts.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from block_sparse_linear_pool_amd import sla2
+from block_sparse_linear_pool_amd import workloads as W
+from oracle import sla2 as oracle
+from tests.gpu_helpers import MAX_ABS_TOL, REL_L2_TOL, check_mask_band, dev, host, max_abs, rel_l2
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def run_and_check(w, plan):
+    """plan: [(keep fraction, [(b, h), ...]), ...] on one generated workload."""
+    q, k, v = W.generate(w)
+    wq, wk, alpha = W.weights(w)
+    t = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    g = [dev(q, t), dev(k, t), dev(v, t), dev(wq), dev(wk), dev(alpha)]
+    ws = sla2.workspace_for(g[0])
+    out = torch.empty(g[0].shape, dtype=torch.float32, device="cuda:0")
+    for keep, samples in plan:
+        O = sla2.sla2_forward(*g, keep, out=out, workspace=ws)
+        _, mask, _ = sla2.sla2_router(g[0], g[1], g[3], g[4], keep, workspace=ws)
+        torch.cuda.synchronize()
+        O, mask = host(O), host(mask)
+        assert np.isfinite(O).all()
+        for b, h in samples:
+            r = oracle.forward_head(q[b, h], k[b, h], v[b, h], wq[h], wk[h], alpha[h], keep)
+            if not np.array_equal(mask[b, h], r["mask"]):
+                differ = check_mask_band(r["P_c"], r["kb"], mask[b, h])
+                say(f"  keep {keep} b{b} h{h}: {differ} rows differ inside the band")
+                r = oracle.forward_head(q[b, h], k[b, h], v[b, h], wq[h], wk[h], alpha[h], keep,
+                                        mask=mask[b, h])
+            e, m = rel_l2(O[b, h], r["O"]), max_abs(O[b, h], r["O"])
+            say(f"  keep {keep} (kb {r['kb']}) b{b} h{h}: O relL2 {e:.2e} maxabs {m:.2e}")
+            assert e <= REL_L2_TOL and m <= MAX_ABS_TOL
+
+
+@pytest.mark.timeout(600)
+def test_sparsity_sweep_b2_full_size():
+    """B = 2 (independent batches), H = 12, N = 32768; kept 20 %, 10 %, 5 %, 3 %. One slice per
+    fraction, alternating batches."""
+    w = W.WORKLOADS["sweep_B2_N32768"]
+    say("sweep", w.keep_frac)
+    run_and_check(w, [(keep, [(n % 2, (5 * n + 2) % w.H)]) for n, keep in enumerate(w.keep_frac)])
+
+
+@pytest.mark.timeout(600)
+def test_wan14b_720p_full_size():
+    """B = 1, H = 40, N = 75648 (591 query blocks, 1182 key blocks), 5 % kept: the largest
+    shape, 591 x 40 = 23640 rows over the persistent grid; one slice checked."""
+    w = W.WORKLOADS["wan14b_720p_N75648"]
+    say("wan14b", w.keep_frac)
+    run_and_check(w, [(w.keep_frac[0], [(0, 27)])])
