@@ -21,6 +21,8 @@ Sparse-Linear Attention v2 for Diffusion Transformers" (zhaifeiyue.github.io;
      O_l = phi(Q_i) H_i / (phi(Q_i) Z_i) with H_i, Z_i summed over the dropped
      key blocks of query block i (step 3; §7 note 2).
   4. O = alpha * O_s + (1 - alpha) * O_l with one alpha per query block (step 4).
+  Comparison workload (forward_head_sla1): the earlier SLA mix O = O_s + O_l Wo with the
+     heuristic router (proj = I), §2 Q2 table of the second page.
   Training-time router (soft_topk): sigma(P_c / tau + lambda_i) with lambda_i set by
      bisection so that each row sums to kb (§4 Eq. 17 of the second page).
 
@@ -323,6 +325,19 @@ def forward_head(Q, K, V, Wq, Wk, alpha_row, keep_frac, quant=True, mask=None):
     O_l, h, z = linear_branch(Q, Ks, V, mask)
     O = combine(O_s, O_l, alpha_row)
     res.update(ops=ops, O_s=O_s, O_l=O_l, O=O, h=h, z=z, Ks=Ks)
+    return res
+
+
+def forward_head_sla1(Q, K, V, Wo, keep_frac, quant=True, mask=None):
+    """The earlier SLA formulation as a comparison workload, one (batch, head) slice
+    ("SLA2: Sparse-Linear Attention v2 for Diffusion Transformers", §2 Q2 before/after table):
+    the heuristic router softmax(Qbar Kbar^T / sqrt(d)) -> Top-k (the learnable router with
+    proj_q = proj_k = I) and the mix O = O_s + Proj(O_l) with one d x d projection,
+    Proj(x) = x @ Wo (no bias, no alpha). The branches are the same as in forward_head.
+    """
+    eye = np.eye(np.shape(Q)[1])
+    res = forward_head(Q, K, V, eye, eye, np.ones(np.shape(Q)[0] // BQ), keep_frac, quant, mask)
+    res["O"] = res["O_s"] + res["O_l"] @ np.asarray(Wo, np.float64)
     return res
 
 

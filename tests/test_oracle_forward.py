@@ -264,3 +264,25 @@ def test_projection_orientation_x_times_w():
     # the transposed reading would give a different answer on this input
     wrong = qbar[:, pi] @ kbar.T / math.sqrt(D)
     assert np.abs(r["G"] - wrong).max() > 1e-3
+
+
+# ----------------------------------------------------------------------------- SLA (v1) mix
+def test_sla1_relates_to_sla2_for_constant_alpha():
+    """With Proj = ((1 - a) / a) I and the heuristic router, a * (O_s + O_l Proj) is the SLA2
+    mix a O_s + (1 - a) O_l (second page, §2 Q2: the projection of the earlier formulation
+    has to absorb the scale that alpha carries explicitly); unquantised and quantised."""
+    q, k, v, _, _, _ = slice_inputs(seed=21, N=1024)
+    eye = np.eye(D, dtype=np.float32)
+    for a in (0.3, 0.8):
+        for quant in (False, True):
+            r1 = sla2.forward_head_sla1(q, k, v, ((1 - a) / a) * np.eye(D), 0.25, quant=quant)
+            r2 = sla2.forward_head(q, k, v, eye, eye, np.full(1024 // 128, a), 0.25, quant=quant)
+            assert np.array_equal(r1["mask"], r2["mask"])
+            assert np.abs(a * r1["O"] - r2["O"]).max() < 1e-12
+
+
+def test_sla1_zero_projection_is_the_sparse_branch():
+    q, k, v, _, _, _ = slice_inputs(seed=22, N=1024)
+    r = sla2.forward_head_sla1(q, k, v, np.zeros((D, D)), 0.25, quant=False)
+    ref = sla2.sparse_exact(q, r["Ks"], v, [np.flatnonzero(m) for m in r["mask"]])
+    assert np.abs(r["O"] - ref).max() < 1e-12
