@@ -39,9 +39,11 @@ def parse():
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run plain device copies of a known size (the calibration "
                          "workload for the FETCH_SIZE / WRITE_SIZE counters), then exit")
-    ap.add_argument("--op", choices=("forward", "router_soft"), default="forward",
+    ap.add_argument("--op", choices=("forward", "router_soft", "sla1"), default="forward",
                     help="forward (default): the inference forward; router_soft: the SoftTop-k "
-                         "router (training-time step 1) on the same workload, its own JSON line")
+                         "router (training-time step 1); sla1: the earlier SLA mix O = O_s + "
+                         "O_l Wo with the heuristic router (comparison workload); each prints "
+                         "its own JSON line")
     ap.add_argument("--tau", type=float, default=0.1, help="SoftTop-k temperature (router_soft)")
     ap.add_argument("--quiet", action="store_true")
     return ap.parse_args()
@@ -203,6 +205,96 @@ def run_router_soft(args, w, q, k, wq, wk, keep):
     print(json.dumps(result), flush=True)
 
 
+def run_sla1(args, w, q, k, v, keep):
+    """Times sla2_forward_sla1 (the earlier SLA mix, a comparison workload) like the forward."""
+    import numpy as np
+    import torch
+
+    from block_sparse_linear_pool_amd import accounting as acc
+    from block_sparse_linear_pool_amd import sla2
+
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    dev = torch.device("cuda:0")
+    gq, gk, gv = (torch.from_numpy(a).to(dev, dt) for a in (q, k, v))
+    rng = np.random.default_rng([w.seed, 99])
+    wo = torch.from_numpy(rng.normal(0.0, 1.0 / np.sqrt(w.d), (w.H, w.d, w.d)).astype(np.float32)).to(dev)
+    out = torch.empty(gq.shape, dtype=torch.float32, device=dev)
+    ol = torch.empty_like(out)
+    ws = sla2.workspace_for(gq)
+    kb = sla2.sla2_blocks_kept(w.n_kb, keep)
+    prob = acc.Problem(w.B, w.H, w.N, kb, in_bytes=2 if dt == torch.bfloat16 else 4)
+
+    def step(events=None):
+        sla2.sla2_forward_sla1(gq, gk, gv, wo, keep, out=out, o_l=ol, workspace=ws, events=events)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    names = acc.KERNELS_SLA1
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(sla2.MAX_STAGES + 1)]
+    per = np.zeros(len(names))
+    for _ in range(args.steps):
+        step(evs)
+        torch.cuda.synchronize()
+        per += [evs[i].elapsed_time(evs[i + 1]) for i in range(len(names))]
+    per /= args.steps
+    kernels = {}
+    for n, t in zip(names, per):
+        fl, by = acc.kernel_flops(prob, n), acc.kernel_bytes(prob, n)
+        kernels[n] = {"ms": round(float(t), 5),
+                      "tflops": round(fl / (t * 1e-3) / 1e12, 2) if fl else None,
+                      "gbs": round(by / (t * 1e-3) / 1e9, 1) if by else None}
+        log(args, f"[bench]   {n:13s} {t * 1e3:9.1f} us  {kernels[n]}")
+    dom = names[int(np.argmax(per))]
+    t_dom = float(np.max(per)) * 1e-3
+    if acc.kernel_bound(dom) == "mfma":
+        achieved = acc.kernel_flops(prob, dom) / t_dom / 1e12
+        peak, unit, bound = acc.MI355X_PEAK["mfma_i8_fp8_tflops"], "TFLOP/s", "mfma"
+    else:
+        achieved = acc.kernel_bytes(prob, dom) / t_dom / 1e9
+        peak, unit, bound = acc.MI355X_PEAK["hbm_gbs"], "GB/s", "hbm"
+    full = acc.full_attention_flops(prob)
+    result = {
+        "metric": "Earlier SLA mix (comparison) fwd full-attn-equiv TFLOPS, N=32768 H=12 d=128 @97%",
+        "value": round(full / (ms * 1e-3) / 1e12, 2),
+        "unit": "TFLOPS (full-attention-equivalent)",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "int8+fp8",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d,
+                   "input_dtype": w.dtype, "keep_frac": keep, "kb": kb},
+        "roofline": {"kernel": dom, "bound": bound, "achieved": round(achieved, 2), "peak": peak,
+                     "unit": unit, "frac": round(achieved / peak, 4), "traffic": None,
+                     "avg_launch_ms": round(t_dom * 1e3, 5)},
+        "kernels": kernels,
+    }
+    if not args.no_cpu:
+        from threadpoolctl import threadpool_limits
+
+        from oracle import sla2 as oracle
+        cores = min(16, len(os.sched_getaffinity(0)))
+        heads = list(range(min(args.cpu_heads, w.H)))
+        wo_h = wo.cpu().numpy()
+        with threadpool_limits(limits=cores):
+            t0 = time.perf_counter()
+            for h in heads:
+                oracle.forward_head_sla1(q[0, h].astype(np.float64), k[0, h].astype(np.float64),
+                                         v[0, h].astype(np.float64), wo_h[h], keep)
+            dt_cpu = time.perf_counter() - t0
+        result["cpu_baseline"] = {
+            "value": round(4.0 * w.N * w.N * w.d * len(heads) / dt_cpu / 1e12, 4),
+            "unit": "TFLOPS (full-attention-equivalent)", "cores": cores, "kind": "oracle",
+            "sample": f"batch 0, heads {heads[0]}-{heads[-1]} of {w.H}, fp64 oracle, {dt_cpu:.1f} s"}
+    print(json.dumps(result), flush=True)
+
+
 def main():
     args = parse()
     if args.copy_probe:
@@ -242,6 +334,10 @@ def main():
     if args.op == "router_soft":
         del gv, out
         run_router_soft(args, w, q, k, wq, wk, keep)
+        return
+    if args.op == "sla1":
+        del gv, out
+        run_sla1(args, w, q, k, v, keep)
         return
 
     def step(events=None):

@@ -25,6 +25,9 @@ KERNELS_FORWARD = ("pool", "colmean", "project", "score_topk", "kv_prep", "linea
 KERNELS_WITH_MASK = ("pool", "colmean", "mask_to_list", "kv_prep", "linear_total", "attn")
 # sla2_router_soft: pool here writes block sums only (no Q codes)
 KERNELS_SOFT_ROUTER = ("pool_sums", "colmean", "project", "score_soft")
+# sla2_forward_sla1 (the earlier SLA mix): identity projections, alpha = 1 fill, O += O_l Wo
+KERNELS_SLA1 = ("pool", "colmean", "project", "score_topk", "fill", "kv_prep", "linear_total",
+                "attn", "sla1_mix")
 
 
 @dataclasses.dataclass
@@ -87,6 +90,9 @@ def kernel_bytes(p: Problem, name: str) -> float:
     if name == "score_soft":
         # A, B^T (fp64) read; the fp32 soft mask and lambda written
         return BH * (p.nqb + p.nkb) * d * 8 + BH * p.nqb * p.nkb * 4 + BH * p.nqb * 4
+    if name == "sla1_mix":
+        # O_l and O read, O written
+        return 3 * E * 4
     if name == "kv_prep":
         # K, V read; INT8 K_s and E4M3 V codes + scales, bf16 h_j^T, z_j, partials written
         return (2 * E * p.in_bytes + 2 * E + BH * p.nkb * 8 + BH * p.nkb * (d * d * 2 + d * 4)
@@ -109,7 +115,7 @@ def kernel_flops(p: Problem, name: str) -> float:
         return 2.0 * p.BH * p.nqb * p.nkb * p.d
     if name == "project":
         return 2.0 * p.BH * (p.nqb + p.nkb) * p.d * p.d
-    if name == "kv_prep":
+    if name in ("kv_prep", "sla1_mix"):
         return 2.0 * p.BH * p.N * p.d * p.d
     return 0.0
 

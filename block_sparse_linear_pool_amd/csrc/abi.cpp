@@ -19,7 +19,7 @@ size_t up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 struct Plan {
   size_t qsum, ksum, mu64, mu32, A, Bt, mask, list, cnt, qc, kc, vc, sq, sk, sv, hbf, z, hpart,
-      zpart, htot, ztot, total;
+      zpart, htot, ztot, ones, total;
 };
 
 Plan make_plan(const Geom& g) {
@@ -53,6 +53,7 @@ Plan make_plan(const Geom& g) {
   p.zpart = take(BH * np * kD * 4);
   p.htot = take(BH * kD * kD * 4);
   p.ztot = take(BH * kD * 4);
+  p.ones = take(static_cast<size_t>(g.H) * nqb * 4);
   p.total = o;
   return p;
 }
@@ -421,6 +422,46 @@ sla2_status sla2_forward(const sla2_shape* shape, const void* Q, const void* K, 
       hipEventRecord(f->done, f->side) != hipSuccess)
     return SLA2_ERR_HIP;
   return run_branches(g, dt, Q, K, V, alpha, O, taps, ws, p, kb, rec, stream, f->done);
+}
+
+sla2_status sla2_forward_sla1(const sla2_shape* shape, const void* Q, const void* K,
+                              const void* V, const float* proj_o, float keep_frac,
+                              sla2_quant quant, float* O, float* O_l, void** stage_events,
+                              void* workspace, size_t workspace_bytes, void* stream_) {
+  Geom g;
+  sla2_status st = check_shape(shape, &g);
+  if (st != SLA2_OK) return st;
+  PtrCheck pc;
+  pc.req(Q); pc.req(K); pc.req(V); pc.req(proj_o); pc.req(O); pc.req(O_l);
+  if (pc.st != SLA2_OK) return pc.st;
+  if (!keep_ok(keep_frac) || quant != SLA2_QUANT_I8_FP8) return SLA2_ERR_BAD_ARGUMENT;
+  if ((st = check_workspace(g, workspace, workspace_bytes)) != SLA2_OK) return st;
+  if ((st = check_device()) != SLA2_OK) return st;
+  hipStream_t stream = static_cast<hipStream_t>(stream_);
+  const Plan p = make_plan(g);
+  const int kb = sla2_blocks_kept(g.nkb, keep_frac);
+  const int dt = shape->dtype == SLA2_FP32 ? 0 : 1;
+  void* ws = workspace;
+  Rec rec(stage_events);
+  if (rec.mark(stream) != hipSuccess) return SLA2_ERR_HIP;
+  SLA2_LAUNCH(launch_pool(g, dt, Q, K, at<double>(ws, p.qsum), at<double>(ws, p.ksum),
+                          at<int8_t>(ws, p.qc), at<float>(ws, p.sq), nullptr, stream));
+  SLA2_LAUNCH(launch_colmean(g, at<double>(ws, p.ksum), at<double>(ws, p.mu64), at<float>(ws, p.mu32),
+                             nullptr, stream));
+  // the heuristic router: proj_q = proj_k = I (null weights select the identity mode)
+  SLA2_LAUNCH(launch_project(g, at<double>(ws, p.qsum), at<double>(ws, p.ksum), at<double>(ws, p.mu64),
+                             nullptr, nullptr, at<double>(ws, p.A), at<double>(ws, p.Bt), stream));
+  SLA2_LAUNCH(launch_score_topk(g, at<double>(ws, p.A), at<double>(ws, p.Bt), kb,
+                                at<uint8_t>(ws, p.mask), at<int32_t>(ws, p.list), kb,
+                                at<int32_t>(ws, p.cnt), nullptr, stream));
+  // both branches with alpha = 1 and the O_l tap: O receives O_s, O_l the linear branch
+  SLA2_LAUNCH(launch_fill(at<float>(ws, p.ones), g.H * g.nqb, 1.0f, stream));
+  sla2_taps tp{};
+  tp.O_l = O_l;
+  st = run_branches(g, dt, Q, K, V, at<float>(ws, p.ones), O, &tp, ws, p, kb, rec, stream);
+  if (st != SLA2_OK) return st;
+  SLA2_LAUNCH(launch_sla1_mix(g, O_l, proj_o, O, stream));
+  return SLA2_OK;
 }
 
 sla2_status sla2_forward_with_mask(const sla2_shape* shape, const void* Q, const void* K,

@@ -373,4 +373,61 @@ hipError_t launch_linear_total(const Geom& g, const float* hpart, const float* z
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------- the earlier SLA mix
+// O += O_l Wo per (batch, head) (comparison workload: the mix O = O_s + Proj(O_l) of the
+// earlier SLA formulation, §2 Q2 table of the second page; O holds O_s on entry). grid
+// (N / 128, BH), 256 threads: the head's Wo staged in LDS (fp32, 64 KB: two workgroups per
+// CU); wavefront w forms rows 32 w .. +31 as four 32 x 32 tiles with fp32 MFMA 32x32x2 (exact
+// fp32 products, fp32 accumulation). K step s pairs k = s (lanes 0-31) with k = 64 + s (lanes
+// 32-63), so each lane's 64 values of its O_l row are one contiguous 256-byte run, loaded
+// straight into registers; the four tiles are four independent accumulation chains.
+__global__ __launch_bounds__(256) void sla1_mix_kernel(const float* __restrict__ Ol,
+                                                       const float* __restrict__ Wo,
+                                                       float* __restrict__ O, int N, int H) {
+  __shared__ float wo[kD][kD];
+  const int bh = blockIdx.y, h = bh % H, t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int l32 = lane & 31, g = lane >> 5;
+  const size_t r0 = static_cast<size_t>(bh) * N + static_cast<size_t>(blockIdx.x) * 128 + 32 * w;
+  // this lane's O_l values: row r0 + l32, k = 64 g .. 64 g + 63
+  float a[64];
+  const float* ap = Ol + (r0 + l32) * kD + 64 * g;
+#pragma unroll
+  for (int u = 0; u < 16; ++u) {
+    const f32x4 v = reinterpret_cast<const f32x4*>(ap)[u];
+    a[4 * u] = v[0]; a[4 * u + 1] = v[1]; a[4 * u + 2] = v[2]; a[4 * u + 3] = v[3];
+  }
+  const float* wsrc = Wo + static_cast<size_t>(h) * kD * kD;
+  for (int e = t; e < kD * kD / 4; e += 256)
+    reinterpret_cast<f32x4*>(&wo[0][0])[e] = reinterpret_cast<const f32x4*>(wsrc)[e];
+  __syncthreads();
+  f32x16 acc[4] = {f32x16{}, f32x16{}, f32x16{}, f32x16{}};
+#pragma unroll
+  for (int s = 0; s < kD / 2; ++s) {
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct)
+      acc[ct] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[s], wo[s + 64 * g][32 * ct + l32], acc[ct],
+                                                      0, 0, 0);
+  }
+  // O += acc: register i of tile ct is row 8 (i / 4) + 4 g + i % 4, column 32 ct + l32; all
+  // loads of O first, then the adds and stores
+  float* ob = O + r0 * kD;
+  float cur[4][16];
+#pragma unroll
+  for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      cur[ct][i] = ob[(8 * (i >> 2) + 4 * g + (i & 3)) * kD + 32 * ct + l32];
+#pragma unroll
+  for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      ob[(8 * (i >> 2) + 4 * g + (i & 3)) * kD + 32 * ct + l32] = cur[ct][i] + acc[ct][i];
+}
+
+hipError_t launch_sla1_mix(const Geom& g, const float* Ol, const float* Wo, float* O,
+                           hipStream_t s) {
+  hipLaunchKernelGGL(sla1_mix_kernel, dim3(g.N / 128, g.BH), dim3(256), 0, s, Ol, Wo, O, g.N, g.H);
+  return hipGetLastError();
+}
+
 }  // namespace sla2

@@ -185,7 +185,7 @@ constexpr int kXPad = kD + 1;
 __global__ __launch_bounds__(256) void project_kernel(
     const double* __restrict__ qsum, const double* __restrict__ ksum,
     const double* __restrict__ mu64, const float* __restrict__ wq, const float* __restrict__ wk,
-    double* __restrict__ A, double* __restrict__ Bt, int nqb, int nkb, int H) {
+    double* __restrict__ A, double* __restrict__ Bt, int nqb, int nkb, int H, int identity) {
   __shared__ double xs[16][kXPad];
   const int bh = blockIdx.y, h = bh % H, t = threadIdx.x;
   const int lane = t & 63, w = t >> 6;
@@ -204,6 +204,17 @@ __global__ __launch_bounds__(256) void project_kernel(
       if (!is_q) v -= mu64[bh * kD + c];
     }
     xs[r][c] = v;
+  }
+  if (identity) {
+    // proj_q = proj_k = I (the heuristic router of the earlier SLA): A = Qbar, B = Kbar - mu
+    __syncthreads();
+    for (int e = t; e < 16 * kD; e += 256) {
+      const int r = e >> 7, c = e & 127;
+      if (r0 + r >= nrows) continue;
+      if (is_q) A[(static_cast<size_t>(bh) * nqb + r0 + r) * kD + c] = xs[r][c];
+      else Bt[(static_cast<size_t>(bh) * kD + c) * nkb + r0 + r] = xs[r][c];
+    }
+    return;
   }
   const float* W = (is_q ? wq : wk) + static_cast<size_t>(h) * kD * kD;
   const int ra = lane & 15, kq = lane >> 4;
@@ -238,7 +249,18 @@ hipError_t launch_project(const Geom& g, const double* qsum, const double* ksum,
                           double* Bt, hipStream_t s) {
   dim3 grid((g.nqb + 15) / 16 + (g.nkb + 15) / 16, g.BH);
   hipLaunchKernelGGL(project_kernel, grid, dim3(256), 0, s, qsum, ksum, mu64, wq, wk, A, Bt,
-                     g.nqb, g.nkb, g.H);
+                     g.nqb, g.nkb, g.H, wq == nullptr ? 1 : 0);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- fill
+__global__ __launch_bounds__(256) void fill_kernel(float* __restrict__ p, int n, float v) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+
+hipError_t launch_fill(float* p, int n, float v, hipStream_t s) {
+  hipLaunchKernelGGL(fill_kernel, dim3((n + 255) / 256), dim3(256), 0, s, p, n, v);
   return hipGetLastError();
 }
 

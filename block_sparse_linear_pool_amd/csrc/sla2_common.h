@@ -236,6 +236,11 @@ hipError_t launch_project(const Geom& g, const double* qsum, const double* ksum,
 hipError_t launch_score_topk(const Geom& g, const double* A, const double* Bt, int kb,
                              uint8_t* mask, int32_t* list, int list_stride, int32_t* cnt,
                              float* scores, hipStream_t s);
+// p[0 .. n) = v (a kernel: no memset node in a captured graph)
+hipError_t launch_fill(float* p, int n, float v, hipStream_t s);
+// the earlier SLA mix: O += O_l Wo per (batch, head); wo [H, d, d] fp32
+hipError_t launch_sla1_mix(const Geom& g, const float* Ol, const float* Wo, float* O,
+                           hipStream_t s);
 // SoftTop-k (training-time router): soft [BH, nqb, nkb] fp32, lam [BH, nqb] fp32 (or null)
 hipError_t launch_score_soft(const Geom& g, const double* A, const double* Bt, int kb,
                              float inv_tau, float* soft, float* lam, hipStream_t s);

@@ -84,10 +84,12 @@ def lib():
                                              vp, sz, vp]
         L.sla2_forward.argtypes = [ctypes.POINTER(Shape), vp, vp, vp, vp, vp, vp, f32, ctypes.c_int,
                                    vp, ctypes.POINTER(Taps), vp, sz, vp]
+        L.sla2_forward_sla1.argtypes = [ctypes.POINTER(Shape), vp, vp, vp, vp, f32, ctypes.c_int,
+                                        vp, vp, ctypes.POINTER(vp), vp, sz, vp]
         L.sla2_forward_with_mask.argtypes = [ctypes.POINTER(Shape), vp, vp, vp, vp, vp, ctypes.c_int,
                                              vp, ctypes.POINTER(Taps), vp, sz, vp]
         for name in ("sla2_router", "sla2_router_soft", "sla2_linear_precompute", "sla2_forward",
-                     "sla2_forward_with_mask"):
+                     "sla2_forward_sla1", "sla2_forward_with_mask"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -266,6 +268,26 @@ def sla2_forward(q, k, v, proj_q, proj_k, alpha, keep_frac, taps=False, out=None
                             ws.numel(), _stream(dev))
     _check(st, "sla2_forward")
     return (o, tdict) if taps else o
+
+
+def sla2_forward_sla1(q, k, v, proj_o, keep_frac, out=None, o_l=None, workspace=None,
+                      events=None):
+    """The earlier SLA mix (comparison workload): returns (O, O_l) fp32 [B,H,N,d].
+
+    `events`: optional list of 10 torch.cuda.Event(enable_timing=True), recorded before the
+    first and after each of the nine kernels on the current stream."""
+    _contig(q, k, v, proj_o, out, o_l)
+    shp = shape_of(q)
+    dev = q.device
+    o = out if out is not None else torch.empty(q.shape, dtype=torch.float32, device=dev)
+    ol = o_l if o_l is not None else torch.empty(q.shape, dtype=torch.float32, device=dev)
+    ws = workspace if workspace is not None else workspace_for(q)
+    evs = event_array(events) if events is not None else None
+    st = lib().sla2_forward_sla1(ctypes.byref(shp), _ptr(q), _ptr(k), _ptr(v), _ptr(proj_o),
+                                 float(keep_frac), SLA2_QUANT_I8_FP8, _ptr(o), _ptr(ol), evs,
+                                 _ptr(ws), ws.numel(), _stream(dev))
+    _check(st, "sla2_forward_sla1")
+    return o, ol
 
 
 def sla2_forward_with_mask(q, k, v, mask, alpha, taps=False, out=None, workspace=None,

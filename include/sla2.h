@@ -164,6 +164,22 @@ sla2_status sla2_forward(const sla2_shape *shape, const void *Q, const void *K, 
                          float keep_frac, sla2_quant quant, float *O, const sla2_taps *taps,
                          void *workspace, size_t workspace_bytes, void *stream);
 
+/* The earlier SLA formulation, as a comparison workload ("SLA2: Sparse-Linear Attention
+ * v2 for Diffusion Transformers", §2 Q2 before/after table): the heuristic router
+ * softmax(Qbar Kbar^T / sqrt(d)) -> Top-k (the learnable router with proj = I), the same
+ * sparse and linear branches, and the mix O = O_s + O_l Wo without alpha.
+ *   proj_o [H,d,d] fp32 Wo, applied as x @ Wo (required)
+ *   O      [B,H,N,d] fp32 output (required)
+ *   O_l    [B,H,N,d] fp32 the linear branch output, written on the way (required)
+ *   stage_events  NULL, or 10 caller-created hipEvent_t handles recorded on the stream
+ *          before the first kernel and after each of pool, colmean, project (identity),
+ *          score_topk, fill (alpha = 1), kv_prep, linear_total, attn and sla1_mix (O += O_l Wo)
+ * O_l Wo is an fp32 matrix product (fp32 MFMA). Same validation as sla2_forward. */
+sla2_status sla2_forward_sla1(const sla2_shape *shape, const void *Q, const void *K,
+                              const void *V, const float *proj_o, float keep_frac,
+                              sla2_quant quant, float *O, float *O_l, void **stage_events,
+                              void *workspace, size_t workspace_bytes, void *stream);
+
 /* The forward with a caller-supplied block mask instead of the router. Any 0/1
  * pattern is accepted (any byte != 0 counts as 1): a row with no kept block gets
  * O_s = 0, a row with no dropped block gets O_l = 0. */

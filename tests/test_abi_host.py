@@ -20,7 +20,7 @@ MIS = 0x10008
 
 def declared_functions():
     text = open(os.path.join(ROOT, "include", "sla2.h")).read()
-    return sorted(set(re.findall(r"\b(sla2_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(sla2_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_library_exports_every_declared_symbol():
@@ -28,7 +28,7 @@ def test_library_exports_every_declared_symbol():
     names = declared_functions()
     assert set(names) == {"sla2_blocks_kept", "sla2_workspace_bytes", "sla2_status_string",
                           "sla2_router", "sla2_router_soft", "sla2_linear_precompute",
-                          "sla2_forward", "sla2_forward_with_mask"}
+                          "sla2_forward", "sla2_forward_sla1", "sla2_forward_with_mask"}
     for n in names:
         assert hasattr(L, n), n
 
@@ -114,6 +114,13 @@ def test_other_entry_points_validate():
     assert soft(ctypes.byref(s), A, A, A, A, 1.5, 0.1, A, None, None, A, need, None) == ARG
     assert soft(ctypes.byref(s), A, A, A, A, 0.25, 0.1, A, MIS, None, A, need, None) == MISAL
     assert soft(ctypes.byref(s), A, A, A, A, 0.25, 0.1, A, None, None, A, need - 1, None) == WS
+    sla1 = L.sla2_forward_sla1
+    assert sla1(ctypes.byref(s), A, A, A, A, 0.25, 1, A, None, None, A, need, None) == NULL   # O_l required
+    assert sla1(ctypes.byref(s), A, A, A, None, 0.25, 1, A, A, None, A, need, None) == NULL  # proj_o required
+    assert sla1(ctypes.byref(s), A, A, A, A, 0.25, 0, A, A, None, A, need, None) == ARG      # quantised only
+    assert sla1(ctypes.byref(s), A, A, A, A, 0.0, 1, A, A, None, A, need, None) == ARG
+    assert sla1(ctypes.byref(s), A, A, A, A, 0.25, 1, A, MIS, None, A, need, None) == MISAL
+    assert sla1(ctypes.byref(s), A, A, A, A, 0.25, 1, A, A, None, A, need - 1, None) == WS
     r = L.sla2_linear_precompute(ctypes.byref(s), A, A, None, None, None, A, A, A, need, None)
     assert r == NULL                                            # k_colmean required
     r = L.sla2_linear_precompute(ctypes.byref(s), A, A, A, MIS, None, A, A, A, need, None)

@@ -1,0 +1,99 @@
+"""The earlier SLA mix (comparison workload) on the GPU: sla2_forward_sla1 against the oracle's
+forward_head_sla1, and against sla2_forward where the two formulations coincide.
+
+Tolerances: O = O_s + O_l Wo carries the linear branch's error through Wo, so O and O_l are held
+to the linear branch's bound (rel L2 5e-3; the sparse branch alone meets 3e-3) and O to max-abs
+2e-2. With Wo = 0 the mix adds exact zeros, so O must equal the sparse-branch tap bit for bit.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from block_sparse_linear_pool_amd import sla2
+from block_sparse_linear_pool_amd import workloads as W
+from oracle import sla2 as oracle
+from tests.gpu_helpers import MAX_ABS_TOL, check_mask_band, dev, host, max_abs, rel_l2
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+TDT = {"fp32": torch.float32, "bf16": torch.bfloat16}
+LIN_TOL = 5e-3
+D = 128
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def proj_o(seed, H):
+    rng = np.random.default_rng([seed, 99])
+    return rng.normal(0.0, 1.0 / np.sqrt(D), (H, D, D)).astype(np.float32)
+
+
+def check(q, k, v, wo, keep, dtype, heads):
+    t = TDT[dtype]
+    gq, gk, gv = dev(q, t), dev(k, t), dev(v, t)
+    O, Ol = sla2.sla2_forward_sla1(gq, gk, gv, dev(wo), keep)
+    eye = dev(np.broadcast_to(np.eye(D, dtype=np.float32), (q.shape[1], D, D)).copy())
+    _, mask, _ = sla2.sla2_router(gq, gk, eye, eye, keep)   # the same (heuristic) router
+    torch.cuda.synchronize()
+    O, Ol, mask = host(O), host(Ol), host(mask)
+    assert np.isfinite(O).all()
+    for b, h in heads:
+        r = oracle.forward_head_sla1(q[b, h], k[b, h], v[b, h], wo[h], keep)
+        if not np.array_equal(mask[b, h], r["mask"]):
+            check_mask_band(r["P_c"], r["kb"], mask[b, h])
+            r = oracle.forward_head_sla1(q[b, h], k[b, h], v[b, h], wo[h], keep, mask=mask[b, h])
+        e_o, e_l, m = rel_l2(O[b, h], r["O"]), rel_l2(Ol[b, h], r["O_l"]), max_abs(O[b, h], r["O"])
+        say(f"  b{b} h{h}: O relL2 {e_o:.2e} maxabs {m:.2e}, O_l relL2 {e_l:.2e}")
+        assert e_o <= LIN_TOL and e_l <= LIN_TOL and m <= MAX_ABS_TOL
+
+
+@pytest.mark.parametrize("name,heads", [("tiny_iid_N2048", None), ("grid_8x32x32_N8192", [1, 8])])
+def test_sla1_matches_oracle(name, heads):
+    w = W.WORKLOADS[name]
+    q, k, v = W.generate(w, heads=heads)
+    H = q.shape[1]
+    say("sla1", name, q.shape)
+    check(q, k, v, proj_o(3, H), w.keep_frac[0], w.dtype,
+          [(b, h) for b in range(q.shape[0]) for h in range(H)])
+
+
+def test_sla1_zero_projection_is_the_sparse_branch_tap():
+    N, keep = 2048, 0.25
+    q, k, v = W.random_qkv(81, 1, 2, N, dtype="bf16")
+    g = [dev(a, torch.bfloat16) for a in (q, k, v)]
+    O, _ = sla2.sla2_forward_sla1(*g, dev(np.zeros((2, D, D), np.float32)), keep)
+    eye = dev(np.stack([np.eye(D, dtype=np.float32)] * 2))
+    _, taps = sla2.sla2_forward(*g, eye, eye, dev(np.ones((2, N // 128), np.float32)), keep,
+                                taps=("O_s",))
+    torch.cuda.synchronize()
+    assert torch.equal(O, taps["O_s"])
+
+
+@pytest.mark.parametrize("a", [0.3, 0.75])
+def test_sla1_relates_to_sla2_for_constant_alpha(a):
+    """a * (O_s + O_l ((1 - a) / a) I) = a O_s + (1 - a) O_l, the SLA2 mix with alpha = a."""
+    N, keep = 2048, 0.25
+    q, k, v = W.random_qkv(83, 1, 2, N, dtype="bf16")
+    g = [dev(x, torch.bfloat16) for x in (q, k, v)]
+    wo = np.stack([((1 - a) / a) * np.eye(D, dtype=np.float32)] * 2)
+    O1, _ = sla2.sla2_forward_sla1(*g, dev(wo), keep)
+    eye = dev(np.stack([np.eye(D, dtype=np.float32)] * 2))
+    O2 = sla2.sla2_forward(*g, eye, eye, dev(np.full((2, N // 128), a, np.float32)), keep)
+    torch.cuda.synchronize()
+    e = rel_l2(a * host(O1).astype(np.float64), host(O2))
+    say(f"  a {a}: relL2 {e:.2e}")
+    assert e < 1e-5
+
+
+def test_sla1_benchmark_size():
+    """The Wan2.1-1.3B 480P-shaped workload (12 heads, N = 32768, 3 %), two heads checked."""
+    w = W.WORKLOADS["wan13b_480p_N32768"]
+    q, k, v = W.generate(w)
+    say("sla1 bench size")
+    check(q, k, v, proj_o(5, w.H), w.keep_frac[-1], w.dtype, [(0, 4), (0, 11)])
