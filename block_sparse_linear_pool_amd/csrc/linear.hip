@@ -17,6 +17,8 @@
 //                   stored as h_j^T ([d_v][d_phi]) in bf16 for the attention kernel's
 //                   gathers; fp32 partial sums of h_j^T and z_j over kKpPerWg blocks.
 //   linear_total  H_tot = sum_j h_j and Z_tot = sum_j z_j from the partials (fixed order).
+//   sla1_mix      O += O_l Wo (the earlier SLA mix, a comparison workload; §2 Q2 table of the
+//                 second page).
 // The bf16 h_j^T and fp32 H_tot^T for the attention kernel are stored in fragment order
 // (htot_frag_index): each of its wavefront loads is then one contiguous run.
 

@@ -9,10 +9,13 @@
 //               the forward) the INT8 codes of Q for the sparse branch.
 //   colmean     mu = colmean(K) from the key-block sums (all blocks have 64 rows), the
 //               K smoothing of §7 note 1 of the second page.
-//   project     A = Qbar Wq, B = (Kbar - mu) Wk in fp64 (Kbar - mu is the mean of K_s).
+//   project     A = Qbar Wq, B = (Kbar - mu) Wk in fp64 (Kbar - mu is the mean of K_s); with
+//               no weights the identity (the heuristic router of the earlier SLA).
 //   score_topk  G = A B^T / sqrt(d) in fp64 into LDS, then one wavefront per query
 //               block selects the kb largest logits exactly (ties to the lower index)
-//               and writes the mask and the ascending block list.
+//               and writes the mask and the ascending block list; in its soft mode the
+//               SoftTop-k mask sigma(P_c / tau + lambda_i) of the training-time router.
+//   fill        a constant into a float array (alpha = 1 for the earlier SLA mix).
 // Ranking by the logit G is ranking by P_c = softmax(G): softmax is monotone per row.
 #include "sla2_common.h"
 
