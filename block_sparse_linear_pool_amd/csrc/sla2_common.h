@@ -150,13 +150,20 @@ __device__ inline float row16_sum(float v) {
 }
 
 // ---------------------------------------------------------------- quantisation steps
-// INT8: code = clamp(rne(fl32(x * inv)), -127, 127), inv = fl32(127 / amax) (0 if amax = 0)
+// INT8: code = clamp(rne(fl32(x * inv)), -127, 127), inv = fl32(127 / amax) (0 if amax = 0).
+// Computed as clamp first (one med3; the bounds are integers, so clamping before or after the
+// rounding gives the same integer), then + 1.5 * 2^23: the fp32 add rounds to the nearest
+// integer, ties to even (as rint), and leaves that integer in the low mantissa bits, whose low
+// byte is the two's-complement code. i8_code returns the code in the low byte of a word whose
+// other bytes are not zero; i8_pack4 keeps only the low bytes.
 __device__ inline uint32_t i8_code(float x, float inv) {
-  const float y = fminf(fmaxf(rintf(x * inv), -127.f), 127.f);
-  return static_cast<uint32_t>(static_cast<int>(y)) & 0xFFu;
+  const float y = __builtin_amdgcn_fmed3f(x * inv, -127.f, 127.f);
+  return __float_as_uint(y + 12582912.0f);   // 1.5 * 2^23
 }
 __device__ inline uint32_t i8_pack4(float a, float b, float c, float d, float inv) {
-  return i8_code(a, inv) | (i8_code(b, inv) << 8) | (i8_code(c, inv) << 16) | (i8_code(d, inv) << 24);
+  const uint32_t ua = i8_code(a, inv) & 0xFFu, ub = i8_code(b, inv) & 0xFFu;
+  const uint32_t uc = i8_code(c, inv) & 0xFFu, ud = i8_code(d, inv);
+  return (ud << 24) | (uc << 16) | (ub << 8) | ua;
 }
 // OCP E4M3 (round to nearest even) of fl32(x * inv) saturated to +-448, four codes per word
 __device__ inline uint32_t e4m3_pack4(float a, float b, float c, float d, float inv) {
