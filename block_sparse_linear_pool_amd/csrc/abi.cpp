@@ -19,7 +19,9 @@ size_t up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 struct Plan {
   size_t qsum, ksum, mu64, mu32, A, Bt, mask, list, cnt, qc, kc, vc, sq, sk, sv, hbf, z, hpart,
-      zpart, htot, ztot, ones, total;
+      zpart, htot, ztot, ones;
+  // backward only
+  size_t tcnt, tlist, lse2, Dd, dht, dz, dhtot, dztot, kcol, kmean, total;
 };
 
 Plan make_plan(const Geom& g) {
@@ -54,6 +56,16 @@ Plan make_plan(const Geom& g) {
   p.htot = take(BH * kD * kD * 4);
   p.ztot = take(BH * kD * 4);
   p.ones = take(static_cast<size_t>(g.H) * nqb * 4);
+  p.tcnt = take(BH * nkb * 4);
+  p.tlist = take(BH * nkb * nqb * 2);
+  p.lse2 = take(BH * N * 4);
+  p.Dd = take(BH * N * 4);
+  p.dht = take(BH * nqb * kD * kD * 2);
+  p.dz = take(BH * nqb * kD * 4);
+  p.dhtot = take(BH * kD * kD * 4);
+  p.dztot = take(BH * kD * 4);
+  p.kcol = take(BH * nkb * kD * 4);
+  p.kmean = take(BH * kD * 4);
   p.total = o;
   return p;
 }
@@ -160,11 +172,12 @@ bool debug_sync() {
 // Optional caller events recorded around every kernel (see sla2_taps.stage_events).
 struct Rec {
   void** ev;
-  int n;
-  explicit Rec(const sla2_taps* t) : ev(t ? t->stage_events : nullptr), n(0) {}
-  explicit Rec(void** events) : ev(events), n(0) {}
+  int n, cap;
+  explicit Rec(const sla2_taps* t)
+      : ev(t ? t->stage_events : nullptr), n(0), cap(SLA2_MAX_STAGES + 1) {}
+  explicit Rec(void** events, int count = SLA2_MAX_STAGES + 1) : ev(events), n(0), cap(count) {}
   hipError_t mark(hipStream_t s) {
-    if (ev == nullptr || n > SLA2_MAX_STAGES) return hipSuccess;
+    if (ev == nullptr || n >= cap) return hipSuccess;
     return hipEventRecord(static_cast<hipEvent_t>(ev[n++]), s);
   }
 };
@@ -492,6 +505,84 @@ sla2_status sla2_forward_with_mask(const sla2_shape* shape, const void* Q, const
   SLA2_LAUNCH(launch_mask_to_list(g, mask, at<uint8_t>(ws, p.mask), at<int32_t>(ws, p.list),
                                   at<int32_t>(ws, p.cnt), stream));
   return run_branches(g, dt, Q, K, V, alpha, O, taps, ws, p, g.nkb, rec, stream);
+}
+
+sla2_status sla2_backward(const sla2_shape* shape, const void* Q, const void* K, const void* V,
+                          const uint8_t* mask, const float* alpha, const float* dO, float* dQ,
+                          float* dK, float* dV, float* dalpha, void** stage_events,
+                          void* workspace, size_t workspace_bytes, void* stream_) {
+  Geom g;
+  sla2_status st = check_shape(shape, &g);
+  if (st != SLA2_OK) return st;
+  PtrCheck pc;
+  pc.req(Q); pc.req(K); pc.req(V); pc.req(mask); pc.req(alpha); pc.req(dO);
+  pc.req(dQ); pc.req(dK); pc.req(dV); pc.req(dalpha);
+  if (pc.st != SLA2_OK) return pc.st;
+  if ((st = check_workspace(g, workspace, workspace_bytes)) != SLA2_OK) return st;
+  if ((st = check_device()) != SLA2_OK) return st;
+  hipStream_t stream = static_cast<hipStream_t>(stream_);
+  const Plan p = make_plan(g);
+  const int dt = shape->dtype == SLA2_FP32 ? 0 : 1;
+  void* ws = workspace;
+  Rec rec(stage_events, 12);
+  if (rec.mark(stream) != hipSuccess) return SLA2_ERR_HIP;
+  // forward pieces: colmean(K), the bf16 h_j^T, z_j and H_tot, Z_tot; the kept lists
+  SLA2_LAUNCH(launch_pool(g, dt, nullptr, K, at<double>(ws, p.qsum), at<double>(ws, p.ksum),
+                          nullptr, nullptr, nullptr, stream));
+  SLA2_LAUNCH(launch_colmean(g, at<double>(ws, p.ksum), at<double>(ws, p.mu64),
+                             at<float>(ws, p.mu32), nullptr, stream));
+  KvArgs kv{};
+  kv.mu32 = at<float>(ws, p.mu32);
+  kv.kc = at<int8_t>(ws, p.kc);
+  kv.vc = at<uint8_t>(ws, p.vc);
+  kv.sk = at<float>(ws, p.sk);
+  kv.sv = at<float>(ws, p.sv);
+  kv.ht_bf16 = at<uint16_t>(ws, p.hbf);
+  kv.z = at<float>(ws, p.z);
+  kv.hpart = at<float>(ws, p.hpart);
+  kv.zpart = at<float>(ws, p.zpart);
+  SLA2_LAUNCH(launch_kv_prep(g, dt, K, V, kv, stream));
+  SLA2_LAUNCH(launch_linear_total(g, at<float>(ws, p.hpart), at<float>(ws, p.zpart),
+                                  at<float>(ws, p.htot), at<float>(ws, p.ztot), 1, stream));
+  SLA2_LAUNCH(launch_mask_to_list(g, mask, at<uint8_t>(ws, p.mask), at<int32_t>(ws, p.list),
+                                  at<int32_t>(ws, p.cnt), stream));
+  SLA2_LAUNCH(launch_key_lists(g, at<uint8_t>(ws, p.mask), at<int32_t>(ws, p.tcnt),
+                               at<uint16_t>(ws, p.tlist), stream));
+  BwdArgs b{};
+  b.Q = Q; b.K = K; b.V = V;
+  b.mu32 = at<float>(ws, p.mu32);
+  b.dO = dO;
+  b.alpha = alpha;
+  b.list = at<int32_t>(ws, p.list);
+  b.cnt = at<int32_t>(ws, p.cnt);
+  b.hbf = at<uint16_t>(ws, p.hbf);
+  b.htot = at<float>(ws, p.htot);
+  b.z = at<float>(ws, p.z);
+  b.ztot = at<float>(ws, p.ztot);
+  b.dQ = dQ;
+  b.dht = at<uint16_t>(ws, p.dht);
+  b.dz = at<float>(ws, p.dz);
+  b.dalpha = dalpha;
+  b.dhtot = at<float>(ws, p.dhtot);
+  b.dztot = at<float>(ws, p.dztot);
+  b.lse2 = at<float>(ws, p.lse2);
+  b.Dd = at<float>(ws, p.Dd);
+  b.tcnt = at<int32_t>(ws, p.tcnt);
+  b.tlist = at<uint16_t>(ws, p.tlist);
+  b.dK = dK;
+  b.dV = dV;
+  b.kcol = at<float>(ws, p.kcol);
+  b.kmean = at<float>(ws, p.kmean);
+  b.H = g.H;
+  b.BH = g.BH;
+  b.nqb = g.nqb;
+  b.nkb = g.nkb;
+  SLA2_LAUNCH(launch_bwd_lin_q(g, dt, b, stream));
+  SLA2_LAUNCH(launch_dh_total(g, b, stream));
+  SLA2_LAUNCH(launch_bwd_q(g, dt, b, stream));
+  SLA2_LAUNCH(launch_bwd_kv(g, dt, b, stream));
+  SLA2_LAUNCH(launch_dk_center(g, b, stream));
+  return SLA2_OK;
 }
 
 }  // extern "C"

@@ -1,0 +1,886 @@
+// SLA2 backward kernels (gfx950 / CDNA4): gradients of the sparse-linear attention with the
+// block mask held fixed, in 16-bit matrix arithmetic (bf16 operands, fp32 accumulation).
+//
+// "SLA2: Sparse-Linear Attention v2 for Diffusion Transformers": the sparse branch trains with
+// a low-bit forward and a 16-bit backward (§3 table, §4 six checks item 4: the
+// straight-through estimator), so the gradient here is that of the unquantised forward; the
+// gradient is derived by hand with the linear branch's dH_i, dZ_i formed first, so that each
+// (key block, query block) pair costs one matrix addition (§7 note 3).
+//
+// Kernels, in launch order (after pool / colmean / kv_prep / linear_total of the forward give
+// colmean(K), bf16 h_j^T, z_j, H_tot, Z_tot, and mask_to_list gives the kept lists):
+//   key_lists    per key block, the ascending query blocks that keep it (transposed mask)
+//   bwd_lin_q    per query block: a = phi(Q_i), H_i, Z_i; O_l, dnum, dden; writes
+//                dQ = a * (da - rowsum(da a)) (the linear part), dH_i^T (bf16), dZ_i, and
+//                dalpha = -sum(dO O_l)
+//   dh_total     dH_tot, dZ_tot: sums over all query blocks
+//   bwd_q        per query block, two passes over its kept key blocks: pass 1 rebuilds the
+//                row softmax (log-sum-exp, O_s) and D = rowsum(dO_s O_s); pass 2 forms
+//                dS = P (dO_s V^T - D) and adds dS K_s / sqrt(d) to dQ; dalpha += sum(dO O_s)
+//   bwd_kv       per key block, over the query blocks that keep it: dV += P^T dO_s,
+//                dK_s += dS^T Q / sqrt(d); then the linear part with
+//                dh_j = dH_tot - sum of dH_i over those query blocks (the one addition per
+//                pair), dz_j likewise: dV += phi(K_s,j) dh_j,
+//                dK_s += phi * (dphi - rowsum(dphi phi)), dphi = V_j dh_j^T + 1 dz_j^T;
+//                writes dK_s and per-key-block column sums of it
+//   dk_mean      column mean of dK_s per head; dk_center: dK = dK_s - mean (K smoothing)
+//
+// MFMA: v_mfma_f32_32x32x16_bf16. Operand A lane (g = lane / 32, l = lane % 32) holds row l,
+// k = 8 g .. 8 g + 7; B holds column l, the same k; the accumulator holds column l and rows
+// 8 (r / 4) + 4 g + r % 4 in register r. So an accumulator C (M x N) serves directly as the B
+// operand of X C or the A operand of C^T Y (both contract over M), with k taken in register
+// order: registers 8 h .. 8 h + 7 are rows 16 h + 4 g .. +3 and 16 h + 8 + 4 g .. +3; the other
+// operand is then read from LDS in that row order. All LDS tiles are bf16 [rows][136]
+// (272-byte rows).
+#include "sla2_common.h"
+
+namespace sla2 {
+
+namespace {
+
+constexpr int kLd = 136;          // bf16 LDS row stride (elements)
+constexpr int kTile = kD * kLd;   // one 128-row bf16 tile
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ inline bf16x8 ld_row8(const uint16_t* p) {
+  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const i32x4*>(p));
+}
+// row elements k0 + 4 g .. +3 and k0 + 8 + 4 g .. +3 (accumulator register order)
+__device__ inline bf16x8 ld_row8_acc(const uint16_t* row, int k0, int g) {
+  const uint2 lo = *reinterpret_cast<const uint2*>(row + k0 + 4 * g);
+  const uint2 hi = *reinterpret_cast<const uint2*>(row + k0 + 8 + 4 * g);
+  const i32x4 v = {static_cast<int>(lo.x), static_cast<int>(lo.y), static_cast<int>(hi.x),
+                   static_cast<int>(hi.y)};
+  return __builtin_bit_cast(bf16x8, v);
+}
+__device__ inline uint32_t ld_pair(const uint16_t* base, int r0, int r1, int col) {
+  return static_cast<uint32_t>(base[r0 * kLd + col]) |
+         (static_cast<uint32_t>(base[r1 * kLd + col]) << 16);
+}
+// column `col`, rows k0 .. k0 + 7
+__device__ inline bf16x8 ld_col8(const uint16_t* base, int col, int k0) {
+  const i32x4 v = {static_cast<int>(ld_pair(base, k0, k0 + 1, col)),
+                   static_cast<int>(ld_pair(base, k0 + 2, k0 + 3, col)),
+                   static_cast<int>(ld_pair(base, k0 + 4, k0 + 5, col)),
+                   static_cast<int>(ld_pair(base, k0 + 6, k0 + 7, col))};
+  return __builtin_bit_cast(bf16x8, v);
+}
+// column `col`, rows k0 + 4 g .. +3 and k0 + 8 + 4 g .. +3 (accumulator register order)
+__device__ inline bf16x8 ld_col8_acc(const uint16_t* base, int col, int k0, int g) {
+  const int a = k0 + 4 * g, b = k0 + 8 + 4 * g;
+  const i32x4 v = {static_cast<int>(ld_pair(base, a, a + 1, col)),
+                   static_cast<int>(ld_pair(base, a + 2, a + 3, col)),
+                   static_cast<int>(ld_pair(base, b, b + 1, col)),
+                   static_cast<int>(ld_pair(base, b + 2, b + 3, col))};
+  return __builtin_bit_cast(bf16x8, v);
+}
+// accumulator registers 8 h .. 8 h + 7 as a bf16 operand
+__device__ inline bf16x8 acc_op(const f32x16& c, int h) {
+  const i32x4 v = {static_cast<int>(pack_bf16x2(c[8 * h], c[8 * h + 1])),
+                   static_cast<int>(pack_bf16x2(c[8 * h + 2], c[8 * h + 3])),
+                   static_cast<int>(pack_bf16x2(c[8 * h + 4], c[8 * h + 5])),
+                   static_cast<int>(pack_bf16x2(c[8 * h + 6], c[8 * h + 7]))};
+  return __builtin_bit_cast(bf16x8, v);
+}
+__device__ inline f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ inline void st_bf16x8(uint16_t* p, const float* v) {
+  const i32x4 w = {static_cast<int>(pack_bf16x2(v[0], v[1])), static_cast<int>(pack_bf16x2(v[2], v[3])),
+                   static_cast<int>(pack_bf16x2(v[4], v[5])), static_cast<int>(pack_bf16x2(v[6], v[7]))};
+  *reinterpret_cast<i32x4*>(p) = w;
+}
+__device__ inline void unpack_bf16x8(const i32x4& v, float* out) {
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const uint32_t w = static_cast<uint32_t>(v[k]);
+    out[2 * k] = __uint_as_float(w << 16);
+    out[2 * k + 1] = __uint_as_float(w & 0xFFFF0000u);
+  }
+}
+__device__ inline float bf(uint16_t v) { return __uint_as_float(static_cast<uint32_t>(v) << 16); }
+
+// Stage a 64-row block of K_s = K - mu (mu given) or V (mu null) as bf16 [64][kLd]:
+// thread t converts rows t / 16 + 16 u, columns 8 (t % 16) .. +7.
+template <typename T>
+__device__ inline void stage64(uint16_t* dst, const T* src, const float* mu, int t) {
+  const int c8 = 8 * (t & 15);
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int r = (t >> 4) + 16 * u;
+    float v[8];
+    load8<T>(src + r * kD + c8, v);
+    if (mu != nullptr) {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) v[k] -= mu[k];
+    }
+    st_bf16x8(dst + r * kLd + c8, v);
+  }
+}
+// Stage a 128-row query block of Q as bf16 [128][kLd], and dO_s = alpha dO (dO fp32).
+template <typename T>
+__device__ inline void stage128_q(uint16_t* qs, uint16_t* dos, const T* q, const float* dO,
+                                  float alpha, int t) {
+  const int c8 = 8 * (t & 15);
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const int r = (t >> 4) + 16 * u;
+    float v[8];
+    load8<T>(q + r * kD + c8, v);
+    st_bf16x8(qs + r * kLd + c8, v);
+    load8<float>(dO + r * kD + c8, v);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[k] *= alpha;
+    st_bf16x8(dos + r * kLd + c8, v);
+  }
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------- key_lists
+// grid (ceil(nkb / 256), BH), 256 threads; thread = key block j: the ascending query blocks
+// whose mask row keeps j (mask already 0/1).
+__global__ __launch_bounds__(256) void key_lists_kernel(const uint8_t* __restrict__ mask,
+                                                        int32_t* __restrict__ tcnt,
+                                                        uint16_t* __restrict__ tlist, int nqb,
+                                                        int nkb) {
+  const int bh = blockIdx.y, j = blockIdx.x * 256 + threadIdx.x;
+  if (j >= nkb) return;
+  const uint8_t* m = mask + static_cast<size_t>(bh) * nqb * nkb + j;
+  uint16_t* out = tlist + (static_cast<size_t>(bh) * nkb + j) * nqb;
+  int c = 0;
+  for (int i = 0; i < nqb; ++i)
+    if (m[static_cast<size_t>(i) * nkb]) out[c++] = static_cast<uint16_t>(i);
+  tcnt[static_cast<size_t>(bh) * nkb + j] = c;
+}
+
+// ---------------------------------------------------------------- bwd_lin_q
+// grid (nqb, BH) (XCD-aware order), 256 threads; wavefront w owns query rows 32 w .. +31 for
+// the products with the query as column index, and output tile w otherwise.
+template <typename T>
+__global__ __launch_bounds__(256) void bwd_lin_q_kernel(BwdArgs x) {
+  __shared__ __attribute__((aligned(16))) uint16_t As[kTile];   // a = phi(Q_i) [q][a]
+  __shared__ __attribute__((aligned(16))) uint16_t Ht[kTile];   // H_i^T [o][a]
+  __shared__ __attribute__((aligned(16))) uint16_t Hn[kTile];   // H_i [a][o]
+  __shared__ __attribute__((aligned(16))) uint16_t DN[kTile];   // dnum [q][o]
+  __shared__ float Zs[kD], ddl[kD], red[4];
+  int i, bh;
+  xcd_block(x.nqb, x.BH, &i, &bh);
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6, g = lane >> 5, l32 = lane & 31;
+  const int N = x.nqb * kBQ, nkb = x.nkb;
+  const size_t qb = static_cast<size_t>(bh) * x.nqb + i;
+  const size_t row0 = static_cast<size_t>(bh) * N + static_cast<size_t>(i) * kBQ;
+  const int ncnt = x.cnt[qb];
+  if (ncnt == nkb) {   // nothing dropped: O_l = 0, no linear gradient
+    for (int e = t; e < kBQ * kD / 4; e += 256)
+      *reinterpret_cast<f32x4*>(x.dQ + row0 * kD + 4 * e) = f32x4{};
+    for (int e = t; e < kD * kD / 8; e += 256)
+      *reinterpret_cast<i32x4*>(x.dht + qb * (kD * kD) + 8 * e) = i32x4{};
+    if (t < kD) x.dz[qb * kD + t] = 0.f;
+    if (t == 0) x.dalpha[qb] = 0.f;
+    return;
+  }
+  // ---- a = phi(Q_i): thread t takes row t / 2, columns 64 (t % 2) .. +63
+  {
+    const int r = t >> 1, c0 = 64 * (t & 1);
+    const T* qp = static_cast<const T*>(x.Q) + (row0 + r) * kD + c0;
+    float v[64];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) load8<T>(qp + 8 * u, v + 8 * u);
+    float mx = v[0];
+#pragma unroll
+    for (int k = 1; k < 64; ++k) mx = fmaxf(mx, v[k]);
+    mx = fmaxf(mx, __shfl_xor(mx, 1));
+    float s = 0.f;
+#pragma unroll
+    for (int k = 0; k < 64; ++k) {
+      v[k] = __expf(v[k] - mx);
+      s += v[k];
+    }
+    s += __shfl_xor(s, 1);
+    const float inv = 1.0f / s;
+#pragma unroll
+    for (int k = 0; k < 64; ++k) v[k] *= inv;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) st_bf16x8(&As[r * kLd + c0 + 8 * u], v + 8 * u);
+  }
+  // ---- H_i = H_tot - sum over kept j of h_j. h_j^T bf16 in fragment order: 16-byte chunk c
+  // holds row o = 32 (c / 512) + c % 32, columns a = 8 ((c / 32) % 16) .. +7. Thread t takes
+  // chunks t + 256 u.
+  {
+    const int32_t* lst = x.list + qb * nkb;
+    const uint16_t* hb = x.hbf + static_cast<size_t>(bh) * nkb * (kD * kD);
+    float acc[8][8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+#pragma unroll
+      for (int k = 0; k < 8; ++k) acc[u][k] = 0.f;
+    for (int n = 0; n < ncnt; ++n) {
+      const int j = lst[n];
+      const uint16_t* hj = hb + static_cast<size_t>(j) * (kD * kD);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const i32x4 v = *reinterpret_cast<const i32x4*>(hj + 8 * (t + 256 * u));
+        float f[8];
+        unpack_bf16x8(v, f);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) acc[u][k] += f[k];
+      }
+    }
+    const float* ht = x.htot + static_cast<size_t>(bh) * (kD * kD);   // H_tot [a][o]
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int c = t + 256 * u;
+      const int o = 32 * (c >> 9) + (c & 31), a0 = 8 * ((c >> 5) & 15);
+      float hv[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) hv[k] = ht[(a0 + k) * kD + o] - acc[u][k];
+      st_bf16x8(&Ht[o * kLd + a0], hv);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) Hn[(a0 + k) * kLd + o] = f32_to_bf16_rne(hv[k]);
+    }
+    if (t < kD) {
+      float zs = 0.f;
+      for (int n = 0; n < ncnt; ++n) zs += x.z[(static_cast<size_t>(bh) * nkb + lst[n]) * kD + t];
+      Zs[t] = x.ztot[static_cast<size_t>(bh) * kD + t] - zs;
+    }
+  }
+  __syncthreads();
+  // ---- num^T = H_i^T a^T: lane = query q = 32 w + l32, registers = o
+  const int q = 32 * w + l32;
+  f32x16 num[4];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) {
+    num[mt] = f32x16{};
+#pragma unroll
+    for (int s = 0; s < 8; ++s)
+      num[mt] = mfma(ld_row8(&Ht[(32 * mt + l32) * kLd + 16 * s + 8 * g]),
+                     ld_row8(&As[q * kLd + 16 * s + 8 * g]), num[mt]);
+  }
+  float den = 0.f;
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const i32x4 v = *reinterpret_cast<const i32x4*>(&As[q * kLd + 64 * g + 8 * u]);
+    float f[8];
+    unpack_bf16x8(v, f);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) den += f[k] * Zs[64 * g + 8 * u + k];
+  }
+  den += __shfl_xor(den, 32);
+  const float al = x.alpha[static_cast<size_t>(bh % x.H) * x.nqb + i];
+  const float oml = 1.0f - al, inv_den = 1.0f / den;
+  // O_l = num / den; sum(dO O_l) per row; dnum = (1 - alpha) dO / den (in num's registers)
+  float sl = 0.f;
+  {
+    const float* dop = x.dO + (row0 + q) * kD;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int k4 = 0; k4 < 4; ++k4) {
+        const f32x4 d4 = *reinterpret_cast<const f32x4*>(dop + 32 * mt + 8 * k4 + 4 * g);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          sl += d4[k] * (num[mt][4 * k4 + k] * inv_den);
+          num[mt][4 * k4 + k] = oml * d4[k] * inv_den;
+        }
+      }
+  }
+  sl += __shfl_xor(sl, 32);
+  const float dden = -oml * sl * inv_den;
+  {
+    const float ws = wave_sum(g == 0 ? sl : 0.f);
+    if (lane == 0) red[w] = ws;
+  }
+  // ---- da^T = H_i dnum^T (+ dden Z_i): lane = q, registers = a; dQ = a (da - rowsum(da a))
+  {
+    f32x16 da[4];
+#pragma unroll
+    for (int at = 0; at < 4; ++at) {
+      da[at] = f32x16{};
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          da[at] = mfma(ld_row8_acc(&Hn[(32 * at + l32) * kLd], 32 * mt + 16 * h, g),
+                        acc_op(num[mt], h), da[at]);
+    }
+    float av[4][16];
+    float cs = 0.f;
+#pragma unroll
+    for (int at = 0; at < 4; ++at)
+#pragma unroll
+      for (int k4 = 0; k4 < 4; ++k4) {
+        const int a0 = 32 * at + 8 * k4 + 4 * g;
+        const uint2 pv = *reinterpret_cast<const uint2*>(&As[q * kLd + a0]);
+        av[at][4 * k4] = __uint_as_float(pv.x << 16);
+        av[at][4 * k4 + 1] = __uint_as_float(pv.x & 0xFFFF0000u);
+        av[at][4 * k4 + 2] = __uint_as_float(pv.y << 16);
+        av[at][4 * k4 + 3] = __uint_as_float(pv.y & 0xFFFF0000u);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          da[at][4 * k4 + k] += dden * Zs[a0 + k];
+          cs += da[at][4 * k4 + k] * av[at][4 * k4 + k];
+        }
+      }
+    cs += __shfl_xor(cs, 32);
+    float* dqp = x.dQ + (row0 + q) * kD;
+#pragma unroll
+    for (int at = 0; at < 4; ++at)
+#pragma unroll
+      for (int k4 = 0; k4 < 4; ++k4) {
+        f32x4 o4;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) o4[k] = av[at][4 * k4 + k] * (da[at][4 * k4 + k] - cs);
+        *reinterpret_cast<f32x4*>(dqp + 32 * at + 8 * k4 + 4 * g) = o4;
+      }
+  }
+  // ---- dnum -> LDS [q][o] (bf16), dden -> LDS
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int k4 = 0; k4 < 4; ++k4)
+      *reinterpret_cast<uint2*>(&DN[q * kLd + 32 * mt + 8 * k4 + 4 * g]) =
+          make_uint2(pack_bf16x2(num[mt][4 * k4], num[mt][4 * k4 + 1]),
+                     pack_bf16x2(num[mt][4 * k4 + 2], num[mt][4 * k4 + 3]));
+  if (g == 0) ddl[q] = dden;
+  __syncthreads();
+  // ---- dH_i^T [o][a] = sum_q dnum[q][o] a[q][a]: wavefront w owns o = 32 w .. +31
+  {
+    uint16_t* out = x.dht + qb * (kD * kD);
+#pragma unroll
+    for (int at = 0; at < 4; ++at) {
+      f32x16 c = f32x16{};
+#pragma unroll
+      for (int s = 0; s < 8; ++s)
+        c = mfma(ld_col8(DN, 32 * w + l32, 16 * s + 8 * g), ld_col8(As, 32 * at + l32, 16 * s + 8 * g), c);
+      const int a = 32 * at + l32;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int o = 32 * w + 8 * (r >> 2) + 4 * g + (r & 3);
+        out[o * kD + a] = f32_to_bf16_rne(c[r]);
+      }
+    }
+  }
+  if (t < kD) {
+    float s = 0.f;
+    for (int r = 0; r < kBQ; ++r) s += bf(As[r * kLd + t]) * ddl[r];
+    x.dz[qb * kD + t] = s;
+  }
+  if (t == 0) x.dalpha[qb] = -((red[0] + red[1]) + (red[2] + red[3]));
+}
+
+// ---------------------------------------------------------------- dh_total
+// grid (9, BH), 256 threads: workgroups 0-7 sum 2048 elements of dH_i^T each over all query
+// blocks (thread: 8 consecutive elements), workgroup 8 sums dZ_i. Fixed order.
+__global__ __launch_bounds__(256) void dh_total_kernel(const uint16_t* __restrict__ dht,
+                                                       const float* __restrict__ dz,
+                                                       float* __restrict__ dhtot,
+                                                       float* __restrict__ dztot, int nqb) {
+  const int bh = blockIdx.y, t = threadIdx.x;
+  if (blockIdx.x < 8) {
+    const size_t e = 2048 * blockIdx.x + 8 * t;
+    const uint16_t* src = dht + static_cast<size_t>(bh) * nqb * (kD * kD) + e;
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < nqb; ++i) {
+      float f[8];
+      unpack_bf16x8(*reinterpret_cast<const i32x4*>(src + static_cast<size_t>(i) * (kD * kD)), f);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) acc[k] += f[k];
+    }
+    float* dst = dhtot + static_cast<size_t>(bh) * (kD * kD) + e;
+    *reinterpret_cast<f32x4*>(dst) = f32x4{acc[0], acc[1], acc[2], acc[3]};
+    *reinterpret_cast<f32x4*>(dst + 4) = f32x4{acc[4], acc[5], acc[6], acc[7]};
+  } else if (t < kD) {
+    float s = 0.f;
+    for (int i = 0; i < nqb; ++i) s += dz[(static_cast<size_t>(bh) * nqb + i) * kD + t];
+    dztot[static_cast<size_t>(bh) * kD + t] = s;
+  }
+}
+
+// ---------------------------------------------------------------- bwd_q
+// grid (nqb, BH) (XCD-aware order), 256 threads; wavefront w owns query rows 32 w .. +31 and
+// holds S^T = K_s,j Q^T with the query as lane (column) and the 64 keys in registers, so row
+// statistics are per lane. Logits are kept in base-2 units: s2 = S log2(e) / sqrt(d).
+template <typename T>
+__global__ __launch_bounds__(256) void bwd_q_kernel(BwdArgs x) {
+  __shared__ __attribute__((aligned(16))) uint16_t Qs[kTile];
+  __shared__ __attribute__((aligned(16))) uint16_t Ds[kTile];   // dO_s = alpha dO
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[kBK * kLd];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs[kBK * kLd];
+  __shared__ float red[4];
+  int i, bh;
+  xcd_block(x.nqb, x.BH, &i, &bh);
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6, g = lane >> 5, l32 = lane & 31;
+  const int N = x.nqb * kBQ, nkb = x.nkb;
+  const size_t qb = static_cast<size_t>(bh) * x.nqb + i;
+  const size_t head = static_cast<size_t>(bh) * N;
+  const size_t row0 = head + static_cast<size_t>(i) * kBQ;
+  const int ncnt = x.cnt[qb];
+  if (ncnt == 0) {   // nothing kept: O_s = 0, no sparse gradient
+    if (t < kBQ) {
+      x.lse2[row0 + t] = 0.f;
+      x.Dd[row0 + t] = 0.f;
+    }
+    return;
+  }
+  const float al = x.alpha[static_cast<size_t>(bh % x.H) * x.nqb + i];
+  stage128_q<T>(Qs, Ds, static_cast<const T*>(x.Q) + row0 * kD, x.dO + row0 * kD, al, t);
+  float mu[8];
+  {
+    const float* mp = x.mu32 + static_cast<size_t>(bh) * kD + 8 * (t & 15);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) mu[k] = mp[k];
+  }
+  const int32_t* lst = x.list + qb * nkb;
+  const float c2 = kLog2e * 0.08838834764831845f;   // log2(e) / sqrt(128)
+  const int q = 32 * w + l32;
+  // ---- pass 1: running max m and sum l (per lane: its 32 keys of each block), O_s^T
+  float m = -INFINITY, l = 0.f;
+  f32x16 oT[4];
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt) oT[dt] = f32x16{};
+  for (int n = 0; n < ncnt; ++n) {
+    const size_t kr = head + static_cast<size_t>(lst[n]) * kBK;
+    __syncthreads();
+    stage64<T>(Ks, static_cast<const T*>(x.K) + kr * kD, mu, t);
+    stage64<T>(Vs, static_cast<const T*>(x.V) + kr * kD, nullptr, t);
+    __syncthreads();
+    f32x16 sT[2];
+#pragma unroll
+    for (int tk = 0; tk < 2; ++tk) {
+      sT[tk] = f32x16{};
+#pragma unroll
+      for (int s = 0; s < 8; ++s)
+        sT[tk] = mfma(ld_row8(&Ks[(32 * tk + l32) * kLd + 16 * s + 8 * g]),
+                      ld_row8(&Qs[q * kLd + 16 * s + 8 * g]), sT[tk]);
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int tk = 0; tk < 2; ++tk)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sT[tk][r]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float mn = fmaxf(m, mx * c2);
+    const float corr = exp2f(m - mn);
+    float ls = 0.f;
+#pragma unroll
+    for (int tk = 0; tk < 2; ++tk)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = exp2f(sT[tk][r] * c2 - mn);
+        sT[tk][r] = p;
+        ls += p;
+      }
+    l = l * corr + ls;
+    m = mn;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
+      oT[dt] *= corr;
+#pragma unroll
+      for (int tk = 0; tk < 2; ++tk)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          oT[dt] = mfma(ld_col8_acc(Vs, 32 * dt + l32, 32 * tk + 16 * h, g), acc_op(sT[tk], h), oT[dt]);
+    }
+  }
+  const float lt = l + __shfl_xor(l, 32);
+  const float lse = m + log2f(lt);
+  const float invl = 1.0f / lt;
+  float sd = 0.f;
+  {
+    const float* dop = x.dO + (row0 + q) * kD;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int k4 = 0; k4 < 4; ++k4) {
+        const f32x4 d4 = *reinterpret_cast<const f32x4*>(dop + 32 * dt + 8 * k4 + 4 * g);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) sd += d4[k] * (oT[dt][4 * k4 + k] * invl);
+      }
+  }
+  sd += __shfl_xor(sd, 32);
+  const float Dq = al * sd;
+  if (g == 0) {
+    x.lse2[row0 + q] = lse;
+    x.Dd[row0 + q] = Dq;
+  }
+  {
+    const float ws = wave_sum(g == 0 ? sd : 0.f);
+    if (lane == 0) red[w] = ws;
+  }
+  // ---- pass 2: P^T, dP^T = V_j dO_s^T, dS^T = P^T (dP^T - D), dQ^T += K_s,j^T dS^T
+  f32x16 dq[4];
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt) dq[dt] = f32x16{};
+  for (int n = 0; n < ncnt; ++n) {
+    const size_t kr = head + static_cast<size_t>(lst[n]) * kBK;
+    __syncthreads();
+    stage64<T>(Ks, static_cast<const T*>(x.K) + kr * kD, mu, t);
+    stage64<T>(Vs, static_cast<const T*>(x.V) + kr * kD, nullptr, t);
+    __syncthreads();
+    f32x16 sT[2], dp[2];
+#pragma unroll
+    for (int tk = 0; tk < 2; ++tk) {
+      sT[tk] = f32x16{};
+      dp[tk] = f32x16{};
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        sT[tk] = mfma(ld_row8(&Ks[(32 * tk + l32) * kLd + 16 * s + 8 * g]),
+                      ld_row8(&Qs[q * kLd + 16 * s + 8 * g]), sT[tk]);
+        dp[tk] = mfma(ld_row8(&Vs[(32 * tk + l32) * kLd + 16 * s + 8 * g]),
+                      ld_row8(&Ds[q * kLd + 16 * s + 8 * g]), dp[tk]);
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = exp2f(sT[tk][r] * c2 - lse);
+        dp[tk][r] = p * (dp[tk][r] - Dq);
+      }
+    }
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int tk = 0; tk < 2; ++tk)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          dq[dt] = mfma(ld_col8_acc(Ks, 32 * dt + l32, 32 * tk + 16 * h, g), acc_op(dp[tk], h), dq[dt]);
+  }
+  {
+    const float sc = 0.08838834764831845f;   // 1 / sqrt(128)
+    float* dqp = x.dQ + (row0 + q) * kD;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int k4 = 0; k4 < 4; ++k4) {
+        f32x4* p = reinterpret_cast<f32x4*>(dqp + 32 * dt + 8 * k4 + 4 * g);
+        f32x4 v = *p;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) v[k] += dq[dt][4 * k4 + k] * sc;
+        *p = v;
+      }
+  }
+  __syncthreads();
+  if (t == 0) x.dalpha[qb] += (red[0] + red[1]) + (red[2] + red[3]);
+}
+
+// ---------------------------------------------------------------- bwd_kv
+// grid (nkb, BH) (XCD-aware order), 256 threads; wavefront w = (kt = w % 2, qh = w / 2)
+// forms S = Q K_s^T for keys 32 kt .. +31 and query rows 64 qh .. +63 of each query block
+// that keeps this key block (query as register index, key as lane), so P and dS serve
+// directly as the A operand of dV = P^T dO_s and dK = dS^T Q. The two query halves are summed
+// through LDS at the end, then the linear part is added.
+constexpr int kKvLds = 2 * kTile * 2 + 2 * kBK * kLd * 2 + kTile * 2 + 4 * kBQ * 4;
+template <typename T>
+__global__ __launch_bounds__(256) void bwd_kv_kernel(BwdArgs x) {
+  __shared__ __attribute__((aligned(16))) char smem[kKvLds];
+  uint16_t* Qs = reinterpret_cast<uint16_t*>(smem);            // [128][kLd]
+  uint16_t* Ds = Qs + kTile;                                   // dO_s [128][kLd]
+  uint16_t* Ks = Ds + kTile;                                   // K_s,j [64][kLd]; later phi
+  uint16_t* Vs = Ks + kBK * kLd;                               // V_j [64][kLd]
+  uint16_t* DH = Vs + kBK * kLd;                               // dh_j^T [o][a]
+  float* lse_s = reinterpret_cast<float*>(DH + kTile);         // [128]
+  float* D_s = lse_s + kBQ;                                    // [128]
+  float* dz_s = D_s + kBQ;                                     // [128]
+  float* crow = dz_s + kBQ;                                    // [2][64]
+  float* X = reinterpret_cast<float*>(smem);                   // after the loop: Qs/Ds area
+  constexpr int kXld = kD + 4;                                 // fp32 row stride
+  float* DKs = X;                                              // [64][kXld]
+  float* DVs = X + kBK * kXld;                                 // [64][kXld]
+  int j, bh;
+  xcd_block(x.nkb, x.BH, &j, &bh);
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6, g = lane >> 5, l32 = lane & 31;
+  const int kt = w & 1, qh = w >> 1;
+  const int nqb = x.nqb, N = nqb * kBQ;
+  const size_t head = static_cast<size_t>(bh) * N;
+  const size_t krow0 = head + static_cast<size_t>(j) * kBK;
+  float mu[8];
+  {
+    const float* mp = x.mu32 + static_cast<size_t>(bh) * kD + 8 * (t & 15);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) mu[k] = mp[k];
+  }
+  stage64<T>(Ks, static_cast<const T*>(x.K) + krow0 * kD, mu, t);
+  stage64<T>(Vs, static_cast<const T*>(x.V) + krow0 * kD, nullptr, t);
+  const int nT = x.tcnt[static_cast<size_t>(bh) * x.nkb + j];
+  const uint16_t* tl = x.tlist + (static_cast<size_t>(bh) * x.nkb + j) * nqb;
+  const float c2 = kLog2e * 0.08838834764831845f;
+  f32x16 dk[4], dv[4];   // lane = d column, registers = keys 32 kt + ...
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt) {
+    dk[dt] = f32x16{};
+    dv[dt] = f32x16{};
+  }
+  for (int n = 0; n < nT; ++n) {
+    const int i = tl[n];
+    const size_t row0 = head + static_cast<size_t>(i) * kBQ;
+    __syncthreads();
+    stage128_q<T>(Qs, Ds, static_cast<const T*>(x.Q) + row0 * kD, x.dO + row0 * kD,
+                  x.alpha[static_cast<size_t>(bh % x.H) * nqb + i], t);
+    if (t < kBQ) {
+      lse_s[t] = x.lse2[row0 + t];
+      D_s[t] = x.Dd[row0 + t];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int qq = 0; qq < 2; ++qq) {
+      const int qt = 2 * qh + qq;
+      f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        s = mfma(ld_row8(&Qs[(32 * qt + l32) * kLd + 16 * u + 8 * g]),
+                 ld_row8(&Ks[(32 * kt + l32) * kLd + 16 * u + 8 * g]), s);
+        dp = mfma(ld_row8(&Ds[(32 * qt + l32) * kLd + 16 * u + 8 * g]),
+                  ld_row8(&Vs[(32 * kt + l32) * kLd + 16 * u + 8 * g]), dp);
+      }
+#pragma unroll
+      for (int k4 = 0; k4 < 4; ++k4) {
+        const int qr = 32 * qt + 8 * k4 + 4 * g;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const float p = exp2f(s[4 * k4 + k] * c2 - lse_s[qr + k]);
+          s[4 * k4 + k] = p;
+          dp[4 * k4 + k] = p * (dp[4 * k4 + k] - D_s[qr + k]);
+        }
+      }
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          dv[dt] = mfma(acc_op(s, h), ld_col8_acc(Ds, 32 * dt + l32, 32 * qt + 16 * h, g), dv[dt]);
+          dk[dt] = mfma(acc_op(dp, h), ld_col8_acc(Qs, 32 * dt + l32, 32 * qt + 16 * h, g), dk[dt]);
+        }
+    }
+  }
+  __syncthreads();   // Qs / Ds free: exchange the two query halves through X
+  const float sc = 0.08838834764831845f;
+  if (qh == 1) {
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = 32 * kt + 8 * (r >> 2) + 4 * g + (r & 3);
+        X[key * kXld + 32 * dt + l32] = dk[dt][r];
+        X[(kBK + key) * kXld + 32 * dt + l32] = dv[dt][r];
+      }
+  }
+  __syncthreads();
+  if (qh == 0) {
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = 32 * kt + 8 * (r >> 2) + 4 * g + (r & 3);
+        dk[dt][r] = (dk[dt][r] + X[key * kXld + 32 * dt + l32]) * sc;
+        dv[dt][r] += X[(kBK + key) * kXld + 32 * dt + l32];
+      }
+  }
+  __syncthreads();
+  if (qh == 0) {   // same positions: DKs = X rows 0-63, DVs = X rows 64-127
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = 32 * kt + 8 * (r >> 2) + 4 * g + (r & 3);
+        DKs[key * kXld + 32 * dt + l32] = dk[dt][r];
+        DVs[key * kXld + 32 * dt + l32] = dv[dt][r];
+      }
+  }
+  // ---- linear part. phi(K_s,j) into Ks (thread: row t / 4, columns 32 (t % 4) .. +31)
+  {
+    const int r = t >> 2, c0 = 32 * (t & 3);
+    const float* mp = x.mu32 + static_cast<size_t>(bh) * kD + c0;
+    float v[32];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) load8<T>(static_cast<const T*>(x.K) + (krow0 + r) * kD + c0 + 8 * u, v + 8 * u);
+    float mx = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < 32; ++k) {
+      v[k] -= mp[k];
+      mx = fmaxf(mx, v[k]);
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 1));
+    mx = fmaxf(mx, __shfl_xor(mx, 2));
+    float s = 0.f;
+#pragma unroll
+    for (int k = 0; k < 32; ++k) {
+      v[k] = __expf(v[k] - mx);
+      s += v[k];
+    }
+    s += __shfl_xor(s, 1);
+    s += __shfl_xor(s, 2);
+    const float inv = 1.0f / s;
+#pragma unroll
+    for (int k = 0; k < 32; ++k) v[k] *= inv;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) st_bf16x8(&Ks[r * kLd + c0 + 8 * u], v + 8 * u);
+  }
+  // dh_j^T = dH_tot^T - sum over the keeping query blocks of dH_i^T (bf16 [o][a]); dz_j
+  {
+    const uint16_t* src = x.dht + static_cast<size_t>(bh) * nqb * (kD * kD);
+    float acc[8][8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+#pragma unroll
+      for (int k = 0; k < 8; ++k) acc[u][k] = 0.f;
+    for (int n = 0; n < nT; ++n) {
+      const uint16_t* hi = src + static_cast<size_t>(tl[n]) * (kD * kD);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        float f[8];
+        unpack_bf16x8(*reinterpret_cast<const i32x4*>(hi + 8 * (t + 256 * u)), f);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) acc[u][k] += f[k];
+      }
+    }
+    const float* tot = x.dhtot + static_cast<size_t>(bh) * (kD * kD);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int c = t + 256 * u, o = c >> 4, a0 = 8 * (c & 15);
+      const f32x4 t0 = *reinterpret_cast<const f32x4*>(tot + 8 * c);
+      const f32x4 t1 = *reinterpret_cast<const f32x4*>(tot + 8 * c + 4);
+      float hv[8] = {t0[0], t0[1], t0[2], t0[3], t1[0], t1[1], t1[2], t1[3]};
+#pragma unroll
+      for (int k = 0; k < 8; ++k) hv[k] -= acc[u][k];
+      st_bf16x8(&DH[o * kLd + a0], hv);
+    }
+    if (t < kD) {
+      float s = 0.f;
+      for (int n = 0; n < nT; ++n) s += x.dz[(static_cast<size_t>(bh) * nqb + tl[n]) * kD + t];
+      dz_s[t] = x.dztot[static_cast<size_t>(bh) * kD + t] - s;
+    }
+  }
+  __syncthreads();
+  // dV += phi dh_j: keys 32 kt .. +31 (rows), o tiles 2 qh, 2 qh + 1 (lane = o)
+#pragma unroll
+  for (int ot = 2 * qh; ot < 2 * qh + 2; ++ot) {
+    f32x16 c = f32x16{};
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      c = mfma(ld_row8(&Ks[(32 * kt + l32) * kLd + 16 * u + 8 * g]),
+               ld_row8(&DH[(32 * ot + l32) * kLd + 16 * u + 8 * g]), c);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int key = 32 * kt + 8 * (r >> 2) + 4 * g + (r & 3);
+      DVs[key * kXld + 32 * ot + l32] += c[r];
+    }
+  }
+  // dphi^T = dh_j V_j^T + dz_j: a tiles 2 qh, 2 qh + 1 (registers), keys 32 kt + lane
+  f32x16 dph[2];
+  float cs = 0.f;
+  const int key = 32 * kt + l32;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int at = 2 * qh + h;
+    dph[h] = f32x16{};
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      dph[h] = mfma(ld_col8(DH, 32 * at + l32, 16 * u + 8 * g),
+                    ld_row8(&Vs[key * kLd + 16 * u + 8 * g]), dph[h]);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int a = 32 * at + 8 * (r >> 2) + 4 * g + (r & 3);
+      dph[h][r] += dz_s[a];
+      cs += dph[h][r] * bf(Ks[key * kLd + a]);
+    }
+  }
+  cs += __shfl_xor(cs, 32);
+  if (g == 0) crow[qh * kBK + key] = cs;
+  __syncthreads();
+  cs = crow[key] + crow[kBK + key];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int at = 2 * qh + h;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int a = 32 * at + 8 * (r >> 2) + 4 * g + (r & 3);
+      DKs[key * kXld + a] += bf(Ks[key * kLd + a]) * (dph[h][r] - cs);
+    }
+  }
+  __syncthreads();
+  // ---- write dK_s, dV; column sums of dK_s for the centring
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const int e = t + 256 * u, r = e >> 5, c4 = 4 * (e & 31);
+    *reinterpret_cast<f32x4*>(x.dK + (krow0 + r) * kD + c4) =
+        *reinterpret_cast<const f32x4*>(&DKs[r * kXld + c4]);
+    *reinterpret_cast<f32x4*>(x.dV + (krow0 + r) * kD + c4) =
+        *reinterpret_cast<const f32x4*>(&DVs[r * kXld + c4]);
+  }
+  if (t < kD) {
+    float s = 0.f;
+    for (int r = 0; r < kBK; ++r) s += DKs[r * kXld + t];
+    x.kcol[(static_cast<size_t>(bh) * x.nkb + j) * kD + t] = s;
+  }
+}
+
+// ---------------------------------------------------------------- dK centring
+// dk_mean: grid (BH), 128 threads: mean over key blocks of the column sums, / N.
+__global__ __launch_bounds__(128) void dk_mean_kernel(const float* __restrict__ kcol,
+                                                      float* __restrict__ kmean, int nkb, int N) {
+  const int bh = blockIdx.x, t = threadIdx.x;
+  const float* src = kcol + static_cast<size_t>(bh) * nkb * kD + t;
+  float a[4] = {0.f, 0.f, 0.f, 0.f};
+  int j = 0;
+  for (; j + 3 < nkb; j += 4)
+#pragma unroll
+    for (int k = 0; k < 4; ++k) a[k] += src[static_cast<size_t>(j + k) * kD];
+  for (; j < nkb; ++j) a[0] += src[static_cast<size_t>(j) * kD];
+  kmean[static_cast<size_t>(bh) * kD + t] = ((a[0] + a[1]) + (a[2] + a[3])) / static_cast<float>(N);
+}
+// dk_center: grid (N * d / 1024, BH), 256 threads: dK -= mean (four elements per thread).
+__global__ __launch_bounds__(256) void dk_center_kernel(float* __restrict__ dK,
+                                                        const float* __restrict__ kmean, int N) {
+  const int bh = blockIdx.y;
+  const size_t e = 1024 * static_cast<size_t>(blockIdx.x) + 4 * threadIdx.x;
+  const f32x4 m = *reinterpret_cast<const f32x4*>(kmean + static_cast<size_t>(bh) * kD + (e & (kD - 1)));
+  f32x4* p = reinterpret_cast<f32x4*>(dK + static_cast<size_t>(bh) * N * kD + e);
+  *p = *p - m;
+}
+
+// ---------------------------------------------------------------- launchers
+hipError_t launch_key_lists(const Geom& g, const uint8_t* mask, int32_t* tcnt, uint16_t* tlist,
+                            hipStream_t s) {
+  hipLaunchKernelGGL(key_lists_kernel, dim3((g.nkb + 255) / 256, g.BH), dim3(256), 0, s, mask,
+                     tcnt, tlist, g.nqb, g.nkb);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_lin_q(const Geom& g, int dtype, const BwdArgs& x, hipStream_t s) {
+  if (dtype == 0)
+    hipLaunchKernelGGL(bwd_lin_q_kernel<float>, dim3(g.nqb, g.BH), dim3(256), 0, s, x);
+  else
+    hipLaunchKernelGGL(bwd_lin_q_kernel<uint16_t>, dim3(g.nqb, g.BH), dim3(256), 0, s, x);
+  return hipGetLastError();
+}
+
+hipError_t launch_dh_total(const Geom& g, const BwdArgs& x, hipStream_t s) {
+  hipLaunchKernelGGL(dh_total_kernel, dim3(9, g.BH), dim3(256), 0, s, x.dht, x.dz, x.dhtot,
+                     x.dztot, g.nqb);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_q(const Geom& g, int dtype, const BwdArgs& x, hipStream_t s) {
+  if (dtype == 0)
+    hipLaunchKernelGGL(bwd_q_kernel<float>, dim3(g.nqb, g.BH), dim3(256), 0, s, x);
+  else
+    hipLaunchKernelGGL(bwd_q_kernel<uint16_t>, dim3(g.nqb, g.BH), dim3(256), 0, s, x);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_kv(const Geom& g, int dtype, const BwdArgs& x, hipStream_t s) {
+  if (dtype == 0)
+    hipLaunchKernelGGL(bwd_kv_kernel<float>, dim3(g.nkb, g.BH), dim3(256), 0, s, x);
+  else
+    hipLaunchKernelGGL(bwd_kv_kernel<uint16_t>, dim3(g.nkb, g.BH), dim3(256), 0, s, x);
+  return hipGetLastError();
+}
+
+hipError_t launch_dk_center(const Geom& g, const BwdArgs& x, hipStream_t s) {
+  hipLaunchKernelGGL(dk_mean_kernel, dim3(g.BH), dim3(kD), 0, s, x.kcol, x.kmean, g.nkb, g.N);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(dk_center_kernel, dim3(g.N * kD / 1024, g.BH), dim3(256), 0, s, x.dK,
+                     x.kmean, g.N);
+  return hipGetLastError();
+}
+
+}  // namespace sla2

@@ -305,4 +305,43 @@ struct AttnArgs {
 hipError_t launch_attn(const Geom& g, int dtype, const void* Q, const AttnArgs& x,
                        hipStream_t s);
 
+// Operands of the backward kernels. Layouts: Q, K, V [BH][N][d] (fp32 or bf16); dO, dQ, dK,
+// dV [BH][N][d] fp32; h_j^T bf16 in fragment order; H_tot standard [a][o] fp32; dH_i^T bf16
+// [BH][nqb][o][a]; dH_tot^T fp32 [BH][o][a]; lse2 = row log-sum-exp of the kept logits in
+// base-2 units (S log2(e) / sqrt(d)); D = rowsum(dO_s O_s); key lists [BH][nkb][nqb] uint16.
+struct BwdArgs {
+  const void *Q, *K, *V;
+  const float* mu32;
+  const float* dO;
+  const float* alpha;
+  const int32_t* list;       // kept lists, stride nkb
+  const int32_t* cnt;
+  const uint16_t* hbf;
+  const float* htot;
+  const float* z;
+  const float* ztot;
+  float* dQ;
+  uint16_t* dht;
+  float* dz;
+  float* dalpha;             // [BH][nqb]
+  float* dhtot;
+  float* dztot;
+  float* lse2;
+  float* Dd;
+  const int32_t* tcnt;
+  const uint16_t* tlist;
+  float *dK, *dV;
+  float* kcol;               // [BH][nkb][d] column sums of dK_s per key block
+  float* kmean;              // [BH][d]
+  int H, BH, nqb, nkb;
+};
+hipError_t launch_key_lists(const Geom& g, const uint8_t* mask, int32_t* tcnt, uint16_t* tlist,
+                            hipStream_t s);
+hipError_t launch_bwd_lin_q(const Geom& g, int dtype, const BwdArgs& x, hipStream_t s);
+hipError_t launch_dh_total(const Geom& g, const BwdArgs& x, hipStream_t s);
+hipError_t launch_bwd_q(const Geom& g, int dtype, const BwdArgs& x, hipStream_t s);
+hipError_t launch_bwd_kv(const Geom& g, int dtype, const BwdArgs& x, hipStream_t s);
+// column mean of dK_s, then dK -= mean (two kernels)
+hipError_t launch_dk_center(const Geom& g, const BwdArgs& x, hipStream_t s);
+
 }  // namespace sla2

@@ -43,10 +43,10 @@ class Taps(ctypes.Structure):
     _fields_ = [(name, ctypes.c_void_p) for name in TAP_NAMES] + [("stage_events", ctypes.c_void_p)]
 
 
-def event_array(events):
+def event_array(events, count=MAX_STAGES + 1):
     """ctypes array of raw hipEvent_t handles of torch.cuda.Event objects (created if needed)."""
-    if len(events) != MAX_STAGES + 1:
-        raise ValueError(f"need {MAX_STAGES + 1} events")
+    if len(events) != count:
+        raise ValueError(f"need {count} events")
     for e in events:
         if e.cuda_event == 0:
             e.record()                         # torch creates the event on first record
@@ -88,8 +88,10 @@ def lib():
                                         vp, vp, ctypes.POINTER(vp), vp, sz, vp]
         L.sla2_forward_with_mask.argtypes = [ctypes.POINTER(Shape), vp, vp, vp, vp, vp, ctypes.c_int,
                                              vp, ctypes.POINTER(Taps), vp, sz, vp]
+        L.sla2_backward.argtypes = [ctypes.POINTER(Shape), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                    ctypes.POINTER(vp), vp, sz, vp]
         for name in ("sla2_router", "sla2_router_soft", "sla2_linear_precompute", "sla2_forward",
-                     "sla2_forward_sla1", "sla2_forward_with_mask"):
+                     "sla2_forward_sla1", "sla2_forward_with_mask", "sla2_backward"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -305,3 +307,33 @@ def sla2_forward_with_mask(q, k, v, mask, alpha, taps=False, out=None, workspace
                                       ws.numel(), _stream(dev))
     _check(st, "sla2_forward_with_mask")
     return (o, tdict) if taps else o
+
+
+BACKWARD_STAGES = 11   # kernels (stage events: one more)
+
+
+def sla2_backward(q, k, v, mask, alpha, grad_out, out=None, workspace=None, events=None):
+    """Gradients of sum(grad_out * O) for the unquantised SLA2 forward with a fixed block mask:
+    returns (dQ, dK, dV, dalpha), fp32 [B,H,N,d] x 3 and [B,H,N/128].
+
+    mask [B,H,N/128,N/64] uint8 (the forward's block mask); alpha [H,N/128] fp32; grad_out
+    [B,H,N,d] fp32. `out`: optional tuple of the four output tensors. `events`: optional list
+    of 12 torch.cuda.Event(enable_timing=True) recorded before the first and after each of the
+    eleven stages on the current stream."""
+    _contig(q, k, v, mask, alpha, grad_out)
+    shp = shape_of(q)
+    dev = q.device
+    B, H, N, _ = q.shape
+    if out is None:
+        out = (torch.empty(q.shape, dtype=torch.float32, device=dev),
+               torch.empty(q.shape, dtype=torch.float32, device=dev),
+               torch.empty(q.shape, dtype=torch.float32, device=dev),
+               torch.empty((B, H, N // 128), dtype=torch.float32, device=dev))
+    _contig(*out)
+    ws = workspace if workspace is not None else workspace_for(q)
+    evs = event_array(events, BACKWARD_STAGES + 1) if events is not None else None
+    st = lib().sla2_backward(ctypes.byref(shp), _ptr(q), _ptr(k), _ptr(v), _ptr(mask),
+                             _ptr(alpha), _ptr(grad_out), _ptr(out[0]), _ptr(out[1]),
+                             _ptr(out[2]), _ptr(out[3]), evs, _ptr(ws), ws.numel(), _stream(dev))
+    _check(st, "sla2_backward")
+    return out

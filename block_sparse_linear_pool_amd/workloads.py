@@ -183,3 +183,15 @@ def random_weights(seed: int, H: int, n_qb: int, d: int = HEAD_DIM, alpha_lo: fl
     wk = rng.normal(0.0, 1.0 / math.sqrt(d), (H, d, d)).astype(np.float32)
     alpha = rng.uniform(alpha_lo, 1.0, (H, n_qb)).astype(np.float32)
     return wq, wk, alpha
+
+
+def grad_out(seed: int, shape) -> np.ndarray:
+    """The upstream gradient dO of a backward test or bench: i.i.d. N(0, 1), fp32."""
+    rng = np.random.default_rng([seed, 11])
+    return rng.standard_normal(shape, dtype=np.float32)
+
+
+def random_mask(seed: int, B: int, H: int, n_qb: int, n_kb: int, frac: float) -> np.ndarray:
+    """A block mask [B, H, n_qb, n_kb] uint8 with each entry kept with probability frac."""
+    rng = np.random.default_rng([seed, 13])
+    return (rng.random((B, H, n_qb, n_kb)) < frac).astype(np.uint8)

@@ -1,5 +1,5 @@
 /*
- * sla2.h — C ABI of libsla2.so: the SLA2 inference forward on one AMD MI355X (gfx950).
+ * sla2.h — C ABI of libsla2.so: the SLA2 forward (and its backward) on one AMD MI355X (gfx950).
  *
  * SLA2 is sparse-linear attention with a learned block router. The four steps
  * follow the computation-flow paragraph (steps 1-4) of the summary page
@@ -187,6 +187,32 @@ sla2_status sla2_forward_with_mask(const sla2_shape *shape, const void *Q, const
                                    const void *V, const uint8_t *mask, const float *alpha,
                                    sla2_quant quant, float *O, const sla2_taps *taps,
                                    void *workspace, size_t workspace_bytes, void *stream);
+
+/* The backward pass ("SLA2: Sparse-Linear Attention v2 for Diffusion Transformers": §3 table
+ * and §4 six checks item 4, low-bit forward with a 16-bit backward, the straight-through
+ * estimator; §7 note 3, the gradient derived by hand with the linear branch's dH_i, dZ_i
+ * formed first). It returns the gradients of sum(dO * O) for the UNQUANTISED forward
+ *   O = alpha O_s + (1 - alpha) O_l,  O_s = softmax over the kept keys of Q K_s^T / sqrt(d) V,
+ *   O_l = phi(Q) H_i / (phi(Q) Z_i) over the dropped key blocks,  K_s = K - colmean(K),
+ * with the block mask held fixed (the hard Top-k router has no gradient).
+ *   mask   [B,H,N/128,N/64] uint8, the forward's block mask (any byte != 0 counts as 1)
+ *   alpha  [H,N/128] fp32, as in the forward
+ *   dO     [B,H,N,d] fp32, the gradient of the loss with respect to O
+ *   dQ, dK, dV  [B,H,N,d] fp32 outputs (overwritten)
+ *   dalpha [B,H,N/128] fp32 output: per batch and head; sum over B for alpha's gradient
+ *   stage_events  NULL, or 12 caller-created hipEvent_t handles recorded on the stream before
+ *          the first kernel and after each of pool (K sums), colmean, kv_prep, linear_total,
+ *          mask_to_list, key_lists (mask transposed), bwd_lin_q (linear branch per query
+ *          block), dh_total, bwd_q (sparse branch per query block: dQ, log-sum-exp, D),
+ *          bwd_kv (per key block: dK_s, dV) and dk_center (dK = dK_s - colmean(dK_s))
+ * Precision: Q, K_s, V, P, dS, dO_s = alpha dO, phi(Q), phi(K_s), H_i, dH_i and dh_j enter
+ * the matrix products as bf16 (fp32 accumulation); softmax statistics, row sums and the
+ * outputs are fp32. A query block with no kept block gets no sparse gradient and one with no
+ * dropped block no linear gradient (their branch output is 0 in the forward). Deterministic. */
+sla2_status sla2_backward(const sla2_shape *shape, const void *Q, const void *K, const void *V,
+                          const uint8_t *mask, const float *alpha, const float *dO, float *dQ,
+                          float *dK, float *dV, float *dalpha, void **stage_events,
+                          void *workspace, size_t workspace_bytes, void *stream);
 
 #ifdef __cplusplus
 }

@@ -28,7 +28,8 @@ def test_library_exports_every_declared_symbol():
     names = declared_functions()
     assert set(names) == {"sla2_blocks_kept", "sla2_workspace_bytes", "sla2_status_string",
                           "sla2_router", "sla2_router_soft", "sla2_linear_precompute",
-                          "sla2_forward", "sla2_forward_sla1", "sla2_forward_with_mask"}
+                          "sla2_forward", "sla2_forward_sla1", "sla2_forward_with_mask",
+                          "sla2_backward"}
     for n in names:
         assert hasattr(L, n), n
 
@@ -131,6 +132,14 @@ def test_other_entry_points_validate():
     assert r == ARG
     r = L.sla2_forward_with_mask(ctypes.byref(shape(N=64)), A, A, A, A, A, 1, A, None, A, need, None)
     assert r == SHAPE
+    bwd = L.sla2_backward
+    assert bwd(ctypes.byref(s), A, A, A, None, A, A, A, A, A, A, None, A, need, None) == NULL  # mask
+    assert bwd(ctypes.byref(s), A, A, A, A, A, None, A, A, A, A, None, A, need, None) == NULL  # dO
+    assert bwd(ctypes.byref(s), A, A, A, A, A, A, A, A, A, None, None, A, need, None) == NULL  # dalpha
+    assert bwd(ctypes.byref(s), A, A, A, A, A, A, A, MIS, A, A, None, A, need, None) == MISAL
+    assert bwd(ctypes.byref(s), A, A, A, A, A, A, A, A, A, A, None, A, need - 1, None) == WS
+    assert bwd(ctypes.byref(shape(N=200)), A, A, A, A, A, A, A, A, A, A, None, A, need,
+               None) == SHAPE
 
 
 def test_valid_arguments_reach_the_device_check_without_a_gpu():
