@@ -39,10 +39,12 @@ def parse():
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run plain device copies of a known size (the calibration "
                          "workload for the FETCH_SIZE / WRITE_SIZE counters), then exit")
-    ap.add_argument("--op", choices=("forward", "router_soft", "sla1"), default="forward",
+    ap.add_argument("--op", choices=("forward", "router_soft", "sla1", "backward"),
+                    default="forward",
                     help="forward (default): the inference forward; router_soft: the SoftTop-k "
                          "router (training-time step 1); sla1: the earlier SLA mix O = O_s + "
-                         "O_l Wo with the heuristic router (comparison workload); each prints "
+                         "O_l Wo with the heuristic router (comparison workload); backward: "
+                         "the gradients dQ, dK, dV, dalpha for the router's mask; each prints "
                          "its own JSON line")
     ap.add_argument("--tau", type=float, default=0.1, help="SoftTop-k temperature (router_soft)")
     ap.add_argument("--quiet", action="store_true")
@@ -295,6 +297,105 @@ def run_sla1(args, w, q, k, v, keep):
     print(json.dumps(result), flush=True)
 
 
+def run_backward(args, w, q, k, v, wq, wk, alpha, keep):
+    """Times sla2_backward (dQ, dK, dV, dalpha for a fixed mask: the router's on these inputs,
+    computed once before the timed region, as the forward would hand it over)."""
+    import numpy as np
+    import torch
+
+    from block_sparse_linear_pool_amd import accounting as acc
+    from block_sparse_linear_pool_amd import sla2
+    from block_sparse_linear_pool_amd import workloads as W
+
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    dev = torch.device("cuda:0")
+    gq, gk, gv = (torch.from_numpy(a).to(dev, dt) for a in (q, k, v))
+    ga = torch.from_numpy(alpha).to(dev)
+    dO_h = W.grad_out(w.seed, q.shape)
+    gdo = torch.from_numpy(dO_h).to(dev)
+    ws = sla2.workspace_for(gq)
+    _, mask, _ = sla2.sla2_router(gq, gk, torch.from_numpy(wq).to(dev),
+                                  torch.from_numpy(wk).to(dev), keep, workspace=ws)
+    out = (torch.empty(gq.shape, dtype=torch.float32, device=dev),
+           torch.empty(gq.shape, dtype=torch.float32, device=dev),
+           torch.empty(gq.shape, dtype=torch.float32, device=dev),
+           torch.empty((w.B, w.H, w.n_qb), dtype=torch.float32, device=dev))
+    kb = sla2.sla2_blocks_kept(w.n_kb, keep)
+    prob = acc.Problem(w.B, w.H, w.N, kb, in_bytes=2 if dt == torch.bfloat16 else 4)
+
+    def step(events=None):
+        sla2.sla2_backward(gq, gk, gv, mask, ga, gdo, out=out, workspace=ws, events=events)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    log(args, f"[bench] backward {ms:.4f} ms/call")
+    names = acc.KERNELS_BACKWARD
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(sla2.BACKWARD_STAGES + 1)]
+    per = np.zeros(len(names))
+    for _ in range(args.steps):
+        step(evs)
+        torch.cuda.synchronize()
+        per += [evs[i].elapsed_time(evs[i + 1]) for i in range(len(names))]
+    per /= args.steps
+    kernels = {}
+    for n, t in zip(names, per):
+        fl, by = acc.kernel_flops(prob, n), acc.kernel_bytes(prob, n)
+        kernels[n] = {"ms": round(float(t), 5),
+                      "tflops": round(fl / (t * 1e-3) / 1e12, 2) if fl else None,
+                      "gbs": round(by / (t * 1e-3) / 1e9, 1) if by else None}
+        log(args, f"[bench]   {n:13s} {t * 1e3:9.1f} us  {kernels[n]}")
+    dom = names[int(np.argmax(per))]
+    t_dom = float(np.max(per)) * 1e-3
+    if acc.kernel_bound(dom) == "mfma_bf16":
+        achieved = acc.kernel_flops(prob, dom) / t_dom / 1e12
+        peak, unit, bound = acc.MI355X_PEAK["mfma_bf16_tflops"], "TFLOP/s", "mfma"
+    else:
+        achieved = acc.kernel_bytes(prob, dom) / t_dom / 1e9
+        peak, unit, bound = acc.MI355X_PEAK["hbm_gbs"], "GB/s", "hbm"
+    full = acc.full_attention_backward_flops(prob)
+    result = {
+        "metric": "SLA2 backward full-attn-bwd-equiv TFLOPS, N=32768 H=12 d=128 @97%",
+        "value": round(full / (ms * 1e-3) / 1e12, 2),
+        "unit": "TFLOPS (full-attention-backward-equivalent, 10 B H N^2 d per call)",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d,
+                   "input_dtype": w.dtype, "keep_frac": keep, "kb": kb},
+        "roofline": {"kernel": dom, "bound": bound, "achieved": round(achieved, 2), "peak": peak,
+                     "unit": unit, "frac": round(achieved / peak, 4), "traffic": None,
+                     "avg_launch_ms": round(t_dom * 1e3, 5)},
+        "kernels": kernels,
+    }
+    if not args.no_cpu:
+        from threadpoolctl import threadpool_limits
+
+        from oracle import sla2_backward as oracle_bw
+        cores = min(16, len(os.sched_getaffinity(0)))
+        heads = list(range(min(args.cpu_heads, w.H)))
+        mask_h = mask.cpu().numpy()
+        with threadpool_limits(limits=cores):
+            t0 = time.perf_counter()
+            for h in heads:
+                oracle_bw.backward(q[0, h], k[0, h], v[0, h], mask_h[0, h], alpha[h], dO_h[0, h])
+            dt_cpu = time.perf_counter() - t0
+        result["cpu_baseline"] = {
+            "value": round(10.0 * w.N * w.N * w.d * len(heads) / dt_cpu / 1e12, 4),
+            "unit": "TFLOPS (full-attention-backward-equivalent)", "cores": cores,
+            "kind": "oracle",
+            "sample": f"batch 0, heads {heads[0]}-{heads[-1]} of {w.H}, fp64 oracle backward, "
+                      f"{dt_cpu:.1f} s"}
+    print(json.dumps(result), flush=True)
+
+
 def main():
     args = parse()
     if args.copy_probe:
@@ -338,6 +439,10 @@ def main():
     if args.op == "sla1":
         del gv, out
         run_sla1(args, w, q, k, v, keep)
+        return
+    if args.op == "backward":
+        del gq, gk, gv, out, ws
+        run_backward(args, w, q, k, v, wq, wk, alpha, keep)
         return
 
     def step(events=None):

@@ -28,6 +28,10 @@ KERNELS_SOFT_ROUTER = ("pool_sums", "colmean", "project", "score_soft")
 # sla2_forward_sla1 (the earlier SLA mix): identity projections, alpha = 1 fill, O += O_l Wo
 KERNELS_SLA1 = ("pool", "colmean", "project", "score_topk", "fill", "kv_prep", "linear_total",
                 "attn", "sla1_mix")
+# sla2_backward (mask given): the forward's linear precompute, the transposed mask, then the
+# gradient kernels; dk_center is the column mean and the subtraction together
+KERNELS_BACKWARD = ("pool_k", "colmean", "kv_prep", "linear_total", "mask_to_list", "key_lists",
+                    "bwd_lin_q", "dh_total", "bwd_q", "bwd_kv", "dk_center")
 
 
 @dataclasses.dataclass
@@ -77,10 +81,33 @@ def linear_flops(p: Problem) -> float:
     return 2.0 * p.BH * p.N * p.d * p.d + 2.0 * p.BH * p.N * p.d * p.d
 
 
+def full_attention_backward_flops(p: Problem) -> float:
+    """Dense attention backward: five N x N x d products (S, dP, dV, dK, dQ), 10 B H N^2 d."""
+    return 10.0 * p.BH * p.N * p.N * p.d
+
+
 def kernel_bytes(p: Problem, name: str) -> float:
     """Compulsory HBM bytes of one launch of kernel `name`."""
     E, BH, d = p.E, p.BH, p.d
     np_ = (p.nkb + 7) // 8
+    if name == "pool_k":
+        # K read; fp64 block sums written
+        return E * p.in_bytes + BH * p.nkb * d * 8
+    if name == "bwd_lin_q":
+        # Q, dO read (and h_j, z_j once), dQ, bf16 dH_i^T and dZ_i written
+        return (E * p.in_bytes + E * 4 + BH * p.nkb * (d * d * 2 + d * 4) + E * 4
+                + BH * p.nqb * (d * d * 2 + d * 4))
+    if name == "dh_total":
+        return BH * p.nqb * (d * d * 2 + d * 4) + BH * (d * d + d) * 4
+    if name == "bwd_q":
+        # Q, dO, K, V read once; dQ read and written; row statistics written
+        return E * p.in_bytes + E * 4 + 2 * E * p.in_bytes + 2 * E * 4 + BH * p.N * 8
+    if name == "bwd_kv":
+        # K, V, Q, dO, row statistics, dH_i^T read once; dK_s, dV written
+        return (3 * E * p.in_bytes + E * 4 + BH * p.N * 8 + BH * p.nqb * d * d * 2
+                + 2 * E * 4)
+    if name == "dk_center":
+        return 2 * E * 4 + BH * p.nkb * d * 4
     if name == "pool":
         # Q, K read; fp64 block sums, INT8 Q codes and scales written
         return 2 * E * p.in_bytes + BH * (p.nqb + p.nkb) * d * 8 + E + BH * p.nqb * 4
@@ -117,14 +144,26 @@ def kernel_flops(p: Problem, name: str) -> float:
         return 2.0 * p.BH * (p.nqb + p.nkb) * p.d * p.d
     if name in ("kv_prep", "sla1_mix"):
         return 2.0 * p.BH * p.N * p.d * p.d
+    if name == "bwd_lin_q":
+        # num = a H_i, da = dnum H_i^T, dH_i = a^T dnum: 6 N d^2 per head
+        return 6.0 * p.BH * p.N * p.d * p.d
+    if name == "bwd_q":
+        # per kept pair: S and P V (pass 1), S, dP and dS K (pass 2)
+        return 5 * 2.0 * 128 * 64 * p.d * p.pairs
+    if name == "bwd_kv":
+        # per kept pair: S, dP, P^T dO_s, dS^T Q; per key block phi dh_j and V dh_j^T
+        return 4 * 2.0 * 128 * 64 * p.d * p.pairs + 4.0 * p.BH * p.N * p.d * p.d
     return 0.0
 
 
 def kernel_bound(name: str) -> str:
-    """Roofline a kernel is priced against: attn on the INT8/FP8 matrix peak, the fp64
-    logits kernels on the fp64 matrix peak, everything else on HBM bandwidth."""
+    """Roofline a kernel is priced against: attn on the INT8/FP8 matrix peak, the backward's
+    matrix kernels on the bf16 matrix peak, the fp64 logits kernels on the fp64 matrix peak,
+    everything else on HBM bandwidth."""
     if name == "attn":
         return "mfma"
+    if name in ("bwd_q", "bwd_kv", "bwd_lin_q"):
+        return "mfma_bf16"
     if name in ("score_topk", "score_soft", "project"):
         return "mfma_fp64"
     return "hbm"
