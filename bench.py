@@ -321,7 +321,15 @@ def run_backward(args, w, q, k, v, wq, wk, alpha, keep):
            torch.empty(gq.shape, dtype=torch.float32, device=dev),
            torch.empty((w.B, w.H, w.n_qb), dtype=torch.float32, device=dev))
     kb = sla2.sla2_blocks_kept(w.n_kb, keep)
-    prob = acc.Problem(w.B, w.H, w.N, kb, in_bytes=2 if dt == torch.bfloat16 else 4)
+    # how the library splits the key lists: at most C query blocks per key block in bwd_kv,
+    # C = max(16, ceil(2 P / nkb)) per head (P kept pairs), the rest in bwd_kv_extra
+    tj = mask.to(torch.int32).sum(dim=2).cpu().numpy().reshape(w.B * w.H, w.n_kb)
+    main_pairs = 0
+    for row in tj:
+        C = max(16, -(-2 * int(row.sum()) // w.n_kb))
+        main_pairs += int(np.minimum(row, C).sum())
+    prob = acc.Problem(w.B, w.H, w.N, kb, in_bytes=2 if dt == torch.bfloat16 else 4,
+                       kv_main_pairs=main_pairs)
 
     def step(events=None):
         sla2.sla2_backward(gq, gk, gv, mask, ga, gdo, out=out, workspace=ws, events=events)
@@ -369,7 +377,8 @@ def run_backward(args, w, q, k, v, wq, wk, alpha, keep):
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d,
-                   "input_dtype": w.dtype, "keep_frac": keep, "kb": kb},
+                   "input_dtype": w.dtype, "keep_frac": keep, "kb": kb,
+                   "kept_pairs": prob.pairs, "kv_main_pairs": main_pairs},
         "roofline": {"kernel": dom, "bound": bound, "achieved": round(achieved, 2), "peak": peak,
                      "unit": unit, "frac": round(achieved / peak, 4), "traffic": None,
                      "avg_launch_ms": round(t_dom * 1e3, 5)},

@@ -31,7 +31,8 @@ KERNELS_SLA1 = ("pool", "colmean", "project", "score_topk", "fill", "kv_prep", "
 # sla2_backward (mask given): the forward's linear precompute, the transposed mask, then the
 # gradient kernels; dk_center is the column mean and the subtraction together
 KERNELS_BACKWARD = ("pool_k", "colmean", "kv_prep", "linear_total", "mask_to_list", "key_lists",
-                    "bwd_lin_q", "dh_total", "bwd_q", "bwd_kv", "dk_center")
+                    "key_plan", "bwd_lin_q", "dh_total", "bwd_q", "bwd_kv_extra", "bwd_kv",
+                    "dk_center")
 
 
 @dataclasses.dataclass
@@ -42,6 +43,7 @@ class Problem:
     kb: int
     d: int = 128
     in_bytes: int = 2            # bf16 inputs
+    kv_main_pairs: int | None = None   # backward: kept pairs done by bwd_kv (rest: bwd_kv_extra)
 
     @property
     def BH(self):
@@ -150,9 +152,12 @@ def kernel_flops(p: Problem, name: str) -> float:
     if name == "bwd_q":
         # per kept pair: S and P V (pass 1), S, dP and dS K (pass 2)
         return 5 * 2.0 * 128 * 64 * p.d * p.pairs
-    if name == "bwd_kv":
-        # per kept pair: S, dP, P^T dO_s, dS^T Q; per key block phi dh_j and V dh_j^T
-        return 4 * 2.0 * 128 * 64 * p.d * p.pairs + 4.0 * p.BH * p.N * p.d * p.d
+    if name in ("bwd_kv", "bwd_kv_extra"):
+        # per kept pair: S, dP, P^T dO_s, dS^T Q; per key block (bwd_kv) phi dh_j and V dh_j^T
+        main = p.pairs if p.kv_main_pairs is None else p.kv_main_pairs
+        if name == "bwd_kv_extra":
+            return 4 * 2.0 * 128 * 64 * p.d * (p.pairs - main)
+        return 4 * 2.0 * 128 * 64 * p.d * main + 4.0 * p.BH * p.N * p.d * p.d
     return 0.0
 
 
@@ -162,7 +167,7 @@ def kernel_bound(name: str) -> str:
     everything else on HBM bandwidth."""
     if name == "attn":
         return "mfma"
-    if name in ("bwd_q", "bwd_kv", "bwd_lin_q"):
+    if name in ("bwd_q", "bwd_kv", "bwd_kv_extra", "bwd_lin_q"):
         return "mfma_bf16"
     if name in ("score_topk", "score_soft", "project"):
         return "mfma_fp64"

@@ -21,9 +21,11 @@ FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
     # never emit packed fp32 VALU ops
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    # keep MFMA accumulators in arch VGPRs: the online-softmax rescale is VALU work on them
-    "-mllvm", "-amdgpu-mfma-vgpr-form",
 ]
+# keep MFMA accumulators in arch VGPRs (the forward's online-softmax rescale is VALU work on
+# them); the backward's kernels hold more accumulators than that and keep them in AGPRs
+VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
+NO_VGPR_FORM = {"backward.hip"}
 
 
 def _hipcc() -> str:
@@ -36,7 +38,8 @@ def _hipcc() -> str:
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
     lang = ["-x", "hip"] if src.endswith(".cpp") else []
-    cmd = [_hipcc(), *FLAGS, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+    extra = [] if src in NO_VGPR_FORM else VGPR_FORM
+    cmd = [_hipcc(), *FLAGS, *extra, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{res.stdout}\n{res.stderr}")

@@ -21,7 +21,9 @@ struct Plan {
   size_t qsum, ksum, mu64, mu32, A, Bt, mask, list, cnt, qc, kc, vc, sq, sk, sv, hbf, z, hpart,
       zpart, htot, ztot, ones;
   // backward only
-  size_t tcnt, tlist, lse2, Dd, dht, dz, dhtot, dztot, kcol, kmean, total;
+  size_t tcnt, tlist, lse2, Dd, dht, dz, dhtot, dztot, kcol, kmean, qbf, vbf, ksb, dos, kplan,
+      xoff, items, xpart, total;
+  int cap;
 };
 
 Plan make_plan(const Geom& g) {
@@ -66,6 +68,15 @@ Plan make_plan(const Geom& g) {
   p.dztot = take(BH * kD * 4);
   p.kcol = take(BH * nkb * kD * 4);
   p.kmean = take(BH * kD * 4);
+  p.qbf = take(BH * N * kD * 2);
+  p.vbf = take(BH * N * kD * 2);
+  p.ksb = take(BH * N * kD * 2);
+  p.dos = take(BH * N * kD * 2);
+  p.cap = static_cast<int>((nkb + 1) / 2);
+  p.kplan = take(BH * 2 * 4);
+  p.xoff = take(BH * nkb * 4);
+  p.items = take(BH * static_cast<size_t>(p.cap) * 4);
+  p.xpart = take(BH * static_cast<size_t>(p.cap) * kSlot * 4);
   p.total = o;
   return p;
 }
@@ -524,7 +535,7 @@ sla2_status sla2_backward(const sla2_shape* shape, const void* Q, const void* K,
   const Plan p = make_plan(g);
   const int dt = shape->dtype == SLA2_FP32 ? 0 : 1;
   void* ws = workspace;
-  Rec rec(stage_events, 12);
+  Rec rec(stage_events, 14);
   if (rec.mark(stream) != hipSuccess) return SLA2_ERR_HIP;
   // forward pieces: colmean(K), the bf16 h_j^T, z_j and H_tot, Z_tot; the kept lists
   SLA2_LAUNCH(launch_pool(g, dt, nullptr, K, at<double>(ws, p.qsum), at<double>(ws, p.ksum),
@@ -548,8 +559,26 @@ sla2_status sla2_backward(const sla2_shape* shape, const void* Q, const void* K,
                                   at<int32_t>(ws, p.cnt), stream));
   SLA2_LAUNCH(launch_key_lists(g, at<uint8_t>(ws, p.mask), at<int32_t>(ws, p.tcnt),
                                at<uint16_t>(ws, p.tlist), stream));
+  SLA2_LAUNCH(launch_key_plan(g, at<int32_t>(ws, p.tcnt), at<int32_t>(ws, p.kplan),
+                              at<int32_t>(ws, p.xoff), at<int32_t>(ws, p.items), p.cap, stream));
   BwdArgs b{};
   b.Q = Q; b.K = K; b.V = V;
+  if (dt == 0) {   // fp32 inputs: bf16 copies of Q and V in the workspace
+    b.qbf_w = at<uint16_t>(ws, p.qbf);
+    b.vbf_w = at<uint16_t>(ws, p.vbf);
+    b.qbf = b.qbf_w;
+    b.vbf = b.vbf_w;
+  } else {
+    b.qbf = static_cast<const uint16_t*>(Q);
+    b.vbf = static_cast<const uint16_t*>(V);
+  }
+  b.ksb = at<uint16_t>(ws, p.ksb);
+  b.dos = at<uint16_t>(ws, p.dos);
+  b.plan = at<int32_t>(ws, p.kplan);
+  b.xoff = at<int32_t>(ws, p.xoff);
+  b.items = at<int32_t>(ws, p.items);
+  b.xpart = at<float>(ws, p.xpart);
+  b.cap = p.cap;
   b.mu32 = at<float>(ws, p.mu32);
   b.dO = dO;
   b.alpha = alpha;
@@ -579,8 +608,9 @@ sla2_status sla2_backward(const sla2_shape* shape, const void* Q, const void* K,
   b.nkb = g.nkb;
   SLA2_LAUNCH(launch_bwd_lin_q(g, dt, b, stream));
   SLA2_LAUNCH(launch_dh_total(g, b, stream));
-  SLA2_LAUNCH(launch_bwd_q(g, dt, b, stream));
-  SLA2_LAUNCH(launch_bwd_kv(g, dt, b, stream));
+  SLA2_LAUNCH(launch_bwd_q(g, b, stream));
+  SLA2_LAUNCH(launch_bwd_kv_extra(g, b, stream));
+  SLA2_LAUNCH(launch_bwd_kv(g, b, stream));
   SLA2_LAUNCH(launch_dk_center(g, b, stream));
   return SLA2_OK;
 }

@@ -41,6 +41,7 @@ namespace {
 constexpr int kLd = 136;          // bf16 LDS row stride (elements)
 constexpr int kTile = kD * kLd;   // one 128-row bf16 tile
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kInvSqrtD = 0.08838834764831845f;   // 1 / sqrt(128)
 
 __device__ inline bf16x8 ld_row8(const uint16_t* p) {
   return __builtin_bit_cast(bf16x8, *reinterpret_cast<const i32x4*>(p));
@@ -99,59 +100,84 @@ __device__ inline void unpack_bf16x8(const i32x4& v, float* out) {
   }
 }
 __device__ inline float bf(uint16_t v) { return __uint_as_float(static_cast<uint32_t>(v) << 16); }
-
-// Stage a 64-row block of K_s = K - mu (mu given) or V (mu null) as bf16 [64][kLd]:
-// thread t converts rows t / 16 + 16 u, columns 8 (t % 16) .. +7.
-template <typename T>
-__device__ inline void stage64(uint16_t* dst, const T* src, const float* mu, int t) {
-  const int c8 = 8 * (t & 15);
-#pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int r = (t >> 4) + 16 * u;
-    float v[8];
-    load8<T>(src + r * kD + c8, v);
-    if (mu != nullptr) {
-#pragma unroll
-      for (int k = 0; k < 8; ++k) v[k] -= mu[k];
-    }
-    st_bf16x8(dst + r * kLd + c8, v);
-  }
-}
-// Stage a 128-row query block of Q as bf16 [128][kLd], and dO_s = alpha dO (dO fp32).
-template <typename T>
-__device__ inline void stage128_q(uint16_t* qs, uint16_t* dos, const T* q, const float* dO,
-                                  float alpha, int t) {
-  const int c8 = 8 * (t & 15);
-#pragma unroll
-  for (int u = 0; u < 8; ++u) {
-    const int r = (t >> 4) + 16 * u;
-    float v[8];
-    load8<T>(q + r * kD + c8, v);
-    st_bf16x8(qs + r * kLd + c8, v);
-    load8<float>(dO + r * kD + c8, v);
-#pragma unroll
-    for (int k = 0; k < 8; ++k) v[k] *= alpha;
-    st_bf16x8(dos + r * kLd + c8, v);
-  }
+__device__ inline int lanes_below(uint64_t m) {
+  return __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m >> 32),
+                                   __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0));
 }
 
 }  // namespace
 
 // ---------------------------------------------------------------- key_lists
-// grid (ceil(nkb / 256), BH), 256 threads; thread = key block j: the ascending query blocks
-// whose mask row keeps j (mask already 0/1).
+// grid (ceil(nkb / 4), BH), 256 threads; wavefront w compacts mask column j = 4 x + w: the
+// ascending query blocks whose mask row keeps key block j (mask already 0/1).
 __global__ __launch_bounds__(256) void key_lists_kernel(const uint8_t* __restrict__ mask,
                                                         int32_t* __restrict__ tcnt,
                                                         uint16_t* __restrict__ tlist, int nqb,
                                                         int nkb) {
-  const int bh = blockIdx.y, j = blockIdx.x * 256 + threadIdx.x;
+  const int bh = blockIdx.y, lane = threadIdx.x & 63;
+  const int j = 4 * blockIdx.x + (threadIdx.x >> 6);
   if (j >= nkb) return;
   const uint8_t* m = mask + static_cast<size_t>(bh) * nqb * nkb + j;
   uint16_t* out = tlist + (static_cast<size_t>(bh) * nkb + j) * nqb;
-  int c = 0;
-  for (int i = 0; i < nqb; ++i)
-    if (m[static_cast<size_t>(i) * nkb]) out[c++] = static_cast<uint16_t>(i);
-  tcnt[static_cast<size_t>(bh) * nkb + j] = c;
+  int before = 0;
+  for (int i0 = 0; i0 < nqb; i0 += 64) {
+    const int i = i0 + lane;
+    const bool sel = i < nqb && m[static_cast<size_t>(i) * nkb] != 0;
+    const uint64_t b = __ballot(sel);
+    if (sel) out[before + lanes_below(b)] = static_cast<uint16_t>(i);
+    before += __popcll(b);
+  }
+  if (lane == 0) tcnt[static_cast<size_t>(bh) * nkb + j] = before;
+}
+
+// ---------------------------------------------------------------- key_plan
+// grid (BH), 1024 threads. Long key lists are cut into work items of at most C query blocks,
+// C = max(kChunk, ceil(2 P / nkb)) for P kept pairs in the head, so the number of items past
+// the first of each key block is at most P / C <= nkb / 2 (the capacity `cap`). Writes C and
+// that count to plan[bh], the first extra item of every key block to xoff, and the items
+// (j << 16 | chunk) in key-block order.
+__global__ __launch_bounds__(1024) void key_plan_kernel(const int32_t* __restrict__ tcnt,
+                                                        int32_t* __restrict__ plan,
+                                                        int32_t* __restrict__ xoff,
+                                                        int32_t* __restrict__ items, int nkb,
+                                                        int cap) {
+  __shared__ int wsum[16];
+  const int bh = blockIdx.x, t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int32_t* tc = tcnt + static_cast<size_t>(bh) * nkb;
+  int p = 0;
+  for (int j = t; j < nkb; j += 1024) p += tc[j];
+  for (int o = 32; o >= 1; o >>= 1) p += __shfl_xor(p, o);
+  if (lane == 0) wsum[w] = p;
+  __syncthreads();
+  int P = 0;
+  for (int k = 0; k < 16; ++k) P += wsum[k];
+  const int C = max(kChunk, (2 * P + nkb - 1) / nkb);
+  int base = 0;
+  for (int j0 = 0; j0 < nkb; j0 += 1024) {
+    __syncthreads();   // wsum reuse
+    const int j = j0 + t;
+    const int e = j < nkb ? max(0, (tc[j] + C - 1) / C - 1) : 0;
+    int inc = e;   // inclusive scan within the wavefront
+    for (int o = 1; o < 64; o <<= 1) {
+      const int v = __shfl_up(inc, o);
+      if (lane >= o) inc += v;
+    }
+    if (lane == 63) wsum[w] = inc;
+    __syncthreads();
+    int before = base;
+    for (int k = 0; k < w; ++k) before += wsum[k];
+    const int off = before + inc - e;
+    if (j < nkb) {
+      xoff[static_cast<size_t>(bh) * nkb + j] = off;
+      for (int c = 1; c <= e; ++c)
+        if (off + c - 1 < cap) items[static_cast<size_t>(bh) * cap + off + c - 1] = (j << 16) | c;
+    }
+    for (int k = 0; k < 16; ++k) base += wsum[k];
+  }
+  if (t == 0) {
+    plan[2 * bh] = C;
+    plan[2 * bh + 1] = min(base, cap);
+  }
 }
 
 // ---------------------------------------------------------------- bwd_lin_q
@@ -171,6 +197,37 @@ __global__ __launch_bounds__(256) void bwd_lin_q_kernel(BwdArgs x) {
   const size_t qb = static_cast<size_t>(bh) * x.nqb + i;
   const size_t row0 = static_cast<size_t>(bh) * N + static_cast<size_t>(i) * kBQ;
   const int ncnt = x.cnt[qb];
+  const float al = x.alpha[static_cast<size_t>(bh % x.H) * x.nqb + i];
+  // ---- bf16 operand copies of this block's 128 rows: Q and V (fp32 inputs only),
+  // K_s = K - colmean(K) (key blocks 2 i, 2 i + 1), dO_s = alpha dO
+  {
+    const int c8 = 8 * (t & 15);
+    float mu[8];
+    const float* mp = x.mu32 + static_cast<size_t>(bh) * kD + c8;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) mu[k] = mp[k];
+#pragma unroll 2
+    for (int u = 0; u < 8; ++u) {
+      const size_t e = (row0 + (t >> 4) + 16 * u) * kD + c8;
+      float v[8];
+      if (x.qbf_w != nullptr) {
+        load8<T>(static_cast<const T*>(x.Q) + e, v);
+        st_bf16x8(x.qbf_w + e, v);
+      }
+      if (x.vbf_w != nullptr) {
+        load8<T>(static_cast<const T*>(x.V) + e, v);
+        st_bf16x8(x.vbf_w + e, v);
+      }
+      load8<T>(static_cast<const T*>(x.K) + e, v);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) v[k] -= mu[k];
+      st_bf16x8(x.ksb + e, v);
+      load8<float>(x.dO + e, v);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) v[k] *= al;
+      st_bf16x8(x.dos + e, v);
+    }
+  }
   if (ncnt == nkb) {   // nothing dropped: O_l = 0, no linear gradient
     for (int e = t; e < kBQ * kD / 4; e += 256)
       *reinterpret_cast<f32x4*>(x.dQ + row0 * kD + 4 * e) = f32x4{};
@@ -267,7 +324,6 @@ __global__ __launch_bounds__(256) void bwd_lin_q_kernel(BwdArgs x) {
     for (int k = 0; k < 8; ++k) den += f[k] * Zs[64 * g + 8 * u + k];
   }
   den += __shfl_xor(den, 32);
-  const float al = x.alpha[static_cast<size_t>(bh % x.H) * x.nqb + i];
   const float oml = 1.0f - al, inv_den = 1.0f / den;
   // O_l = num / den; sum(dO O_l) per row; dnum = (1 - alpha) dO / den (in num's registers)
   float sl = 0.f;
@@ -369,39 +425,12 @@ __global__ __launch_bounds__(256) void bwd_lin_q_kernel(BwdArgs x) {
   if (t == 0) x.dalpha[qb] = -((red[0] + red[1]) + (red[2] + red[3]));
 }
 
-// ---------------------------------------------------------------- dh_total
-// grid (9, BH), 256 threads: workgroups 0-7 sum 2048 elements of dH_i^T each over all query
-// blocks (thread: 8 consecutive elements), workgroup 8 sums dZ_i. Fixed order.
-__global__ __launch_bounds__(256) void dh_total_kernel(const uint16_t* __restrict__ dht,
-                                                       const float* __restrict__ dz,
-                                                       float* __restrict__ dhtot,
-                                                       float* __restrict__ dztot, int nqb) {
-  const int bh = blockIdx.y, t = threadIdx.x;
-  if (blockIdx.x < 8) {
-    const size_t e = 2048 * blockIdx.x + 8 * t;
-    const uint16_t* src = dht + static_cast<size_t>(bh) * nqb * (kD * kD) + e;
-    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int i = 0; i < nqb; ++i) {
-      float f[8];
-      unpack_bf16x8(*reinterpret_cast<const i32x4*>(src + static_cast<size_t>(i) * (kD * kD)), f);
-#pragma unroll
-      for (int k = 0; k < 8; ++k) acc[k] += f[k];
-    }
-    float* dst = dhtot + static_cast<size_t>(bh) * (kD * kD) + e;
-    *reinterpret_cast<f32x4*>(dst) = f32x4{acc[0], acc[1], acc[2], acc[3]};
-    *reinterpret_cast<f32x4*>(dst + 4) = f32x4{acc[4], acc[5], acc[6], acc[7]};
-  } else if (t < kD) {
-    float s = 0.f;
-    for (int i = 0; i < nqb; ++i) s += dz[(static_cast<size_t>(bh) * nqb + i) * kD + t];
-    dztot[static_cast<size_t>(bh) * kD + t] = s;
-  }
-}
-
 // ---------------------------------------------------------------- bwd_q
 // grid (nqb, BH) (XCD-aware order), 256 threads; wavefront w owns query rows 32 w .. +31 and
 // holds S^T = K_s,j Q^T with the query as lane (column) and the 64 keys in registers, so row
-// statistics are per lane. Logits are kept in base-2 units: s2 = S log2(e) / sqrt(d).
-template <typename T>
+// statistics are per lane. Logits are kept in base-2 units: s2 = S log2(e) / sqrt(d). The
+// bf16 K_s and V of the next kept block are loaded into registers while the current one is
+// processed.
 __global__ __launch_bounds__(256) void bwd_q_kernel(BwdArgs x) {
   __shared__ __attribute__((aligned(16))) uint16_t Qs[kTile];
   __shared__ __attribute__((aligned(16))) uint16_t Ds[kTile];   // dO_s = alpha dO
@@ -424,27 +453,46 @@ __global__ __launch_bounds__(256) void bwd_q_kernel(BwdArgs x) {
     return;
   }
   const float al = x.alpha[static_cast<size_t>(bh % x.H) * x.nqb + i];
-  stage128_q<T>(Qs, Ds, static_cast<const T*>(x.Q) + row0 * kD, x.dO + row0 * kD, al, t);
-  float mu[8];
-  {
-    const float* mp = x.mu32 + static_cast<size_t>(bh) * kD + 8 * (t & 15);
+  const int c8 = 8 * (t & 15);
 #pragma unroll
-    for (int k = 0; k < 8; ++k) mu[k] = mp[k];
+  for (int u = 0; u < 8; ++u) {
+    const int r = (t >> 4) + 16 * u;
+    const size_t e = (row0 + r) * kD + c8;
+    *reinterpret_cast<i32x4*>(&Qs[r * kLd + c8]) = *reinterpret_cast<const i32x4*>(x.qbf + e);
+    *reinterpret_cast<i32x4*>(&Ds[r * kLd + c8]) = *reinterpret_cast<const i32x4*>(x.dos + e);
   }
   const int32_t* lst = x.list + qb * nkb;
-  const float c2 = kLog2e * 0.08838834764831845f;   // log2(e) / sqrt(128)
+  const float c2 = kLog2e * kInvSqrtD;
   const int q = 32 * w + l32;
+  i32x4 pk[4], pv[4];
+  auto fetch = [&](int j) {
+    const size_t kr = head + static_cast<size_t>(j) * kBK;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const size_t e = (kr + (t >> 4) + 16 * u) * kD + c8;
+      pk[u] = *reinterpret_cast<const i32x4*>(x.ksb + e);
+      pv[u] = *reinterpret_cast<const i32x4*>(x.vbf + e);
+    }
+  };
+  auto put = [&]() {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int r = (t >> 4) + 16 * u;
+      *reinterpret_cast<i32x4*>(&Ks[r * kLd + c8]) = pk[u];
+      *reinterpret_cast<i32x4*>(&Vs[r * kLd + c8]) = pv[u];
+    }
+  };
   // ---- pass 1: running max m and sum l (per lane: its 32 keys of each block), O_s^T
   float m = -INFINITY, l = 0.f;
   f32x16 oT[4];
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt) oT[dt] = f32x16{};
+  fetch(lst[0]);
   for (int n = 0; n < ncnt; ++n) {
-    const size_t kr = head + static_cast<size_t>(lst[n]) * kBK;
     __syncthreads();
-    stage64<T>(Ks, static_cast<const T*>(x.K) + kr * kD, mu, t);
-    stage64<T>(Vs, static_cast<const T*>(x.V) + kr * kD, nullptr, t);
+    put();
     __syncthreads();
+    if (n + 1 < ncnt) fetch(lst[n + 1]);
     f32x16 sT[2];
 #pragma unroll
     for (int tk = 0; tk < 2; ++tk) {
@@ -483,6 +531,7 @@ __global__ __launch_bounds__(256) void bwd_q_kernel(BwdArgs x) {
           oT[dt] = mfma(ld_col8_acc(Vs, 32 * dt + l32, 32 * tk + 16 * h, g), acc_op(sT[tk], h), oT[dt]);
     }
   }
+  fetch(lst[0]);   // pass 2 starts over; in flight during the row statistics below
   const float lt = l + __shfl_xor(l, 32);
   const float lse = m + log2f(lt);
   const float invl = 1.0f / lt;
@@ -513,11 +562,10 @@ __global__ __launch_bounds__(256) void bwd_q_kernel(BwdArgs x) {
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt) dq[dt] = f32x16{};
   for (int n = 0; n < ncnt; ++n) {
-    const size_t kr = head + static_cast<size_t>(lst[n]) * kBK;
     __syncthreads();
-    stage64<T>(Ks, static_cast<const T*>(x.K) + kr * kD, mu, t);
-    stage64<T>(Vs, static_cast<const T*>(x.V) + kr * kD, nullptr, t);
+    put();
     __syncthreads();
+    if (n + 1 < ncnt) fetch(lst[n + 1]);
     f32x16 sT[2], dp[2];
 #pragma unroll
     for (int tk = 0; tk < 2; ++tk) {
@@ -545,7 +593,6 @@ __global__ __launch_bounds__(256) void bwd_q_kernel(BwdArgs x) {
           dq[dt] = mfma(ld_col8_acc(Ks, 32 * dt + l32, 32 * tk + 16 * h, g), acc_op(dp[tk], h), dq[dt]);
   }
   {
-    const float sc = 0.08838834764831845f;   // 1 / sqrt(128)
     float* dqp = x.dQ + (row0 + q) * kD;
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)
@@ -554,7 +601,7 @@ __global__ __launch_bounds__(256) void bwd_q_kernel(BwdArgs x) {
         f32x4* p = reinterpret_cast<f32x4*>(dqp + 32 * dt + 8 * k4 + 4 * g);
         f32x4 v = *p;
 #pragma unroll
-        for (int k = 0; k < 4; ++k) v[k] += dq[dt][4 * k4 + k] * sc;
+        for (int k = 0; k < 4; ++k) v[k] += dq[dt][4 * k4 + k] * kInvSqrtD;
         *p = v;
       }
   }
@@ -563,103 +610,103 @@ __global__ __launch_bounds__(256) void bwd_q_kernel(BwdArgs x) {
 }
 
 // ---------------------------------------------------------------- bwd_kv
-// grid (nkb, BH) (XCD-aware order), 256 threads; wavefront w = (kt = w % 2, qh = w / 2)
-// forms S = Q K_s^T for keys 32 kt .. +31 and query rows 64 qh .. +63 of each query block
-// that keeps this key block (query as register index, key as lane), so P and dS serve
-// directly as the A operand of dV = P^T dO_s and dK = dS^T Q. The two query halves are summed
-// through LDS at the end, then the linear part is added.
-constexpr int kKvLds = 2 * kTile * 2 + 2 * kBK * kLd * 2 + kTile * 2 + 4 * kBQ * 4;
-template <typename T>
-__global__ __launch_bounds__(256) void bwd_kv_kernel(BwdArgs x) {
-  __shared__ __attribute__((aligned(16))) char smem[kKvLds];
-  uint16_t* Qs = reinterpret_cast<uint16_t*>(smem);            // [128][kLd]
-  uint16_t* Ds = Qs + kTile;                                   // dO_s [128][kLd]
-  uint16_t* Ks = Ds + kTile;                                   // K_s,j [64][kLd]; later phi
-  uint16_t* Vs = Ks + kBK * kLd;                               // V_j [64][kLd]
-  uint16_t* DH = Vs + kBK * kLd;                               // dh_j^T [o][a]
-  float* lse_s = reinterpret_cast<float*>(DH + kTile);         // [128]
-  float* D_s = lse_s + kBQ;                                    // [128]
-  float* dz_s = D_s + kBQ;                                     // [128]
-  float* crow = dz_s + kBQ;                                    // [2][64]
-  float* X = reinterpret_cast<float*>(smem);                   // after the loop: Qs/Ds area
-  constexpr int kXld = kD + 4;                                 // fp32 row stride
-  float* DKs = X;                                              // [64][kXld]
-  float* DVs = X + kBK * kXld;                                 // [64][kXld]
-  int j, bh;
-  xcd_block(x.nkb, x.BH, &j, &bh);
-  const int t = threadIdx.x, lane = t & 63, w = t >> 6, g = lane >> 5, l32 = lane & 31;
-  const int kt = w & 1, qh = w >> 1;
-  const int nqb = x.nqb, N = nqb * kBQ;
-  const size_t head = static_cast<size_t>(bh) * N;
-  const size_t krow0 = head + static_cast<size_t>(j) * kBK;
-  float mu[8];
-  {
-    const float* mp = x.mu32 + static_cast<size_t>(bh) * kD + 8 * (t & 15);
-#pragma unroll
-    for (int k = 0; k < 8; ++k) mu[k] = mp[k];
-  }
-  stage64<T>(Ks, static_cast<const T*>(x.K) + krow0 * kD, mu, t);
-  stage64<T>(Vs, static_cast<const T*>(x.V) + krow0 * kD, nullptr, t);
-  const int nT = x.tcnt[static_cast<size_t>(bh) * x.nkb + j];
-  const uint16_t* tl = x.tlist + (static_cast<size_t>(bh) * x.nkb + j) * nqb;
-  const float c2 = kLog2e * 0.08838834764831845f;
+// One work item = one key block j and a range of its keeping query blocks. Wavefront
+// w = (kt = w % 2, qh = w / 2) forms S = Q K_s^T for keys 32 kt .. +31 and query rows
+// 64 qh .. +63 of each query block in the range (query as register index, key as lane), so P
+// and dS serve directly as the A operand of dV = P^T dO_s and dK = dS^T Q. The bf16 Q and dO_s
+// of the next query block are loaded into registers while the current one is processed.
+// At the end the two query halves are summed through LDS (fp32 [128][kXld], over the Q/dO_s
+// tiles): rows 0-63 dK_s (scaled by 1 / sqrt(d)), rows 64-127 dV.
+constexpr int kXld = kD + 4;   // fp32 row stride of the exchange tiles
+struct KvLds {
+  uint16_t* Qs;
+  uint16_t* Ds;
+  uint16_t* Ks;
+  uint16_t* Vs;
+  float* lse_s;
+  float* D_s;
+  float* X;
+};
+
+__device__ inline void kv_sparse(const BwdArgs& x, size_t head, const uint16_t* tl, int n0,
+                                 int n1, const KvLds& L, int t, int g, int l32, int kt, int qh) {
+  const int c8 = 8 * (t & 15);
+  const float c2 = kLog2e * kInvSqrtD;
   f32x16 dk[4], dv[4];   // lane = d column, registers = keys 32 kt + ...
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt) {
     dk[dt] = f32x16{};
     dv[dt] = f32x16{};
   }
-  for (int n = 0; n < nT; ++n) {
-    const int i = tl[n];
+  i32x4 pq[8], pd[8];
+  float pl = 0.f, pD = 0.f;
+  auto fetch = [&](int i) {
     const size_t row0 = head + static_cast<size_t>(i) * kBQ;
-    __syncthreads();
-    stage128_q<T>(Qs, Ds, static_cast<const T*>(x.Q) + row0 * kD, x.dO + row0 * kD,
-                  x.alpha[static_cast<size_t>(bh % x.H) * nqb + i], t);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const size_t e = (row0 + (t >> 4) + 16 * u) * kD + c8;
+      pq[u] = *reinterpret_cast<const i32x4*>(x.qbf + e);
+      pd[u] = *reinterpret_cast<const i32x4*>(x.dos + e);
+    }
     if (t < kBQ) {
-      lse_s[t] = x.lse2[row0 + t];
-      D_s[t] = x.Dd[row0 + t];
+      pl = x.lse2[row0 + t];
+      pD = x.Dd[row0 + t];
+    }
+  };
+  if (n0 < n1) fetch(tl[n0]);
+  for (int n = n0; n < n1; ++n) {
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int r = (t >> 4) + 16 * u;
+      *reinterpret_cast<i32x4*>(&L.Qs[r * kLd + c8]) = pq[u];
+      *reinterpret_cast<i32x4*>(&L.Ds[r * kLd + c8]) = pd[u];
+    }
+    if (t < kBQ) {
+      L.lse_s[t] = pl;
+      L.D_s[t] = pD;
     }
     __syncthreads();
+    if (n + 1 < n1) fetch(tl[n + 1]);
 #pragma unroll
     for (int qq = 0; qq < 2; ++qq) {
       const int qt = 2 * qh + qq;
       f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
-        s = mfma(ld_row8(&Qs[(32 * qt + l32) * kLd + 16 * u + 8 * g]),
-                 ld_row8(&Ks[(32 * kt + l32) * kLd + 16 * u + 8 * g]), s);
-        dp = mfma(ld_row8(&Ds[(32 * qt + l32) * kLd + 16 * u + 8 * g]),
-                  ld_row8(&Vs[(32 * kt + l32) * kLd + 16 * u + 8 * g]), dp);
+        s = mfma(ld_row8(&L.Qs[(32 * qt + l32) * kLd + 16 * u + 8 * g]),
+                 ld_row8(&L.Ks[(32 * kt + l32) * kLd + 16 * u + 8 * g]), s);
+        dp = mfma(ld_row8(&L.Ds[(32 * qt + l32) * kLd + 16 * u + 8 * g]),
+                  ld_row8(&L.Vs[(32 * kt + l32) * kLd + 16 * u + 8 * g]), dp);
       }
 #pragma unroll
       for (int k4 = 0; k4 < 4; ++k4) {
         const int qr = 32 * qt + 8 * k4 + 4 * g;
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-          const float p = exp2f(s[4 * k4 + k] * c2 - lse_s[qr + k]);
+          const float p = exp2f(s[4 * k4 + k] * c2 - L.lse_s[qr + k]);
           s[4 * k4 + k] = p;
-          dp[4 * k4 + k] = p * (dp[4 * k4 + k] - D_s[qr + k]);
+          dp[4 * k4 + k] = p * (dp[4 * k4 + k] - L.D_s[qr + k]);
         }
       }
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-          dv[dt] = mfma(acc_op(s, h), ld_col8_acc(Ds, 32 * dt + l32, 32 * qt + 16 * h, g), dv[dt]);
-          dk[dt] = mfma(acc_op(dp, h), ld_col8_acc(Qs, 32 * dt + l32, 32 * qt + 16 * h, g), dk[dt]);
+          dv[dt] = mfma(acc_op(s, h), ld_col8_acc(L.Ds, 32 * dt + l32, 32 * qt + 16 * h, g), dv[dt]);
+          dk[dt] = mfma(acc_op(dp, h), ld_col8_acc(L.Qs, 32 * dt + l32, 32 * qt + 16 * h, g), dk[dt]);
         }
     }
   }
-  __syncthreads();   // Qs / Ds free: exchange the two query halves through X
-  const float sc = 0.08838834764831845f;
+  __syncthreads();   // Q / dO_s tiles free: exchange the two query halves through X
   if (qh == 1) {
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int key = 32 * kt + 8 * (r >> 2) + 4 * g + (r & 3);
-        X[key * kXld + 32 * dt + l32] = dk[dt][r];
-        X[(kBK + key) * kXld + 32 * dt + l32] = dv[dt][r];
+        L.X[key * kXld + 32 * dt + l32] = dk[dt][r];
+        L.X[(kBK + key) * kXld + 32 * dt + l32] = dv[dt][r];
       }
   }
   __syncthreads();
@@ -669,34 +716,159 @@ __global__ __launch_bounds__(256) void bwd_kv_kernel(BwdArgs x) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int key = 32 * kt + 8 * (r >> 2) + 4 * g + (r & 3);
-        dk[dt][r] = (dk[dt][r] + X[key * kXld + 32 * dt + l32]) * sc;
-        dv[dt][r] += X[(kBK + key) * kXld + 32 * dt + l32];
+        dk[dt][r] = (dk[dt][r] + L.X[key * kXld + 32 * dt + l32]) * kInvSqrtD;
+        dv[dt][r] += L.X[(kBK + key) * kXld + 32 * dt + l32];
       }
   }
   __syncthreads();
-  if (qh == 0) {   // same positions: DKs = X rows 0-63, DVs = X rows 64-127
+  if (qh == 0) {
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int key = 32 * kt + 8 * (r >> 2) + 4 * g + (r & 3);
-        DKs[key * kXld + 32 * dt + l32] = dk[dt][r];
-        DVs[key * kXld + 32 * dt + l32] = dv[dt][r];
+        L.X[key * kXld + 32 * dt + l32] = dk[dt][r];
+        L.X[(kBK + key) * kXld + 32 * dt + l32] = dv[dt][r];
       }
+  }
+  __syncthreads();
+}
+
+constexpr int kKvLds = 2 * kTile * 2 + 2 * kBK * kLd * 2 + kTile * 2 + 4 * kBQ * 4;
+
+__device__ inline KvLds kv_lds(char* smem) {
+  KvLds L;
+  L.Qs = reinterpret_cast<uint16_t*>(smem);   // [128][kLd]
+  L.Ds = L.Qs + kTile;                        // dO_s [128][kLd]
+  L.Ks = L.Ds + kTile;                        // K_s,j [64][kLd]; later phi(K_s,j)
+  L.Vs = L.Ks + kBK * kLd;                    // V_j [64][kLd]
+  L.lse_s = reinterpret_cast<float*>(L.Vs + kBK * kLd + kTile);   // after DH
+  L.D_s = L.lse_s + kBQ;
+  L.X = reinterpret_cast<float*>(smem);       // over Qs / Ds after the loop
+  return L;
+}
+
+__device__ inline void stage_kv_block(const BwdArgs& x, size_t krow0, const KvLds& L, int t) {
+  const int c8 = 8 * (t & 15);
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int r = (t >> 4) + 16 * u;
+    const size_t e = (krow0 + r) * kD + c8;
+    *reinterpret_cast<i32x4*>(&L.Ks[r * kLd + c8]) = *reinterpret_cast<const i32x4*>(x.ksb + e);
+    *reinterpret_cast<i32x4*>(&L.Vs[r * kLd + c8]) = *reinterpret_cast<const i32x4*>(x.vbf + e);
+  }
+}
+
+// Extra work items: grid (cap, BH); item e < plan[bh].count covers the query blocks
+// [c C, min((c + 1) C, T_j)) of key block j; writes its partial dK_s, dV and the sums of dH_i^T
+// and dZ_i over its query blocks into slot e.
+__global__ __launch_bounds__(256) void bwd_kv_extra_kernel(BwdArgs x) {
+  __shared__ __attribute__((aligned(16))) char smem[kKvLds];
+  const int e = blockIdx.x, bh = blockIdx.y;
+  if (e >= x.plan[2 * bh + 1]) return;
+  const KvLds L = kv_lds(smem);
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6, g = lane >> 5, l32 = lane & 31;
+  const int kt = w & 1, qh = w >> 1;
+  const int item = x.items[static_cast<size_t>(bh) * x.cap + e];
+  const int j = item >> 16, c = item & 0xFFFF, C = x.plan[2 * bh];
+  const int nqb = x.nqb, N = nqb * kBQ;
+  const size_t head = static_cast<size_t>(bh) * N;
+  const int nT = x.tcnt[static_cast<size_t>(bh) * x.nkb + j];
+  const uint16_t* tl = x.tlist + (static_cast<size_t>(bh) * x.nkb + j) * nqb;
+  const int n0 = c * C, n1 = min(nT, n0 + C);
+  stage_kv_block(x, head + static_cast<size_t>(j) * kBK, L, t);
+  kv_sparse(x, head, tl, n0, n1, L, t, g, l32, kt, qh);
+  float* slot = x.xpart + (static_cast<size_t>(bh) * x.cap + e) * kSlot;
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const int f = t + 256 * u, r = f >> 5, c4 = 4 * (f & 31);
+    *reinterpret_cast<f32x4*>(slot + r * kD + c4) = *reinterpret_cast<const f32x4*>(&L.X[r * kXld + c4]);
+    *reinterpret_cast<f32x4*>(slot + kBK * kD + r * kD + c4) =
+        *reinterpret_cast<const f32x4*>(&L.X[(kBK + r) * kXld + c4]);
+  }
+  // sums of dH_i^T (chunk f = t + 256 u: 8 elements at 8 f) and dZ_i over the range
+  const uint16_t* src = x.dht + static_cast<size_t>(bh) * nqb * (kD * kD);
+  float acc[8][8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u)
+#pragma unroll
+    for (int k = 0; k < 8; ++k) acc[u][k] = 0.f;
+  for (int n = n0; n < n1; ++n) {
+    const uint16_t* hi = src + static_cast<size_t>(tl[n]) * (kD * kD);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      float f8[8];
+      unpack_bf16x8(*reinterpret_cast<const i32x4*>(hi + 8 * (t + 256 * u)), f8);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) acc[u][k] += f8[k];
+    }
+  }
+  float* sh = slot + 2 * kBK * kD;
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const int f = t + 256 * u;
+    *reinterpret_cast<f32x4*>(sh + 8 * f) = f32x4{acc[u][0], acc[u][1], acc[u][2], acc[u][3]};
+    *reinterpret_cast<f32x4*>(sh + 8 * f + 4) = f32x4{acc[u][4], acc[u][5], acc[u][6], acc[u][7]};
+  }
+  if (t < kD) {
+    float s = 0.f;
+    for (int n = n0; n < n1; ++n) s += x.dz[(static_cast<size_t>(bh) * nqb + tl[n]) * kD + t];
+    sh[kD * kD + t] = s;
+  }
+}
+
+// Main work items: grid (nkb, BH) (XCD-aware order). Key block j: its first C keeping query
+// blocks, then the extra items' partials in item order, then the linear part; writes dK_s, dV
+// and the column sums of dK_s.
+__global__ __launch_bounds__(256) void bwd_kv_kernel(BwdArgs x) {
+  __shared__ __attribute__((aligned(16))) char smem[kKvLds];
+  const KvLds L = kv_lds(smem);
+  uint16_t* DH = L.Vs + kBK * kLd;   // dh_j^T [o][a]
+  float* dz_s = L.D_s + kBQ;         // [128]
+  float* crow = dz_s + kBQ;          // [2][64]
+  float* DKs = L.X;                  // [64][kXld]
+  float* DVs = L.X + kBK * kXld;     // [64][kXld]
+  int j, bh;
+  xcd_block(x.nkb, x.BH, &j, &bh);
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6, g = lane >> 5, l32 = lane & 31;
+  const int kt = w & 1, qh = w >> 1;
+  const int nqb = x.nqb, N = nqb * kBQ;
+  const size_t head = static_cast<size_t>(bh) * N;
+  const size_t krow0 = head + static_cast<size_t>(j) * kBK;
+  const int nT = x.tcnt[static_cast<size_t>(bh) * x.nkb + j];
+  const uint16_t* tl = x.tlist + (static_cast<size_t>(bh) * x.nkb + j) * nqb;
+  const int C = x.plan[2 * bh];
+  const int n1 = min(nT, C);
+  const int nx = nT > C ? (nT + C - 1) / C - 1 : 0;
+  const float* xs = x.xpart + (static_cast<size_t>(bh) * x.cap + x.xoff[static_cast<size_t>(bh) * x.nkb + j]) * kSlot;
+  stage_kv_block(x, krow0, L, t);
+  kv_sparse(x, head, tl, 0, n1, L, t, g, l32, kt, qh);
+  // partials of the extra items (fixed order)
+  for (int e = 0; e < nx; ++e) {
+    const float* sl = xs + static_cast<size_t>(e) * kSlot;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int f = t + 256 * u, r = f >> 5, c4 = 4 * (f & 31);
+      f32x4* pk = reinterpret_cast<f32x4*>(&DKs[r * kXld + c4]);
+      f32x4* pv = reinterpret_cast<f32x4*>(&DVs[r * kXld + c4]);
+      *pk = *pk + *reinterpret_cast<const f32x4*>(sl + r * kD + c4);
+      *pv = *pv + *reinterpret_cast<const f32x4*>(sl + kBK * kD + r * kD + c4);
+    }
   }
   // ---- linear part. phi(K_s,j) into Ks (thread: row t / 4, columns 32 (t % 4) .. +31)
   {
     const int r = t >> 2, c0 = 32 * (t & 3);
-    const float* mp = x.mu32 + static_cast<size_t>(bh) * kD + c0;
     float v[32];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) load8<T>(static_cast<const T*>(x.K) + (krow0 + r) * kD + c0 + 8 * u, v + 8 * u);
-    float mx = -INFINITY;
+    for (int u = 0; u < 4; ++u) {
+      float f8[8];
+      unpack_bf16x8(*reinterpret_cast<const i32x4*>(x.ksb + (krow0 + r) * kD + c0 + 8 * u), f8);
 #pragma unroll
-    for (int k = 0; k < 32; ++k) {
-      v[k] -= mp[k];
-      mx = fmaxf(mx, v[k]);
+      for (int k = 0; k < 8; ++k) v[8 * u + k] = f8[k];
     }
+    float mx = v[0];
+#pragma unroll
+    for (int k = 1; k < 32; ++k) mx = fmaxf(mx, v[k]);
     mx = fmaxf(mx, __shfl_xor(mx, 1));
     mx = fmaxf(mx, __shfl_xor(mx, 2));
     float s = 0.f;
@@ -710,8 +882,9 @@ __global__ __launch_bounds__(256) void bwd_kv_kernel(BwdArgs x) {
     const float inv = 1.0f / s;
 #pragma unroll
     for (int k = 0; k < 32; ++k) v[k] *= inv;
+    __syncthreads();   // Ks no longer read by the sparse part
 #pragma unroll
-    for (int u = 0; u < 4; ++u) st_bf16x8(&Ks[r * kLd + c0 + 8 * u], v + 8 * u);
+    for (int u = 0; u < 4; ++u) st_bf16x8(&L.Ks[r * kLd + c0 + 8 * u], v + 8 * u);
   }
   // dh_j^T = dH_tot^T - sum over the keeping query blocks of dH_i^T (bf16 [o][a]); dz_j
   {
@@ -721,22 +894,36 @@ __global__ __launch_bounds__(256) void bwd_kv_kernel(BwdArgs x) {
     for (int u = 0; u < 8; ++u)
 #pragma unroll
       for (int k = 0; k < 8; ++k) acc[u][k] = 0.f;
-    for (int n = 0; n < nT; ++n) {
+    for (int n = 0; n < n1; ++n) {
       const uint16_t* hi = src + static_cast<size_t>(tl[n]) * (kD * kD);
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
-        float f[8];
-        unpack_bf16x8(*reinterpret_cast<const i32x4*>(hi + 8 * (t + 256 * u)), f);
+        float f8[8];
+        unpack_bf16x8(*reinterpret_cast<const i32x4*>(hi + 8 * (t + 256 * u)), f8);
 #pragma unroll
-        for (int k = 0; k < 8; ++k) acc[u][k] += f[k];
+        for (int k = 0; k < 8; ++k) acc[u][k] += f8[k];
+      }
+    }
+    for (int e = 0; e < nx; ++e) {
+      const float* sh = xs + static_cast<size_t>(e) * kSlot + 2 * kBK * kD;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int f = t + 256 * u;
+        const f32x4 a0 = *reinterpret_cast<const f32x4*>(sh + 8 * f);
+        const f32x4 a1 = *reinterpret_cast<const f32x4*>(sh + 8 * f + 4);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          acc[u][k] += a0[k];
+          acc[u][4 + k] += a1[k];
+        }
       }
     }
     const float* tot = x.dhtot + static_cast<size_t>(bh) * (kD * kD);
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-      const int c = t + 256 * u, o = c >> 4, a0 = 8 * (c & 15);
-      const f32x4 t0 = *reinterpret_cast<const f32x4*>(tot + 8 * c);
-      const f32x4 t1 = *reinterpret_cast<const f32x4*>(tot + 8 * c + 4);
+      const int f = t + 256 * u, o = f >> 4, a0 = 8 * (f & 15);
+      const f32x4 t0 = *reinterpret_cast<const f32x4*>(tot + 8 * f);
+      const f32x4 t1 = *reinterpret_cast<const f32x4*>(tot + 8 * f + 4);
       float hv[8] = {t0[0], t0[1], t0[2], t0[3], t1[0], t1[1], t1[2], t1[3]};
 #pragma unroll
       for (int k = 0; k < 8; ++k) hv[k] -= acc[u][k];
@@ -744,7 +931,8 @@ __global__ __launch_bounds__(256) void bwd_kv_kernel(BwdArgs x) {
     }
     if (t < kD) {
       float s = 0.f;
-      for (int n = 0; n < nT; ++n) s += x.dz[(static_cast<size_t>(bh) * nqb + tl[n]) * kD + t];
+      for (int n = 0; n < n1; ++n) s += x.dz[(static_cast<size_t>(bh) * nqb + tl[n]) * kD + t];
+      for (int e = 0; e < nx; ++e) s += xs[static_cast<size_t>(e) * kSlot + 2 * kBK * kD + kD * kD + t];
       dz_s[t] = x.dztot[static_cast<size_t>(bh) * kD + t] - s;
     }
   }
@@ -755,7 +943,7 @@ __global__ __launch_bounds__(256) void bwd_kv_kernel(BwdArgs x) {
     f32x16 c = f32x16{};
 #pragma unroll
     for (int u = 0; u < 8; ++u)
-      c = mfma(ld_row8(&Ks[(32 * kt + l32) * kLd + 16 * u + 8 * g]),
+      c = mfma(ld_row8(&L.Ks[(32 * kt + l32) * kLd + 16 * u + 8 * g]),
                ld_row8(&DH[(32 * ot + l32) * kLd + 16 * u + 8 * g]), c);
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
@@ -774,12 +962,12 @@ __global__ __launch_bounds__(256) void bwd_kv_kernel(BwdArgs x) {
 #pragma unroll
     for (int u = 0; u < 8; ++u)
       dph[h] = mfma(ld_col8(DH, 32 * at + l32, 16 * u + 8 * g),
-                    ld_row8(&Vs[key * kLd + 16 * u + 8 * g]), dph[h]);
+                    ld_row8(&L.Vs[key * kLd + 16 * u + 8 * g]), dph[h]);
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int a = 32 * at + 8 * (r >> 2) + 4 * g + (r & 3);
       dph[h][r] += dz_s[a];
-      cs += dph[h][r] * bf(Ks[key * kLd + a]);
+      cs += dph[h][r] * bf(L.Ks[key * kLd + a]);
     }
   }
   cs += __shfl_xor(cs, 32);
@@ -792,14 +980,14 @@ __global__ __launch_bounds__(256) void bwd_kv_kernel(BwdArgs x) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int a = 32 * at + 8 * (r >> 2) + 4 * g + (r & 3);
-      DKs[key * kXld + a] += bf(Ks[key * kLd + a]) * (dph[h][r] - cs);
+      DKs[key * kXld + a] += bf(L.Ks[key * kLd + a]) * (dph[h][r] - cs);
     }
   }
   __syncthreads();
   // ---- write dK_s, dV; column sums of dK_s for the centring
 #pragma unroll
   for (int u = 0; u < 8; ++u) {
-    const int e = t + 256 * u, r = e >> 5, c4 = 4 * (e & 31);
+    const int f = t + 256 * u, r = f >> 5, c4 = 4 * (f & 31);
     *reinterpret_cast<f32x4*>(x.dK + (krow0 + r) * kD + c4) =
         *reinterpret_cast<const f32x4*>(&DKs[r * kXld + c4]);
     *reinterpret_cast<f32x4*>(x.dV + (krow0 + r) * kD + c4) =
@@ -812,19 +1000,63 @@ __global__ __launch_bounds__(256) void bwd_kv_kernel(BwdArgs x) {
   }
 }
 
-// ---------------------------------------------------------------- dK centring
-// dk_mean: grid (BH), 128 threads: mean over key blocks of the column sums, / N.
-__global__ __launch_bounds__(128) void dk_mean_kernel(const float* __restrict__ kcol,
-                                                      float* __restrict__ kmean, int nkb, int N) {
-  const int bh = blockIdx.x, t = threadIdx.x;
-  const float* src = kcol + static_cast<size_t>(bh) * nkb * kD + t;
-  float a[4] = {0.f, 0.f, 0.f, 0.f};
-  int j = 0;
-  for (; j + 3 < nkb; j += 4)
+// ---------------------------------------------------------------- dh_total
+// grid (65, BH), 256 threads. Workgroup x < 64 sums elements 256 x .. +255 of dH_i^T over all
+// query blocks: thread (chunk t % 32 of 8 elements, query-block group t / 32) sums the blocks
+// i = group, group + 8, ...; the 8 group sums are added in a fixed order. Workgroup 64 sums dZ_i
+// the same way (column t % 128, group t / 128).
+__global__ __launch_bounds__(256) void dh_total_kernel(const uint16_t* __restrict__ dht,
+                                                       const float* __restrict__ dz,
+                                                       float* __restrict__ dhtot,
+                                                       float* __restrict__ dztot, int nqb) {
+  __shared__ float part[8][256 + 4];
+  const int bh = blockIdx.y, t = threadIdx.x;
+  if (blockIdx.x < 64) {
+    const int ch = t & 31, grp = t >> 5;
+    const size_t e = 256 * blockIdx.x + 8 * ch;
+    const uint16_t* src = dht + static_cast<size_t>(bh) * nqb * (kD * kD) + e;
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int i = grp; i < nqb; i += 8) {
+      float f[8];
+      unpack_bf16x8(*reinterpret_cast<const i32x4*>(src + static_cast<size_t>(i) * (kD * kD)), f);
 #pragma unroll
-    for (int k = 0; k < 4; ++k) a[k] += src[static_cast<size_t>(j + k) * kD];
-  for (; j < nkb; ++j) a[0] += src[static_cast<size_t>(j) * kD];
-  kmean[static_cast<size_t>(bh) * kD + t] = ((a[0] + a[1]) + (a[2] + a[3])) / static_cast<float>(N);
+      for (int k = 0; k < 8; ++k) acc[k] += f[k];
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) part[grp][8 * ch + k] = acc[k];
+    __syncthreads();
+    float v = 0.f;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) v += part[q][t];
+    dhtot[static_cast<size_t>(bh) * (kD * kD) + 256 * blockIdx.x + t] = v;
+  } else {
+    const int a = t & 127, grp = t >> 7;
+    float s = 0.f;
+    for (int i = grp; i < nqb; i += 2) s += dz[(static_cast<size_t>(bh) * nqb + i) * kD + a];
+    part[grp][a] = s;
+    __syncthreads();
+    if (t < kD) dztot[static_cast<size_t>(bh) * kD + t] = part[0][t] + part[1][t];
+  }
+}
+
+// ---------------------------------------------------------------- dK centring
+// dk_mean: grid (BH), 1024 threads: column t % 128, key-block group t / 128 (8 groups, summed
+// in a fixed order), divided by N.
+__global__ __launch_bounds__(1024) void dk_mean_kernel(const float* __restrict__ kcol,
+                                                       float* __restrict__ kmean, int nkb, int N) {
+  __shared__ float part[8][kD];
+  const int bh = blockIdx.x, t = threadIdx.x, col = t & 127, grp = t >> 7;
+  const float* src = kcol + static_cast<size_t>(bh) * nkb * kD + col;
+  float s = 0.f;
+  for (int j = grp; j < nkb; j += 8) s += src[static_cast<size_t>(j) * kD];
+  part[grp][col] = s;
+  __syncthreads();
+  if (t < kD) {
+    float v = 0.f;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) v += part[q][t];
+    kmean[static_cast<size_t>(bh) * kD + t] = v / static_cast<float>(N);
+  }
 }
 // dk_center: grid (N * d / 1024, BH), 256 threads: dK -= mean (four elements per thread).
 __global__ __launch_bounds__(256) void dk_center_kernel(float* __restrict__ dK,
@@ -839,8 +1071,15 @@ __global__ __launch_bounds__(256) void dk_center_kernel(float* __restrict__ dK,
 // ---------------------------------------------------------------- launchers
 hipError_t launch_key_lists(const Geom& g, const uint8_t* mask, int32_t* tcnt, uint16_t* tlist,
                             hipStream_t s) {
-  hipLaunchKernelGGL(key_lists_kernel, dim3((g.nkb + 255) / 256, g.BH), dim3(256), 0, s, mask,
+  hipLaunchKernelGGL(key_lists_kernel, dim3((g.nkb + 3) / 4, g.BH), dim3(256), 0, s, mask,
                      tcnt, tlist, g.nqb, g.nkb);
+  return hipGetLastError();
+}
+
+hipError_t launch_key_plan(const Geom& g, const int32_t* tcnt, int32_t* plan, int32_t* xoff,
+                           int32_t* items, int cap, hipStream_t s) {
+  hipLaunchKernelGGL(key_plan_kernel, dim3(g.BH), dim3(1024), 0, s, tcnt, plan, xoff, items,
+                     g.nkb, cap);
   return hipGetLastError();
 }
 
@@ -853,29 +1092,28 @@ hipError_t launch_bwd_lin_q(const Geom& g, int dtype, const BwdArgs& x, hipStrea
 }
 
 hipError_t launch_dh_total(const Geom& g, const BwdArgs& x, hipStream_t s) {
-  hipLaunchKernelGGL(dh_total_kernel, dim3(9, g.BH), dim3(256), 0, s, x.dht, x.dz, x.dhtot,
+  hipLaunchKernelGGL(dh_total_kernel, dim3(65, g.BH), dim3(256), 0, s, x.dht, x.dz, x.dhtot,
                      x.dztot, g.nqb);
   return hipGetLastError();
 }
 
-hipError_t launch_bwd_q(const Geom& g, int dtype, const BwdArgs& x, hipStream_t s) {
-  if (dtype == 0)
-    hipLaunchKernelGGL(bwd_q_kernel<float>, dim3(g.nqb, g.BH), dim3(256), 0, s, x);
-  else
-    hipLaunchKernelGGL(bwd_q_kernel<uint16_t>, dim3(g.nqb, g.BH), dim3(256), 0, s, x);
+hipError_t launch_bwd_q(const Geom& g, const BwdArgs& x, hipStream_t s) {
+  hipLaunchKernelGGL(bwd_q_kernel, dim3(g.nqb, g.BH), dim3(256), 0, s, x);
   return hipGetLastError();
 }
 
-hipError_t launch_bwd_kv(const Geom& g, int dtype, const BwdArgs& x, hipStream_t s) {
-  if (dtype == 0)
-    hipLaunchKernelGGL(bwd_kv_kernel<float>, dim3(g.nkb, g.BH), dim3(256), 0, s, x);
-  else
-    hipLaunchKernelGGL(bwd_kv_kernel<uint16_t>, dim3(g.nkb, g.BH), dim3(256), 0, s, x);
+hipError_t launch_bwd_kv_extra(const Geom& g, const BwdArgs& x, hipStream_t s) {
+  hipLaunchKernelGGL(bwd_kv_extra_kernel, dim3(x.cap, g.BH), dim3(256), 0, s, x);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_kv(const Geom& g, const BwdArgs& x, hipStream_t s) {
+  hipLaunchKernelGGL(bwd_kv_kernel, dim3(g.nkb, g.BH), dim3(256), 0, s, x);
   return hipGetLastError();
 }
 
 hipError_t launch_dk_center(const Geom& g, const BwdArgs& x, hipStream_t s) {
-  hipLaunchKernelGGL(dk_mean_kernel, dim3(g.BH), dim3(kD), 0, s, x.kcol, x.kmean, g.nkb, g.N);
+  hipLaunchKernelGGL(dk_mean_kernel, dim3(g.BH), dim3(1024), 0, s, x.kcol, x.kmean, g.nkb, g.N);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(dk_center_kernel, dim3(g.N * kD / 1024, g.BH), dim3(256), 0, s, x.dK,

@@ -12,6 +12,8 @@ constexpr int kBQ = 128;   // query block rows (b_q)
 constexpr int kBK = 64;    // key block rows (b_k)
 constexpr int kMaxN = 262144;
 constexpr int kKpPerWg = 8;  // key blocks per workgroup in the linear precompute
+constexpr int kChunk = 16;   // fewest query blocks per key-block work item of the backward
+constexpr int kSlot = 2 * kBK * kD + kD * kD + kD;   // floats per extra backward work item
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
@@ -311,6 +313,15 @@ hipError_t launch_attn(const Geom& g, int dtype, const void* Q, const AttnArgs& 
 // base-2 units (S log2(e) / sqrt(d)); D = rowsum(dO_s O_s); key lists [BH][nkb][nqb] uint16.
 struct BwdArgs {
   const void *Q, *K, *V;
+  // bf16 operand copies: Q and V are the inputs themselves when they are bf16, else written by
+  // bwd_lin_q (qbf_w, vbf_w non-null); K_s = K - colmean(K) and dO_s = alpha dO always written
+  const uint16_t *qbf, *vbf;
+  uint16_t *qbf_w, *vbf_w, *ksb, *dos;
+  const int32_t* plan;       // [BH][2]: chunk size C, number of extra items
+  const int32_t* xoff;       // [BH][nkb] first extra item of each key block
+  const int32_t* items;      // [BH][cap] (j << 16 | chunk)
+  float* xpart;              // [BH][cap][kSlot]: dK, dV [64][128], dH^T sum [128][128], dz sum
+  int cap;
   const float* mu32;
   const float* dO;
   const float* alpha;
@@ -337,10 +348,14 @@ struct BwdArgs {
 };
 hipError_t launch_key_lists(const Geom& g, const uint8_t* mask, int32_t* tcnt, uint16_t* tlist,
                             hipStream_t s);
+hipError_t launch_key_plan(const Geom& g, const int32_t* tcnt, int32_t* plan, int32_t* xoff,
+                           int32_t* items, int cap, hipStream_t s);
+// the work items past the first of each long key list (partials into xpart)
+hipError_t launch_bwd_kv_extra(const Geom& g, const BwdArgs& x, hipStream_t s);
 hipError_t launch_bwd_lin_q(const Geom& g, int dtype, const BwdArgs& x, hipStream_t s);
 hipError_t launch_dh_total(const Geom& g, const BwdArgs& x, hipStream_t s);
-hipError_t launch_bwd_q(const Geom& g, int dtype, const BwdArgs& x, hipStream_t s);
-hipError_t launch_bwd_kv(const Geom& g, int dtype, const BwdArgs& x, hipStream_t s);
+hipError_t launch_bwd_q(const Geom& g, const BwdArgs& x, hipStream_t s);
+hipError_t launch_bwd_kv(const Geom& g, const BwdArgs& x, hipStream_t s);
 // column mean of dK_s, then dK -= mean (two kernels)
 hipError_t launch_dk_center(const Geom& g, const BwdArgs& x, hipStream_t s);
 

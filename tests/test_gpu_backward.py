@@ -66,6 +66,21 @@ def test_backward_random_masks_with_empty_and_full_rows():
     check(q, k, v, mask, alpha, dO, "fp32", [(0, 0), (0, 1)])
 
 
+def test_backward_long_key_lists():
+    """Key blocks kept by every query block (64 of them at N = 8192): their lists are cut into
+    work items of 16 query blocks whose partial sums are added back in a fixed order."""
+    B, H, N = 1, 1, 8192
+    q, k, v = W.random_qkv(95, B, H, N, dtype="bf16")
+    mask = W.random_mask(95, B, H, N // 128, N // 64, 0.05)
+    mask[:, :, :, 3] = 1
+    mask[:, :, :, 77] = 1
+    mask[:, :, 5, :] = 1
+    _, _, alpha = W.random_weights(95, H, N // 128, alpha_lo=0.1)
+    dO = W.grad_out(95, q.shape)
+    say("backward long key lists")
+    check(q, k, v, mask, alpha, dO, "bf16", [(0, 0)])
+
+
 @pytest.mark.parametrize("fill", [0, 1])
 def test_backward_uniform_masks(fill):
     """Every block dropped (pure linear attention) or every block kept (full attention)."""
