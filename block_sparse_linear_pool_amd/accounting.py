@@ -31,8 +31,8 @@ KERNELS_SLA1 = ("pool", "colmean", "project", "score_topk", "fill", "kv_prep", "
 # sla2_backward (mask given): the forward's linear precompute, the transposed mask, then the
 # gradient kernels; dk_center is the column mean and the subtraction together
 KERNELS_BACKWARD = ("pool_k", "colmean", "kv_prep", "linear_total", "mask_to_list", "key_lists",
-                    "key_plan", "bwd_lin_q", "dh_total", "bwd_q", "bwd_kv_extra", "bwd_kv",
-                    "dk_center")
+                    "key_plan", "bwd_prep", "bwd_lin_q", "dh_total", "bwd_q", "bwd_kv_extra",
+                    "bwd_kv", "dk_center")
 
 
 @dataclasses.dataclass
@@ -95,6 +95,11 @@ def kernel_bytes(p: Problem, name: str) -> float:
     if name == "pool_k":
         # K read; fp64 block sums written
         return E * p.in_bytes + BH * p.nkb * d * 8
+    if name == "bwd_prep":
+        # K, dO (and Q, V if fp32) read; bf16 K_s, alpha dO (and Q, V if fp32) written
+        copies = 2 if p.in_bytes == 2 else 4
+        return (E * p.in_bytes + E * 4 + (0 if p.in_bytes == 2 else 2 * E * p.in_bytes)
+                + copies * E * 2)
     if name == "bwd_lin_q":
         # Q, dO read (and h_j, z_j once), dQ, bf16 dH_i^T and dZ_i written
         return (E * p.in_bytes + E * 4 + BH * p.nkb * (d * d * 2 + d * 4) + E * 4

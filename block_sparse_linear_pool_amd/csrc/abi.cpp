@@ -535,7 +535,7 @@ sla2_status sla2_backward(const sla2_shape* shape, const void* Q, const void* K,
   const Plan p = make_plan(g);
   const int dt = shape->dtype == SLA2_FP32 ? 0 : 1;
   void* ws = workspace;
-  Rec rec(stage_events, 14);
+  Rec rec(stage_events, 15);
   if (rec.mark(stream) != hipSuccess) return SLA2_ERR_HIP;
   // forward pieces: colmean(K), the bf16 h_j^T, z_j and H_tot, Z_tot; the kept lists
   SLA2_LAUNCH(launch_pool(g, dt, nullptr, K, at<double>(ws, p.qsum), at<double>(ws, p.ksum),
@@ -606,6 +606,7 @@ sla2_status sla2_backward(const sla2_shape* shape, const void* Q, const void* K,
   b.BH = g.BH;
   b.nqb = g.nqb;
   b.nkb = g.nkb;
+  SLA2_LAUNCH(launch_bwd_prep(g, dt, b, stream));
   SLA2_LAUNCH(launch_bwd_lin_q(g, dt, b, stream));
   SLA2_LAUNCH(launch_dh_total(g, b, stream));
   SLA2_LAUNCH(launch_bwd_q(g, b, stream));

@@ -10,6 +10,8 @@
 // Kernels, in launch order (after pool / colmean / kv_prep / linear_total of the forward give
 // colmean(K), bf16 h_j^T, z_j, H_tot, Z_tot, and mask_to_list gives the kept lists):
 //   key_lists    per key block, the ascending query blocks that keep it (transposed mask)
+//   key_plan     long key lists cut into work items of at most C query blocks
+//   bwd_prep     bf16 copies: Q, V (fp32 inputs), K_s = K - colmean(K), dO_s = alpha dO
 //   bwd_lin_q    per query block: a = phi(Q_i), H_i, Z_i; O_l, dnum, dden; writes
 //                dQ = a * (da - rowsum(da a)) (the linear part), dH_i^T (bf16), dZ_i, and
 //                dalpha = -sum(dO O_l)
@@ -17,6 +19,7 @@
 //   bwd_q        per query block, two passes over its kept key blocks: pass 1 rebuilds the
 //                row softmax (log-sum-exp, O_s) and D = rowsum(dO_s O_s); pass 2 forms
 //                dS = P (dO_s V^T - D) and adds dS K_s / sqrt(d) to dQ; dalpha += sum(dO O_s)
+//   bwd_kv_extra the work items past the first of each key list: partial dK_s, dV, dH, dz
 //   bwd_kv       per key block, over the query blocks that keep it: dV += P^T dO_s,
 //                dK_s += dS^T Q / sqrt(d); then the linear part with
 //                dh_j = dH_tot - sum of dH_i over those query blocks (the one addition per
@@ -30,7 +33,8 @@
 // 8 (r / 4) + 4 g + r % 4 in register r. So an accumulator C (M x N) serves directly as the B
 // operand of X C or the A operand of C^T Y (both contract over M), with k taken in register
 // order: registers 8 h .. 8 h + 7 are rows 16 h + 4 g .. +3 and 16 h + 8 + 4 g .. +3; the other
-// operand is then read from LDS in that row order. All LDS tiles are bf16 [rows][136]
+// operand is then read from LDS in that row order; operands that run down the columns of a
+// row-major LDS tile use the transposing LDS read. All LDS tiles are bf16 [rows][136]
 // (272-byte rows).
 #include "sla2_common.h"
 
@@ -46,33 +50,34 @@ constexpr float kInvSqrtD = 0.08838834764831845f;   // 1 / sqrt(128)
 __device__ inline bf16x8 ld_row8(const uint16_t* p) {
   return __builtin_bit_cast(bf16x8, *reinterpret_cast<const i32x4*>(p));
 }
-// row elements k0 + 4 g .. +3 and k0 + 8 + 4 g .. +3 (accumulator register order)
-__device__ inline bf16x8 ld_row8_acc(const uint16_t* row, int k0, int g) {
-  const uint2 lo = *reinterpret_cast<const uint2*>(row + k0 + 4 * g);
-  const uint2 hi = *reinterpret_cast<const uint2*>(row + k0 + 8 + 4 * g);
-  const i32x4 v = {static_cast<int>(lo.x), static_cast<int>(lo.y), static_cast<int>(hi.x),
-                   static_cast<int>(hi.y)};
+// Transposing LDS read (ds_read_b64_tr_b16): in each group of 16 lanes, source lane s gives
+// the address of 4 consecutive 16-bit elements and result lane l receives element l % 4 of
+// source lanes l / 4, 4 + l / 4, 8 + l / 4, 12 + l / 4 (in that order). With source lane
+// s = 4 k + j pointing at row r0 + k, columns c0 + 4 j .. +3, lane l so gets rows r0 .. r0 + 3
+// of column c0 + l.
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+__device__ inline uint2 ld_tr4(const uint16_t* p) {
+  const v4i16 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      reinterpret_cast<__attribute__((address_space(3))) v4i16*>(reinterpret_cast<uintptr_t>(p)));
+  return __builtin_bit_cast(uint2, v);
+}
+// Operand rows of a 32-column tile starting at column c0 of a [rows][kLd] tile: lane
+// (g, l) gets column c0 + l, rows k0 + 8 g .. +7 (natural order).
+__device__ inline bf16x8 ld_col8(const uint16_t* base, int c0, int k0, int g, int lane) {
+  const int s = lane & 15;
+  const uint16_t* p = base + (k0 + 8 * g + (s >> 2)) * kLd + c0 + 16 * ((lane >> 4) & 1) + 4 * (s & 3);
+  const uint2 a = ld_tr4(p), b = ld_tr4(p + 4 * kLd);
+  const i32x4 v = {static_cast<int>(a.x), static_cast<int>(a.y), static_cast<int>(b.x),
+                   static_cast<int>(b.y)};
   return __builtin_bit_cast(bf16x8, v);
 }
-__device__ inline uint32_t ld_pair(const uint16_t* base, int r0, int r1, int col) {
-  return static_cast<uint32_t>(base[r0 * kLd + col]) |
-         (static_cast<uint32_t>(base[r1 * kLd + col]) << 16);
-}
-// column `col`, rows k0 .. k0 + 7
-__device__ inline bf16x8 ld_col8(const uint16_t* base, int col, int k0) {
-  const i32x4 v = {static_cast<int>(ld_pair(base, k0, k0 + 1, col)),
-                   static_cast<int>(ld_pair(base, k0 + 2, k0 + 3, col)),
-                   static_cast<int>(ld_pair(base, k0 + 4, k0 + 5, col)),
-                   static_cast<int>(ld_pair(base, k0 + 6, k0 + 7, col))};
-  return __builtin_bit_cast(bf16x8, v);
-}
-// column `col`, rows k0 + 4 g .. +3 and k0 + 8 + 4 g .. +3 (accumulator register order)
-__device__ inline bf16x8 ld_col8_acc(const uint16_t* base, int col, int k0, int g) {
-  const int a = k0 + 4 * g, b = k0 + 8 + 4 * g;
-  const i32x4 v = {static_cast<int>(ld_pair(base, a, a + 1, col)),
-                   static_cast<int>(ld_pair(base, a + 2, a + 3, col)),
-                   static_cast<int>(ld_pair(base, b, b + 1, col)),
-                   static_cast<int>(ld_pair(base, b + 2, b + 3, col))};
+// The same with rows k0 + 4 g .. +3 and k0 + 8 + 4 g .. +3 (accumulator register order).
+__device__ inline bf16x8 ld_col8_acc(const uint16_t* base, int c0, int k0, int g, int lane) {
+  const int s = lane & 15;
+  const uint16_t* p = base + (k0 + 4 * g + (s >> 2)) * kLd + c0 + 16 * ((lane >> 4) & 1) + 4 * (s & 3);
+  const uint2 a = ld_tr4(p), b = ld_tr4(p + 8 * kLd);
+  const i32x4 v = {static_cast<int>(a.x), static_cast<int>(a.y), static_cast<int>(b.x),
+                   static_cast<int>(b.y)};
   return __builtin_bit_cast(bf16x8, v);
 }
 // accumulator registers 8 h .. 8 h + 7 as a bf16 operand
@@ -105,7 +110,90 @@ __device__ inline int lanes_below(uint64_t m) {
                                    __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0));
 }
 
+// acc[u][k] += element 8 (t + 256 u) + k of the bf16 d x d tiles src + idx(n) d^2 for n in
+// [n0, n1), added in n order; two tiles' loads are issued together.
+template <typename Idx>
+__device__ inline void sum_tiles(float (&acc)[8][8], const uint16_t* src, Idx idx, int n0, int n1,
+                                 int t) {
+  int n = n0;
+  for (; n + 1 < n1; n += 2) {
+    const uint16_t* a = src + static_cast<size_t>(idx(n)) * (kD * kD);
+    const uint16_t* b = src + static_cast<size_t>(idx(n + 1)) * (kD * kD);
+    i32x4 va[8], vb[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      va[u] = *reinterpret_cast<const i32x4*>(a + 8 * (t + 256 * u));
+      vb[u] = *reinterpret_cast<const i32x4*>(b + 8 * (t + 256 * u));
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      float fa[8], fb[8];
+      unpack_bf16x8(va[u], fa);
+      unpack_bf16x8(vb[u], fb);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) acc[u][k] = (acc[u][k] + fa[k]) + fb[k];
+    }
+  }
+  if (n < n1) {
+    const uint16_t* a = src + static_cast<size_t>(idx(n)) * (kD * kD);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      float fa[8];
+      unpack_bf16x8(*reinterpret_cast<const i32x4*>(a + 8 * (t + 256 * u)), fa);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) acc[u][k] += fa[k];
+    }
+  }
+}
+// sum of src[idx(n) * kD + col] over n in [n0, n1), in n order, four loads in flight
+template <typename Idx>
+__device__ inline float sum_rows(const float* src, Idx idx, int n0, int n1, int col) {
+  float s = 0.f;
+  int n = n0;
+  for (; n + 3 < n1; n += 4) {
+    const float a = src[static_cast<size_t>(idx(n)) * kD + col];
+    const float b = src[static_cast<size_t>(idx(n + 1)) * kD + col];
+    const float c = src[static_cast<size_t>(idx(n + 2)) * kD + col];
+    const float d = src[static_cast<size_t>(idx(n + 3)) * kD + col];
+    s = (((s + a) + b) + c) + d;
+  }
+  for (; n < n1; ++n) s += src[static_cast<size_t>(idx(n)) * kD + col];
+  return s;
+}
+
 }  // namespace
+
+// ---------------------------------------------------------------- bwd_prep
+// grid (N / 16, BH), 256 threads; thread: one 8-element chunk. bf16 operand copies for the
+// backward kernels: Q and V (fp32 inputs only), K_s = K - colmean(K), dO_s = alpha dO.
+template <typename T>
+__global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs x) {
+  const int bh = blockIdx.y;
+  const int N = x.nqb * kBQ;
+  const size_t loc = (static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x) * 8;   // in the head
+  const int row = static_cast<int>(loc / kD), c8 = static_cast<int>(loc % kD);
+  const size_t e = static_cast<size_t>(bh) * N * kD + loc;
+  const float al = x.alpha[static_cast<size_t>(bh % x.H) * x.nqb + row / kBQ];
+  const float* mp = x.mu32 + static_cast<size_t>(bh) * kD + c8;
+  float k8[8], d8[8], v[8];
+  load8<T>(static_cast<const T*>(x.K) + e, k8);
+  load8<float>(x.dO + e, d8);
+  if (x.qbf_w != nullptr) {
+    load8<T>(static_cast<const T*>(x.Q) + e, v);
+    st_bf16x8(x.qbf_w + e, v);
+  }
+  if (x.vbf_w != nullptr) {
+    load8<T>(static_cast<const T*>(x.V) + e, v);
+    st_bf16x8(x.vbf_w + e, v);
+  }
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    k8[k] -= mp[k];
+    d8[k] *= al;
+  }
+  st_bf16x8(x.ksb + e, k8);
+  st_bf16x8(x.dos + e, d8);
+}
 
 // ---------------------------------------------------------------- key_lists
 // grid (ceil(nkb / 4), BH), 256 threads; wavefront w compacts mask column j = 4 x + w: the
@@ -187,7 +275,6 @@ template <typename T>
 __global__ __launch_bounds__(256) void bwd_lin_q_kernel(BwdArgs x) {
   __shared__ __attribute__((aligned(16))) uint16_t As[kTile];   // a = phi(Q_i) [q][a]
   __shared__ __attribute__((aligned(16))) uint16_t Ht[kTile];   // H_i^T [o][a]
-  __shared__ __attribute__((aligned(16))) uint16_t Hn[kTile];   // H_i [a][o]
   __shared__ __attribute__((aligned(16))) uint16_t DN[kTile];   // dnum [q][o]
   __shared__ float Zs[kD], ddl[kD], red[4];
   int i, bh;
@@ -198,36 +285,6 @@ __global__ __launch_bounds__(256) void bwd_lin_q_kernel(BwdArgs x) {
   const size_t row0 = static_cast<size_t>(bh) * N + static_cast<size_t>(i) * kBQ;
   const int ncnt = x.cnt[qb];
   const float al = x.alpha[static_cast<size_t>(bh % x.H) * x.nqb + i];
-  // ---- bf16 operand copies of this block's 128 rows: Q and V (fp32 inputs only),
-  // K_s = K - colmean(K) (key blocks 2 i, 2 i + 1), dO_s = alpha dO
-  {
-    const int c8 = 8 * (t & 15);
-    float mu[8];
-    const float* mp = x.mu32 + static_cast<size_t>(bh) * kD + c8;
-#pragma unroll
-    for (int k = 0; k < 8; ++k) mu[k] = mp[k];
-#pragma unroll 2
-    for (int u = 0; u < 8; ++u) {
-      const size_t e = (row0 + (t >> 4) + 16 * u) * kD + c8;
-      float v[8];
-      if (x.qbf_w != nullptr) {
-        load8<T>(static_cast<const T*>(x.Q) + e, v);
-        st_bf16x8(x.qbf_w + e, v);
-      }
-      if (x.vbf_w != nullptr) {
-        load8<T>(static_cast<const T*>(x.V) + e, v);
-        st_bf16x8(x.vbf_w + e, v);
-      }
-      load8<T>(static_cast<const T*>(x.K) + e, v);
-#pragma unroll
-      for (int k = 0; k < 8; ++k) v[k] -= mu[k];
-      st_bf16x8(x.ksb + e, v);
-      load8<float>(x.dO + e, v);
-#pragma unroll
-      for (int k = 0; k < 8; ++k) v[k] *= al;
-      st_bf16x8(x.dos + e, v);
-    }
-  }
   if (ncnt == nkb) {   // nothing dropped: O_l = 0, no linear gradient
     for (int e = t; e < kBQ * kD / 4; e += 256)
       *reinterpret_cast<f32x4*>(x.dQ + row0 * kD + 4 * e) = f32x4{};
@@ -272,18 +329,7 @@ __global__ __launch_bounds__(256) void bwd_lin_q_kernel(BwdArgs x) {
     for (int u = 0; u < 8; ++u)
 #pragma unroll
       for (int k = 0; k < 8; ++k) acc[u][k] = 0.f;
-    for (int n = 0; n < ncnt; ++n) {
-      const int j = lst[n];
-      const uint16_t* hj = hb + static_cast<size_t>(j) * (kD * kD);
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const i32x4 v = *reinterpret_cast<const i32x4*>(hj + 8 * (t + 256 * u));
-        float f[8];
-        unpack_bf16x8(v, f);
-#pragma unroll
-        for (int k = 0; k < 8; ++k) acc[u][k] += f[k];
-      }
-    }
+    sum_tiles(acc, hb, [&](int n) { return lst[n]; }, 0, ncnt, t);
     const float* ht = x.htot + static_cast<size_t>(bh) * (kD * kD);   // H_tot [a][o]
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
@@ -293,12 +339,10 @@ __global__ __launch_bounds__(256) void bwd_lin_q_kernel(BwdArgs x) {
 #pragma unroll
       for (int k = 0; k < 8; ++k) hv[k] = ht[(a0 + k) * kD + o] - acc[u][k];
       st_bf16x8(&Ht[o * kLd + a0], hv);
-#pragma unroll
-      for (int k = 0; k < 8; ++k) Hn[(a0 + k) * kLd + o] = f32_to_bf16_rne(hv[k]);
     }
     if (t < kD) {
-      float zs = 0.f;
-      for (int n = 0; n < ncnt; ++n) zs += x.z[(static_cast<size_t>(bh) * nkb + lst[n]) * kD + t];
+      const float zs = sum_rows(x.z + static_cast<size_t>(bh) * nkb * kD,
+                                [&](int n) { return lst[n]; }, 0, ncnt, t);
       Zs[t] = x.ztot[static_cast<size_t>(bh) * kD + t] - zs;
     }
   }
@@ -357,7 +401,7 @@ __global__ __launch_bounds__(256) void bwd_lin_q_kernel(BwdArgs x) {
       for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
         for (int h = 0; h < 2; ++h)
-          da[at] = mfma(ld_row8_acc(&Hn[(32 * at + l32) * kLd], 32 * mt + 16 * h, g),
+          da[at] = mfma(ld_col8_acc(Ht, 32 * at, 32 * mt + 16 * h, g, lane),
                         acc_op(num[mt], h), da[at]);
     }
     float av[4][16];
@@ -408,7 +452,7 @@ __global__ __launch_bounds__(256) void bwd_lin_q_kernel(BwdArgs x) {
       f32x16 c = f32x16{};
 #pragma unroll
       for (int s = 0; s < 8; ++s)
-        c = mfma(ld_col8(DN, 32 * w + l32, 16 * s + 8 * g), ld_col8(As, 32 * at + l32, 16 * s + 8 * g), c);
+        c = mfma(ld_col8(DN, 32 * w, 16 * s, g, lane), ld_col8(As, 32 * at, 16 * s, g, lane), c);
       const int a = 32 * at + l32;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -528,7 +572,7 @@ __global__ __launch_bounds__(256) void bwd_q_kernel(BwdArgs x) {
       for (int tk = 0; tk < 2; ++tk)
 #pragma unroll
         for (int h = 0; h < 2; ++h)
-          oT[dt] = mfma(ld_col8_acc(Vs, 32 * dt + l32, 32 * tk + 16 * h, g), acc_op(sT[tk], h), oT[dt]);
+          oT[dt] = mfma(ld_col8_acc(Vs, 32 * dt, 32 * tk + 16 * h, g, lane), acc_op(sT[tk], h), oT[dt]);
     }
   }
   fetch(lst[0]);   // pass 2 starts over; in flight during the row statistics below
@@ -590,7 +634,7 @@ __global__ __launch_bounds__(256) void bwd_q_kernel(BwdArgs x) {
       for (int tk = 0; tk < 2; ++tk)
 #pragma unroll
         for (int h = 0; h < 2; ++h)
-          dq[dt] = mfma(ld_col8_acc(Ks, 32 * dt + l32, 32 * tk + 16 * h, g), acc_op(dp[tk], h), dq[dt]);
+          dq[dt] = mfma(ld_col8_acc(Ks, 32 * dt, 32 * tk + 16 * h, g, lane), acc_op(dp[tk], h), dq[dt]);
   }
   {
     float* dqp = x.dQ + (row0 + q) * kD;
@@ -630,7 +674,7 @@ struct KvLds {
 
 __device__ inline void kv_sparse(const BwdArgs& x, size_t head, const uint16_t* tl, int n0,
                                  int n1, const KvLds& L, int t, int g, int l32, int kt, int qh) {
-  const int c8 = 8 * (t & 15);
+  const int c8 = 8 * (t & 15), lane = t & 63;
   const float c2 = kLog2e * kInvSqrtD;
   f32x16 dk[4], dv[4];   // lane = d column, registers = keys 32 kt + ...
 #pragma unroll
@@ -693,8 +737,8 @@ __device__ inline void kv_sparse(const BwdArgs& x, size_t head, const uint16_t* 
       for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-          dv[dt] = mfma(acc_op(s, h), ld_col8_acc(L.Ds, 32 * dt + l32, 32 * qt + 16 * h, g), dv[dt]);
-          dk[dt] = mfma(acc_op(dp, h), ld_col8_acc(L.Qs, 32 * dt + l32, 32 * qt + 16 * h, g), dk[dt]);
+          dv[dt] = mfma(acc_op(s, h), ld_col8_acc(L.Ds, 32 * dt, 32 * qt + 16 * h, g, lane), dv[dt]);
+          dk[dt] = mfma(acc_op(dp, h), ld_col8_acc(L.Qs, 32 * dt, 32 * qt + 16 * h, g, lane), dk[dt]);
         }
     }
   }
@@ -793,16 +837,7 @@ __global__ __launch_bounds__(256) void bwd_kv_extra_kernel(BwdArgs x) {
   for (int u = 0; u < 8; ++u)
 #pragma unroll
     for (int k = 0; k < 8; ++k) acc[u][k] = 0.f;
-  for (int n = n0; n < n1; ++n) {
-    const uint16_t* hi = src + static_cast<size_t>(tl[n]) * (kD * kD);
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      float f8[8];
-      unpack_bf16x8(*reinterpret_cast<const i32x4*>(hi + 8 * (t + 256 * u)), f8);
-#pragma unroll
-      for (int k = 0; k < 8; ++k) acc[u][k] += f8[k];
-    }
-  }
+  sum_tiles(acc, src, [&](int n) { return static_cast<int>(tl[n]); }, n0, n1, t);
   float* sh = slot + 2 * kBK * kD;
 #pragma unroll
   for (int u = 0; u < 8; ++u) {
@@ -812,7 +847,8 @@ __global__ __launch_bounds__(256) void bwd_kv_extra_kernel(BwdArgs x) {
   }
   if (t < kD) {
     float s = 0.f;
-    for (int n = n0; n < n1; ++n) s += x.dz[(static_cast<size_t>(bh) * nqb + tl[n]) * kD + t];
+    s = sum_rows(x.dz + static_cast<size_t>(bh) * nqb * kD,
+                 [&](int n) { return static_cast<int>(tl[n]); }, n0, n1, t);
     sh[kD * kD + t] = s;
   }
 }
@@ -894,16 +930,7 @@ __global__ __launch_bounds__(256) void bwd_kv_kernel(BwdArgs x) {
     for (int u = 0; u < 8; ++u)
 #pragma unroll
       for (int k = 0; k < 8; ++k) acc[u][k] = 0.f;
-    for (int n = 0; n < n1; ++n) {
-      const uint16_t* hi = src + static_cast<size_t>(tl[n]) * (kD * kD);
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        float f8[8];
-        unpack_bf16x8(*reinterpret_cast<const i32x4*>(hi + 8 * (t + 256 * u)), f8);
-#pragma unroll
-        for (int k = 0; k < 8; ++k) acc[u][k] += f8[k];
-      }
-    }
+    sum_tiles(acc, src, [&](int n) { return static_cast<int>(tl[n]); }, 0, n1, t);
     for (int e = 0; e < nx; ++e) {
       const float* sh = xs + static_cast<size_t>(e) * kSlot + 2 * kBK * kD;
 #pragma unroll
@@ -931,7 +958,8 @@ __global__ __launch_bounds__(256) void bwd_kv_kernel(BwdArgs x) {
     }
     if (t < kD) {
       float s = 0.f;
-      for (int n = 0; n < n1; ++n) s += x.dz[(static_cast<size_t>(bh) * nqb + tl[n]) * kD + t];
+      s = sum_rows(x.dz + static_cast<size_t>(bh) * nqb * kD,
+                   [&](int n) { return static_cast<int>(tl[n]); }, 0, n1, t);
       for (int e = 0; e < nx; ++e) s += xs[static_cast<size_t>(e) * kSlot + 2 * kBK * kD + kD * kD + t];
       dz_s[t] = x.dztot[static_cast<size_t>(bh) * kD + t] - s;
     }
@@ -961,7 +989,7 @@ __global__ __launch_bounds__(256) void bwd_kv_kernel(BwdArgs x) {
     dph[h] = f32x16{};
 #pragma unroll
     for (int u = 0; u < 8; ++u)
-      dph[h] = mfma(ld_col8(DH, 32 * at + l32, 16 * u + 8 * g),
+      dph[h] = mfma(ld_col8(DH, 32 * at, 16 * u, g, lane),
                     ld_row8(&L.Vs[key * kLd + 16 * u + 8 * g]), dph[h]);
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
@@ -1080,6 +1108,14 @@ hipError_t launch_key_plan(const Geom& g, const int32_t* tcnt, int32_t* plan, in
                            int32_t* items, int cap, hipStream_t s) {
   hipLaunchKernelGGL(key_plan_kernel, dim3(g.BH), dim3(1024), 0, s, tcnt, plan, xoff, items,
                      g.nkb, cap);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_prep(const Geom& g, int dtype, const BwdArgs& x, hipStream_t s) {
+  if (dtype == 0)
+    hipLaunchKernelGGL(bwd_prep_kernel<float>, dim3(g.N / 16, g.BH), dim3(256), 0, s, x);
+  else
+    hipLaunchKernelGGL(bwd_prep_kernel<uint16_t>, dim3(g.N / 16, g.BH), dim3(256), 0, s, x);
   return hipGetLastError();
 }
 

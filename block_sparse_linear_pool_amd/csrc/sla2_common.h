@@ -314,7 +314,7 @@ hipError_t launch_attn(const Geom& g, int dtype, const void* Q, const AttnArgs& 
 struct BwdArgs {
   const void *Q, *K, *V;
   // bf16 operand copies: Q and V are the inputs themselves when they are bf16, else written by
-  // bwd_lin_q (qbf_w, vbf_w non-null); K_s = K - colmean(K) and dO_s = alpha dO always written
+  // bwd_prep (qbf_w, vbf_w non-null); K_s = K - colmean(K) and dO_s = alpha dO always written
   const uint16_t *qbf, *vbf;
   uint16_t *qbf_w, *vbf_w, *ksb, *dos;
   const int32_t* plan;       // [BH][2]: chunk size C, number of extra items
@@ -352,6 +352,7 @@ hipError_t launch_key_plan(const Geom& g, const int32_t* tcnt, int32_t* plan, in
                            int32_t* items, int cap, hipStream_t s);
 // the work items past the first of each long key list (partials into xpart)
 hipError_t launch_bwd_kv_extra(const Geom& g, const BwdArgs& x, hipStream_t s);
+hipError_t launch_bwd_prep(const Geom& g, int dtype, const BwdArgs& x, hipStream_t s);
 hipError_t launch_bwd_lin_q(const Geom& g, int dtype, const BwdArgs& x, hipStream_t s);
 hipError_t launch_dh_total(const Geom& g, const BwdArgs& x, hipStream_t s);
 hipError_t launch_bwd_q(const Geom& g, const BwdArgs& x, hipStream_t s);

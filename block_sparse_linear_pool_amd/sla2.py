@@ -309,7 +309,7 @@ def sla2_forward_with_mask(q, k, v, mask, alpha, taps=False, out=None, workspace
     return (o, tdict) if taps else o
 
 
-BACKWARD_STAGES = 13   # kernels (stage events: one more)
+BACKWARD_STAGES = 14   # kernels (stage events: one more)
 
 
 def sla2_backward(q, k, v, mask, alpha, grad_out, out=None, workspace=None, events=None):
@@ -318,8 +318,8 @@ def sla2_backward(q, k, v, mask, alpha, grad_out, out=None, workspace=None, even
 
     mask [B,H,N/128,N/64] uint8 (the forward's block mask); alpha [H,N/128] fp32; grad_out
     [B,H,N,d] fp32. `out`: optional tuple of the four output tensors. `events`: optional list
-    of 14 torch.cuda.Event(enable_timing=True) recorded before the first and after each of the
-    thirteen stages on the current stream."""
+    of 15 torch.cuda.Event(enable_timing=True) recorded before the first and after each of the
+    fourteen stages on the current stream."""
     _contig(q, k, v, mask, alpha, grad_out)
     shp = shape_of(q)
     dev = q.device

@@ -200,11 +200,12 @@ sla2_status sla2_forward_with_mask(const sla2_shape *shape, const void *Q, const
  *   dO     [B,H,N,d] fp32, the gradient of the loss with respect to O
  *   dQ, dK, dV  [B,H,N,d] fp32 outputs (overwritten)
  *   dalpha [B,H,N/128] fp32 output: per batch and head; sum over B for alpha's gradient
- *   stage_events  NULL, or 14 caller-created hipEvent_t handles recorded on the stream before
+ *   stage_events  NULL, or 15 caller-created hipEvent_t handles recorded on the stream before
  *          the first kernel and after each of pool (K sums), colmean, kv_prep, linear_total,
  *          mask_to_list, key_lists (mask transposed: the query blocks keeping each key block),
  *          key_plan (long key lists cut into work items of at most C query blocks),
- *          bwd_lin_q (linear branch per query block; bf16 copies of Q, K_s, V, alpha dO),
+ *          bwd_prep (bf16 copies of Q, K_s, V and alpha dO), bwd_lin_q (linear branch per
+ *          query block),
  *          dh_total, bwd_q (sparse branch per query block: dQ, log-sum-exp, D),
  *          bwd_kv_extra (work items past the first of each key list: partial sums),
  *          bwd_kv (per key block: first work item, the partials, the linear part: dK_s, dV)
