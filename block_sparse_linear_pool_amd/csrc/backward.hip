@@ -470,20 +470,51 @@ __global__ __launch_bounds__(256) void bwd_lin_q_kernel(BwdArgs x) {
 }
 
 // ---------------------------------------------------------------- bwd_q
-// grid (nqb, BH) (XCD-aware order), 256 threads; wavefront w owns query rows 32 w .. +31 and
-// holds S^T = K_s,j Q^T with the query as lane (column) and the 64 keys in registers, so row
-// statistics are per lane. Logits are kept in base-2 units: s2 = S log2(e) / sqrt(d). The
-// bf16 K_s and V of the next kept block are loaded into registers while the current one is
-// processed.
-__global__ __launch_bounds__(256) void bwd_q_kernel(BwdArgs x) {
-  __shared__ __attribute__((aligned(16))) uint16_t Qs[kTile];
-  __shared__ __attribute__((aligned(16))) uint16_t Ds[kTile];   // dO_s = alpha dO
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[kBK * kLd];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs[kBK * kLd];
-  __shared__ float red[4];
+// grid (nqb, BH) (XCD-aware order), 512 threads. MFMA 16x16x32 bf16 (A lane (G = lane / 16,
+// l = lane % 16): row l, k = 8 G .. +7; B: column l, same k; accumulator: column l, rows
+// 4 G .. +3). Wavefront w owns query rows 16 w .. +15 and holds S^T = K_s,j Q^T with the query
+// as column (lane) and the 64 keys in its four 16-row tiles, so row statistics are per lane
+// plus a reduction over the four lane groups. Its Q and dO_s rows stay in registers as B
+// operands. K_s and V tiles are double-buffered in LDS; the next-but-one block is loaded into
+// registers while the current one is processed (one barrier per block). Logits are kept in
+// base-2 units: s2 = S log2(e) / sqrt(d).
+constexpr int kQThreads = 512;
+__device__ inline f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+// two accumulator tiles (rows 0-15 and 16-31 of a 32-deep k chunk) as a bf16 operand:
+// element i of lane group G is row 4 G + i (i < 4) or 16 + 4 G + i - 4
+__device__ inline bf16x8 acc_op16(const f32x4& a, const f32x4& b) {
+  const i32x4 v = {static_cast<int>(pack_bf16x2(a[0], a[1])), static_cast<int>(pack_bf16x2(a[2], a[3])),
+                   static_cast<int>(pack_bf16x2(b[0], b[1])), static_cast<int>(pack_bf16x2(b[2], b[3]))};
+  return __builtin_bit_cast(bf16x8, v);
+}
+// the matching operand read down the columns of a row-major tile: lane (G, l) gets column
+// c0 + l, rows r0 + 4 G .. +3 and r0 + 16 + 4 G .. +3
+__device__ inline bf16x8 ld_col8_16(const uint16_t* base, int c0, int r0, int G, int lane) {
+  const int s = lane & 15;
+  const uint16_t* p = base + (r0 + 4 * G + (s >> 2)) * kLd + c0 + 4 * (s & 3);
+  const uint2 a = ld_tr4(p), b = ld_tr4(p + 16 * kLd);
+  const i32x4 v = {static_cast<int>(a.x), static_cast<int>(a.y), static_cast<int>(b.x),
+                   static_cast<int>(b.y)};
+  return __builtin_bit_cast(bf16x8, v);
+}
+__device__ inline float group4_max(float v) {
+  v = fmaxf(v, __shfl_xor(v, 16));
+  return fmaxf(v, __shfl_xor(v, 32));
+}
+__device__ inline float group4_sum(float v) {
+  v += __shfl_xor(v, 16);
+  return v + __shfl_xor(v, 32);
+}
+
+__global__ __launch_bounds__(kQThreads) __attribute__((amdgpu_waves_per_eu(4))) void bwd_q_kernel(BwdArgs x) {
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][kBK * kLd];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs[2][kBK * kLd];
+  __shared__ float red[8];
   int i, bh;
   xcd_block(x.nqb, x.BH, &i, &bh);
-  const int t = threadIdx.x, lane = t & 63, w = t >> 6, g = lane >> 5, l32 = lane & 31;
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6, G = lane >> 4, l16 = lane & 15;
   const int N = x.nqb * kBQ, nkb = x.nkb;
   const size_t qb = static_cast<size_t>(bh) * x.nqb + i;
   const size_t head = static_cast<size_t>(bh) * N;
@@ -497,160 +528,165 @@ __global__ __launch_bounds__(256) void bwd_q_kernel(BwdArgs x) {
     return;
   }
   const float al = x.alpha[static_cast<size_t>(bh % x.H) * x.nqb + i];
-  const int c8 = 8 * (t & 15);
+  const int q = 16 * w + l16;
+  bf16x8 qop[4], dop[4];   // B operands: row q, d = 32 c + 8 G .. +7 (dO_s: loaded for pass 2)
 #pragma unroll
-  for (int u = 0; u < 8; ++u) {
-    const int r = (t >> 4) + 16 * u;
-    const size_t e = (row0 + r) * kD + c8;
-    *reinterpret_cast<i32x4*>(&Qs[r * kLd + c8]) = *reinterpret_cast<const i32x4*>(x.qbf + e);
-    *reinterpret_cast<i32x4*>(&Ds[r * kLd + c8]) = *reinterpret_cast<const i32x4*>(x.dos + e);
-  }
+  for (int c = 0; c < 4; ++c)
+    qop[c] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const i32x4*>(x.qbf + (row0 + q) * kD + 32 * c + 8 * G));
   const int32_t* lst = x.list + qb * nkb;
   const float c2 = kLog2e * kInvSqrtD;
-  const int q = 32 * w + l32;
-  i32x4 pk[4], pv[4];
+  i32x4 pk[2], pv[2];
   auto fetch = [&](int j) {
     const size_t kr = head + static_cast<size_t>(j) * kBK;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const size_t e = (kr + (t >> 4) + 16 * u) * kD + c8;
+    for (int u = 0; u < 2; ++u) {
+      const int ch = t + kQThreads * u;
+      const size_t e = (kr + (ch >> 4)) * kD + 8 * (ch & 15);
       pk[u] = *reinterpret_cast<const i32x4*>(x.ksb + e);
       pv[u] = *reinterpret_cast<const i32x4*>(x.vbf + e);
     }
   };
-  auto put = [&]() {
+  auto put = [&](int b) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int r = (t >> 4) + 16 * u;
-      *reinterpret_cast<i32x4*>(&Ks[r * kLd + c8]) = pk[u];
-      *reinterpret_cast<i32x4*>(&Vs[r * kLd + c8]) = pv[u];
+    for (int u = 0; u < 2; ++u) {
+      const int ch = t + kQThreads * u;
+      const int o = (ch >> 4) * kLd + 8 * (ch & 15);
+      *reinterpret_cast<i32x4*>(&Ks[b][o]) = pk[u];
+      *reinterpret_cast<i32x4*>(&Vs[b][o]) = pv[u];
     }
   };
-  // ---- pass 1: running max m and sum l (per lane: its 32 keys of each block), O_s^T
-  float m = -INFINITY, l = 0.f;
-  f32x16 oT[4];
+  auto scores = [&](const uint16_t* kt, f32x4 (&sT)[4]) {
 #pragma unroll
-  for (int dt = 0; dt < 4; ++dt) oT[dt] = f32x16{};
-  fetch(lst[0]);
-  for (int n = 0; n < ncnt; ++n) {
-    __syncthreads();
-    put();
-    __syncthreads();
-    if (n + 1 < ncnt) fetch(lst[n + 1]);
-    f32x16 sT[2];
+    for (int T = 0; T < 4; ++T) {
+      sT[T] = f32x4{};
 #pragma unroll
-    for (int tk = 0; tk < 2; ++tk) {
-      sT[tk] = f32x16{};
-#pragma unroll
-      for (int s = 0; s < 8; ++s)
-        sT[tk] = mfma(ld_row8(&Ks[(32 * tk + l32) * kLd + 16 * s + 8 * g]),
-                      ld_row8(&Qs[q * kLd + 16 * s + 8 * g]), sT[tk]);
+      for (int c = 0; c < 4; ++c)
+        sT[T] = mfma16(ld_row8(&kt[(16 * T + l16) * kLd + 32 * c + 8 * G]), qop[c], sT[T]);
     }
+  };
+  // ---- pass 1: running max m and sum l (per lane: its 16 keys of each block), O_s^T
+  float m = -INFINITY, l = 0.f;
+  f32x4 oT[8];
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) oT[dt] = f32x4{};
+  fetch(lst[0]);
+  put(0);
+  __syncthreads();
+  if (ncnt > 1) fetch(lst[1]);
+  for (int n = 0; n < ncnt; ++n) {
+    const int b = n & 1;
+    f32x4 sT[4];
+    scores(Ks[b], sT);
     float mx = -INFINITY;
 #pragma unroll
-    for (int tk = 0; tk < 2; ++tk)
+    for (int T = 0; T < 4; ++T)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sT[tk][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+      for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sT[T][r]);
+    mx = group4_max(mx);
     const float mn = fmaxf(m, mx * c2);
     const float corr = exp2f(m - mn);
     float ls = 0.f;
 #pragma unroll
-    for (int tk = 0; tk < 2; ++tk)
+    for (int T = 0; T < 4; ++T)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = exp2f(sT[tk][r] * c2 - mn);
-        sT[tk][r] = p;
+      for (int r = 0; r < 4; ++r) {
+        const float p = exp2f(sT[T][r] * c2 - mn);
+        sT[T][r] = p;
         ls += p;
       }
     l = l * corr + ls;
     m = mn;
+    if (__ballot(corr != 1.0f) != 0) {
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt) {
-      oT[dt] *= corr;
-#pragma unroll
-      for (int tk = 0; tk < 2; ++tk)
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-          oT[dt] = mfma(ld_col8_acc(Vs, 32 * dt, 32 * tk + 16 * h, g, lane), acc_op(sT[tk], h), oT[dt]);
+      for (int dt = 0; dt < 8; ++dt) oT[dt] *= corr;
     }
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+      for (int cc = 0; cc < 2; ++cc)
+        oT[dt] = mfma16(ld_col8_16(Vs[b], 16 * dt, 32 * cc, G, lane),
+                        acc_op16(sT[2 * cc], sT[2 * cc + 1]), oT[dt]);
+    if (n + 1 < ncnt) put(b ^ 1);
+    __syncthreads();
+    if (n + 2 < ncnt) fetch(lst[n + 2]);
   }
   fetch(lst[0]);   // pass 2 starts over; in flight during the row statistics below
-  const float lt = l + __shfl_xor(l, 32);
+  const float lt = group4_sum(l);
   const float lse = m + log2f(lt);
   const float invl = 1.0f / lt;
   float sd = 0.f;
   {
-    const float* dop = x.dO + (row0 + q) * kD;
+    const float* dp_ = x.dO + (row0 + q) * kD + 4 * G;
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
+    for (int dt = 0; dt < 8; ++dt) {
+      const f32x4 d4 = *reinterpret_cast<const f32x4*>(dp_ + 16 * dt);
 #pragma unroll
-      for (int k4 = 0; k4 < 4; ++k4) {
-        const f32x4 d4 = *reinterpret_cast<const f32x4*>(dop + 32 * dt + 8 * k4 + 4 * g);
-#pragma unroll
-        for (int k = 0; k < 4; ++k) sd += d4[k] * (oT[dt][4 * k4 + k] * invl);
-      }
+      for (int r = 0; r < 4; ++r) sd += d4[r] * (oT[dt][r] * invl);
+    }
   }
-  sd += __shfl_xor(sd, 32);
+  sd = group4_sum(sd);
   const float Dq = al * sd;
-  if (g == 0) {
+  if (G == 0) {
     x.lse2[row0 + q] = lse;
     x.Dd[row0 + q] = Dq;
   }
   {
-    const float ws = wave_sum(g == 0 ? sd : 0.f);
+    const float ws = wave_sum(G == 0 ? sd : 0.f);
     if (lane == 0) red[w] = ws;
   }
   // ---- pass 2: P^T, dP^T = V_j dO_s^T, dS^T = P^T (dP^T - D), dQ^T += K_s,j^T dS^T
-  f32x16 dq[4];
 #pragma unroll
-  for (int dt = 0; dt < 4; ++dt) dq[dt] = f32x16{};
+  for (int c = 0; c < 4; ++c)
+    dop[c] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const i32x4*>(x.dos + (row0 + q) * kD + 32 * c + 8 * G));
+  put(0);
+  __syncthreads();
+  if (ncnt > 1) fetch(lst[1]);
+  f32x4 dq[8];
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) dq[dt] = f32x4{};
   for (int n = 0; n < ncnt; ++n) {
-    __syncthreads();
-    put();
-    __syncthreads();
-    if (n + 1 < ncnt) fetch(lst[n + 1]);
-    f32x16 sT[2], dp[2];
+    const int b = n & 1;
+    f32x4 sT[4], dp[4];
+    scores(Ks[b], sT);
 #pragma unroll
-    for (int tk = 0; tk < 2; ++tk) {
-      sT[tk] = f32x16{};
-      dp[tk] = f32x16{};
+    for (int T = 0; T < 4; ++T) {
+      dp[T] = f32x4{};
 #pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        sT[tk] = mfma(ld_row8(&Ks[(32 * tk + l32) * kLd + 16 * s + 8 * g]),
-                      ld_row8(&Qs[q * kLd + 16 * s + 8 * g]), sT[tk]);
-        dp[tk] = mfma(ld_row8(&Vs[(32 * tk + l32) * kLd + 16 * s + 8 * g]),
-                      ld_row8(&Ds[q * kLd + 16 * s + 8 * g]), dp[tk]);
-      }
+      for (int c = 0; c < 4; ++c)
+        dp[T] = mfma16(ld_row8(&Vs[b][(16 * T + l16) * kLd + 32 * c + 8 * G]), dop[c], dp[T]);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = exp2f(sT[tk][r] * c2 - lse);
-        dp[tk][r] = p * (dp[tk][r] - Dq);
+      for (int r = 0; r < 4; ++r) {
+        const float p = exp2f(sT[T][r] * c2 - lse);
+        dp[T][r] = p * (dp[T][r] - Dq);
       }
     }
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
+    for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
-      for (int tk = 0; tk < 2; ++tk)
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-          dq[dt] = mfma(ld_col8_acc(Ks, 32 * dt, 32 * tk + 16 * h, g, lane), acc_op(dp[tk], h), dq[dt]);
+      for (int cc = 0; cc < 2; ++cc)
+        dq[dt] = mfma16(ld_col8_16(Ks[b], 16 * dt, 32 * cc, G, lane),
+                        acc_op16(dp[2 * cc], dp[2 * cc + 1]), dq[dt]);
+    if (n + 1 < ncnt) put(b ^ 1);
+    __syncthreads();
+    if (n + 2 < ncnt) fetch(lst[n + 2]);
   }
   {
-    float* dqp = x.dQ + (row0 + q) * kD;
+    float* dqp = x.dQ + (row0 + q) * kD + 4 * G;
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
+    for (int dt = 0; dt < 8; ++dt) {
+      f32x4* p = reinterpret_cast<f32x4*>(dqp + 16 * dt);
+      f32x4 v = *p;
 #pragma unroll
-      for (int k4 = 0; k4 < 4; ++k4) {
-        f32x4* p = reinterpret_cast<f32x4*>(dqp + 32 * dt + 8 * k4 + 4 * g);
-        f32x4 v = *p;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) v[k] += dq[dt][4 * k4 + k] * kInvSqrtD;
-        *p = v;
-      }
+      for (int r = 0; r < 4; ++r) v[r] += dq[dt][r] * kInvSqrtD;
+      *p = v;
+    }
   }
-  __syncthreads();
-  if (t == 0) x.dalpha[qb] += (red[0] + red[1]) + (red[2] + red[3]);
+  if (t == 0) {
+    float s = 0.f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) s += red[k];
+    x.dalpha[qb] += s;
+  }
 }
 
 // ---------------------------------------------------------------- bwd_kv
@@ -1134,7 +1170,7 @@ hipError_t launch_dh_total(const Geom& g, const BwdArgs& x, hipStream_t s) {
 }
 
 hipError_t launch_bwd_q(const Geom& g, const BwdArgs& x, hipStream_t s) {
-  hipLaunchKernelGGL(bwd_q_kernel, dim3(g.nqb, g.BH), dim3(256), 0, s, x);
+  hipLaunchKernelGGL(bwd_q_kernel, dim3(g.nqb, g.BH), dim3(kQThreads), 0, s, x);
   return hipGetLastError();
 }
 
