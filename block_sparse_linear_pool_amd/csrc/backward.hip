@@ -690,41 +690,63 @@ __global__ __launch_bounds__(kQThreads) __attribute__((amdgpu_waves_per_eu(4))) 
 }
 
 // ---------------------------------------------------------------- bwd_kv
-// One work item = one key block j and a range of its keeping query blocks. Wavefront
-// w = (kt = w % 2, qh = w / 2) forms S = Q K_s^T for keys 32 kt .. +31 and query rows
-// 64 qh .. +63 of each query block in the range (query as register index, key as lane), so P
-// and dS serve directly as the A operand of dV = P^T dO_s and dK = dS^T Q. The bf16 Q and dO_s
-// of the next query block are loaded into registers while the current one is processed.
-// At the end the two query halves are summed through LDS (fp32 [128][kXld], over the Q/dO_s
-// tiles): rows 0-63 dK_s (scaled by 1 / sqrt(d)), rows 64-127 dV.
+// One work item = one key block j and a range of its keeping query blocks; 512 threads.
+// Wavefront w = (kt = w % 4, qh = w / 4): keys 16 kt .. +15 and, in the sparse loop, query rows
+// 64 qh .. +63 of each query block. MFMA 16x16x32 bf16 with S = Q K_s^T and dP = dO_s V^T held
+// with the key as column (lane) and the query in registers, so P and dS are directly the A
+// operand of dV = P^T dO_s and dK = dS^T Q; the B operands run down the columns of the Q and
+// dO_s tiles (transposing LDS read). K_s and V rows of the wavefront's keys stay in registers.
+// Q and dO_s tiles are double-buffered in LDS, the next-but-one query block loaded into
+// registers while the current one is processed. dK and dV accumulate as eight 16 x 16 tiles
+// (lane = d, registers = keys); after the loop the two query halves are summed through LDS so
+// that wavefront (kt, qh) holds the totals of d tiles 4 qh .. 4 qh + 3.
+constexpr int kKvT = 512;
 constexpr int kXld = kD + 4;   // fp32 row stride of the exchange tiles
-struct KvLds {
-  uint16_t* Qs;
-  uint16_t* Ds;
-  uint16_t* Ks;
-  uint16_t* Vs;
-  float* lse_s;
-  float* D_s;
-  float* X;
+// LDS (bytes): Q tiles [2] at 0, dO_s tiles [2] at 69632, lse [2][128] and D [2][128] at
+// 139264; after the loop the first 122880 bytes hold the exchange tiles (fp32 [2][64][kXld]),
+// phi(K_s,j) (bf16 [64][kLd]), dh_j^T (bf16 [128][kLd]), dz_j, row and column sums.
+constexpr int kKvLds = 4 * kTile * 2 + 4 * kBQ * 4;
+constexpr int kOffX = 0, kOffPK = 67584, kOffDH = 84992, kOffDz = 119808, kOffCrow = 120320,
+              kOffKred = 120832;
+
+// rows k0 + 8 G .. +7 of column c0 + l (natural order; 16x16x32 operand down the columns)
+__device__ inline bf16x8 ld_col8n_16(const uint16_t* base, int c0, int r0, int G, int lane) {
+  const int s = lane & 15;
+  const uint16_t* p = base + (r0 + 8 * G + (s >> 2)) * kLd + c0 + 4 * (s & 3);
+  const uint2 a = ld_tr4(p), b = ld_tr4(p + 4 * kLd);
+  const i32x4 v = {static_cast<int>(a.x), static_cast<int>(a.y), static_cast<int>(b.x),
+                   static_cast<int>(b.y)};
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+struct KvState {
+  f32x4 dk[8], dv[8];   // lane = d column 16 dt + l16, registers = keys 16 kt + 4 G + r
 };
 
+// The sparse loop over tl[n0 .. n1) plus the query-half exchange. On return, the wavefront's
+// dk[4 qh .. 4 qh + 3] (scaled by 1 / sqrt(d)) and dv[4 qh .. 4 qh + 3] are its key block's totals
+// over the range.
 __device__ inline void kv_sparse(const BwdArgs& x, size_t head, const uint16_t* tl, int n0,
-                                 int n1, const KvLds& L, int t, int g, int l32, int kt, int qh) {
-  const int c8 = 8 * (t & 15), lane = t & 63;
+                                 int n1, char* smem, const bf16x8 (&kop)[4],
+                                 const bf16x8 (&vop)[4], KvState& st, int t, int lane, int G,
+                                 int l16, int kt, int qh) {
+  uint16_t* const Q0 = reinterpret_cast<uint16_t*>(smem);   // Q tiles b = 0, 1; dO_s at + 2 kTile
+  float* lse_s = reinterpret_cast<float*>(smem + 4 * kTile * 2);   // [2][128]
+  float* D_s = lse_s + 2 * kBQ;                                     // [2][128]
   const float c2 = kLog2e * kInvSqrtD;
-  f32x16 dk[4], dv[4];   // lane = d column, registers = keys 32 kt + ...
 #pragma unroll
-  for (int dt = 0; dt < 4; ++dt) {
-    dk[dt] = f32x16{};
-    dv[dt] = f32x16{};
+  for (int dt = 0; dt < 8; ++dt) {
+    st.dk[dt] = f32x4{};
+    st.dv[dt] = f32x4{};
   }
-  i32x4 pq[8], pd[8];
+  i32x4 pq[4], pd[4];
   float pl = 0.f, pD = 0.f;
   auto fetch = [&](int i) {
     const size_t row0 = head + static_cast<size_t>(i) * kBQ;
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const size_t e = (row0 + (t >> 4) + 16 * u) * kD + c8;
+    for (int u = 0; u < 4; ++u) {
+      const int ch = t + kKvT * u;
+      const size_t e = (row0 + (ch >> 4)) * kD + 8 * (ch & 15);
       pq[u] = *reinterpret_cast<const i32x4*>(x.qbf + e);
       pd[u] = *reinterpret_cast<const i32x4*>(x.dos + e);
     }
@@ -733,177 +755,199 @@ __device__ inline void kv_sparse(const BwdArgs& x, size_t head, const uint16_t* 
       pD = x.Dd[row0 + t];
     }
   };
-  if (n0 < n1) fetch(tl[n0]);
-  for (int n = n0; n < n1; ++n) {
-    __syncthreads();
+  auto put = [&](int b) {
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int r = (t >> 4) + 16 * u;
-      *reinterpret_cast<i32x4*>(&L.Qs[r * kLd + c8]) = pq[u];
-      *reinterpret_cast<i32x4*>(&L.Ds[r * kLd + c8]) = pd[u];
+    for (int u = 0; u < 4; ++u) {
+      const int ch = t + kKvT * u;
+      const int o = (ch >> 4) * kLd + 8 * (ch & 15);
+      *reinterpret_cast<i32x4*>(&Q0[b * kTile + o]) = pq[u];
+      *reinterpret_cast<i32x4*>(&Q0[(2 + b) * kTile + o]) = pd[u];
     }
     if (t < kBQ) {
-      L.lse_s[t] = pl;
-      L.D_s[t] = pD;
+      lse_s[b * kBQ + t] = pl;
+      D_s[b * kBQ + t] = pD;
     }
+  };
+  if (n0 < n1) {
+    fetch(tl[n0]);
+    put(0);
     __syncthreads();
-    if (n + 1 < n1) fetch(tl[n + 1]);
+    if (n0 + 1 < n1) fetch(tl[n0 + 1]);
+  }
+  for (int n = n0; n < n1; ++n) {
+    const int b = (n - n0) & 1;
+    const uint16_t* Q = Q0 + b * kTile;
+    const uint16_t* Dm = Q0 + (2 + b) * kTile;
+    f32x4 s[4], ds[4];
 #pragma unroll
-    for (int qq = 0; qq < 2; ++qq) {
-      const int qt = 2 * qh + qq;
-      f32x16 s = f32x16{}, dp = f32x16{};
+    for (int T = 0; T < 4; ++T) {
+      const int qr = 64 * qh + 16 * T;
+      f32x4 sv = f32x4{}, dp = f32x4{};
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        s = mfma(ld_row8(&L.Qs[(32 * qt + l32) * kLd + 16 * u + 8 * g]),
-                 ld_row8(&L.Ks[(32 * kt + l32) * kLd + 16 * u + 8 * g]), s);
-        dp = mfma(ld_row8(&L.Ds[(32 * qt + l32) * kLd + 16 * u + 8 * g]),
-                  ld_row8(&L.Vs[(32 * kt + l32) * kLd + 16 * u + 8 * g]), dp);
+      for (int c = 0; c < 4; ++c) {
+        sv = mfma16(ld_row8(&Q[(qr + l16) * kLd + 32 * c + 8 * G]), kop[c], sv);
+        dp = mfma16(ld_row8(&Dm[(qr + l16) * kLd + 32 * c + 8 * G]), vop[c], dp);
       }
+      const f32x4 l4 = *reinterpret_cast<const f32x4*>(&lse_s[b * kBQ + qr + 4 * G]);
+      const f32x4 d4 = *reinterpret_cast<const f32x4*>(&D_s[b * kBQ + qr + 4 * G]);
 #pragma unroll
-      for (int k4 = 0; k4 < 4; ++k4) {
-        const int qr = 32 * qt + 8 * k4 + 4 * g;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const float p = exp2f(s[4 * k4 + k] * c2 - L.lse_s[qr + k]);
-          s[4 * k4 + k] = p;
-          dp[4 * k4 + k] = p * (dp[4 * k4 + k] - L.D_s[qr + k]);
-        }
+      for (int r = 0; r < 4; ++r) {
+        const float p = exp2f(sv[r] * c2 - l4[r]);
+        s[T][r] = p;
+        ds[T][r] = p * (dp[r] - d4[r]);
       }
+    }
 #pragma unroll
-      for (int dt = 0; dt < 4; ++dt)
+    for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          dv[dt] = mfma(acc_op(s, h), ld_col8_acc(L.Ds, 32 * dt, 32 * qt + 16 * h, g, lane), dv[dt]);
-          dk[dt] = mfma(acc_op(dp, h), ld_col8_acc(L.Qs, 32 * dt, 32 * qt + 16 * h, g, lane), dk[dt]);
-        }
+      for (int cc = 0; cc < 2; ++cc) {
+        st.dv[dt] = mfma16(acc_op16(s[2 * cc], s[2 * cc + 1]),
+                           ld_col8_16(Dm, 16 * dt, 64 * qh + 32 * cc, G, lane), st.dv[dt]);
+        st.dk[dt] = mfma16(acc_op16(ds[2 * cc], ds[2 * cc + 1]),
+                           ld_col8_16(Q, 16 * dt, 64 * qh + 32 * cc, G, lane), st.dk[dt]);
+      }
+    if (n + 1 < n1) put(b ^ 1);
+    __syncthreads();
+    if (n + 2 < n1) fetch(tl[n + 2]);
+  }
+  // exchange: send the other half's d tiles, receive the partner's contribution to ours
+  float* X = reinterpret_cast<float*>(smem + kOffX);   // [2][64][kXld]
+  __syncthreads();
+  // (tile indices stay compile-time constants: the wavefront's half is a uniform predicate)
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) {
+    if ((dt >> 2) == qh) continue;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int key = 16 * kt + 4 * G + r;
+      X[key * kXld + 16 * dt + l16] = st.dk[dt][r];
+      X[(kBK + key) * kXld + 16 * dt + l16] = st.dv[dt][r];
     }
   }
-  __syncthreads();   // Q / dO_s tiles free: exchange the two query halves through X
-  if (qh == 1) {
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = 32 * kt + 8 * (r >> 2) + 4 * g + (r & 3);
-        L.X[key * kXld + 32 * dt + l32] = dk[dt][r];
-        L.X[(kBK + key) * kXld + 32 * dt + l32] = dv[dt][r];
-      }
-  }
   __syncthreads();
-  if (qh == 0) {
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
+  for (int dt = 0; dt < 8; ++dt) {
+    if ((dt >> 2) != qh) continue;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = 32 * kt + 8 * (r >> 2) + 4 * g + (r & 3);
-        dk[dt][r] = (dk[dt][r] + L.X[key * kXld + 32 * dt + l32]) * kInvSqrtD;
-        dv[dt][r] += L.X[(kBK + key) * kXld + 32 * dt + l32];
-      }
+    for (int r = 0; r < 4; ++r) {
+      const int key = 16 * kt + 4 * G + r;
+      st.dk[dt][r] = (st.dk[dt][r] + X[key * kXld + 16 * dt + l16]) * kInvSqrtD;
+      st.dv[dt][r] += X[(kBK + key) * kXld + 16 * dt + l16];
+    }
   }
-  __syncthreads();
-  if (qh == 0) {
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = 32 * kt + 8 * (r >> 2) + 4 * g + (r & 3);
-        L.X[key * kXld + 32 * dt + l32] = dk[dt][r];
-        L.X[(kBK + key) * kXld + 32 * dt + l32] = dv[dt][r];
-      }
-  }
-  __syncthreads();
+  __syncthreads();   // X free again
 }
 
-constexpr int kKvLds = 2 * kTile * 2 + 2 * kBK * kLd * 2 + kTile * 2 + 4 * kBQ * 4;
-
-__device__ inline KvLds kv_lds(char* smem) {
-  KvLds L;
-  L.Qs = reinterpret_cast<uint16_t*>(smem);   // [128][kLd]
-  L.Ds = L.Qs + kTile;                        // dO_s [128][kLd]
-  L.Ks = L.Ds + kTile;                        // K_s,j [64][kLd]; later phi(K_s,j)
-  L.Vs = L.Ks + kBK * kLd;                    // V_j [64][kLd]
-  L.lse_s = reinterpret_cast<float*>(L.Vs + kBK * kLd + kTile);   // after DH
-  L.D_s = L.lse_s + kBQ;
-  L.X = reinterpret_cast<float*>(smem);       // over Qs / Ds after the loop
-  return L;
+__device__ inline void load_kv_ops(const BwdArgs& x, size_t krow0, int kt, int G, int l16,
+                                   bf16x8 (&kop)[4], bf16x8 (&vop)[4]) {
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const size_t e = (krow0 + 16 * kt + l16) * kD + 32 * c + 8 * G;
+    kop[c] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const i32x4*>(x.ksb + e));
+    vop[c] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const i32x4*>(x.vbf + e));
+  }
 }
 
-__device__ inline void stage_kv_block(const BwdArgs& x, size_t krow0, const KvLds& L, int t) {
-  const int c8 = 8 * (t & 15);
+// sum over n in [n0, n1) of the bf16 dH_i^T tiles of query blocks tl[n] (thread: chunks
+// t + 512 u, u < 4), two tiles in flight
+__device__ inline void sum_dh(float (&acc)[4][8], const uint16_t* src, const uint16_t* tl, int n0,
+                              int n1, int t) {
+  int n = n0;
+  for (; n + 1 < n1; n += 2) {
+    const uint16_t* a = src + static_cast<size_t>(tl[n]) * (kD * kD);
+    const uint16_t* b = src + static_cast<size_t>(tl[n + 1]) * (kD * kD);
+    i32x4 va[4], vb[4];
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int r = (t >> 4) + 16 * u;
-    const size_t e = (krow0 + r) * kD + c8;
-    *reinterpret_cast<i32x4*>(&L.Ks[r * kLd + c8]) = *reinterpret_cast<const i32x4*>(x.ksb + e);
-    *reinterpret_cast<i32x4*>(&L.Vs[r * kLd + c8]) = *reinterpret_cast<const i32x4*>(x.vbf + e);
+    for (int u = 0; u < 4; ++u) {
+      va[u] = *reinterpret_cast<const i32x4*>(a + 8 * (t + kKvT * u));
+      vb[u] = *reinterpret_cast<const i32x4*>(b + 8 * (t + kKvT * u));
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      float fa[8], fb[8];
+      unpack_bf16x8(va[u], fa);
+      unpack_bf16x8(vb[u], fb);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) acc[u][k] = (acc[u][k] + fa[k]) + fb[k];
+    }
+  }
+  if (n < n1) {
+    const uint16_t* a = src + static_cast<size_t>(tl[n]) * (kD * kD);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      float fa[8];
+      unpack_bf16x8(*reinterpret_cast<const i32x4*>(a + 8 * (t + kKvT * u)), fa);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) acc[u][k] += fa[k];
+    }
   }
 }
 
 // Extra work items: grid (cap, BH); item e < plan[bh].count covers the query blocks
-// [c C, min((c + 1) C, T_j)) of key block j; writes its partial dK_s, dV and the sums of dH_i^T
-// and dZ_i over its query blocks into slot e.
-__global__ __launch_bounds__(256) void bwd_kv_extra_kernel(BwdArgs x) {
+// [c C, min((c + 1) C, T_j)) of key block j; writes its partial dK_s, dV ([64][128] each) and
+// the sums of dH_i^T and dZ_i over its query blocks into slot e.
+__global__ __launch_bounds__(kKvT) void bwd_kv_extra_kernel(BwdArgs x) {
   __shared__ __attribute__((aligned(16))) char smem[kKvLds];
   const int e = blockIdx.x, bh = blockIdx.y;
   if (e >= x.plan[2 * bh + 1]) return;
-  const KvLds L = kv_lds(smem);
-  const int t = threadIdx.x, lane = t & 63, w = t >> 6, g = lane >> 5, l32 = lane & 31;
-  const int kt = w & 1, qh = w >> 1;
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6, G = lane >> 4, l16 = lane & 15;
+  const int kt = w & 3, qh = w >> 2;
   const int item = x.items[static_cast<size_t>(bh) * x.cap + e];
   const int j = item >> 16, c = item & 0xFFFF, C = x.plan[2 * bh];
   const int nqb = x.nqb, N = nqb * kBQ;
   const size_t head = static_cast<size_t>(bh) * N;
+  const size_t krow0 = head + static_cast<size_t>(j) * kBK;
   const int nT = x.tcnt[static_cast<size_t>(bh) * x.nkb + j];
   const uint16_t* tl = x.tlist + (static_cast<size_t>(bh) * x.nkb + j) * nqb;
   const int n0 = c * C, n1 = min(nT, n0 + C);
-  stage_kv_block(x, head + static_cast<size_t>(j) * kBK, L, t);
-  kv_sparse(x, head, tl, n0, n1, L, t, g, l32, kt, qh);
+  bf16x8 kop[4], vop[4];
+  load_kv_ops(x, krow0, kt, G, l16, kop, vop);
+  KvState st;
+  kv_sparse(x, head, tl, n0, n1, smem, kop, vop, st, t, lane, G, l16, kt, qh);
   float* slot = x.xpart + (static_cast<size_t>(bh) * x.cap + e) * kSlot;
 #pragma unroll
-  for (int u = 0; u < 8; ++u) {
-    const int f = t + 256 * u, r = f >> 5, c4 = 4 * (f & 31);
-    *reinterpret_cast<f32x4*>(slot + r * kD + c4) = *reinterpret_cast<const f32x4*>(&L.X[r * kXld + c4]);
-    *reinterpret_cast<f32x4*>(slot + kBK * kD + r * kD + c4) =
-        *reinterpret_cast<const f32x4*>(&L.X[(kBK + r) * kXld + c4]);
-  }
-  // sums of dH_i^T (chunk f = t + 256 u: 8 elements at 8 f) and dZ_i over the range
-  const uint16_t* src = x.dht + static_cast<size_t>(bh) * nqb * (kD * kD);
-  float acc[8][8];
+  for (int dt = 0; dt < 8; ++dt) {
+    if ((dt >> 2) != qh) continue;
 #pragma unroll
-  for (int u = 0; u < 8; ++u)
+    for (int r = 0; r < 4; ++r) {
+      const int key = 16 * kt + 4 * G + r;
+      slot[key * kD + 16 * dt + l16] = st.dk[dt][r];
+      slot[kBK * kD + key * kD + 16 * dt + l16] = st.dv[dt][r];
+    }
+  }
+  // sums of dH_i^T (chunk f = t + 512 u: 8 elements at 8 f) and dZ_i over the range
+  float acc[4][8];
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
 #pragma unroll
     for (int k = 0; k < 8; ++k) acc[u][k] = 0.f;
-  sum_tiles(acc, src, [&](int n) { return static_cast<int>(tl[n]); }, n0, n1, t);
+  sum_dh(acc, x.dht + static_cast<size_t>(bh) * nqb * (kD * kD), tl, n0, n1, t);
   float* sh = slot + 2 * kBK * kD;
 #pragma unroll
-  for (int u = 0; u < 8; ++u) {
-    const int f = t + 256 * u;
+  for (int u = 0; u < 4; ++u) {
+    const int f = t + kKvT * u;
     *reinterpret_cast<f32x4*>(sh + 8 * f) = f32x4{acc[u][0], acc[u][1], acc[u][2], acc[u][3]};
     *reinterpret_cast<f32x4*>(sh + 8 * f + 4) = f32x4{acc[u][4], acc[u][5], acc[u][6], acc[u][7]};
   }
-  if (t < kD) {
-    float s = 0.f;
-    s = sum_rows(x.dz + static_cast<size_t>(bh) * nqb * kD,
-                 [&](int n) { return static_cast<int>(tl[n]); }, n0, n1, t);
-    sh[kD * kD + t] = s;
-  }
+  if (t < kD)
+    sh[kD * kD + t] = sum_rows(x.dz + static_cast<size_t>(bh) * nqb * kD,
+                               [&](int n) { return static_cast<int>(tl[n]); }, n0, n1, t);
 }
 
 // Main work items: grid (nkb, BH) (XCD-aware order). Key block j: its first C keeping query
 // blocks, then the extra items' partials in item order, then the linear part; writes dK_s, dV
 // and the column sums of dK_s.
-__global__ __launch_bounds__(256) void bwd_kv_kernel(BwdArgs x) {
+__global__ __launch_bounds__(kKvT) void bwd_kv_kernel(BwdArgs x) {
   __shared__ __attribute__((aligned(16))) char smem[kKvLds];
-  const KvLds L = kv_lds(smem);
-  uint16_t* DH = L.Vs + kBK * kLd;   // dh_j^T [o][a]
-  float* dz_s = L.D_s + kBQ;         // [128]
-  float* crow = dz_s + kBQ;          // [2][64]
-  float* DKs = L.X;                  // [64][kXld]
-  float* DVs = L.X + kBK * kXld;     // [64][kXld]
+  uint16_t* PK = reinterpret_cast<uint16_t*>(smem + kOffPK);   // phi(K_s,j) [64][kLd]
+  uint16_t* DH = reinterpret_cast<uint16_t*>(smem + kOffDH);   // dh_j^T [o][a]
+  float* dz_s = reinterpret_cast<float*>(smem + kOffDz);        // [128]
+  float* crow = reinterpret_cast<float*>(smem + kOffCrow);      // [2][64]
+  float* kred = reinterpret_cast<float*>(smem + kOffKred);      // [4][128]
   int j, bh;
   xcd_block(x.nkb, x.BH, &j, &bh);
-  const int t = threadIdx.x, lane = t & 63, w = t >> 6, g = lane >> 5, l32 = lane & 31;
-  const int kt = w & 1, qh = w >> 1;
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6, G = lane >> 4, l16 = lane & 15;
+  const int kt = w & 3, qh = w >> 2;
   const int nqb = x.nqb, N = nqb * kBQ;
   const size_t head = static_cast<size_t>(bh) * N;
   const size_t krow0 = head + static_cast<size_t>(j) * kBK;
@@ -913,65 +957,65 @@ __global__ __launch_bounds__(256) void bwd_kv_kernel(BwdArgs x) {
   const int n1 = min(nT, C);
   const int nx = nT > C ? (nT + C - 1) / C - 1 : 0;
   const float* xs = x.xpart + (static_cast<size_t>(bh) * x.cap + x.xoff[static_cast<size_t>(bh) * x.nkb + j]) * kSlot;
-  stage_kv_block(x, krow0, L, t);
-  kv_sparse(x, head, tl, 0, n1, L, t, g, l32, kt, qh);
+  bf16x8 kop[4], vop[4];
+  load_kv_ops(x, krow0, kt, G, l16, kop, vop);
+  KvState st;
+  kv_sparse(x, head, tl, 0, n1, smem, kop, vop, st, t, lane, G, l16, kt, qh);
   // partials of the extra items (fixed order)
   for (int e = 0; e < nx; ++e) {
     const float* sl = xs + static_cast<size_t>(e) * kSlot;
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int f = t + 256 * u, r = f >> 5, c4 = 4 * (f & 31);
-      f32x4* pk = reinterpret_cast<f32x4*>(&DKs[r * kXld + c4]);
-      f32x4* pv = reinterpret_cast<f32x4*>(&DVs[r * kXld + c4]);
-      *pk = *pk + *reinterpret_cast<const f32x4*>(sl + r * kD + c4);
-      *pv = *pv + *reinterpret_cast<const f32x4*>(sl + kBK * kD + r * kD + c4);
+    for (int dt = 0; dt < 8; ++dt) {
+      if ((dt >> 2) != qh) continue;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int key = 16 * kt + 4 * G + r;
+        st.dk[dt][r] += sl[key * kD + 16 * dt + l16];
+        st.dv[dt][r] += sl[kBK * kD + key * kD + 16 * dt + l16];
+      }
     }
   }
-  // ---- linear part. phi(K_s,j) into Ks (thread: row t / 4, columns 32 (t % 4) .. +31)
+  // ---- linear part. phi(K_s,j) (thread: row t / 8, columns 16 (t % 8) .. +15)
   {
-    const int r = t >> 2, c0 = 32 * (t & 3);
-    float v[32];
+    const int r = t >> 3, c0 = 16 * (t & 7);
+    float v[16];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      float f8[8];
-      unpack_bf16x8(*reinterpret_cast<const i32x4*>(x.ksb + (krow0 + r) * kD + c0 + 8 * u), f8);
-#pragma unroll
-      for (int k = 0; k < 8; ++k) v[8 * u + k] = f8[k];
-    }
+    for (int u = 0; u < 2; ++u)
+      unpack_bf16x8(*reinterpret_cast<const i32x4*>(x.ksb + (krow0 + r) * kD + c0 + 8 * u), v + 8 * u);
     float mx = v[0];
 #pragma unroll
-    for (int k = 1; k < 32; ++k) mx = fmaxf(mx, v[k]);
+    for (int k = 1; k < 16; ++k) mx = fmaxf(mx, v[k]);
     mx = fmaxf(mx, __shfl_xor(mx, 1));
     mx = fmaxf(mx, __shfl_xor(mx, 2));
+    mx = fmaxf(mx, __shfl_xor(mx, 4));
     float s = 0.f;
 #pragma unroll
-    for (int k = 0; k < 32; ++k) {
+    for (int k = 0; k < 16; ++k) {
       v[k] = __expf(v[k] - mx);
       s += v[k];
     }
     s += __shfl_xor(s, 1);
     s += __shfl_xor(s, 2);
+    s += __shfl_xor(s, 4);
     const float inv = 1.0f / s;
 #pragma unroll
-    for (int k = 0; k < 32; ++k) v[k] *= inv;
-    __syncthreads();   // Ks no longer read by the sparse part
+    for (int k = 0; k < 16; ++k) v[k] *= inv;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) st_bf16x8(&L.Ks[r * kLd + c0 + 8 * u], v + 8 * u);
+    for (int u = 0; u < 2; ++u) st_bf16x8(&PK[r * kLd + c0 + 8 * u], v + 8 * u);
   }
-  // dh_j^T = dH_tot^T - sum over the keeping query blocks of dH_i^T (bf16 [o][a]); dz_j
+  // dh_j^T = dH_tot^T - sum over the keeping query blocks of dH_i^T; dz_j
   {
-    const uint16_t* src = x.dht + static_cast<size_t>(bh) * nqb * (kD * kD);
-    float acc[8][8];
+    float acc[4][8];
 #pragma unroll
-    for (int u = 0; u < 8; ++u)
+    for (int u = 0; u < 4; ++u)
 #pragma unroll
       for (int k = 0; k < 8; ++k) acc[u][k] = 0.f;
-    sum_tiles(acc, src, [&](int n) { return static_cast<int>(tl[n]); }, 0, n1, t);
+    sum_dh(acc, x.dht + static_cast<size_t>(bh) * nqb * (kD * kD), tl, 0, n1, t);
     for (int e = 0; e < nx; ++e) {
       const float* sh = xs + static_cast<size_t>(e) * kSlot + 2 * kBK * kD;
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int f = t + 256 * u;
+      for (int u = 0; u < 4; ++u) {
+        const int f = t + kKvT * u;
         const f32x4 a0 = *reinterpret_cast<const f32x4*>(sh + 8 * f);
         const f32x4 a1 = *reinterpret_cast<const f32x4*>(sh + 8 * f + 4);
 #pragma unroll
@@ -983,8 +1027,8 @@ __global__ __launch_bounds__(256) void bwd_kv_kernel(BwdArgs x) {
     }
     const float* tot = x.dhtot + static_cast<size_t>(bh) * (kD * kD);
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int f = t + 256 * u, o = f >> 4, a0 = 8 * (f & 15);
+    for (int u = 0; u < 4; ++u) {
+      const int f = t + kKvT * u, o = f >> 4, a0 = 8 * (f & 15);
       const f32x4 t0 = *reinterpret_cast<const f32x4*>(tot + 8 * f);
       const f32x4 t1 = *reinterpret_cast<const f32x4*>(tot + 8 * f + 4);
       float hv[8] = {t0[0], t0[1], t0[2], t0[3], t1[0], t1[1], t1[2], t1[3]};
@@ -993,75 +1037,79 @@ __global__ __launch_bounds__(256) void bwd_kv_kernel(BwdArgs x) {
       st_bf16x8(&DH[o * kLd + a0], hv);
     }
     if (t < kD) {
-      float s = 0.f;
-      s = sum_rows(x.dz + static_cast<size_t>(bh) * nqb * kD,
-                   [&](int n) { return static_cast<int>(tl[n]); }, 0, n1, t);
+      float s = sum_rows(x.dz + static_cast<size_t>(bh) * nqb * kD,
+                         [&](int n) { return static_cast<int>(tl[n]); }, 0, n1, t);
       for (int e = 0; e < nx; ++e) s += xs[static_cast<size_t>(e) * kSlot + 2 * kBK * kD + kD * kD + t];
       dz_s[t] = x.dztot[static_cast<size_t>(bh) * kD + t] - s;
     }
   }
   __syncthreads();
-  // dV += phi dh_j: keys 32 kt .. +31 (rows), o tiles 2 qh, 2 qh + 1 (lane = o)
+  // dV += phi dh_j (o tiles 4 qh .. +3); dphi = V dh_j^T + dz_j (a tiles 4 qh .. +3)
+  float cs[4] = {0.f, 0.f, 0.f, 0.f};
+  f32x4 dph[8];
 #pragma unroll
-  for (int ot = 2 * qh; ot < 2 * qh + 2; ++ot) {
-    f32x16 c = f32x16{};
+  for (int ot = 0; ot < 8; ++ot) {
+    dph[ot] = f32x4{};
+    if ((ot >> 2) != qh) continue;
+    f32x4 cv = f32x4{}, cp = f32x4{};
 #pragma unroll
-    for (int u = 0; u < 8; ++u)
-      c = mfma(ld_row8(&L.Ks[(32 * kt + l32) * kLd + 16 * u + 8 * g]),
-               ld_row8(&DH[(32 * ot + l32) * kLd + 16 * u + 8 * g]), c);
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int key = 32 * kt + 8 * (r >> 2) + 4 * g + (r & 3);
-      DVs[key * kXld + 32 * ot + l32] += c[r];
+    for (int c = 0; c < 4; ++c) {
+      cv = mfma16(ld_row8(&PK[(16 * kt + l16) * kLd + 32 * c + 8 * G]),
+                  ld_row8(&DH[(16 * ot + l16) * kLd + 32 * c + 8 * G]), cv);
+      cp = mfma16(vop[c], ld_col8n_16(DH, 16 * ot, 32 * c, G, lane), cp);
     }
+    st.dv[ot] += cv;
+    const int a = 16 * ot + l16;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int key = 16 * kt + 4 * G + r;
+      cp[r] += dz_s[a];
+      cs[r] += cp[r] * bf(PK[key * kLd + a]);
+    }
+    dph[ot] = cp;
   }
-  // dphi^T = dh_j V_j^T + dz_j: a tiles 2 qh, 2 qh + 1 (registers), keys 32 kt + lane
-  f32x16 dph[2];
-  float cs = 0.f;
-  const int key = 32 * kt + l32;
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int at = 2 * qh + h;
-    dph[h] = f32x16{};
-#pragma unroll
-    for (int u = 0; u < 8; ++u)
-      dph[h] = mfma(ld_col8(DH, 32 * at, 16 * u, g, lane),
-                    ld_row8(&L.Vs[key * kLd + 16 * u + 8 * g]), dph[h]);
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int a = 32 * at + 8 * (r >> 2) + 4 * g + (r & 3);
-      dph[h][r] += dz_s[a];
-      cs += dph[h][r] * bf(L.Ks[key * kLd + a]);
-    }
-  }
-  cs += __shfl_xor(cs, 32);
-  if (g == 0) crow[qh * kBK + key] = cs;
-  __syncthreads();
-  cs = crow[key] + crow[kBK + key];
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int at = 2 * qh + h;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int a = 32 * at + 8 * (r >> 2) + 4 * g + (r & 3);
-      DKs[key * kXld + a] += bf(L.Ks[key * kLd + a]) * (dph[h][r] - cs);
-    }
+  for (int r = 0; r < 4; ++r) {
+    cs[r] = row16_sum(cs[r]);
+    if (l16 == 0) crow[qh * kBK + 16 * kt + 4 * G + r] = cs[r];
   }
   __syncthreads();
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int key = 16 * kt + 4 * G + r;
+    cs[r] = crow[key] + crow[kBK + key];
+  }
+#pragma unroll
+  for (int at = 0; at < 8; ++at) {
+    if ((at >> 2) != qh) continue;
+    const int a = 16 * at + l16;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int key = 16 * kt + 4 * G + r;
+      st.dk[at][r] += bf(PK[key * kLd + a]) * (dph[at][r] - cs[r]);
+    }
+  }
   // ---- write dK_s, dV; column sums of dK_s for the centring
 #pragma unroll
-  for (int u = 0; u < 8; ++u) {
-    const int f = t + 256 * u, r = f >> 5, c4 = 4 * (f & 31);
-    *reinterpret_cast<f32x4*>(x.dK + (krow0 + r) * kD + c4) =
-        *reinterpret_cast<const f32x4*>(&DKs[r * kXld + c4]);
-    *reinterpret_cast<f32x4*>(x.dV + (krow0 + r) * kD + c4) =
-        *reinterpret_cast<const f32x4*>(&DVs[r * kXld + c4]);
+  for (int dt = 0; dt < 8; ++dt) {
+    if ((dt >> 2) != qh) continue;
+    const int d = 16 * dt + l16;
+    float cd = 0.f;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const size_t o = (krow0 + 16 * kt + 4 * G + r) * kD + d;
+      x.dK[o] = st.dk[dt][r];
+      x.dV[o] = st.dv[dt][r];
+      cd += st.dk[dt][r];
+    }
+    cd += __shfl_xor(cd, 16);
+    cd += __shfl_xor(cd, 32);
+    if (G == 0) kred[kt * kD + d] = cd;
   }
-  if (t < kD) {
-    float s = 0.f;
-    for (int r = 0; r < kBK; ++r) s += DKs[r * kXld + t];
-    x.kcol[(static_cast<size_t>(bh) * x.nkb + j) * kD + t] = s;
-  }
+  __syncthreads();
+  if (t < kD)
+    x.kcol[(static_cast<size_t>(bh) * x.nkb + j) * kD + t] =
+        (kred[t] + kred[kD + t]) + (kred[2 * kD + t] + kred[3 * kD + t]);
 }
 
 // ---------------------------------------------------------------- dh_total
@@ -1175,12 +1223,12 @@ hipError_t launch_bwd_q(const Geom& g, const BwdArgs& x, hipStream_t s) {
 }
 
 hipError_t launch_bwd_kv_extra(const Geom& g, const BwdArgs& x, hipStream_t s) {
-  hipLaunchKernelGGL(bwd_kv_extra_kernel, dim3(x.cap, g.BH), dim3(256), 0, s, x);
+  hipLaunchKernelGGL(bwd_kv_extra_kernel, dim3(x.cap, g.BH), dim3(kKvT), 0, s, x);
   return hipGetLastError();
 }
 
 hipError_t launch_bwd_kv(const Geom& g, const BwdArgs& x, hipStream_t s) {
-  hipLaunchKernelGGL(bwd_kv_kernel, dim3(g.nkb, g.BH), dim3(256), 0, s, x);
+  hipLaunchKernelGGL(bwd_kv_kernel, dim3(g.nkb, g.BH), dim3(kKvT), 0, s, x);
   return hipGetLastError();
 }
 
