@@ -470,7 +470,7 @@ __global__ __launch_bounds__(256) void bwd_lin_q_kernel(BwdArgs x) {
 }
 
 // ---------------------------------------------------------------- bwd_q
-// grid (nqb, BH) (XCD-aware order), 512 threads. MFMA 16x16x32 bf16 (A lane (G = lane / 16,
+// grid (nqb, BH), plain block order, 512 threads. MFMA 16x16x32 bf16 (A lane (G = lane / 16,
 // l = lane % 16): row l, k = 8 G .. +7; B: column l, same k; accumulator: column l, rows
 // 4 G .. +3). Wavefront w owns query rows 16 w .. +15 and holds S^T = K_s,j Q^T with the query
 // as column (lane) and the 64 keys in its four 16-row tiles, so row statistics are per lane
@@ -513,7 +513,8 @@ __global__ __launch_bounds__(kQThreads) __attribute__((amdgpu_waves_per_eu(4))) 
   __shared__ __attribute__((aligned(16))) uint16_t Vs[2][kBK * kLd];
   __shared__ float red[8];
   int i, bh;
-  xcd_block(x.nqb, x.BH, &i, &bh);
+  i = blockIdx.x;
+  bh = blockIdx.y;
   const int t = threadIdx.x, lane = t & 63, w = t >> 6, G = lane >> 4, l16 = lane & 15;
   const int N = x.nqb * kBQ, nkb = x.nkb;
   const size_t qb = static_cast<size_t>(bh) * x.nqb + i;
@@ -934,7 +935,8 @@ __global__ __launch_bounds__(kKvT) void bwd_kv_extra_kernel(BwdArgs x) {
                                [&](int n) { return static_cast<int>(tl[n]); }, n0, n1, t);
 }
 
-// Main work items: grid (nkb, BH) (XCD-aware order). Key block j: its first C keeping query
+// Main work items: grid (nkb, BH), plain block order (all XCDs on the same head at a time: its
+// Q and dO_s tiles, read once per keeping pair, stay in the shared cache). Key block j: its first C keeping query
 // blocks, then the extra items' partials in item order, then the linear part; writes dK_s, dV
 // and the column sums of dK_s.
 __global__ __launch_bounds__(kKvT) void bwd_kv_kernel(BwdArgs x) {
@@ -945,7 +947,8 @@ __global__ __launch_bounds__(kKvT) void bwd_kv_kernel(BwdArgs x) {
   float* crow = reinterpret_cast<float*>(smem + kOffCrow);      // [2][64]
   float* kred = reinterpret_cast<float*>(smem + kOffKred);      // [4][128]
   int j, bh;
-  xcd_block(x.nkb, x.BH, &j, &bh);
+  j = blockIdx.x;
+  bh = blockIdx.y;
   const int t = threadIdx.x, lane = t & 63, w = t >> 6, G = lane >> 4, l16 = lane & 15;
   const int kt = w & 3, qh = w >> 2;
   const int nqb = x.nqb, N = nqb * kBQ;
