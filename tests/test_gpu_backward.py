@@ -66,6 +66,17 @@ def test_backward_random_masks_with_empty_and_full_rows():
     check(q, k, v, mask, alpha, dO, "fp32", [(0, 0), (0, 1)])
 
 
+def test_backward_two_batches_fp32():
+    """B = 2 (alpha shared by the batches, dalpha per batch), fp32 inputs, N = 1024."""
+    B, H, N = 2, 2, 1024
+    q, k, v = W.random_qkv(96, B, H, N)
+    mask = W.random_mask(96, B, H, N // 128, N // 64, 0.25)
+    _, _, alpha = W.random_weights(96, H, N // 128, alpha_lo=0.1)
+    dO = W.grad_out(96, q.shape)
+    say("backward two batches")
+    check(q, k, v, mask, alpha, dO, "fp32", [(0, 1), (1, 0), (1, 1)])
+
+
 def test_backward_long_key_lists():
     """Key blocks kept by every query block (64 of them at N = 8192): their lists are cut into
     work items of 16 query blocks whose partial sums are added back in a fixed order."""
