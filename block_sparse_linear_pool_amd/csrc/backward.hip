@@ -111,30 +111,30 @@ __device__ inline int lanes_below(uint64_t m) {
 }
 
 // acc[u][k] += element 8 (t + 256 u) + k of the bf16 d x d tiles src + idx(n) d^2 for n in
-// [n0, n1), added in n order; two tiles' loads are issued together.
-template <typename Idx>
+// [n0, n1), added in n order; kF tiles' loads are issued together.
+template <int kF = 2, typename Idx>
 __device__ inline void sum_tiles(float (&acc)[8][8], const uint16_t* src, Idx idx, int n0, int n1,
                                  int t) {
   int n = n0;
-  for (; n + 1 < n1; n += 2) {
-    const uint16_t* a = src + static_cast<size_t>(idx(n)) * (kD * kD);
-    const uint16_t* b = src + static_cast<size_t>(idx(n + 1)) * (kD * kD);
-    i32x4 va[8], vb[8];
+  for (; n + kF - 1 < n1; n += kF) {
+    i32x4 v[kF][8];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      va[u] = *reinterpret_cast<const i32x4*>(a + 8 * (t + 256 * u));
-      vb[u] = *reinterpret_cast<const i32x4*>(b + 8 * (t + 256 * u));
+    for (int f = 0; f < kF; ++f) {
+      const uint16_t* a = src + static_cast<size_t>(idx(n + f)) * (kD * kD);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[f][u] = *reinterpret_cast<const i32x4*>(a + 8 * (t + 256 * u));
     }
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      float fa[8], fb[8];
-      unpack_bf16x8(va[u], fa);
-      unpack_bf16x8(vb[u], fb);
+    for (int f = 0; f < kF; ++f)
 #pragma unroll
-      for (int k = 0; k < 8; ++k) acc[u][k] = (acc[u][k] + fa[k]) + fb[k];
-    }
+      for (int u = 0; u < 8; ++u) {
+        float fa[8];
+        unpack_bf16x8(v[f][u], fa);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) acc[u][k] += fa[k];
+      }
   }
-  if (n < n1) {
+  for (; n < n1; ++n) {
     const uint16_t* a = src + static_cast<size_t>(idx(n)) * (kD * kD);
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
@@ -329,7 +329,7 @@ __global__ __launch_bounds__(256) void bwd_lin_q_kernel(BwdArgs x) {
     for (int u = 0; u < 8; ++u)
 #pragma unroll
       for (int k = 0; k < 8; ++k) acc[u][k] = 0.f;
-    sum_tiles(acc, hb, [&](int n) { return lst[n]; }, 0, ncnt, t);
+    sum_tiles<4>(acc, hb, [&](int n) { return lst[n]; }, 0, ncnt, t);
     const float* ht = x.htot + static_cast<size_t>(bh) * (kD * kD);   // H_tot [a][o]
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
@@ -444,27 +444,39 @@ __global__ __launch_bounds__(256) void bwd_lin_q_kernel(BwdArgs x) {
                      pack_bf16x2(num[mt][4 * k4 + 2], num[mt][4 * k4 + 3]));
   if (g == 0) ddl[q] = dden;
   __syncthreads();
-  // ---- dH_i^T [o][a] = sum_q dnum[q][o] a[q][a]: wavefront w owns o = 32 w .. +31
+  // ---- dH_i^T [o][a] = sum_q dnum[q][o] a[q][a]: wavefront w owns o = 32 w .. +31, staged as
+  // bf16 in the H_i^T tile (no longer read) and stored in 16-byte pieces
+#pragma unroll
+  for (int at = 0; at < 4; ++at) {
+    f32x16 c = f32x16{};
+#pragma unroll
+    for (int s = 0; s < 8; ++s)
+      c = mfma(ld_col8(DN, 32 * w, 16 * s, g, lane), ld_col8(As, 32 * at, 16 * s, g, lane), c);
+    const int a = 32 * at + l32;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int o = 32 * w + 8 * (r >> 2) + 4 * g + (r & 3);
+      Ht[o * kLd + a] = f32_to_bf16_rne(c[r]);
+    }
+  }
+  // dZ_i[a] = sum_q a[q][a] dden[q]: two threads per column, 64 query rows each
+  {
+    const int a = t & (kD - 1), h = t >> 7;
+    float s = 0.f;
+#pragma unroll 8
+    for (int r = 64 * h; r < 64 * h + 64; ++r) s += bf(As[r * kLd + a]) * ddl[r];
+    __syncthreads();   // Zs (no longer read) takes the second half's sums
+    if (h == 1) Zs[a] = s;
+    __syncthreads();
+    if (h == 0) x.dz[qb * kD + a] = s + Zs[a];
+  }
   {
     uint16_t* out = x.dht + qb * (kD * kD);
 #pragma unroll
-    for (int at = 0; at < 4; ++at) {
-      f32x16 c = f32x16{};
-#pragma unroll
-      for (int s = 0; s < 8; ++s)
-        c = mfma(ld_col8(DN, 32 * w, 16 * s, g, lane), ld_col8(As, 32 * at, 16 * s, g, lane), c);
-      const int a = 32 * at + l32;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int o = 32 * w + 8 * (r >> 2) + 4 * g + (r & 3);
-        out[o * kD + a] = f32_to_bf16_rne(c[r]);
-      }
+    for (int u = 0; u < 8; ++u) {
+      const int c = t + 256 * u, o = c >> 4, a0 = 8 * (c & 15);
+      *reinterpret_cast<i32x4*>(out + o * kD + a0) = *reinterpret_cast<const i32x4*>(&Ht[o * kLd + a0]);
     }
-  }
-  if (t < kD) {
-    float s = 0.f;
-    for (int r = 0; r < kBQ; ++r) s += bf(As[r * kLd + t]) * ddl[r];
-    x.dz[qb * kD + t] = s;
   }
   if (t == 0) x.dalpha[qb] = -((red[0] + red[1]) + (red[2] + red[3]));
 }
