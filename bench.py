@@ -39,13 +39,14 @@ def parse():
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run plain device copies of a known size (the calibration "
                          "workload for the FETCH_SIZE / WRITE_SIZE counters), then exit")
-    ap.add_argument("--op", choices=("forward", "router_soft", "sla1", "backward"),
+    ap.add_argument("--op", choices=("forward", "router_soft", "sla1", "backward", "fit_alpha"),
                     default="forward",
                     help="forward (default): the inference forward; router_soft: the SoftTop-k "
                          "router (training-time step 1); sla1: the earlier SLA mix O = O_s + "
                          "O_l Wo with the heuristic router (comparison workload); backward: "
-                         "the gradients dQ, dK, dV, dalpha for the router's mask; each prints "
-                         "its own JSON line")
+                         "the gradients dQ, dK, dV, dalpha for the router's mask; fit_alpha: "
+                         "the stage-1 alpha fit against full attention; each prints its own "
+                         "JSON line")
     ap.add_argument("--tau", type=float, default=0.1, help="SoftTop-k temperature (router_soft)")
     ap.add_argument("--quiet", action="store_true")
     return ap.parse_args()
@@ -405,6 +406,78 @@ def run_backward(args, w, q, k, v, wq, wk, alpha, keep):
     print(json.dumps(result), flush=True)
 
 
+def run_fit_alpha(args, w, q, k, v, wq, wk, keep):
+    """Times sla2_fit_alpha on the taps of this workload: O_full from sla2_forward with every
+    block kept, O_s and O_l from sla2_forward with the router (both computed once, before the
+    timed region)."""
+    import numpy as np
+    import torch
+
+    from block_sparse_linear_pool_amd import sla2
+
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    dev = torch.device("cuda:0")
+    gq, gk, gv = (torch.from_numpy(a).to(dev, dt) for a in (q, k, v))
+    eye = torch.eye(w.d, device=dev).expand(w.H, w.d, w.d).contiguous()
+    ones = torch.ones((w.H, w.n_qb), device=dev)
+    ws = sla2.workspace_for(gq)
+    o_full = sla2.sla2_forward(gq, gk, gv, eye, eye, ones, 1.0, workspace=ws)
+    _, taps = sla2.sla2_forward(gq, gk, gv, torch.from_numpy(wq).to(dev),
+                                torch.from_numpy(wk).to(dev), ones, keep, taps=("O_s", "O_l"),
+                                workspace=ws)
+    o_s, o_l = taps["O_s"], taps["O_l"]
+    alpha = torch.empty((w.H, w.n_qb), device=dev)
+    del ws, gq, gk, gv
+    for _ in range(args.warmup):
+        sla2.sla2_fit_alpha(o_full, o_s, o_l, out=alpha)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        sla2.sla2_fit_alpha(o_full, o_s, o_l, out=alpha)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    E = w.B * w.H * w.N * w.d
+    nbytes = 3 * E * 4 + w.H * w.n_qb * 4
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    a = alpha.cpu().numpy()
+    result = {
+        "metric": "SLA2 stage-1 alpha fit GB/s, N=32768 H=12 d=128 @97%",
+        "value": round(gbs, 1), "unit": "GB/s (three fp32 [B,H,N,d] tensors read)",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f64",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d,
+                   "input_dtype": w.dtype, "keep_frac": keep,
+                   "alpha_mean": round(float(a.mean()), 4),
+                   "alpha_range": [round(float(a.min()), 4), round(float(a.max()), 4)]},
+        "roofline": {"kernel": "fit_alpha", "bound": "hbm", "achieved": round(gbs, 1),
+                     "peak": 8000.0, "unit": "GB/s", "frac": round(gbs / 8000.0, 4),
+                     "traffic": None, "avg_launch_ms": round(ms, 5)},
+    }
+    if not args.no_cpu:
+        from threadpoolctl import threadpool_limits
+
+        from oracle import sla2_fit as oracle_fit
+        cores = min(16, len(os.sched_getaffinity(0)))
+        heads = list(range(min(4, w.H)))
+        f, s_, l_ = (t[:, heads].cpu().numpy() for t in (o_full, o_s, o_l))
+        with threadpool_limits(limits=cores):
+            t0 = time.perf_counter()
+            reps = 0
+            while time.perf_counter() - t0 < 10.0:
+                oracle_fit.fit_alpha(f, s_, l_)
+                reps += 1
+            dt_cpu = time.perf_counter() - t0
+        result["cpu_baseline"] = {
+            "value": round(3 * f.size * 4 * reps / dt_cpu / 1e9, 2), "unit": "GB/s",
+            "cores": cores, "kind": "oracle",
+            "sample": f"batch 0, heads {heads[0]}-{heads[-1]} of {w.H}, fp64 oracle fit, "
+                      f"{reps} repetitions in {dt_cpu:.1f} s"}
+    print(json.dumps(result), flush=True)
+
+
 def main():
     args = parse()
     if args.copy_probe:
@@ -452,6 +525,10 @@ def main():
     if args.op == "backward":
         del gq, gk, gv, out, ws
         run_backward(args, w, q, k, v, wq, wk, alpha, keep)
+        return
+    if args.op == "fit_alpha":
+        del gq, gk, gv, out, ws
+        run_fit_alpha(args, w, q, k, v, wq, wk, keep)
         return
 
     def step(events=None):

@@ -8,6 +8,7 @@
 
 #include "../../include/sla2.h"
 #include "sla2_common.h"
+#include "sla2_fit.h"
 
 using namespace sla2;
 
@@ -613,6 +614,22 @@ sla2_status sla2_backward(const sla2_shape* shape, const void* Q, const void* K,
   SLA2_LAUNCH(launch_bwd_kv_extra(g, b, stream));
   SLA2_LAUNCH(launch_bwd_kv(g, b, stream));
   SLA2_LAUNCH(launch_dk_center(g, b, stream));
+  return SLA2_OK;
+}
+
+sla2_status sla2_fit_alpha(const sla2_shape* shape, const float* O_full, const float* O_s,
+                           const float* O_l, float* alpha, void* stream_) {
+  Geom g;
+  sla2_status st = check_shape(shape, &g);
+  if (st != SLA2_OK) return st;
+  PtrCheck pc;
+  pc.req(O_full); pc.req(O_s); pc.req(O_l); pc.req(alpha);
+  if (pc.st != SLA2_OK) return pc.st;
+  if ((st = check_device()) != SLA2_OK) return st;
+  hipStream_t stream = static_cast<hipStream_t>(stream_);
+  if (launch_fit_alpha(g.B, g.H, g.N, O_full, O_s, O_l, alpha, stream) != hipSuccess)
+    return SLA2_ERR_HIP;
+  if (debug_sync() && hipStreamSynchronize(stream) != hipSuccess) return SLA2_ERR_HIP;
   return SLA2_OK;
 }
 

@@ -90,8 +90,10 @@ def lib():
                                              vp, ctypes.POINTER(Taps), vp, sz, vp]
         L.sla2_backward.argtypes = [ctypes.POINTER(Shape), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                     ctypes.POINTER(vp), vp, sz, vp]
+        L.sla2_fit_alpha.argtypes = [ctypes.POINTER(Shape), vp, vp, vp, vp, vp]
         for name in ("sla2_router", "sla2_router_soft", "sla2_linear_precompute", "sla2_forward",
-                     "sla2_forward_sla1", "sla2_forward_with_mask", "sla2_backward"):
+                     "sla2_forward_sla1", "sla2_forward_with_mask", "sla2_backward",
+                     "sla2_fit_alpha"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -337,3 +339,17 @@ def sla2_backward(q, k, v, mask, alpha, grad_out, out=None, workspace=None, even
                              _ptr(out[2]), _ptr(out[3]), evs, _ptr(ws), ws.numel(), _stream(dev))
     _check(st, "sla2_backward")
     return out
+
+
+def sla2_fit_alpha(o_full, o_s, o_l, out=None):
+    """Stage-1 alpha fit: [H, N/128] fp32 alpha minimising the MSE of alpha O_s + (1 - alpha) O_l
+    against O_full (all [B,H,N,d] fp32), clipped to [0, 1]."""
+    _contig(o_full, o_s, o_l, out)
+    B, H, N, d = o_s.shape
+    shp = Shape(B, H, N, d, SLA2_FP32)
+    a = out if out is not None else torch.empty((H, N // 128), dtype=torch.float32,
+                                                device=o_s.device)
+    st = lib().sla2_fit_alpha(ctypes.byref(shp), _ptr(o_full), _ptr(o_s), _ptr(o_l), _ptr(a),
+                              _stream(o_s.device))
+    _check(st, "sla2_fit_alpha")
+    return a

@@ -219,6 +219,20 @@ sla2_status sla2_backward(const sla2_shape *shape, const void *Q, const void *K,
                           float *dK, float *dV, float *dalpha, void **stage_events,
                           void *workspace, size_t workspace_bytes, void *stream);
 
+/* Stage-1 alpha fit, the alpha part ("SLA2: Sparse-Linear Attention v2 for Diffusion
+ * Transformers", §4 six checks item 5: alpha is fitted with an MSE loss against full attention;
+ * §3 mixing, §4 check 2: alpha in [0, 1]). With the router (the block mask) fixed the output is
+ * affine in alpha, so the MSE of each (head, query block) over its 128 rows, d columns and all B
+ * batches is minimised by
+ *   alpha[h][i] = clip(<O_full - O_l, O_s - O_l> / |O_s - O_l|^2, 0, 1)   (1 where O_s = O_l).
+ *   O_full [B,H,N,d] fp32, the full-attention target (e.g. sla2_forward at keep_frac = 1)
+ *   O_s, O_l [B,H,N,d] fp32, the branch outputs under the mask (sla2_taps.O_s, O_l)
+ *   alpha  [H,N/128] fp32 output
+ * shape->dtype is not used (all four arrays are fp32). fp64 accumulation, fixed order
+ * (deterministic). No workspace. The router part of stage 1 is not provided. */
+sla2_status sla2_fit_alpha(const sla2_shape *shape, const float *O_full, const float *O_s,
+                           const float *O_l, float *alpha, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

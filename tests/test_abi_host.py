@@ -29,7 +29,7 @@ def test_library_exports_every_declared_symbol():
     assert set(names) == {"sla2_blocks_kept", "sla2_workspace_bytes", "sla2_status_string",
                           "sla2_router", "sla2_router_soft", "sla2_linear_precompute",
                           "sla2_forward", "sla2_forward_sla1", "sla2_forward_with_mask",
-                          "sla2_backward"}
+                          "sla2_backward", "sla2_fit_alpha"}
     for n in names:
         assert hasattr(L, n), n
 
@@ -140,6 +140,10 @@ def test_other_entry_points_validate():
     assert bwd(ctypes.byref(s), A, A, A, A, A, A, A, A, A, A, None, A, need - 1, None) == WS
     assert bwd(ctypes.byref(shape(N=200)), A, A, A, A, A, A, A, A, A, A, None, A, need,
                None) == SHAPE
+    fa = L.sla2_fit_alpha
+    assert fa(ctypes.byref(s), A, A, None, A, None) == NULL
+    assert fa(ctypes.byref(s), A, MIS, A, A, None) == MISAL
+    assert fa(ctypes.byref(shape(N=100)), A, A, A, A, None) == SHAPE
 
 
 def test_valid_arguments_reach_the_device_check_without_a_gpu():
