@@ -28,7 +28,9 @@
 //                writes dK_s and per-key-block column sums of it
 //   dk_mean      column mean of dK_s per head; dk_center: dK = dK_s - mean (K smoothing)
 //
-// MFMA: v_mfma_f32_32x32x16_bf16. Operand A lane (g = lane / 32, l = lane % 32) holds row l,
+// MFMA (bwd_lin_q; bwd_q and bwd_kv use the 16x16x32 form described at bwd_q, with the same
+// accumulator-as-operand idea): v_mfma_f32_32x32x16_bf16. Operand A lane (g = lane / 32,
+// l = lane % 32) holds row l,
 // k = 8 g .. 8 g + 7; B holds column l, the same k; the accumulator holds column l and rows
 // 8 (r / 4) + 4 g + r % 4 in register r. So an accumulator C (M x N) serves directly as the B
 // operand of X C or the A operand of C^T Y (both contract over M), with k taken in register
