@@ -158,3 +158,26 @@ def test_backward_benchmark_size_and_determinism():
         errs = [rel_l2(x[b, h], r[n]) for x, n in zip(got, NAMES)]
         say(f"  b{b} h{h}: " + ", ".join(f"{n} {e:.2e}" for n, e in zip(NAMES, errs)))
         assert max(errs) <= TOL
+
+
+@pytest.mark.timeout(900)
+def test_backward_wan14b_full_size():
+    """The largest shape: B = 1, H = 40, N = 75648 (591 query blocks, 1182 key blocks), 5 %
+    kept, the router's mask; every head in one call, one head against the oracle."""
+    w = W.WORKLOADS["wan14b_720p_N75648"]
+    q, k, v = W.generate(w)
+    wq, wk, alpha = W.weights(w)
+    t = TDT[w.dtype]
+    g = [dev(q, t), dev(k, t), dev(v, t)]
+    _, mask, _ = sla2.sla2_router(g[0], g[1], dev(wq), dev(wk), w.keep_frac[0])
+    dO = W.grad_out(w.seed, q.shape)
+    got = [host(x) for x in sla2.sla2_backward(*g, mask, dev(alpha), dev(dO))]
+    for x in got:
+        assert np.isfinite(x).all()
+    mask = host(mask)
+    b, h = 0, 27
+    say("backward wan14b: oracle on one head")
+    r = bw.backward(q[b, h], k[b, h], v[b, h], mask[b, h], alpha[h], dO[b, h])
+    errs = [rel_l2(x[b, h], r[n]) for x, n in zip(got, NAMES)]
+    say(f"  b{b} h{h}: " + ", ".join(f"{n} {e:.2e}" for n, e in zip(NAMES, errs)))
+    assert max(errs) <= TOL
