@@ -864,29 +864,30 @@ __device__ inline void load_kv_ops(const BwdArgs& x, size_t krow0, int kt, int G
 }
 
 // sum over n in [n0, n1) of the bf16 dH_i^T tiles of query blocks tl[n] (thread: chunks
-// t + 512 u, u < 4), two tiles in flight
+// t + 512 u, u < 4), added in n order, four tiles' loads in flight
 __device__ inline void sum_dh(float (&acc)[4][8], const uint16_t* src, const uint16_t* tl, int n0,
                               int n1, int t) {
+  constexpr int kF = 4;
   int n = n0;
-  for (; n + 1 < n1; n += 2) {
-    const uint16_t* a = src + static_cast<size_t>(tl[n]) * (kD * kD);
-    const uint16_t* b = src + static_cast<size_t>(tl[n + 1]) * (kD * kD);
-    i32x4 va[4], vb[4];
+  for (; n + kF - 1 < n1; n += kF) {
+    i32x4 v[kF][4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      va[u] = *reinterpret_cast<const i32x4*>(a + 8 * (t + kKvT * u));
-      vb[u] = *reinterpret_cast<const i32x4*>(b + 8 * (t + kKvT * u));
+    for (int f = 0; f < kF; ++f) {
+      const uint16_t* a = src + static_cast<size_t>(tl[n + f]) * (kD * kD);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) v[f][u] = *reinterpret_cast<const i32x4*>(a + 8 * (t + kKvT * u));
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      float fa[8], fb[8];
-      unpack_bf16x8(va[u], fa);
-      unpack_bf16x8(vb[u], fb);
+    for (int f = 0; f < kF; ++f)
 #pragma unroll
-      for (int k = 0; k < 8; ++k) acc[u][k] = (acc[u][k] + fa[k]) + fb[k];
-    }
+      for (int u = 0; u < 4; ++u) {
+        float fa[8];
+        unpack_bf16x8(v[f][u], fa);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) acc[u][k] += fa[k];
+      }
   }
-  if (n < n1) {
+  for (; n < n1; ++n) {
     const uint16_t* a = src + static_cast<size_t>(tl[n]) * (kD * kD);
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
@@ -978,6 +979,23 @@ __global__ __launch_bounds__(kKvT) void bwd_kv_kernel(BwdArgs x) {
   load_kv_ops(x, krow0, kt, G, l16, kop, vop);
   KvState st;
   kv_sparse(x, head, tl, 0, n1, smem, kop, vop, st, t, lane, G, l16, kt, qh);
+  // the linear part's independent loads, issued together before they are needed: the K_s
+  // rows for phi (thread: row t / 8, columns 16 (t % 8) .. +15) and dH_tot^T (chunks t + 512 u)
+  i32x4 kraw[2];
+  f32x4 tot4[4][2];
+  {
+    const int r = t >> 3, c0 = 16 * (t & 7);
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+      kraw[u] = *reinterpret_cast<const i32x4*>(x.ksb + (krow0 + r) * kD + c0 + 8 * u);
+    const float* tot = x.dhtot + static_cast<size_t>(bh) * (kD * kD);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int f = t + kKvT * u;
+      tot4[u][0] = *reinterpret_cast<const f32x4*>(tot + 8 * f);
+      tot4[u][1] = *reinterpret_cast<const f32x4*>(tot + 8 * f + 4);
+    }
+  }
   // partials of the extra items (fixed order)
   for (int e = 0; e < nx; ++e) {
     const float* sl = xs + static_cast<size_t>(e) * kSlot;
@@ -992,13 +1010,12 @@ __global__ __launch_bounds__(kKvT) void bwd_kv_kernel(BwdArgs x) {
       }
     }
   }
-  // ---- linear part. phi(K_s,j) (thread: row t / 8, columns 16 (t % 8) .. +15)
+  // ---- linear part. phi(K_s,j)
   {
     const int r = t >> 3, c0 = 16 * (t & 7);
     float v[16];
 #pragma unroll
-    for (int u = 0; u < 2; ++u)
-      unpack_bf16x8(*reinterpret_cast<const i32x4*>(x.ksb + (krow0 + r) * kD + c0 + 8 * u), v + 8 * u);
+    for (int u = 0; u < 2; ++u) unpack_bf16x8(kraw[u], v + 8 * u);
     float mx = v[0];
 #pragma unroll
     for (int k = 1; k < 16; ++k) mx = fmaxf(mx, v[k]);
@@ -1042,12 +1059,10 @@ __global__ __launch_bounds__(kKvT) void bwd_kv_kernel(BwdArgs x) {
         }
       }
     }
-    const float* tot = x.dhtot + static_cast<size_t>(bh) * (kD * kD);
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int f = t + kKvT * u, o = f >> 4, a0 = 8 * (f & 15);
-      const f32x4 t0 = *reinterpret_cast<const f32x4*>(tot + 8 * f);
-      const f32x4 t1 = *reinterpret_cast<const f32x4*>(tot + 8 * f + 4);
+      const f32x4 t0 = tot4[u][0], t1 = tot4[u][1];
       float hv[8] = {t0[0], t0[1], t0[2], t0[3], t1[0], t1[1], t1[2], t1[3]};
 #pragma unroll
       for (int k = 0; k < 8; ++k) hv[k] -= acc[u][k];
