@@ -181,3 +181,16 @@ def test_backward_wan14b_full_size():
     errs = [rel_l2(x[b, h], r[n]) for x, n in zip(got, NAMES)]
     say(f"  b{b} h{h}: " + ", ".join(f"{n} {e:.2e}" for n, e in zip(NAMES, errs)))
     assert max(errs) <= TOL
+
+
+@pytest.mark.parametrize("row", [(1, 0), (0, 1), (1, 1), (0, 0)])
+def test_backward_smallest_shape(row):
+    """N = 128: one query block, two key blocks, every mask row (one kept, the other kept,
+    both kept: no linear branch, none kept: no sparse branch); bf16 inputs."""
+    B, H, N = 1, 1, 128
+    q, k, v = W.random_qkv(97, B, H, N, dtype="bf16")
+    mask = np.array(row, np.uint8).reshape(1, 1, 1, 2)
+    alpha = np.full((H, 1), 0.6, np.float32)
+    dO = W.grad_out(97, q.shape)
+    say("backward N=128, mask row", row)
+    check(q, k, v, mask, alpha, dO, "bf16", [(0, 0)])
