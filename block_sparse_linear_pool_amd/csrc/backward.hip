@@ -1191,8 +1191,17 @@ __global__ __launch_bounds__(1024) void dk_mean_kernel(const float* __restrict__
   __shared__ float part[8][kD];
   const int bh = blockIdx.x, t = threadIdx.x, col = t & 127, grp = t >> 7;
   const float* src = kcol + static_cast<size_t>(bh) * nkb * kD + col;
+  // key blocks grp, grp + 8, ... in order; eight loads in flight
   float s = 0.f;
-  for (int j = grp; j < nkb; j += 8) s += src[static_cast<size_t>(j) * kD];
+  int j = grp;
+  for (; j + 56 < nkb; j += 64) {
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = src[static_cast<size_t>(j + 8 * u) * kD];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) s += v[u];
+  }
+  for (; j < nkb; j += 8) s += src[static_cast<size_t>(j) * kD];
   part[grp][col] = s;
   __syncthreads();
   if (t < kD) {
