@@ -31,7 +31,10 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="wan13b_480p_N32768")
     ap.add_argument("--keep", type=float, default=None, help="kept fraction (default: workload's)")
-    ap.add_argument("--cpu-heads", type=int, default=2, help="heads in the CPU-oracle sample")
+    ap.add_argument("--cpu-heads", type=int, default=2,
+                    help="fewest heads in the CPU-oracle sample")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="the CPU-oracle sample takes heads 0, 1, ... until at least this long")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--traffic", default=None,
                     help="JSON with the measured HBM bytes per launch of the dominant kernel "
@@ -85,6 +88,17 @@ def log(args, *a):
         print(*a, file=sys.stderr, flush=True)
 
 
+def timed_heads(args, w, work):
+    """Run work(h) for heads 0, 1, ... of batch 0 until at least args.cpu_seconds have passed
+    (at least args.cpu_heads heads, at most all of them); returns (heads done, seconds)."""
+    t0 = time.perf_counter()
+    h = 0
+    while h < w.H and (h < args.cpu_heads or time.perf_counter() - t0 < args.cpu_seconds):
+        work(h)
+        h += 1
+    return list(range(h)), time.perf_counter() - t0
+
+
 def cpu_baseline(args, w, q, k, v, wq, wk, alpha, keep, acc):
     """Time the fp64 oracle (as it stands) on the first heads of batch 0."""
     import numpy as np
@@ -93,14 +107,10 @@ def cpu_baseline(args, w, q, k, v, wq, wk, alpha, keep, acc):
     from oracle import sla2 as oracle
 
     cores = min(16, len(os.sched_getaffinity(0)))
-    heads = list(range(min(args.cpu_heads, w.H)))
     with threadpool_limits(limits=cores):
-        t0 = time.perf_counter()
-        for h in heads:
-            oracle.forward_head(q[0, h].astype(np.float64), k[0, h].astype(np.float64),
-                                v[0, h].astype(np.float64), wq[h], wk[h], alpha[h], keep,
-                                quant=True)
-        dt = time.perf_counter() - t0
+        heads, dt = timed_heads(args, w, lambda h: oracle.forward_head(
+            q[0, h].astype(np.float64), k[0, h].astype(np.float64), v[0, h].astype(np.float64),
+            wq[h], wk[h], alpha[h], keep, quant=True))
     flops = 4.0 * w.N * w.N * w.d * len(heads)
     return {
         "value": flops / dt / 1e12,
@@ -189,17 +199,16 @@ def run_router_soft(args, w, q, k, wq, wk, keep):
 
         from oracle import sla2 as oracle
         cores = min(16, len(os.sched_getaffinity(0)))
-        heads = list(range(min(args.cpu_heads, w.H)))
+
+        def one_head(h):
+            K = k[0, h].astype(np.float64)
+            mu, mu32 = oracle.colmean(K)
+            _, P = oracle.router_scores(oracle.block_mean(q[0, h].astype(np.float64), 128),
+                                        oracle.block_mean(oracle.smooth_k(K, mu32), 64),
+                                        wq[h], wk[h])
+            oracle.soft_topk(P, kb, args.tau)
         with threadpool_limits(limits=cores):
-            t0 = time.perf_counter()
-            for h in heads:
-                K = k[0, h].astype(np.float64)
-                mu, mu32 = oracle.colmean(K)
-                _, P = oracle.router_scores(oracle.block_mean(q[0, h].astype(np.float64), 128),
-                                            oracle.block_mean(oracle.smooth_k(K, mu32), 64),
-                                            wq[h], wk[h])
-                oracle.soft_topk(P, kb, args.tau)
-            dt_cpu = time.perf_counter() - t0
+            heads, dt_cpu = timed_heads(args, w, one_head)
         result["cpu_baseline"] = {
             "value": round(len(heads) * w.n_qb / dt_cpu, 1), "unit": "query-block rows/s",
             "cores": cores, "kind": "oracle",
@@ -283,14 +292,11 @@ def run_sla1(args, w, q, k, v, keep):
 
         from oracle import sla2 as oracle
         cores = min(16, len(os.sched_getaffinity(0)))
-        heads = list(range(min(args.cpu_heads, w.H)))
         wo_h = wo.cpu().numpy()
         with threadpool_limits(limits=cores):
-            t0 = time.perf_counter()
-            for h in heads:
-                oracle.forward_head_sla1(q[0, h].astype(np.float64), k[0, h].astype(np.float64),
-                                         v[0, h].astype(np.float64), wo_h[h], keep)
-            dt_cpu = time.perf_counter() - t0
+            heads, dt_cpu = timed_heads(args, w, lambda h: oracle.forward_head_sla1(
+                q[0, h].astype(np.float64), k[0, h].astype(np.float64),
+                v[0, h].astype(np.float64), wo_h[h], keep))
         result["cpu_baseline"] = {
             "value": round(4.0 * w.N * w.N * w.d * len(heads) / dt_cpu / 1e12, 4),
             "unit": "TFLOPS (full-attention-equivalent)", "cores": cores, "kind": "oracle",
@@ -390,13 +396,10 @@ def run_backward(args, w, q, k, v, wq, wk, alpha, keep):
 
         from oracle import sla2_backward as oracle_bw
         cores = min(16, len(os.sched_getaffinity(0)))
-        heads = list(range(min(args.cpu_heads, w.H)))
         mask_h = mask.cpu().numpy()
         with threadpool_limits(limits=cores):
-            t0 = time.perf_counter()
-            for h in heads:
-                oracle_bw.backward(q[0, h], k[0, h], v[0, h], mask_h[0, h], alpha[h], dO_h[0, h])
-            dt_cpu = time.perf_counter() - t0
+            heads, dt_cpu = timed_heads(args, w, lambda h: oracle_bw.backward(
+                q[0, h], k[0, h], v[0, h], mask_h[0, h], alpha[h], dO_h[0, h]))
         result["cpu_baseline"] = {
             "value": round(10.0 * w.N * w.N * w.d * len(heads) / dt_cpu / 1e12, 4),
             "unit": "TFLOPS (full-attention-backward-equivalent)", "cores": cores,
