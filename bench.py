@@ -89,14 +89,23 @@ def log(args, *a):
 
 
 def timed_heads(args, w, work):
-    """Run work(h) for heads 0, 1, ... of batch 0 until at least args.cpu_seconds have passed
-    (at least args.cpu_heads heads, at most all of them); returns (heads done, seconds)."""
+    """Run work(h) for heads 0, 1, ... of batch 0 (starting over after the last head) until at
+    least args.cpu_seconds have passed and at least args.cpu_heads heads were done; returns
+    (the heads done, in order, with repeats; seconds)."""
     t0 = time.perf_counter()
-    h = 0
-    while h < w.H and (h < args.cpu_heads or time.perf_counter() - t0 < args.cpu_seconds):
+    done = []
+    while len(done) < args.cpu_heads or time.perf_counter() - t0 < args.cpu_seconds:
+        h = len(done) % w.H
         work(h)
-        h += 1
-    return list(range(h)), time.perf_counter() - t0
+        done.append(h)
+    return done, time.perf_counter() - t0
+
+
+def heads_text(heads, w):
+    """'heads 0-6 of 12', or 'heads 0-11 of 12 (30 head passes)' when the sample went round."""
+    top = min(len(heads), w.H) - 1
+    text = f"heads 0-{top} of {w.H}"
+    return text + (f" ({len(heads)} head passes)" if len(heads) > w.H else "")
 
 
 def cpu_baseline(args, w, q, k, v, wq, wk, alpha, keep, acc):
@@ -117,7 +126,7 @@ def cpu_baseline(args, w, q, k, v, wq, wk, alpha, keep, acc):
         "unit": "TFLOPS (full-attention-equivalent)",
         "cores": cores,
         "kind": "oracle",
-        "sample": f"batch 0, heads {heads[0]}-{heads[-1]} of {w.H} ({len(heads)}/{w.B * w.H} of one "
+        "sample": f"batch 0, {heads_text(heads, w)} ({len(heads)}/{w.B * w.H} of one "
                   f"call), fp64 numpy oracle with quantisation, {dt:.1f} s; "
                   f"ms/call extrapolated {dt * 1e3 * w.B * w.H / len(heads):.0f}",
         "cpu": platform.processor() or platform.machine(),
@@ -212,7 +221,7 @@ def run_router_soft(args, w, q, k, wq, wk, keep):
         result["cpu_baseline"] = {
             "value": round(len(heads) * w.n_qb / dt_cpu, 1), "unit": "query-block rows/s",
             "cores": cores, "kind": "oracle",
-            "sample": f"batch 0, heads {heads[0]}-{heads[-1]} of {w.H}: the oracle's router up to "
+            "sample": f"batch 0, {heads_text(heads, w)}: the oracle's router up to "
                       f"P_c and its fp64-bisection SoftTop-k, {dt_cpu:.2f} s"}
     print(json.dumps(result), flush=True)
 
@@ -300,7 +309,7 @@ def run_sla1(args, w, q, k, v, keep):
         result["cpu_baseline"] = {
             "value": round(4.0 * w.N * w.N * w.d * len(heads) / dt_cpu / 1e12, 4),
             "unit": "TFLOPS (full-attention-equivalent)", "cores": cores, "kind": "oracle",
-            "sample": f"batch 0, heads {heads[0]}-{heads[-1]} of {w.H}, fp64 oracle, {dt_cpu:.1f} s"}
+            "sample": f"batch 0, {heads_text(heads, w)}, fp64 oracle, {dt_cpu:.1f} s"}
     print(json.dumps(result), flush=True)
 
 
@@ -404,7 +413,7 @@ def run_backward(args, w, q, k, v, wq, wk, alpha, keep):
             "value": round(10.0 * w.N * w.N * w.d * len(heads) / dt_cpu / 1e12, 4),
             "unit": "TFLOPS (full-attention-backward-equivalent)", "cores": cores,
             "kind": "oracle",
-            "sample": f"batch 0, heads {heads[0]}-{heads[-1]} of {w.H}, fp64 oracle backward, "
+            "sample": f"batch 0, {heads_text(heads, w)}, fp64 oracle backward, "
                       f"{dt_cpu:.1f} s"}
     print(json.dumps(result), flush=True)
 
