@@ -28,8 +28,8 @@
 //                writes dK_s and per-key-block column sums of it
 //   dk_mean      column mean of dK_s per head; dk_center: dK = dK_s - mean (K smoothing)
 //
-// MFMA (bwd_lin_q; bwd_q and bwd_kv use the 16x16x32 form described at bwd_q, with the same
-// accumulator-as-operand idea): v_mfma_f32_32x32x16_bf16. Operand A lane (g = lane / 32,
+// MFMA: the sparse and linear kernels use v_mfma_f32_16x16x32_bf16 (layout at the helpers
+// below). The idea, shown here for its 32x32x16 form: v_mfma_f32_32x32x16_bf16. Operand A lane (g = lane / 32,
 // l = lane % 32) holds row l,
 // k = 8 g .. 8 g + 7; B holds column l, the same k; the accumulator holds column l and rows
 // 8 (r / 4) + 4 g + r % 4 in register r. So an accumulator C (M x N) serves directly as the B
@@ -163,6 +163,84 @@ __device__ inline float sum_rows(const float* src, Idx idx, int n0, int n1, int 
   return s;
 }
 
+// sum over n in [n0, n1) of the bf16 d x d tiles src + idx(n) d^2 (thread: chunks t + 512 u,
+// u < 4), added in n order, four tiles' loads in flight
+template <typename Idx>
+__device__ inline void sum_tiles512(float (&acc)[4][8], const uint16_t* src, Idx idx, int n0,
+                                    int n1, int t) {
+  constexpr int kF = 4;
+  int n = n0;
+  for (; n + kF - 1 < n1; n += kF) {
+    i32x4 v[kF][4];
+#pragma unroll
+    for (int f = 0; f < kF; ++f) {
+      const uint16_t* a = src + static_cast<size_t>(idx(n + f)) * (kD * kD);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) v[f][u] = *reinterpret_cast<const i32x4*>(a + 8 * (t + 512 * u));
+    }
+#pragma unroll
+    for (int f = 0; f < kF; ++f)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        float fa[8];
+        unpack_bf16x8(v[f][u], fa);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) acc[u][k] += fa[k];
+      }
+  }
+  for (; n < n1; ++n) {
+    const uint16_t* a = src + static_cast<size_t>(idx(n)) * (kD * kD);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      float fa[8];
+      unpack_bf16x8(*reinterpret_cast<const i32x4*>(a + 8 * (t + 512 * u)), fa);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) acc[u][k] += fa[k];
+    }
+  }
+}
+
+// ---- 16x16x32 MFMA helpers (A lane (G = lane / 16, l = lane % 16): row l, k = 8 G .. +7; B:
+// column l, same k; accumulator: column l, rows 4 G .. +3)
+__device__ inline f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+// two accumulator tiles (rows 0-15 and 16-31 of a 32-deep k chunk) as a bf16 operand:
+// element i of lane group G is row 4 G + i (i < 4) or 16 + 4 G + i - 4
+__device__ inline bf16x8 acc_op16(const f32x4& a, const f32x4& b) {
+  const i32x4 v = {static_cast<int>(pack_bf16x2(a[0], a[1])), static_cast<int>(pack_bf16x2(a[2], a[3])),
+                   static_cast<int>(pack_bf16x2(b[0], b[1])), static_cast<int>(pack_bf16x2(b[2], b[3]))};
+  return __builtin_bit_cast(bf16x8, v);
+}
+// the matching operand read down the columns of a row-major tile: lane (G, l) gets column
+// c0 + l, rows r0 + 4 G .. +3 and r0 + 16 + 4 G .. +3
+__device__ inline bf16x8 ld_col8_16(const uint16_t* base, int c0, int r0, int G, int lane) {
+  const int s = lane & 15;
+  const uint16_t* p = base + (r0 + 4 * G + (s >> 2)) * kLd + c0 + 4 * (s & 3);
+  const uint2 a = ld_tr4(p), b = ld_tr4(p + 16 * kLd);
+  const i32x4 v = {static_cast<int>(a.x), static_cast<int>(a.y), static_cast<int>(b.x),
+                   static_cast<int>(b.y)};
+  return __builtin_bit_cast(bf16x8, v);
+}
+__device__ inline float group4_max(float v) {
+  v = fmaxf(v, __shfl_xor(v, 16));
+  return fmaxf(v, __shfl_xor(v, 32));
+}
+__device__ inline float group4_sum(float v) {
+  v += __shfl_xor(v, 16);
+  return v + __shfl_xor(v, 32);
+}
+
+// rows k0 + 8 G .. +7 of column c0 + l (natural order; 16x16x32 operand down the columns)
+__device__ inline bf16x8 ld_col8n_16(const uint16_t* base, int c0, int r0, int G, int lane) {
+  const int s = lane & 15;
+  const uint16_t* p = base + (r0 + 8 * G + (s >> 2)) * kLd + c0 + 4 * (s & 3);
+  const uint2 a = ld_tr4(p), b = ld_tr4(p + 4 * kLd);
+  const i32x4 v = {static_cast<int>(a.x), static_cast<int>(a.y), static_cast<int>(b.x),
+                   static_cast<int>(b.y)};
+  return __builtin_bit_cast(bf16x8, v);
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------- bwd_prep
@@ -271,71 +349,77 @@ __global__ __launch_bounds__(1024) void key_plan_kernel(const int32_t* __restric
 }
 
 // ---------------------------------------------------------------- bwd_lin_q
-// grid (nqb, BH) (XCD-aware order), 256 threads; wavefront w owns query rows 32 w .. +31 for
-// the products with the query as column index, and output tile w otherwise.
+// grid (nqb, BH) (XCD-aware order), 512 threads; MFMA 16x16x32 bf16. Wavefront w owns query
+// rows 16 w .. +15 (the lane's column) for num^T = H_i^T a^T and da^T = H_i dnum^T (the query
+// as column, so row sums are per lane plus the four lane groups), and o rows 16 w .. +15 of
+// dH_i^T = dnum^T a. LDS: a = phi(Q_i) [q][a], H_i^T [o][a] (later the dH_i^T staging tile),
+// dnum [q][o], all bf16.
+constexpr int kLinT = 512;
 template <typename T>
-__global__ __launch_bounds__(256) void bwd_lin_q_kernel(BwdArgs x) {
+__global__ __launch_bounds__(kLinT) void bwd_lin_q_kernel(BwdArgs x) {
   __shared__ __attribute__((aligned(16))) uint16_t As[kTile];   // a = phi(Q_i) [q][a]
   __shared__ __attribute__((aligned(16))) uint16_t Ht[kTile];   // H_i^T [o][a]
   __shared__ __attribute__((aligned(16))) uint16_t DN[kTile];   // dnum [q][o]
-  __shared__ float Zs[kD], ddl[kD], red[4];
+  __shared__ float Zs[kD], ddl[kD], red[8], zq[4][kD];
   int i, bh;
   xcd_block(x.nqb, x.BH, &i, &bh);
-  const int t = threadIdx.x, lane = t & 63, w = t >> 6, g = lane >> 5, l32 = lane & 31;
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6, G = lane >> 4, l16 = lane & 15;
   const int N = x.nqb * kBQ, nkb = x.nkb;
   const size_t qb = static_cast<size_t>(bh) * x.nqb + i;
   const size_t row0 = static_cast<size_t>(bh) * N + static_cast<size_t>(i) * kBQ;
   const int ncnt = x.cnt[qb];
   const float al = x.alpha[static_cast<size_t>(bh % x.H) * x.nqb + i];
   if (ncnt == nkb) {   // nothing dropped: O_l = 0, no linear gradient
-    for (int e = t; e < kBQ * kD / 4; e += 256)
+    for (int e = t; e < kBQ * kD / 4; e += kLinT)
       *reinterpret_cast<f32x4*>(x.dQ + row0 * kD + 4 * e) = f32x4{};
-    for (int e = t; e < kD * kD / 8; e += 256)
+    for (int e = t; e < kD * kD / 8; e += kLinT)
       *reinterpret_cast<i32x4*>(x.dht + qb * (kD * kD) + 8 * e) = i32x4{};
     if (t < kD) x.dz[qb * kD + t] = 0.f;
     if (t == 0) x.dalpha[qb] = 0.f;
     return;
   }
-  // ---- a = phi(Q_i): thread t takes row t / 2, columns 64 (t % 2) .. +63
+  // ---- a = phi(Q_i): thread t takes row t / 4, columns 32 (t % 4) .. +31
   {
-    const int r = t >> 1, c0 = 64 * (t & 1);
+    const int r = t >> 2, c0 = 32 * (t & 3);
     const T* qp = static_cast<const T*>(x.Q) + (row0 + r) * kD + c0;
-    float v[64];
+    float v[32];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) load8<T>(qp + 8 * u, v + 8 * u);
+    for (int u = 0; u < 4; ++u) load8<T>(qp + 8 * u, v + 8 * u);
     float mx = v[0];
 #pragma unroll
-    for (int k = 1; k < 64; ++k) mx = fmaxf(mx, v[k]);
+    for (int k = 1; k < 32; ++k) mx = fmaxf(mx, v[k]);
     mx = fmaxf(mx, __shfl_xor(mx, 1));
-    float s = 0.f;
+    mx = fmaxf(mx, __shfl_xor(mx, 2));
+    float sum = 0.f;
 #pragma unroll
-    for (int k = 0; k < 64; ++k) {
+    for (int k = 0; k < 32; ++k) {
       v[k] = __expf(v[k] - mx);
-      s += v[k];
+      sum += v[k];
     }
-    s += __shfl_xor(s, 1);
-    const float inv = 1.0f / s;
+    sum += __shfl_xor(sum, 1);
+    sum += __shfl_xor(sum, 2);
+    const float inv = 1.0f / sum;
 #pragma unroll
-    for (int k = 0; k < 64; ++k) v[k] *= inv;
+    for (int k = 0; k < 32; ++k) v[k] *= inv;
 #pragma unroll
-    for (int u = 0; u < 8; ++u) st_bf16x8(&As[r * kLd + c0 + 8 * u], v + 8 * u);
+    for (int u = 0; u < 4; ++u) st_bf16x8(&As[r * kLd + c0 + 8 * u], v + 8 * u);
   }
   // ---- H_i = H_tot - sum over kept j of h_j. h_j^T bf16 in fragment order: 16-byte chunk c
   // holds row o = 32 (c / 512) + c % 32, columns a = 8 ((c / 32) % 16) .. +7. Thread t takes
-  // chunks t + 256 u.
+  // chunks t + 512 u.
   {
     const int32_t* lst = x.list + qb * nkb;
-    const uint16_t* hb = x.hbf + static_cast<size_t>(bh) * nkb * (kD * kD);
-    float acc[8][8];
+    float acc[4][8];
 #pragma unroll
-    for (int u = 0; u < 8; ++u)
+    for (int u = 0; u < 4; ++u)
 #pragma unroll
       for (int k = 0; k < 8; ++k) acc[u][k] = 0.f;
-    sum_tiles<4>(acc, hb, [&](int n) { return lst[n]; }, 0, ncnt, t);
+    sum_tiles512(acc, x.hbf + static_cast<size_t>(bh) * nkb * (kD * kD),
+                 [&](int n) { return lst[n]; }, 0, ncnt, t);
     const float* ht = x.htot + static_cast<size_t>(bh) * (kD * kD);   // H_tot [a][o]
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int c = t + 256 * u;
+    for (int u = 0; u < 4; ++u) {
+      const int c = t + kLinT * u;
       const int o = 32 * (c >> 9) + (c & 31), a0 = 8 * ((c >> 5) & 15);
       float hv[8];
 #pragma unroll
@@ -349,138 +433,127 @@ __global__ __launch_bounds__(256) void bwd_lin_q_kernel(BwdArgs x) {
     }
   }
   __syncthreads();
-  // ---- num^T = H_i^T a^T: lane = query q = 32 w + l32, registers = o
-  const int q = 32 * w + l32;
-  f32x16 num[4];
+  // ---- num^T = H_i^T a^T: lane = query q = 16 w + l16, registers = o (tile ot: 16 ot + 4 G + r)
+  const int q = 16 * w + l16;
+  f32x4 num[8];
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt) {
-    num[mt] = f32x16{};
+  for (int ot = 0; ot < 8; ++ot) {
+    num[ot] = f32x4{};
 #pragma unroll
-    for (int s = 0; s < 8; ++s)
-      num[mt] = mfma(ld_row8(&Ht[(32 * mt + l32) * kLd + 16 * s + 8 * g]),
-                     ld_row8(&As[q * kLd + 16 * s + 8 * g]), num[mt]);
+    for (int c = 0; c < 4; ++c)
+      num[ot] = mfma16(ld_row8(&Ht[(16 * ot + l16) * kLd + 32 * c + 8 * G]),
+                       ld_row8(&As[q * kLd + 32 * c + 8 * G]), num[ot]);
   }
   float den = 0.f;
 #pragma unroll
-  for (int u = 0; u < 8; ++u) {
-    const i32x4 v = *reinterpret_cast<const i32x4*>(&As[q * kLd + 64 * g + 8 * u]);
+  for (int u = 0; u < 4; ++u) {
     float f[8];
-    unpack_bf16x8(v, f);
+    unpack_bf16x8(*reinterpret_cast<const i32x4*>(&As[q * kLd + 32 * G + 8 * u]), f);
 #pragma unroll
-    for (int k = 0; k < 8; ++k) den += f[k] * Zs[64 * g + 8 * u + k];
+    for (int k = 0; k < 8; ++k) den += f[k] * Zs[32 * G + 8 * u + k];
   }
-  den += __shfl_xor(den, 32);
+  den = group4_sum(den);
   const float oml = 1.0f - al, inv_den = 1.0f / den;
   // O_l = num / den; sum(dO O_l) per row; dnum = (1 - alpha) dO / den (in num's registers)
   float sl = 0.f;
   {
-    const float* dop = x.dO + (row0 + q) * kD;
+    const float* dop = x.dO + (row0 + q) * kD + 4 * G;
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
+    for (int ot = 0; ot < 8; ++ot) {
+      const f32x4 d4 = *reinterpret_cast<const f32x4*>(dop + 16 * ot);
 #pragma unroll
-      for (int k4 = 0; k4 < 4; ++k4) {
-        const f32x4 d4 = *reinterpret_cast<const f32x4*>(dop + 32 * mt + 8 * k4 + 4 * g);
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          sl += d4[k] * (num[mt][4 * k4 + k] * inv_den);
-          num[mt][4 * k4 + k] = oml * d4[k] * inv_den;
-        }
+      for (int r = 0; r < 4; ++r) {
+        sl += d4[r] * (num[ot][r] * inv_den);
+        num[ot][r] = oml * d4[r] * inv_den;
       }
+    }
   }
-  sl += __shfl_xor(sl, 32);
+  sl = group4_sum(sl);
   const float dden = -oml * sl * inv_den;
   {
-    const float ws = wave_sum(g == 0 ? sl : 0.f);
+    const float ws = wave_sum(G == 0 ? sl : 0.f);
     if (lane == 0) red[w] = ws;
   }
   // ---- da^T = H_i dnum^T (+ dden Z_i): lane = q, registers = a; dQ = a (da - rowsum(da a))
   {
-    f32x16 da[4];
+    f32x4 da[8];
 #pragma unroll
-    for (int at = 0; at < 4; ++at) {
-      da[at] = f32x16{};
+    for (int at = 0; at < 8; ++at) {
+      da[at] = f32x4{};
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-          da[at] = mfma(ld_col8_acc(Ht, 32 * at, 32 * mt + 16 * h, g, lane),
-                        acc_op(num[mt], h), da[at]);
+      for (int c = 0; c < 4; ++c)
+        da[at] = mfma16(ld_col8_16(Ht, 16 * at, 32 * c, G, lane), acc_op16(num[2 * c], num[2 * c + 1]),
+                        da[at]);
     }
-    float av[4][16];
+    float av[8][4];
     float cs = 0.f;
 #pragma unroll
-    for (int at = 0; at < 4; ++at)
+    for (int at = 0; at < 8; ++at) {
+      const int a0 = 16 * at + 4 * G;
+      const uint2 pv = *reinterpret_cast<const uint2*>(&As[q * kLd + a0]);
+      av[at][0] = __uint_as_float(pv.x << 16);
+      av[at][1] = __uint_as_float(pv.x & 0xFFFF0000u);
+      av[at][2] = __uint_as_float(pv.y << 16);
+      av[at][3] = __uint_as_float(pv.y & 0xFFFF0000u);
 #pragma unroll
-      for (int k4 = 0; k4 < 4; ++k4) {
-        const int a0 = 32 * at + 8 * k4 + 4 * g;
-        const uint2 pv = *reinterpret_cast<const uint2*>(&As[q * kLd + a0]);
-        av[at][4 * k4] = __uint_as_float(pv.x << 16);
-        av[at][4 * k4 + 1] = __uint_as_float(pv.x & 0xFFFF0000u);
-        av[at][4 * k4 + 2] = __uint_as_float(pv.y << 16);
-        av[at][4 * k4 + 3] = __uint_as_float(pv.y & 0xFFFF0000u);
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          da[at][4 * k4 + k] += dden * Zs[a0 + k];
-          cs += da[at][4 * k4 + k] * av[at][4 * k4 + k];
-        }
+      for (int r = 0; r < 4; ++r) {
+        da[at][r] += dden * Zs[a0 + r];
+        cs += da[at][r] * av[at][r];
       }
-    cs += __shfl_xor(cs, 32);
-    float* dqp = x.dQ + (row0 + q) * kD;
+    }
+    cs = group4_sum(cs);
+    float* dqp = x.dQ + (row0 + q) * kD + 4 * G;
 #pragma unroll
-    for (int at = 0; at < 4; ++at)
+    for (int at = 0; at < 8; ++at) {
+      f32x4 o4;
 #pragma unroll
-      for (int k4 = 0; k4 < 4; ++k4) {
-        f32x4 o4;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) o4[k] = av[at][4 * k4 + k] * (da[at][4 * k4 + k] - cs);
-        *reinterpret_cast<f32x4*>(dqp + 32 * at + 8 * k4 + 4 * g) = o4;
-      }
+      for (int r = 0; r < 4; ++r) o4[r] = av[at][r] * (da[at][r] - cs);
+      *reinterpret_cast<f32x4*>(dqp + 16 * at) = o4;
+    }
   }
   // ---- dnum -> LDS [q][o] (bf16), dden -> LDS
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-    for (int k4 = 0; k4 < 4; ++k4)
-      *reinterpret_cast<uint2*>(&DN[q * kLd + 32 * mt + 8 * k4 + 4 * g]) =
-          make_uint2(pack_bf16x2(num[mt][4 * k4], num[mt][4 * k4 + 1]),
-                     pack_bf16x2(num[mt][4 * k4 + 2], num[mt][4 * k4 + 3]));
-  if (g == 0) ddl[q] = dden;
+  for (int ot = 0; ot < 8; ++ot)
+    *reinterpret_cast<uint2*>(&DN[q * kLd + 16 * ot + 4 * G]) =
+        make_uint2(pack_bf16x2(num[ot][0], num[ot][1]), pack_bf16x2(num[ot][2], num[ot][3]));
+  if (G == 0) ddl[q] = dden;
   __syncthreads();
-  // ---- dH_i^T [o][a] = sum_q dnum[q][o] a[q][a]: wavefront w owns o = 32 w .. +31, staged as
+  // ---- dH_i^T [o][a] = sum_q dnum[q][o] a[q][a]: wavefront w owns o = 16 w .. +15, staged as
   // bf16 in the H_i^T tile (no longer read) and stored in 16-byte pieces
 #pragma unroll
-  for (int at = 0; at < 4; ++at) {
-    f32x16 c = f32x16{};
+  for (int at = 0; at < 8; ++at) {
+    f32x4 c = f32x4{};
 #pragma unroll
-    for (int s = 0; s < 8; ++s)
-      c = mfma(ld_col8(DN, 32 * w, 16 * s, g, lane), ld_col8(As, 32 * at, 16 * s, g, lane), c);
-    const int a = 32 * at + l32;
+    for (int cq = 0; cq < 4; ++cq)
+      c = mfma16(ld_col8n_16(DN, 16 * w, 32 * cq, G, lane), ld_col8n_16(As, 16 * at, 32 * cq, G, lane), c);
+    const int a = 16 * at + l16;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int o = 32 * w + 8 * (r >> 2) + 4 * g + (r & 3);
-      Ht[o * kLd + a] = f32_to_bf16_rne(c[r]);
-    }
+    for (int r = 0; r < 4; ++r) Ht[(16 * w + 4 * G + r) * kLd + a] = f32_to_bf16_rne(c[r]);
   }
-  // dZ_i[a] = sum_q a[q][a] dden[q]: two threads per column, 64 query rows each
+  // dZ_i[a] = sum_q a[q][a] dden[q]: four threads per column, 32 query rows each
   {
     const int a = t & (kD - 1), h = t >> 7;
     float s = 0.f;
 #pragma unroll 8
-    for (int r = 64 * h; r < 64 * h + 64; ++r) s += bf(As[r * kLd + a]) * ddl[r];
-    __syncthreads();   // Zs (no longer read) takes the second half's sums
-    if (h == 1) Zs[a] = s;
-    __syncthreads();
-    if (h == 0) x.dz[qb * kD + a] = s + Zs[a];
+    for (int r = 32 * h; r < 32 * h + 32; ++r) s += bf(As[r * kLd + a]) * ddl[r];
+    zq[h][a] = s;
   }
+  __syncthreads();
+  if (t < kD) x.dz[qb * kD + t] = (zq[0][t] + zq[1][t]) + (zq[2][t] + zq[3][t]);
   {
     uint16_t* out = x.dht + qb * (kD * kD);
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int c = t + 256 * u, o = c >> 4, a0 = 8 * (c & 15);
+    for (int u = 0; u < 4; ++u) {
+      const int c = t + kLinT * u, o = c >> 4, a0 = 8 * (c & 15);
       *reinterpret_cast<i32x4*>(out + o * kD + a0) = *reinterpret_cast<const i32x4*>(&Ht[o * kLd + a0]);
     }
   }
-  if (t == 0) x.dalpha[qb] = -((red[0] + red[1]) + (red[2] + red[3]));
+  if (t == 0) {
+    float sdl = 0.f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) sdl += red[k];
+    x.dalpha[qb] = -sdl;
+  }
 }
 
 // ---------------------------------------------------------------- bwd_q
@@ -493,35 +566,6 @@ __global__ __launch_bounds__(256) void bwd_lin_q_kernel(BwdArgs x) {
 // registers while the current one is processed (one barrier per block). Logits are kept in
 // base-2 units: s2 = S log2(e) / sqrt(d).
 constexpr int kQThreads = 512;
-__device__ inline f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-// two accumulator tiles (rows 0-15 and 16-31 of a 32-deep k chunk) as a bf16 operand:
-// element i of lane group G is row 4 G + i (i < 4) or 16 + 4 G + i - 4
-__device__ inline bf16x8 acc_op16(const f32x4& a, const f32x4& b) {
-  const i32x4 v = {static_cast<int>(pack_bf16x2(a[0], a[1])), static_cast<int>(pack_bf16x2(a[2], a[3])),
-                   static_cast<int>(pack_bf16x2(b[0], b[1])), static_cast<int>(pack_bf16x2(b[2], b[3]))};
-  return __builtin_bit_cast(bf16x8, v);
-}
-// the matching operand read down the columns of a row-major tile: lane (G, l) gets column
-// c0 + l, rows r0 + 4 G .. +3 and r0 + 16 + 4 G .. +3
-__device__ inline bf16x8 ld_col8_16(const uint16_t* base, int c0, int r0, int G, int lane) {
-  const int s = lane & 15;
-  const uint16_t* p = base + (r0 + 4 * G + (s >> 2)) * kLd + c0 + 4 * (s & 3);
-  const uint2 a = ld_tr4(p), b = ld_tr4(p + 16 * kLd);
-  const i32x4 v = {static_cast<int>(a.x), static_cast<int>(a.y), static_cast<int>(b.x),
-                   static_cast<int>(b.y)};
-  return __builtin_bit_cast(bf16x8, v);
-}
-__device__ inline float group4_max(float v) {
-  v = fmaxf(v, __shfl_xor(v, 16));
-  return fmaxf(v, __shfl_xor(v, 32));
-}
-__device__ inline float group4_sum(float v) {
-  v += __shfl_xor(v, 16);
-  return v + __shfl_xor(v, 32);
-}
-
 __global__ __launch_bounds__(kQThreads) __attribute__((amdgpu_waves_per_eu(4))) void bwd_q_kernel(BwdArgs x) {
   __shared__ __attribute__((aligned(16))) uint16_t Ks[2][kBK * kLd];
   __shared__ __attribute__((aligned(16))) uint16_t Vs[2][kBK * kLd];
@@ -724,16 +768,6 @@ constexpr int kKvLds = 4 * kTile * 2 + 4 * kBQ * 4;
 constexpr int kOffX = 0, kOffPK = 67584, kOffDH = 84992, kOffDz = 119808, kOffCrow = 120320,
               kOffKred = 120832;
 
-// rows k0 + 8 G .. +7 of column c0 + l (natural order; 16x16x32 operand down the columns)
-__device__ inline bf16x8 ld_col8n_16(const uint16_t* base, int c0, int r0, int G, int lane) {
-  const int s = lane & 15;
-  const uint16_t* p = base + (r0 + 8 * G + (s >> 2)) * kLd + c0 + 4 * (s & 3);
-  const uint2 a = ld_tr4(p), b = ld_tr4(p + 4 * kLd);
-  const i32x4 v = {static_cast<int>(a.x), static_cast<int>(a.y), static_cast<int>(b.x),
-                   static_cast<int>(b.y)};
-  return __builtin_bit_cast(bf16x8, v);
-}
-
 struct KvState {
   f32x4 dk[8], dv[8];   // lane = d column 16 dt + l16, registers = keys 16 kt + 4 G + r
 };
@@ -863,42 +897,6 @@ __device__ inline void load_kv_ops(const BwdArgs& x, size_t krow0, int kt, int G
   }
 }
 
-// sum over n in [n0, n1) of the bf16 dH_i^T tiles of query blocks tl[n] (thread: chunks
-// t + 512 u, u < 4), added in n order, four tiles' loads in flight
-__device__ inline void sum_dh(float (&acc)[4][8], const uint16_t* src, const uint16_t* tl, int n0,
-                              int n1, int t) {
-  constexpr int kF = 4;
-  int n = n0;
-  for (; n + kF - 1 < n1; n += kF) {
-    i32x4 v[kF][4];
-#pragma unroll
-    for (int f = 0; f < kF; ++f) {
-      const uint16_t* a = src + static_cast<size_t>(tl[n + f]) * (kD * kD);
-#pragma unroll
-      for (int u = 0; u < 4; ++u) v[f][u] = *reinterpret_cast<const i32x4*>(a + 8 * (t + kKvT * u));
-    }
-#pragma unroll
-    for (int f = 0; f < kF; ++f)
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        float fa[8];
-        unpack_bf16x8(v[f][u], fa);
-#pragma unroll
-        for (int k = 0; k < 8; ++k) acc[u][k] += fa[k];
-      }
-  }
-  for (; n < n1; ++n) {
-    const uint16_t* a = src + static_cast<size_t>(tl[n]) * (kD * kD);
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      float fa[8];
-      unpack_bf16x8(*reinterpret_cast<const i32x4*>(a + 8 * (t + kKvT * u)), fa);
-#pragma unroll
-      for (int k = 0; k < 8; ++k) acc[u][k] += fa[k];
-    }
-  }
-}
-
 // Extra work items: grid (cap, BH); item e < plan[bh].count covers the query blocks
 // [c C, min((c + 1) C, T_j)) of key block j; writes its partial dK_s, dV ([64][128] each) and
 // the sums of dH_i^T and dZ_i over its query blocks into slot e.
@@ -937,7 +935,7 @@ __global__ __launch_bounds__(kKvT) void bwd_kv_extra_kernel(BwdArgs x) {
   for (int u = 0; u < 4; ++u)
 #pragma unroll
     for (int k = 0; k < 8; ++k) acc[u][k] = 0.f;
-  sum_dh(acc, x.dht + static_cast<size_t>(bh) * nqb * (kD * kD), tl, n0, n1, t);
+  sum_tiles512(acc, x.dht + static_cast<size_t>(bh) * nqb * (kD * kD), [&](int n) { return static_cast<int>(tl[n]); }, n0, n1, t);
   float* sh = slot + 2 * kBK * kD;
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
@@ -1044,7 +1042,7 @@ __global__ __launch_bounds__(kKvT) void bwd_kv_kernel(BwdArgs x) {
     for (int u = 0; u < 4; ++u)
 #pragma unroll
       for (int k = 0; k < 8; ++k) acc[u][k] = 0.f;
-    sum_dh(acc, x.dht + static_cast<size_t>(bh) * nqb * (kD * kD), tl, 0, n1, t);
+    sum_tiles512(acc, x.dht + static_cast<size_t>(bh) * nqb * (kD * kD), [&](int n) { return static_cast<int>(tl[n]); }, 0, n1, t);
     for (int e = 0; e < nx; ++e) {
       const float* sh = xs + static_cast<size_t>(e) * kSlot + 2 * kBK * kD;
 #pragma unroll
@@ -1246,9 +1244,9 @@ hipError_t launch_bwd_prep(const Geom& g, int dtype, const BwdArgs& x, hipStream
 
 hipError_t launch_bwd_lin_q(const Geom& g, int dtype, const BwdArgs& x, hipStream_t s) {
   if (dtype == 0)
-    hipLaunchKernelGGL(bwd_lin_q_kernel<float>, dim3(g.nqb, g.BH), dim3(256), 0, s, x);
+    hipLaunchKernelGGL(bwd_lin_q_kernel<float>, dim3(g.nqb, g.BH), dim3(kLinT), 0, s, x);
   else
-    hipLaunchKernelGGL(bwd_lin_q_kernel<uint16_t>, dim3(g.nqb, g.BH), dim3(256), 0, s, x);
+    hipLaunchKernelGGL(bwd_lin_q_kernel<uint16_t>, dim3(g.nqb, g.BH), dim3(kLinT), 0, s, x);
   return hipGetLastError();
 }
 
