@@ -352,14 +352,14 @@ __global__ __launch_bounds__(1024) void key_plan_kernel(const int32_t* __restric
 // grid (nqb, BH) (XCD-aware order), 512 threads; MFMA 16x16x32 bf16. Wavefront w owns query
 // rows 16 w .. +15 (the lane's column) for num^T = H_i^T a^T and da^T = H_i dnum^T (the query
 // as column, so row sums are per lane plus the four lane groups), and o rows 16 w .. +15 of
-// dH_i^T = dnum^T a. LDS: a = phi(Q_i) [q][a], H_i^T [o][a] (later the dH_i^T staging tile),
-// dnum [q][o], all bf16.
+// dH_i^T = dnum^T a. LDS (two bf16 tiles, so that two workgroups fit per CU): a = phi(Q_i)
+// [q][a], and one tile that holds H_i^T [o][a], then dnum [q][o], then the dH_i^T staging.
 constexpr int kLinT = 512;
 template <typename T>
 __global__ __launch_bounds__(kLinT) void bwd_lin_q_kernel(BwdArgs x) {
   __shared__ __attribute__((aligned(16))) uint16_t As[kTile];   // a = phi(Q_i) [q][a]
-  __shared__ __attribute__((aligned(16))) uint16_t Ht[kTile];   // H_i^T [o][a]
-  __shared__ __attribute__((aligned(16))) uint16_t DN[kTile];   // dnum [q][o]
+  __shared__ __attribute__((aligned(16))) uint16_t Ht[kTile];   // H_i^T [o][a]; dnum; dH_i^T
+  uint16_t* const DN = Ht;                                      // dnum [q][o]
   __shared__ float Zs[kD], ddl[kD], red[8], zq[4][kD];
   int i, bh;
   xcd_block(x.nqb, x.BH, &i, &bh);
@@ -511,24 +511,24 @@ __global__ __launch_bounds__(kLinT) void bwd_lin_q_kernel(BwdArgs x) {
       *reinterpret_cast<f32x4*>(dqp + 16 * at) = o4;
     }
   }
-  // ---- dnum -> LDS [q][o] (bf16), dden -> LDS
+  // ---- dnum -> LDS [q][o] (bf16, over H_i^T once every wavefront is done with it), dden
+  __syncthreads();
 #pragma unroll
   for (int ot = 0; ot < 8; ++ot)
     *reinterpret_cast<uint2*>(&DN[q * kLd + 16 * ot + 4 * G]) =
         make_uint2(pack_bf16x2(num[ot][0], num[ot][1]), pack_bf16x2(num[ot][2], num[ot][3]));
   if (G == 0) ddl[q] = dden;
   __syncthreads();
-  // ---- dH_i^T [o][a] = sum_q dnum[q][o] a[q][a]: wavefront w owns o = 16 w .. +15, staged as
-  // bf16 in the H_i^T tile (no longer read) and stored in 16-byte pieces
+  // ---- dH_i^T [o][a] = sum_q dnum[q][o] a[q][a]: wavefront w owns o = 16 w .. +15; staged as
+  // bf16 over dnum once every wavefront is done with it, and stored in 16-byte pieces
+  f32x4 dh[8];
 #pragma unroll
   for (int at = 0; at < 8; ++at) {
-    f32x4 c = f32x4{};
+    dh[at] = f32x4{};
 #pragma unroll
     for (int cq = 0; cq < 4; ++cq)
-      c = mfma16(ld_col8n_16(DN, 16 * w, 32 * cq, G, lane), ld_col8n_16(As, 16 * at, 32 * cq, G, lane), c);
-    const int a = 16 * at + l16;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) Ht[(16 * w + 4 * G + r) * kLd + a] = f32_to_bf16_rne(c[r]);
+      dh[at] = mfma16(ld_col8n_16(DN, 16 * w, 32 * cq, G, lane), ld_col8n_16(As, 16 * at, 32 * cq, G, lane),
+                      dh[at]);
   }
   // dZ_i[a] = sum_q a[q][a] dden[q]: four threads per column, 32 query rows each
   {
@@ -537,6 +537,13 @@ __global__ __launch_bounds__(kLinT) void bwd_lin_q_kernel(BwdArgs x) {
 #pragma unroll 8
     for (int r = 32 * h; r < 32 * h + 32; ++r) s += bf(As[r * kLd + a]) * ddl[r];
     zq[h][a] = s;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int at = 0; at < 8; ++at) {
+    const int a = 16 * at + l16;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) Ht[(16 * w + 4 * G + r) * kLd + a] = f32_to_bf16_rne(dh[at][r]);
   }
   __syncthreads();
   if (t < kD) x.dz[qb * kD + t] = (zq[0][t] + zq[1][t]) + (zq[2][t] + zq[3][t]);
