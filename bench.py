@@ -64,12 +64,29 @@ def kernel_source_hash(kernel):
     they change."""
     import hashlib
     files = {"attn": ["sparse.hip"], "kv_prep": ["linear.hip"], "linear_total": ["linear.hip"]}
+    if kernel.startswith("bwd_") or kernel in ("key_lists", "key_plan", "dh_total", "dk_center"):
+        files[kernel] = ["backward.hip"]
     files = files.get(kernel, ["router.hip"]) + ["sla2_common.h"]
     h = hashlib.sha256()
     for f in files:
         with open(os.path.join(HERE, "block_sparse_linear_pool_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
+
+
+def stored_traffic(args, kernel, w, keep):
+    """HBM bytes per launch of `kernel` from its rocprofv3 counter record under profiles/
+    (FETCH_SIZE and WRITE_SIZE runs, scaled by a copy of known size), or None when there is
+    none for this workload or the kernel's sources have changed since it was taken."""
+    tpath = args.traffic or os.path.join(HERE, "profiles", f"{kernel}_traffic_{w.name}.json")
+    if not os.path.exists(tpath):
+        return None
+    with open(tpath) as f:
+        tr = json.load(f)
+    if (tr.get("kernel") == kernel and tr.get("workload") == w.name and tr.get("keep_frac") == keep
+            and tr.get("source_sha256") == kernel_source_hash(kernel)):
+        return tr.get("bytes_per_launch")
+    return None
 
 
 def copy_probe():
@@ -396,7 +413,8 @@ def run_backward(args, w, q, k, v, wq, wk, alpha, keep):
                    "input_dtype": w.dtype, "keep_frac": keep, "kb": kb,
                    "kept_pairs": prob.pairs, "kv_main_pairs": main_pairs},
         "roofline": {"kernel": dom, "bound": bound, "achieved": round(achieved, 2), "peak": peak,
-                     "unit": unit, "frac": round(achieved / peak, 4), "traffic": None,
+                     "unit": unit, "frac": round(achieved / peak, 4),
+                     "traffic": stored_traffic(args, dom, w, keep),
                      "avg_launch_ms": round(t_dom * 1e3, 5)},
         "kernels": kernels,
     }
@@ -586,14 +604,7 @@ def main():
     else:
         achieved = acc.kernel_bytes(prob, dom) / t_dom / 1e9
         peak, unit = acc.MI355X_PEAK["hbm_gbs"], "GB/s"
-    traffic = None
-    tpath = args.traffic or os.path.join(HERE, "profiles", f"{dom}_traffic_{w.name}.json")
-    if os.path.exists(tpath):
-        with open(tpath) as f:
-            tr = json.load(f)
-        if (tr.get("kernel") == dom and tr.get("workload") == w.name and tr.get("keep_frac") == keep
-                and tr.get("source_sha256") == kernel_source_hash(dom)):
-            traffic = tr.get("bytes_per_launch")
+    traffic = stored_traffic(args, dom, w, keep)
     roofline = {"kernel": dom, "bound": acc.kernel_bound(dom), "achieved": round(achieved, 2),
                 "peak": peak, "unit": unit, "frac": round(achieved / peak, 4),
                 "traffic": traffic, "avg_launch_ms": round(t_dom * 1e3, 5)}
