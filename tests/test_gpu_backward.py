@@ -66,6 +66,19 @@ def test_backward_random_masks_with_empty_and_full_rows():
     check(q, k, v, mask, alpha, dO, "fp32", [(0, 0), (0, 1)])
 
 
+@pytest.mark.parametrize("B,H,N,dtype,frac", [(1, 3, 640, "bf16", 0.3), (3, 1, 1152, "fp32", 0.15),
+                                              (1, 1, 2176, "bf16", 0.6)])
+def test_backward_ragged_block_counts(B, H, N, dtype, frac):
+    """Odd numbers of query blocks (5, 9, 17) and key blocks (10, 18, 34), odd head and batch
+    counts, sparse to dense masks (key lists of 5 to 16 of the 17 query blocks at 60 %)."""
+    q, k, v = W.random_qkv(N + B, B, H, N, dtype=dtype)
+    mask = W.random_mask(N + B, B, H, N // 128, N // 64, frac)
+    _, _, alpha = W.random_weights(N + B, H, N // 128, alpha_lo=0.05)
+    dO = W.grad_out(N + B, q.shape)
+    say("backward ragged", q.shape, dtype)
+    check(q, k, v, mask, alpha, dO, dtype, [(b, h) for b in range(B) for h in range(H)])
+
+
 def test_backward_two_batches_fp32():
     """B = 2 (alpha shared by the batches, dalpha per batch), fp32 inputs, N = 1024."""
     B, H, N = 2, 2, 1024
