@@ -96,3 +96,22 @@ def test_fit_end_to_end_and_backward_at_the_minimum():
         float(np.max(np.abs(g0[inner]) / np.abs(g1[inner] - g0[inner]))))
     assert inner.any()
     assert np.all(np.abs(g0[inner]) <= 0.25 * np.abs(g1[inner] - g0[inner]))
+
+
+@pytest.mark.timeout(300)
+def test_fit_full_size_two_batches():
+    """The bench's shape with two batches (B = 2, H = 12, N = 32768: 256 query blocks a head),
+    per-block mixing weights drawn from [-0.3, 1.3] so that about three in eight are clipped."""
+    B, H, N, D = 2, 12, 32768, 128
+    nqb = N // 128
+    rng = np.random.default_rng(103)
+    O_s = rng.standard_normal((B, H, N, D), dtype=np.float32)
+    O_l = rng.standard_normal((B, H, N, D), dtype=np.float32)
+    a = np.repeat(rng.uniform(-0.3, 1.3, (1, H, nqb)), 128, axis=2)[..., None].astype(np.float32)
+    O_full = a * O_s + (1 - a) * O_l + 0.3 * rng.standard_normal((B, H, N, D), dtype=np.float32)
+    got = host(sla2.sla2_fit_alpha(dev(O_full), dev(O_s), dev(O_l)))
+    ref = fit.fit_alpha(O_full, O_s, O_l)
+    clipped = int(((ref == 0.0) | (ref == 1.0)).sum())
+    say(f"full size: max |alpha - oracle| {np.abs(got - ref).max():.2e}, {clipped} of {H * nqb} clipped")
+    assert np.abs(got - ref).max() <= 1e-6
+    assert clipped > 0
