@@ -76,9 +76,11 @@ def test_soft_router_matches_oracle(name, heads, tau):
     check(q, k, wq, wk, keep, tau, w.dtype, [(b, h) for b in range(B) for h in range(H)])
 
 
-@pytest.mark.parametrize("N,keep", [(128, 0.5), (128, 1.0), (640, 0.1), (1024, 1e-3)])
+@pytest.mark.parametrize("N,keep", [(128, 0.5), (128, 1.0), (640, 0.1), (1024, 1e-3),
+                                    (262144, 0.002)])
 def test_soft_router_small_and_edge_keeps(N, keep):
-    """Smallest shape, every block kept (ones, lambda = inf), a ragged grid, kb = 1."""
+    """Smallest shape, every block kept (ones, lambda = inf), a ragged grid, kb = 1, and the
+    largest length (4096 key blocks a row, kb = 8)."""
     q, k, _ = W.random_qkv(61 + N, 1, 2, N)
     wq, wk, _ = W.random_weights(61 + N, 2, N // 128)
     say("soft router edge", N, keep)
