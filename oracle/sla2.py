@@ -51,10 +51,15 @@ case (the heuristic router) against torch pooling; smoothing invariance; the
 online loop with identity codecs against the exact masked softmax; the codecs
 (see codecs.py).
 
-Parity unpinned: the composition of the quantised sparse branch (where the
-codecs sit inside the online loop). No page prints a worked value or an error
-bound for it; its loop is pinned by the identity-codec reduction and its codecs
-exhaustively, but the quantised end result itself rests on the readings above.
+The quantised sparse branch (the codecs inside the online loop) is pinned by a
+closed form of that loop, rebuilt densely in torch with its own float8_e4m3fn
+and INT8 codes (tests/test_oracle_quantised.py): block b's P encoded against the
+running maximum M_b, rescaled by e^(M_b - M), over 448 times the sum of the
+unquantised exp(S - M); planted mistakes (the normaliser over the quantised P,
+P against the final maximum, no rescale, no factor 448) each fail it. No page
+prints a worked value or an error bound for the quantised result, so what the
+pins fix is the composition the readings above state, not a number the pages
+give.
 """
 
 from __future__ import annotations
