@@ -164,7 +164,7 @@ def run_router_soft(args, w, q, k, wq, wk, keep):
     gq, gk = (torch.from_numpy(a).to(dev, dt) for a in (q, k))
     gwq, gwk = (torch.from_numpy(a).to(dev) for a in (wq, wk))
     soft = torch.empty((w.B, w.H, w.n_qb, w.n_kb), dtype=torch.float32, device=dev)
-    ws = sla2.workspace_for(gq)
+    ws = sla2.workspace_for(gq, "router_soft")
     kb = sla2.sla2_blocks_kept(w.n_kb, keep)
     prob = acc.Problem(w.B, w.H, w.N, kb, in_bytes=2 if dt == torch.bfloat16 else 4)
 
@@ -258,7 +258,7 @@ def run_sla1(args, w, q, k, v, keep):
     wo = torch.from_numpy(rng.normal(0.0, 1.0 / np.sqrt(w.d), (w.H, w.d, w.d)).astype(np.float32)).to(dev)
     out = torch.empty(gq.shape, dtype=torch.float32, device=dev)
     ol = torch.empty_like(out)
-    ws = sla2.workspace_for(gq)
+    ws = sla2.workspace_for(gq, "forward_sla1", keep)
     kb = sla2.sla2_blocks_kept(w.n_kb, keep)
     prob = acc.Problem(w.B, w.H, w.N, kb, in_bytes=2 if dt == torch.bfloat16 else 4)
 
@@ -346,7 +346,7 @@ def run_backward(args, w, q, k, v, wq, wk, alpha, keep):
     ga = torch.from_numpy(alpha).to(dev)
     dO_h = W.grad_out(w.seed, q.shape)
     gdo = torch.from_numpy(dO_h).to(dev)
-    ws = sla2.workspace_for(gq)
+    ws = sla2.workspace_for(gq, "backward")   # also serves the router call (a smaller plan)
     _, mask, _ = sla2.sla2_router(gq, gk, torch.from_numpy(wq).to(dev),
                                   torch.from_numpy(wk).to(dev), keep, workspace=ws)
     out = (torch.empty(gq.shape, dtype=torch.float32, device=dev),
@@ -450,7 +450,7 @@ def run_fit_alpha(args, w, q, k, v, wq, wk, keep):
     gq, gk, gv = (torch.from_numpy(a).to(dev, dt) for a in (q, k, v))
     eye = torch.eye(w.d, device=dev).expand(w.H, w.d, w.d).contiguous()
     ones = torch.ones((w.H, w.n_qb), device=dev)
-    ws = sla2.workspace_for(gq)
+    ws = sla2.workspace_for(gq, "forward", 1.0)
     o_full = sla2.sla2_forward(gq, gk, gv, eye, eye, ones, 1.0, workspace=ws)
     _, taps = sla2.sla2_forward(gq, gk, gv, torch.from_numpy(wq).to(dev),
                                 torch.from_numpy(wk).to(dev), ones, keep, taps=("O_s", "O_l"),
@@ -541,7 +541,7 @@ def main():
     gq, gk, gv = (torch.from_numpy(a).to(dev, dt) for a in (q, k, v))
     gwq, gwk, ga = (torch.from_numpy(a).to(dev) for a in (wq, wk, alpha))
     out = torch.empty(gq.shape, dtype=torch.float32, device=dev)
-    ws = sla2.workspace_for(gq)
+    ws = sla2.workspace_for(gq, "forward", keep)
     kb = sla2.sla2_blocks_kept(w.n_kb, keep)
     prob = acc.Problem(w.B, w.H, w.N, kb, in_bytes=2 if dt == torch.bfloat16 else 4)
     if args.op == "router_soft":

@@ -4,7 +4,6 @@
 #include <cmath>
 #include <cstdlib>
 #include <cstring>
-#include <mutex>
 
 #include "../../include/sla2.h"
 #include "sla2_common.h"
@@ -19,15 +18,17 @@ constexpr size_t kAlign = 256;
 size_t up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 struct Plan {
-  size_t qsum, ksum, mu64, mu32, A, Bt, mask, list, cnt, qc, kc, vc, sq, sk, sv, hbf, z, hpart,
-      zpart, htot, ztot, ones;
+  size_t err, qsum, ksum, mu64, mu32, A, Bt, mask, list, cnt, qc, kc, vc, sq, sk, sv, hbf, z,
+      hpart, zpart, htot, ztot, ones;
   // backward only
   size_t tcnt, tlist, lse2, Dd, dht, dz, dhtot, dztot, kcol, kmean, qbf, vbf, ksb, dos, kplan,
       xoff, items, xpart, total;
   int cap;
 };
 
-Plan make_plan(const Geom& g) {
+// Workspace regions of one entry point (256-byte aligned; regions an entry does not use are
+// left at offset 0 and never touched). `kb` is the list stride of the forward entries.
+Plan make_plan(const Geom& g, sla2_entry e, int kb) {
   Plan p{};
   size_t o = 0;
   auto take = [&](size_t bytes) {
@@ -37,50 +38,69 @@ Plan make_plan(const Geom& g) {
   };
   const size_t BH = static_cast<size_t>(g.BH), N = g.N, nqb = g.nqb, nkb = g.nkb;
   const size_t np = (nkb + kKpPerWg - 1) / kKpPerWg;
-  p.qsum = take(BH * nqb * kD * 8);
+  const bool router = e == SLA2_ENTRY_ROUTER || e == SLA2_ENTRY_ROUTER_SOFT ||
+                      e == SLA2_ENTRY_FORWARD || e == SLA2_ENTRY_FORWARD_SLA1;
+  const bool fwd = e == SLA2_ENTRY_FORWARD || e == SLA2_ENTRY_FORWARD_WITH_MASK ||
+                   e == SLA2_ENTRY_FORWARD_SLA1;
+  const bool bwd = e == SLA2_ENTRY_BACKWARD;
+  p.err = take(4);                     // offset 0: the attention kernel's error word
+  p.qsum = take(BH * nqb * kD * 8);    // the pool pass always writes both block sums
   p.ksum = take(BH * nkb * kD * 8);
   p.mu64 = take(BH * kD * 8);
   p.mu32 = take(BH * kD * 4);
-  p.A = take(BH * nqb * kD * 8);
-  p.Bt = take(BH * nkb * kD * 8);
-  p.mask = take(BH * nqb * nkb);
-  p.list = take(BH * nqb * nkb * 4);
-  p.cnt = take(BH * nqb * 4);
-  p.qc = take(BH * N * kD);
-  p.kc = take(BH * N * kD);
-  p.vc = take(BH * N * kD);
-  p.sq = take(BH * nqb * 4);
-  p.sk = take(BH * nkb * 4);
-  p.sv = take(BH * nkb * 4);
-  p.hbf = take(BH * nkb * kD * kD * 2);
-  p.z = take(BH * nkb * kD * 4);
-  p.hpart = take(BH * np * kD * kD * 4);
-  p.zpart = take(BH * np * kD * 4);
-  p.htot = take(BH * kD * kD * 4);
-  p.ztot = take(BH * kD * 4);
-  p.ones = take(static_cast<size_t>(g.H) * nqb * 4);
-  p.tcnt = take(BH * nkb * 4);
-  p.tlist = take(BH * nkb * nqb * 2);
-  p.lse2 = take(BH * N * 4);
-  p.Dd = take(BH * N * 4);
-  p.dht = take(BH * nqb * kD * kD * 2);
-  p.dz = take(BH * nqb * kD * 4);
-  p.dhtot = take(BH * kD * kD * 4);
-  p.dztot = take(BH * kD * 4);
-  p.kcol = take(BH * nkb * kD * 4);
-  p.kmean = take(BH * kD * 4);
-  p.qbf = take(BH * N * kD * 2);
-  p.vbf = take(BH * N * kD * 2);
-  p.ksb = take(BH * N * kD * 2);
-  p.dos = take(BH * N * kD * 2);
-  p.cap = static_cast<int>((nkb + 1) / 2);
-  p.kplan = take(BH * 2 * 4);
-  p.xoff = take(BH * nkb * 4);
-  p.items = take(BH * static_cast<size_t>(p.cap) * 4);
-  p.xpart = take(BH * static_cast<size_t>(p.cap) * kSlot * 4);
+  if (router) {
+    p.A = take(BH * nqb * kD * 8);
+    p.Bt = take(BH * nkb * kD * 8);
+  }
+  if (fwd || bwd) {
+    const size_t stride = e == SLA2_ENTRY_FORWARD || e == SLA2_ENTRY_FORWARD_SLA1 ? kb : nkb;
+    p.mask = take(BH * nqb * nkb);
+    p.list = take(BH * nqb * stride * 4);
+    p.cnt = take(BH * nqb * 4);
+    p.kc = take(BH * N * kD);
+    p.vc = take(BH * N * kD);
+    p.sk = take(BH * nkb * 4);
+    p.sv = take(BH * nkb * 4);
+    p.hbf = take(BH * nkb * kD * kD * 2);
+    p.htot = take(BH * kD * kD * 4);
+    p.ztot = take(BH * kD * 4);
+  }
+  if (fwd) {
+    p.qc = take(BH * N * kD);
+    p.sq = take(BH * nqb * 4);
+  }
+  if (fwd || bwd || e == SLA2_ENTRY_LINEAR_PRECOMPUTE) {
+    p.z = take(BH * nkb * kD * 4);
+    p.hpart = take(BH * np * kD * kD * 4);
+    p.zpart = take(BH * np * kD * 4);
+  }
+  if (e == SLA2_ENTRY_FORWARD_SLA1) p.ones = take(static_cast<size_t>(g.H) * nqb * 4);
+  if (bwd) {
+    p.tcnt = take(BH * nkb * 4);
+    p.tlist = take(BH * nkb * nqb * 2);
+    p.lse2 = take(BH * N * 4);
+    p.Dd = take(BH * N * 4);
+    p.dht = take(BH * nqb * kD * kD * 2);
+    p.dz = take(BH * nqb * kD * 4);
+    p.dhtot = take(BH * kD * kD * 4);
+    p.dztot = take(BH * kD * 4);
+    p.kcol = take(BH * nkb * kD * 4);
+    p.kmean = take(BH * kD * 4);
+    p.qbf = take(BH * N * kD * 2);
+    p.vbf = take(BH * N * kD * 2);
+    p.ksb = take(BH * N * kD * 2);
+    p.dos = take(BH * N * kD * 2);
+    p.cap = static_cast<int>((nkb + 1) / 2);
+    p.kplan = take(BH * 2 * 4);
+    p.xoff = take(BH * nkb * 4);
+    p.items = take(BH * static_cast<size_t>(p.cap) * 4);
+    p.xpart = take(BH * static_cast<size_t>(p.cap) * kSlot * 4);
+  }
   p.total = o;
   return p;
 }
+
+bool entry_ok(int e) { return e >= SLA2_ENTRY_ROUTER && e <= SLA2_ENTRY_BACKWARD; }
 
 template <typename T>
 T* at(void* ws, size_t off) {
@@ -120,38 +140,15 @@ struct PtrCheck {
   }
 };
 
-sla2_status check_workspace(const Geom& g, const void* ws, size_t bytes) {
-  const size_t need = make_plan(g).total;
+sla2_status check_workspace(const Plan& p, const void* ws, size_t bytes) {
   if (ws == nullptr) return SLA2_ERR_NULL_POINTER;
   if (!aligned16(ws)) return SLA2_ERR_MISALIGNED;
-  if (bytes < need) return SLA2_ERR_WORKSPACE_TOO_SMALL;
+  if (bytes < p.total) return SLA2_ERR_WORKSPACE_TOO_SMALL;
   return SLA2_OK;
 }
 
-// A helper stream and two events per device (created with the device check on the first
-// call, before any graph capture; default priority; kept until the process ends). sla2_forward runs the router's projection and scoring on the
-// helper stream while the key-block precompute runs on the caller's stream: after colmean the
-// two chains are independent (the first is latency-bound, the second bandwidth-bound), and
-// the attention kernel needs both. `ready` forks the helper stream after colmean, `done`
-// joins it before attn. The mutex keeps one call's record/wait pairs together when several
-// host threads share a device.
-struct Fork {
-  hipStream_t side = nullptr;
-  hipEvent_t ready = nullptr, done = nullptr;
-};
-std::mutex g_fork_mu;
-Fork g_fork[64];
-hipError_t make_fork(int dev) {   // caller holds g_fork_mu
-  Fork& f = g_fork[dev];
-  if (f.side == nullptr) {
-    hipError_t e = hipStreamCreateWithFlags(&f.side, hipStreamNonBlocking);
-    if (e == hipSuccess) e = hipEventCreateWithFlags(&f.ready, hipEventDisableTiming);
-    if (e == hipSuccess) e = hipEventCreateWithFlags(&f.done, hipEventDisableTiming);
-    if (e != hipSuccess) return e;
-  }
-  return hipSuccess;
-}
-
+// The one piece of state the library keeps: per device, whether it is a gfx950 (checked, and
+// the scoring kernel's LDS limit raised, on the first call on that device).
 std::atomic<int> g_dev_ok[64];  // 0 unknown, 1 gfx950, 2 other
 
 sla2_status check_device() {
@@ -164,10 +161,6 @@ sla2_status check_device() {
     if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return SLA2_ERR_HIP;
     st = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
     if (st == 1 && configure_router() != hipSuccess) return SLA2_ERR_HIP;
-    if (st == 1) {
-      std::lock_guard<std::mutex> lock(g_fork_mu);
-      if (make_fork(dev) != hipSuccess) return SLA2_ERR_HIP;
-    }
     g_dev_ok[dev].store(st, std::memory_order_relaxed);
   }
   return st == 1 ? SLA2_OK : SLA2_ERR_UNSUPPORTED_DEVICE;
@@ -203,6 +196,15 @@ struct Rec {
       return SLA2_ERR_HIP;                                                  \
   } while (0)
 
+// The workspace's error word (set by a bounded wait of the attention kernel that gave up).
+sla2_status read_error_word(const void* ws, hipStream_t stream) {
+  uint32_t word = 0;
+  if (hipMemcpyAsync(&word, ws, sizeof(word), hipMemcpyDeviceToHost, stream) != hipSuccess ||
+      hipStreamSynchronize(stream) != hipSuccess)
+    return SLA2_ERR_HIP;
+  return word != 0 ? SLA2_ERR_WAIT_TIMEOUT : SLA2_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -216,10 +218,22 @@ int32_t sla2_blocks_kept(int32_t n_key_blocks, float keep_frac) {
   return static_cast<int32_t>(kb);
 }
 
-size_t sla2_workspace_bytes(const sla2_shape* shape) {
+size_t sla2_workspace_bytes(const sla2_shape* shape, sla2_entry entry, float keep_frac) {
   Geom g;
-  if (check_shape(shape, &g) != SLA2_OK) return 0;
-  return make_plan(g).total;
+  if (check_shape(shape, &g) != SLA2_OK || !entry_ok(entry)) return 0;
+  int kb = g.nkb;
+  if (entry == SLA2_ENTRY_FORWARD || entry == SLA2_ENTRY_FORWARD_SLA1) {
+    if (!keep_ok(keep_frac)) return 0;
+    kb = sla2_blocks_kept(g.nkb, keep_frac);
+  }
+  return make_plan(g, entry, kb).total;
+}
+
+sla2_status sla2_workspace_status(const void* workspace, size_t workspace_bytes, void* stream) {
+  if (workspace == nullptr) return SLA2_ERR_NULL_POINTER;
+  if (!aligned16(workspace)) return SLA2_ERR_MISALIGNED;
+  if (workspace_bytes < kAlign) return SLA2_ERR_WORKSPACE_TOO_SMALL;
+  return read_error_word(workspace, static_cast<hipStream_t>(stream));
 }
 
 const char* sla2_status_string(sla2_status s) {
@@ -231,10 +245,15 @@ const char* sla2_status_string(sla2_status s) {
              "B*H <= 65535";
     case SLA2_ERR_BAD_DTYPE: return "unsupported dtype (SLA2_FP32 or SLA2_BF16)";
     case SLA2_ERR_MISALIGNED: return "a device pointer is not 16-byte aligned";
-    case SLA2_ERR_BAD_ARGUMENT: return "bad argument (keep_frac must lie in (0, 1]; quant must be SLA2_QUANT_I8_FP8)";
-    case SLA2_ERR_WORKSPACE_TOO_SMALL: return "workspace smaller than sla2_workspace_bytes()";
+    case SLA2_ERR_BAD_ARGUMENT:
+      return "bad argument (keep_frac must lie in (0, 1]; quant must be SLA2_QUANT_NONE or "
+             "SLA2_QUANT_I8_FP8; tau finite and > 0)";
+    case SLA2_ERR_WORKSPACE_TOO_SMALL:
+      return "workspace smaller than sla2_workspace_bytes() for this entry point";
     case SLA2_ERR_UNSUPPORTED_DEVICE: return "the current HIP device is not gfx950 (MI355X)";
     case SLA2_ERR_HIP: return "a HIP call or kernel launch failed";
+    case SLA2_ERR_WAIT_TIMEOUT:
+      return "a bounded wait inside the attention kernel gave up; the output is unreliable";
   }
   return "unknown status";
 }
@@ -251,17 +270,17 @@ sla2_status sla2_router(const sla2_shape* shape, const void* Q, const void* K,
   pc.opt(mask); pc.opt(scores);
   if (pc.st != SLA2_OK) return pc.st;
   if (!keep_ok(keep_frac)) return SLA2_ERR_BAD_ARGUMENT;
-  if ((st = check_workspace(g, workspace, workspace_bytes)) != SLA2_OK) return st;
+  const int kb = sla2_blocks_kept(g.nkb, keep_frac);
+  const Plan p = make_plan(g, SLA2_ENTRY_ROUTER, kb);
+  if ((st = check_workspace(p, workspace, workspace_bytes)) != SLA2_OK) return st;
   if ((st = check_device()) != SLA2_OK) return st;
   hipStream_t stream = static_cast<hipStream_t>(stream_);
-  const Plan p = make_plan(g);
-  const int kb = sla2_blocks_kept(g.nkb, keep_frac);
   const int dt = shape->dtype == SLA2_FP32 ? 0 : 1;
   Rec rec(static_cast<void**>(nullptr));
   SLA2_LAUNCH(launch_pool(g, dt, Q, K, at<double>(workspace, p.qsum), at<double>(workspace, p.ksum),
                           nullptr, nullptr, nullptr, stream));
   SLA2_LAUNCH(launch_colmean(g, at<double>(workspace, p.ksum), at<double>(workspace, p.mu64),
-                             at<float>(workspace, p.mu32), nullptr, stream));
+                             at<float>(workspace, p.mu32), nullptr, nullptr, stream));
   SLA2_LAUNCH(launch_project(g, at<double>(workspace, p.qsum), at<double>(workspace, p.ksum),
                              at<double>(workspace, p.mu64), proj_q, proj_k,
                              at<double>(workspace, p.A), at<double>(workspace, p.Bt), stream));
@@ -283,18 +302,18 @@ sla2_status sla2_router_soft(const sla2_shape* shape, const void* Q, const void*
   if (pc.st != SLA2_OK) return pc.st;
   if (!keep_ok(keep_frac) || !std::isfinite(tau) || !(tau > 0.f) || !std::isfinite(1.0f / tau))
     return SLA2_ERR_BAD_ARGUMENT;
-  if ((st = check_workspace(g, workspace, workspace_bytes)) != SLA2_OK) return st;
+  const int kb = sla2_blocks_kept(g.nkb, keep_frac);
+  const Plan p = make_plan(g, SLA2_ENTRY_ROUTER_SOFT, kb);
+  if ((st = check_workspace(p, workspace, workspace_bytes)) != SLA2_OK) return st;
   if ((st = check_device()) != SLA2_OK) return st;
   hipStream_t stream = static_cast<hipStream_t>(stream_);
-  const Plan p = make_plan(g);
-  const int kb = sla2_blocks_kept(g.nkb, keep_frac);
   const int dt = shape->dtype == SLA2_FP32 ? 0 : 1;
-  Rec rec(stage_events);
+  Rec rec(stage_events, 5);
   if (rec.mark(stream) != hipSuccess) return SLA2_ERR_HIP;
   SLA2_LAUNCH(launch_pool(g, dt, Q, K, at<double>(workspace, p.qsum), at<double>(workspace, p.ksum),
                           nullptr, nullptr, nullptr, stream));
   SLA2_LAUNCH(launch_colmean(g, at<double>(workspace, p.ksum), at<double>(workspace, p.mu64),
-                             at<float>(workspace, p.mu32), nullptr, stream));
+                             at<float>(workspace, p.mu32), nullptr, nullptr, stream));
   SLA2_LAUNCH(launch_project(g, at<double>(workspace, p.qsum), at<double>(workspace, p.ksum),
                              at<double>(workspace, p.mu64), proj_q, proj_k,
                              at<double>(workspace, p.A), at<double>(workspace, p.Bt), stream));
@@ -314,16 +333,16 @@ sla2_status sla2_linear_precompute(const sla2_shape* shape, const void* K, const
   pc.req(K); pc.req(V); pc.req(k_colmean); pc.req(h_total); pc.req(z_total);
   pc.opt(h); pc.opt(z);
   if (pc.st != SLA2_OK) return pc.st;
-  if ((st = check_workspace(g, workspace, workspace_bytes)) != SLA2_OK) return st;
+  const Plan p = make_plan(g, SLA2_ENTRY_LINEAR_PRECOMPUTE, g.nkb);
+  if ((st = check_workspace(p, workspace, workspace_bytes)) != SLA2_OK) return st;
   if ((st = check_device()) != SLA2_OK) return st;
   hipStream_t stream = static_cast<hipStream_t>(stream_);
-  const Plan p = make_plan(g);
   const int dt = shape->dtype == SLA2_FP32 ? 0 : 1;
   Rec rec(static_cast<void**>(nullptr));
   SLA2_LAUNCH(launch_pool(g, dt, nullptr, K, at<double>(workspace, p.qsum),
                           at<double>(workspace, p.ksum), nullptr, nullptr, nullptr, stream));
   SLA2_LAUNCH(launch_colmean(g, at<double>(workspace, p.ksum), at<double>(workspace, p.mu64),
-                             at<float>(workspace, p.mu32), k_colmean, stream));
+                             at<float>(workspace, p.mu32), k_colmean, nullptr, stream));
   KvArgs kv{};
   kv.mu32 = at<float>(workspace, p.mu32);
   kv.h_f32 = h;
@@ -339,24 +358,27 @@ sla2_status sla2_linear_precompute(const sla2_shape* shape, const void* K, const
 namespace {
 
 // Everything after the block lists exist: K, V operands and the linear precompute, H_tot,
-// then the fused sparse branch + linear branch + combine. Q codes come from the pool pass.
-sla2_status run_branches(const Geom& g, int dt, const void* Q, const void* K, const void* V,
-                         const float* alpha, float* O, const sla2_taps* taps, void* ws,
-                         const Plan& p, int list_stride, Rec& rec, hipStream_t stream,
-                         hipEvent_t join = nullptr) {
+// then the attention kernel (sparse branch + linear branch + combine). Low-bit quantisation:
+// Q codes come from the pool pass and the one attention kernel does everything. Without
+// quantisation: the attention kernel runs its linear branch alone (O = (1 - alpha) O_l), then
+// the fp32 sparse kernel adds alpha O_s.
+sla2_status run_branches(const Geom& g, int dt, sla2_quant quant, const void* Q, const void* K,
+                         const void* V, const float* alpha, float* O, const sla2_taps* taps,
+                         void* ws, const Plan& p, int list_stride, Rec& rec, hipStream_t stream) {
   const sla2_taps none{};
   const sla2_taps& tp = taps ? *taps : none;
-  const float* sq = tp.s_q ? tp.s_q : at<float>(ws, p.sq);
-  float* sk = tp.s_k ? tp.s_k : at<float>(ws, p.sk);
-  float* sv = tp.s_v ? tp.s_v : at<float>(ws, p.sv);
+  const bool lowbit = quant == SLA2_QUANT_I8_FP8;
+  const float* sq = lowbit && tp.s_q ? tp.s_q : at<float>(ws, p.sq);
+  float* sk = lowbit && tp.s_k ? tp.s_k : at<float>(ws, p.sk);
+  float* sv = lowbit && tp.s_v ? tp.s_v : at<float>(ws, p.sv);
   KvArgs kv{};
   kv.mu32 = at<float>(ws, p.mu32);
   kv.kc = at<int8_t>(ws, p.kc);
   kv.vc = at<uint8_t>(ws, p.vc);
   kv.sk = sk;
   kv.sv = sv;
-  kv.k_tap = tp.k_codes;
-  kv.v_tap = tp.v_codes;
+  kv.k_tap = lowbit ? tp.k_codes : nullptr;
+  kv.v_tap = lowbit ? tp.v_codes : nullptr;
   kv.ht_bf16 = at<uint16_t>(ws, p.hbf);
   kv.z = at<float>(ws, p.z);
   kv.hpart = at<float>(ws, p.hpart);
@@ -383,8 +405,23 @@ sla2_status run_branches(const Geom& g, int dt, const void* Q, const void* K, co
   x.O = O;
   x.O_s_tap = tp.O_s;
   x.O_l_tap = tp.O_l;
-  if (join != nullptr && hipStreamWaitEvent(stream, join, 0) != hipSuccess) return SLA2_ERR_HIP;
+  x.err = at<uint32_t>(ws, p.err);
+  x.sparse = lowbit;
   SLA2_LAUNCH(launch_attn(g, dt, Q, x, stream));
+  if (!lowbit) {
+    ExactArgs e{};
+    e.K = K;
+    e.V = V;
+    e.mu32 = at<float>(ws, p.mu32);
+    e.list = x.list;
+    e.list_stride = list_stride;
+    e.cnt = x.cnt;
+    e.alpha = alpha;
+    e.O = O;
+    e.O_s_tap = tp.O_s;
+    SLA2_LAUNCH(launch_attn_exact(g, dt, Q, e, stream));
+  }
+  if (debug_sync()) return read_error_word(ws, stream);
   return SLA2_OK;
 }
 
@@ -393,6 +430,8 @@ void check_taps(PtrCheck& pc, const sla2_taps* t) {
   pc.opt(t->O_s); pc.opt(t->O_l); pc.opt(t->q_codes); pc.opt(t->k_codes); pc.opt(t->v_codes);
   pc.opt(t->s_q); pc.opt(t->s_k); pc.opt(t->s_v); pc.opt(t->k_colmean);
 }
+
+bool quant_ok(sla2_quant q) { return q == SLA2_QUANT_NONE || q == SLA2_QUANT_I8_FP8; }
 
 }  // namespace
 
@@ -407,46 +446,29 @@ sla2_status sla2_forward(const sla2_shape* shape, const void* Q, const void* K, 
   pc.req(Q); pc.req(K); pc.req(V); pc.req(proj_q); pc.req(proj_k); pc.req(alpha); pc.req(O);
   check_taps(pc, taps);
   if (pc.st != SLA2_OK) return pc.st;
-  if (!keep_ok(keep_frac) || quant != SLA2_QUANT_I8_FP8) return SLA2_ERR_BAD_ARGUMENT;
-  if ((st = check_workspace(g, workspace, workspace_bytes)) != SLA2_OK) return st;
+  if (!keep_ok(keep_frac) || !quant_ok(quant)) return SLA2_ERR_BAD_ARGUMENT;
+  const int kb = sla2_blocks_kept(g.nkb, keep_frac);
+  const Plan p = make_plan(g, SLA2_ENTRY_FORWARD, kb);
+  if ((st = check_workspace(p, workspace, workspace_bytes)) != SLA2_OK) return st;
   if ((st = check_device()) != SLA2_OK) return st;
   hipStream_t stream = static_cast<hipStream_t>(stream_);
-  const Plan p = make_plan(g);
-  const int kb = sla2_blocks_kept(g.nkb, keep_frac);
   const int dt = shape->dtype == SLA2_FP32 ? 0 : 1;
+  const bool lowbit = quant == SLA2_QUANT_I8_FP8;
   void* ws = workspace;
   Rec rec(taps);
   if (rec.mark(stream) != hipSuccess) return SLA2_ERR_HIP;
   SLA2_LAUNCH(launch_pool(g, dt, Q, K, at<double>(ws, p.qsum), at<double>(ws, p.ksum),
-                          at<int8_t>(ws, p.qc), taps && taps->s_q ? taps->s_q : at<float>(ws, p.sq),
-                          taps ? taps->q_codes : nullptr, stream));
+                          lowbit ? at<int8_t>(ws, p.qc) : nullptr,
+                          lowbit && taps && taps->s_q ? taps->s_q : at<float>(ws, p.sq),
+                          lowbit && taps ? taps->q_codes : nullptr, stream));
   SLA2_LAUNCH(launch_colmean(g, at<double>(ws, p.ksum), at<double>(ws, p.mu64), at<float>(ws, p.mu32),
-                             taps ? taps->k_colmean : nullptr, stream));
-  auto router_tail = [&](hipStream_t s) -> bool {
-    return launch_project(g, at<double>(ws, p.qsum), at<double>(ws, p.ksum), at<double>(ws, p.mu64),
-                          proj_q, proj_k, at<double>(ws, p.A), at<double>(ws, p.Bt), s) == hipSuccess &&
-           launch_score_topk(g, at<double>(ws, p.A), at<double>(ws, p.Bt), kb,
-                             at<uint8_t>(ws, p.mask), at<int32_t>(ws, p.list), kb,
-                             at<int32_t>(ws, p.cnt), nullptr, s) == hipSuccess;
-  };
-  if (rec.ev != nullptr || debug_sync()) {
-    // per-kernel events or debugging: every kernel in order on the caller's stream
-    SLA2_LAUNCH(launch_project(g, at<double>(ws, p.qsum), at<double>(ws, p.ksum), at<double>(ws, p.mu64),
-                               proj_q, proj_k, at<double>(ws, p.A), at<double>(ws, p.Bt), stream));
-    SLA2_LAUNCH(launch_score_topk(g, at<double>(ws, p.A), at<double>(ws, p.Bt), kb,
-                                  at<uint8_t>(ws, p.mask), at<int32_t>(ws, p.list), kb,
-                                  at<int32_t>(ws, p.cnt), nullptr, stream));
-    return run_branches(g, dt, Q, K, V, alpha, O, taps, ws, p, kb, rec, stream);
-  }
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return SLA2_ERR_HIP;
-  std::lock_guard<std::mutex> lock(g_fork_mu);
-  const Fork* f = &g_fork[dev];
-  if (hipEventRecord(f->ready, stream) != hipSuccess ||
-      hipStreamWaitEvent(f->side, f->ready, 0) != hipSuccess || !router_tail(f->side) ||
-      hipEventRecord(f->done, f->side) != hipSuccess)
-    return SLA2_ERR_HIP;
-  return run_branches(g, dt, Q, K, V, alpha, O, taps, ws, p, kb, rec, stream, f->done);
+                             taps ? taps->k_colmean : nullptr, at<uint32_t>(ws, p.err), stream));
+  SLA2_LAUNCH(launch_project(g, at<double>(ws, p.qsum), at<double>(ws, p.ksum), at<double>(ws, p.mu64),
+                             proj_q, proj_k, at<double>(ws, p.A), at<double>(ws, p.Bt), stream));
+  SLA2_LAUNCH(launch_score_topk(g, at<double>(ws, p.A), at<double>(ws, p.Bt), kb,
+                                at<uint8_t>(ws, p.mask), at<int32_t>(ws, p.list), kb,
+                                at<int32_t>(ws, p.cnt), nullptr, stream));
+  return run_branches(g, dt, quant, Q, K, V, alpha, O, taps, ws, p, kb, rec, stream);
 }
 
 sla2_status sla2_forward_sla1(const sla2_shape* shape, const void* Q, const void* K,
@@ -459,20 +481,22 @@ sla2_status sla2_forward_sla1(const sla2_shape* shape, const void* Q, const void
   PtrCheck pc;
   pc.req(Q); pc.req(K); pc.req(V); pc.req(proj_o); pc.req(O); pc.req(O_l);
   if (pc.st != SLA2_OK) return pc.st;
-  if (!keep_ok(keep_frac) || quant != SLA2_QUANT_I8_FP8) return SLA2_ERR_BAD_ARGUMENT;
-  if ((st = check_workspace(g, workspace, workspace_bytes)) != SLA2_OK) return st;
+  if (!keep_ok(keep_frac) || !quant_ok(quant)) return SLA2_ERR_BAD_ARGUMENT;
+  const int kb = sla2_blocks_kept(g.nkb, keep_frac);
+  const Plan p = make_plan(g, SLA2_ENTRY_FORWARD_SLA1, kb);
+  if ((st = check_workspace(p, workspace, workspace_bytes)) != SLA2_OK) return st;
   if ((st = check_device()) != SLA2_OK) return st;
   hipStream_t stream = static_cast<hipStream_t>(stream_);
-  const Plan p = make_plan(g);
-  const int kb = sla2_blocks_kept(g.nkb, keep_frac);
   const int dt = shape->dtype == SLA2_FP32 ? 0 : 1;
+  const bool lowbit = quant == SLA2_QUANT_I8_FP8;
   void* ws = workspace;
   Rec rec(stage_events);
   if (rec.mark(stream) != hipSuccess) return SLA2_ERR_HIP;
   SLA2_LAUNCH(launch_pool(g, dt, Q, K, at<double>(ws, p.qsum), at<double>(ws, p.ksum),
-                          at<int8_t>(ws, p.qc), at<float>(ws, p.sq), nullptr, stream));
+                          lowbit ? at<int8_t>(ws, p.qc) : nullptr, at<float>(ws, p.sq), nullptr,
+                          stream));
   SLA2_LAUNCH(launch_colmean(g, at<double>(ws, p.ksum), at<double>(ws, p.mu64), at<float>(ws, p.mu32),
-                             nullptr, stream));
+                             nullptr, at<uint32_t>(ws, p.err), stream));
   // the heuristic router: proj_q = proj_k = I (null weights select the identity mode)
   SLA2_LAUNCH(launch_project(g, at<double>(ws, p.qsum), at<double>(ws, p.ksum), at<double>(ws, p.mu64),
                              nullptr, nullptr, at<double>(ws, p.A), at<double>(ws, p.Bt), stream));
@@ -483,7 +507,7 @@ sla2_status sla2_forward_sla1(const sla2_shape* shape, const void* Q, const void
   SLA2_LAUNCH(launch_fill(at<float>(ws, p.ones), g.H * g.nqb, 1.0f, stream));
   sla2_taps tp{};
   tp.O_l = O_l;
-  st = run_branches(g, dt, Q, K, V, at<float>(ws, p.ones), O, &tp, ws, p, kb, rec, stream);
+  st = run_branches(g, dt, quant, Q, K, V, at<float>(ws, p.ones), O, &tp, ws, p, kb, rec, stream);
   if (st != SLA2_OK) return st;
   SLA2_LAUNCH(launch_sla1_mix(g, O_l, proj_o, O, stream));
   return SLA2_OK;
@@ -500,23 +524,25 @@ sla2_status sla2_forward_with_mask(const sla2_shape* shape, const void* Q, const
   pc.req(Q); pc.req(K); pc.req(V); pc.req(mask); pc.req(alpha); pc.req(O);
   check_taps(pc, taps);
   if (pc.st != SLA2_OK) return pc.st;
-  if (quant != SLA2_QUANT_I8_FP8) return SLA2_ERR_BAD_ARGUMENT;
-  if ((st = check_workspace(g, workspace, workspace_bytes)) != SLA2_OK) return st;
+  if (!quant_ok(quant)) return SLA2_ERR_BAD_ARGUMENT;
+  const Plan p = make_plan(g, SLA2_ENTRY_FORWARD_WITH_MASK, g.nkb);
+  if ((st = check_workspace(p, workspace, workspace_bytes)) != SLA2_OK) return st;
   if ((st = check_device()) != SLA2_OK) return st;
   hipStream_t stream = static_cast<hipStream_t>(stream_);
-  const Plan p = make_plan(g);
   const int dt = shape->dtype == SLA2_FP32 ? 0 : 1;
+  const bool lowbit = quant == SLA2_QUANT_I8_FP8;
   void* ws = workspace;
   Rec rec(taps);
   if (rec.mark(stream) != hipSuccess) return SLA2_ERR_HIP;
   SLA2_LAUNCH(launch_pool(g, dt, Q, K, at<double>(ws, p.qsum), at<double>(ws, p.ksum),
-                          at<int8_t>(ws, p.qc), taps && taps->s_q ? taps->s_q : at<float>(ws, p.sq),
-                          taps ? taps->q_codes : nullptr, stream));
+                          lowbit ? at<int8_t>(ws, p.qc) : nullptr,
+                          lowbit && taps && taps->s_q ? taps->s_q : at<float>(ws, p.sq),
+                          lowbit && taps ? taps->q_codes : nullptr, stream));
   SLA2_LAUNCH(launch_colmean(g, at<double>(ws, p.ksum), at<double>(ws, p.mu64), at<float>(ws, p.mu32),
-                             taps ? taps->k_colmean : nullptr, stream));
+                             taps ? taps->k_colmean : nullptr, at<uint32_t>(ws, p.err), stream));
   SLA2_LAUNCH(launch_mask_to_list(g, mask, at<uint8_t>(ws, p.mask), at<int32_t>(ws, p.list),
                                   at<int32_t>(ws, p.cnt), stream));
-  return run_branches(g, dt, Q, K, V, alpha, O, taps, ws, p, g.nkb, rec, stream);
+  return run_branches(g, dt, quant, Q, K, V, alpha, O, taps, ws, p, g.nkb, rec, stream);
 }
 
 sla2_status sla2_backward(const sla2_shape* shape, const void* Q, const void* K, const void* V,
@@ -530,10 +556,10 @@ sla2_status sla2_backward(const sla2_shape* shape, const void* Q, const void* K,
   pc.req(Q); pc.req(K); pc.req(V); pc.req(mask); pc.req(alpha); pc.req(dO);
   pc.req(dQ); pc.req(dK); pc.req(dV); pc.req(dalpha);
   if (pc.st != SLA2_OK) return pc.st;
-  if ((st = check_workspace(g, workspace, workspace_bytes)) != SLA2_OK) return st;
+  const Plan p = make_plan(g, SLA2_ENTRY_BACKWARD, g.nkb);
+  if ((st = check_workspace(p, workspace, workspace_bytes)) != SLA2_OK) return st;
   if ((st = check_device()) != SLA2_OK) return st;
   hipStream_t stream = static_cast<hipStream_t>(stream_);
-  const Plan p = make_plan(g);
   const int dt = shape->dtype == SLA2_FP32 ? 0 : 1;
   void* ws = workspace;
   Rec rec(stage_events, 15);
@@ -542,7 +568,7 @@ sla2_status sla2_backward(const sla2_shape* shape, const void* Q, const void* K,
   SLA2_LAUNCH(launch_pool(g, dt, nullptr, K, at<double>(ws, p.qsum), at<double>(ws, p.ksum),
                           nullptr, nullptr, nullptr, stream));
   SLA2_LAUNCH(launch_colmean(g, at<double>(ws, p.ksum), at<double>(ws, p.mu64),
-                             at<float>(ws, p.mu32), nullptr, stream));
+                             at<float>(ws, p.mu32), nullptr, nullptr, stream));
   KvArgs kv{};
   kv.mu32 = at<float>(ws, p.mu32);
   kv.kc = at<int8_t>(ws, p.kc);

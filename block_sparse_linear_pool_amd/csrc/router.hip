@@ -140,10 +140,12 @@ hipError_t launch_pool(const Geom& g, int dtype, const void* Q, const void* K, d
 __global__ __launch_bounds__(256) void colmean_kernel(const double* __restrict__ ksum,
                                                       double* __restrict__ mu64,
                                                       float* __restrict__ mu32,
-                                                      float* __restrict__ mu32_tap, int nkb,
+                                                      float* __restrict__ mu32_tap,
+                                                      uint32_t* __restrict__ err, int nkb,
                                                       int N) {
   __shared__ double part[16][17];
   const int bh = blockIdx.y, t = threadIdx.x, c = 16 * blockIdx.x + (t & 15), sl = t >> 4;
+  if (err != nullptr && blockIdx.x == 0 && blockIdx.y == 0 && t == 0) *err = 0u;
   const double* p = ksum + static_cast<size_t>(bh) * nkb * kD + c;
   double a0 = 0.0, a1 = 0.0, a2 = 0.0, a3 = 0.0;
   int j = sl;
@@ -167,9 +169,9 @@ __global__ __launch_bounds__(256) void colmean_kernel(const double* __restrict__
 }
 
 hipError_t launch_colmean(const Geom& g, const double* ksum, double* mu64, float* mu32,
-                          float* mu32_tap, hipStream_t s) {
+                          float* mu32_tap, uint32_t* err, hipStream_t s) {
   hipLaunchKernelGGL(colmean_kernel, dim3(kD / 16, g.BH), dim3(256), 0, s, ksum, mu64, mu32,
-                     mu32_tap, g.nkb, g.N);
+                     mu32_tap, err, g.nkb, g.N);
   return hipGetLastError();
 }
 

@@ -237,8 +237,9 @@ hipError_t launch_pool(const Geom& g, int dtype, const void* Q, const void* K, d
                        double* ksum, int8_t* qc, float* sq, int8_t* q_tap, hipStream_t s);
 // one-time per-device set-up (dynamic LDS limit of the scoring kernel)
 hipError_t configure_router();
+// err (optional): the attention kernel's error word, cleared here (one launch before it)
 hipError_t launch_colmean(const Geom& g, const double* ksum, double* mu64, float* mu32,
-                          float* mu32_tap, hipStream_t s);
+                          float* mu32_tap, uint32_t* err, hipStream_t s);
 hipError_t launch_project(const Geom& g, const double* qsum, const double* ksum,
                           const double* mu64, const float* wq, const float* wk, double* A,
                           double* Bt, hipStream_t s);
@@ -303,9 +304,25 @@ struct AttnArgs {
   float* O;
   float* O_s_tap;              // optional
   float* O_l_tap;              // optional
+  uint32_t* err;               // error word: set if a bounded wait gives up
+  bool sparse;                 // false: the linear branch only, O = (1 - alpha) O_l
 };
 hipError_t launch_attn(const Geom& g, int dtype, const void* Q, const AttnArgs& x,
                        hipStream_t s);
+// The unquantised sparse branch (fp32 operands): O += alpha O_s (after the attention kernel
+// ran its linear branch alone); O_s_tap (optional) receives O_s.
+struct ExactArgs {
+  const void *K, *V;
+  const float* mu32;
+  const int32_t* list;
+  int list_stride;
+  const int32_t* cnt;
+  const float* alpha;
+  float* O;
+  float* O_s_tap;
+};
+hipError_t launch_attn_exact(const Geom& g, int dtype, const void* Q, const ExactArgs& x,
+                             hipStream_t s);
 
 // Operands of the backward kernels. Layouts: Q, K, V [BH][N][d] (fp32 or bf16); dO, dQ, dK,
 // dV [BH][N][d] fp32; h_j^T bf16 in fragment order; H_tot standard [a][o] fp32; dH_i^T bf16

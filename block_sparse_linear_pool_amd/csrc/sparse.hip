@@ -94,8 +94,9 @@ __device__ inline void issue_tile(int8_t* kdst, int8_t* vdst, const int8_t* kt, 
 // whole workgroup, and the two groups advance at their own pace). Each wavefront counts its
 // arrivals in a word of its own: an arrival waits for the wavefront's LDS operations to
 // complete, then adds one. A wait polls the group's four words (one 16-byte read) until each
-// has reached the target. The poll is bounded (kSpinLimit sleeps of 64 clocks), so a
-// miscounted wait ends with a wrong result instead of waiting forever. The counter accesses
+// has reached the target. The poll is bounded (kSpinLimit sleeps of 64 clocks): a miscounted
+// wait ends instead of waiting forever, and sets the error word `err` (the host reads it back
+// with sla2_workspace_status), since the output is then unreliable. The counter accesses
 // are written in asm (the poll waits for its read inside the same asm block): the compiler
 // would otherwise treat them as possibly overlapping the loads into LDS still in flight and
 // wait for all of them first.
@@ -116,15 +117,16 @@ __device__ inline void group_arrive(uint32_t group, int w) {
       : "v"(group + 4 * w), "v"(1u)
       : "memory");
 }
-__device__ inline void group_wait(uint32_t group, uint32_t target) {
+__device__ inline void group_wait(uint32_t group, uint32_t target, uint32_t* err) {
   for (int it = 0; it < kSpinLimit; ++it) {
     i32x4 v;
     asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(group) : "memory");
     const uint32_t lo = min(min(static_cast<uint32_t>(v[0]), static_cast<uint32_t>(v[1])),
                             min(static_cast<uint32_t>(v[2]), static_cast<uint32_t>(v[3])));
-    if (__builtin_amdgcn_readfirstlane(lo) >= target) break;
+    if (__builtin_amdgcn_readfirstlane(lo) >= target) return;
     __builtin_amdgcn_s_sleep(1);
   }
+  if (__builtin_amdgcn_mbcnt_lo(~0u, 0u) == 0u) atomicOr(err, 1u);   // lane 0: gave up
 }
 
 __device__ inline int lane_value(int v, int k) { return __builtin_amdgcn_readlane(v, k); }
@@ -160,7 +162,9 @@ struct RowStage {
 
 // Persistent grid: gridDim.x workgroups (one per CU), each taking rows blockIdx.x + gridDim.x k
 // (remapped per XCD); kAttnThreads threads. kTaps: also write O_s and O_l (debug taps).
-template <typename T, bool kTaps>
+// kSparse = false: the linear branch alone, O = (1 - alpha) O_l (the unquantised sparse branch
+// is then added by its own kernel); the sparse wavefronts only do the combine.
+template <typename T, bool kTaps, bool kSparse>
 __global__ __launch_bounds__(kAttnThreads) void attn_kernel(
     const T* __restrict__ Q, const int8_t* __restrict__ qc, const int8_t* __restrict__ kc,
     const uint8_t* __restrict__ vc, const float* __restrict__ sq, const float* __restrict__ sk,
@@ -169,7 +173,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(
     const float* __restrict__ ztot, const uint8_t* __restrict__ mask,
     const int32_t* __restrict__ list, int list_stride, const int32_t* __restrict__ cnt,
     const float* __restrict__ alpha, float* __restrict__ O, float* __restrict__ O_s_tap,
-    float* __restrict__ O_l_tap, int N, int H, int BH) {
+    float* __restrict__ O_l_tap, uint32_t* __restrict__ err, int N, int H, int BH) {
   __shared__ __attribute__((aligned(16))) int8_t smem[kLdsBytes];
   // arrival counters of the sparse (0-3) and linear (4-7) wavefronts: an object of their own
   __shared__ __attribute__((aligned(16))) uint32_t ctr[8];
@@ -226,7 +230,12 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(
     int n, nuns;
     float a;
     bool do_lin;
-    {
+    if constexpr (!kSparse) {
+      n = cnt[row];
+      a = alpha[static_cast<size_t>(rw.bh % H) * nqb + rw.i];
+      nuns = nkb - n;
+      do_lin = nuns > 0 && (kTaps || a != 1.f);
+    } else {
       // block index, s_k and s_v of kept blocks 0 .. 127, one per lane (later ones are read
       // from memory when needed). The first row reads them itself: the list row without
       // waiting for the count n (entries past n are never used, and clamping keeps their
@@ -254,7 +263,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(
         // every sparse wavefront has read the previous row's hand-over (over the rings)
         group_arrive(cs, w);
         ++narr;
-        group_wait(cs, narr);
+        group_wait(cs, narr, err);
         const RowStage& st = stage[kr & 1];
         n = st.n;
         a = st.a;
@@ -339,7 +348,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(
       group_arrive(cs, w);
       ++narr;
       const uint32_t base = narr;   // arrivals after the prologue's
-      group_wait(cs, base);
+      group_wait(cs, base, err);
       // S^T of block k into (s0, s1): key tiles 0-31 and 32-63; the first product takes a
       // literal zero accumulator (the MFMA's inline constant, no register fill)
       auto qk = [&](int k, i32x16& s0, i32x16& s1) {
@@ -359,7 +368,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(
       // with the softmax arithmetic and the P V products with the rescale.
       auto step = [&](int e, const i32x16& c0, const i32x16& c1, i32x16& n0, i32x16& n1,
                       auto small) {
-        if (e >= 1) group_wait(cs, base - 1 + e);
+        if (e >= 1) group_wait(cs, base - 1 + e, err);
         refill(e, small);
         const float c = cq * sk_of(e, small);
         const float svj = sv_of(e, small);
@@ -648,7 +657,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(
   }
   group_arrive(cl, w);
   ++larr;
-  group_wait(cl, larr);   // block list and phi(Q_i) visible
+  group_wait(cl, larr, err);   // block list and phi(Q_i) visible
   // ---- gathers. A = sgn I: fragment m has lane row l32 = 16 m + 8 g + b set at element b; B
   // fragment f = 2 tl4 + m of block j: row d_v = 32 w + l32 of h_j^T, d_phi = 32 tl4 + 16 m +
   // 8 g .. +7, which in fragment order is chunk (8 w + f) * 64 + lane. Each lane also sums
@@ -709,7 +718,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(
   }
   group_arrive(cl, w);
   ++larr;
-  group_wait(cl, larr);   // Z_i visible
+  group_wait(cl, larr, err);   // Z_i visible
   {
     // den = phi(q) . Z_i from the half row of phi in LDS (read by the sparse wavefronts after
     // the hand-over). Chunk c of group G holds d = 16 G + 8 (b / 4) + 4 c + b % 4 at element b.
@@ -804,20 +813,25 @@ static int cu_count() {
   return cache[dev];
 }
 
+template <typename T, bool kTaps, bool kSparse>
+static void launch_attn_v(const Geom& g, const void* Q, const AttnArgs& x, hipStream_t s) {
+  dim3 grid(std::min(g.nqb * g.BH, cu_count()));
+  hipLaunchKernelGGL((attn_kernel<T, kTaps, kSparse>), grid, dim3(kAttnThreads), 0, s,
+                     static_cast<const T*>(Q), x.qc, x.kc, x.vc, x.sq, x.sk, x.sv, x.ht_bf16, x.z,
+                     x.htot_t, x.ztot, x.mask, x.list, x.list_stride, x.cnt, x.alpha, x.O,
+                     x.O_s_tap, x.O_l_tap, x.err, g.N, g.H, g.BH);
+}
+
 template <typename T>
 static void launch_attn_t(const Geom& g, const void* Q, const AttnArgs& x, bool taps,
                           hipStream_t s) {
-  dim3 grid(std::min(g.nqb * g.BH, cu_count()));
-  if (taps)
-    hipLaunchKernelGGL((attn_kernel<T, true>), grid, dim3(kAttnThreads), 0, s, static_cast<const T*>(Q),
-                       x.qc, x.kc, x.vc, x.sq, x.sk, x.sv, x.ht_bf16, x.z, x.htot_t, x.ztot,
-                       x.mask, x.list, x.list_stride, x.cnt, x.alpha, x.O, x.O_s_tap, x.O_l_tap,
-                       g.N, g.H, g.BH);
-  else
-    hipLaunchKernelGGL((attn_kernel<T, false>), grid, dim3(kAttnThreads), 0, s, static_cast<const T*>(Q),
-                       x.qc, x.kc, x.vc, x.sq, x.sk, x.sv, x.ht_bf16, x.z, x.htot_t, x.ztot,
-                       x.mask, x.list, x.list_stride, x.cnt, x.alpha, x.O, x.O_s_tap, x.O_l_tap,
-                       g.N, g.H, g.BH);
+  if (x.sparse) {
+    if (taps) launch_attn_v<T, true, true>(g, Q, x, s);
+    else launch_attn_v<T, false, true>(g, Q, x, s);
+  } else {
+    if (taps) launch_attn_v<T, true, false>(g, Q, x, s);
+    else launch_attn_v<T, false, false>(g, Q, x, s);
+  }
 }
 
 hipError_t launch_attn(const Geom& g, int dtype, const void* Q, const AttnArgs& x,

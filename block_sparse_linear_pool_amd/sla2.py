@@ -20,13 +20,17 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libsla2.so")
 
 SLA2_FP32, SLA2_BF16 = 0, 1
-SLA2_QUANT_I8_FP8 = 1
+SLA2_QUANT_NONE, SLA2_QUANT_I8_FP8 = 0, 1
+QUANT = {"none": SLA2_QUANT_NONE, "i8_fp8": SLA2_QUANT_I8_FP8}
+# sla2_entry: the entry point a workspace is sized for
+ENTRY = {"router": 0, "router_soft": 1, "linear_precompute": 2, "forward": 3,
+         "forward_with_mask": 4, "forward_sla1": 5, "backward": 6}
 D = 128
 
 STATUS = {
     0: "SLA2_OK", 1: "SLA2_ERR_NULL_POINTER", 2: "SLA2_ERR_BAD_SHAPE", 3: "SLA2_ERR_BAD_DTYPE",
     4: "SLA2_ERR_MISALIGNED", 5: "SLA2_ERR_BAD_ARGUMENT", 6: "SLA2_ERR_WORKSPACE_TOO_SMALL",
-    7: "SLA2_ERR_UNSUPPORTED_DEVICE", 8: "SLA2_ERR_HIP",
+    7: "SLA2_ERR_UNSUPPORTED_DEVICE", 8: "SLA2_ERR_HIP", 9: "SLA2_ERR_WAIT_TIMEOUT",
 }
 
 
@@ -73,8 +77,10 @@ def lib():
         vp, sz, f32, i32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_float, ctypes.c_int32
         L.sla2_blocks_kept.argtypes = [i32, f32]
         L.sla2_blocks_kept.restype = i32
-        L.sla2_workspace_bytes.argtypes = [ctypes.POINTER(Shape)]
+        L.sla2_workspace_bytes.argtypes = [ctypes.POINTER(Shape), ctypes.c_int, f32]
         L.sla2_workspace_bytes.restype = sz
+        L.sla2_workspace_status.argtypes = [vp, sz, vp]
+        L.sla2_workspace_status.restype = ctypes.c_int
         L.sla2_status_string.argtypes = [ctypes.c_int]
         L.sla2_status_string.restype = ctypes.c_char_p
         L.sla2_router.argtypes = [ctypes.POINTER(Shape), vp, vp, vp, vp, f32, vp, vp, vp, vp, sz, vp]
@@ -133,18 +139,32 @@ def sla2_blocks_kept(n_key_blocks: int, keep_frac: float) -> int:
     return int(lib().sla2_blocks_kept(int(n_key_blocks), float(keep_frac)))
 
 
-def sla2_workspace_bytes(B: int, H: int, N: int, dtype=torch.bfloat16, d: int = D) -> int:
+def sla2_workspace_bytes(B: int, H: int, N: int, dtype=torch.bfloat16, entry: str = "forward",
+                         keep_frac: float = 1.0, d: int = D) -> int:
+    """Workspace bytes of one entry point (ENTRY names) for this shape; keep_frac matters for
+    "forward" and "forward_sla1" only (0 for an invalid shape, entry or keep_frac)."""
     dt = SLA2_FP32 if dtype == torch.float32 else SLA2_BF16
-    return int(lib().sla2_workspace_bytes(ctypes.byref(Shape(B, H, N, d, dt))))
+    e = ENTRY.get(entry, -1) if isinstance(entry, str) else int(entry)
+    return int(lib().sla2_workspace_bytes(ctypes.byref(Shape(B, H, N, d, dt)), e,
+                                          float(keep_frac)))
+
+
+def sla2_workspace_status(workspace: torch.Tensor) -> int:
+    """Status of the workspace's error word after the work enqueued so far (synchronises the
+    current stream): 0, or 9 (SLA2_ERR_WAIT_TIMEOUT) if a bounded wait in the attention kernel
+    of the last forward on this workspace gave up."""
+    return int(lib().sla2_workspace_status(_ptr(workspace), workspace.numel(),
+                                           _stream(workspace.device)))
 
 
 def sla2_status_string(status: int) -> str:
     return lib().sla2_status_string(int(status)).decode()
 
 
-def workspace_for(q: torch.Tensor) -> torch.Tensor:
+def workspace_for(q: torch.Tensor, entry: str = "forward", keep_frac: float = 1.0) -> torch.Tensor:
+    """A device workspace for `entry` on q's shape (keep_frac: see sla2_workspace_bytes)."""
     B, H, N, _ = q.shape
-    n = sla2_workspace_bytes(B, H, N, q.dtype)
+    n = sla2_workspace_bytes(B, H, N, q.dtype, entry, keep_frac)
     if n == 0:
         raise SLA2Error(2, "sla2_workspace_bytes")
     return torch.empty(n, dtype=torch.uint8, device=q.device)
@@ -165,7 +185,7 @@ def sla2_router(q, k, proj_q, proj_k, keep_frac, want_mask=True, want_scores=Fal
     blocks = torch.empty((B, H, nqb, kb), dtype=torch.int32, device=dev)
     mask = torch.empty((B, H, nqb, nkb), dtype=torch.uint8, device=dev) if want_mask else None
     scores = torch.empty((B, H, nqb, nkb), dtype=torch.float32, device=dev) if want_scores else None
-    ws = workspace if workspace is not None else workspace_for(q)
+    ws = workspace if workspace is not None else workspace_for(q, "router")
     st = lib().sla2_router(ctypes.byref(shp), _ptr(q), _ptr(k), _ptr(proj_q), _ptr(proj_k),
                            float(keep_frac), _ptr(mask), _ptr(blocks), _ptr(scores), _ptr(ws),
                            ws.numel(), _stream(dev))
@@ -186,7 +206,7 @@ def sla2_router_soft(q, k, proj_q, proj_k, keep_frac, tau=0.1, want_lambda=True,
     dev = q.device
     soft = out if out is not None else torch.empty((B, H, nqb, nkb), dtype=torch.float32, device=dev)
     lam = torch.empty((B, H, nqb), dtype=torch.float32, device=dev) if want_lambda else None
-    ws = workspace if workspace is not None else workspace_for(q)
+    ws = workspace if workspace is not None else workspace_for(q, "router_soft")
     evs = None
     if events is not None:
         if len(events) < 5:
@@ -216,7 +236,7 @@ def sla2_linear_precompute(k, v, want_h=True, want_z=True, workspace=None):
         "h_total": torch.empty((B, H, d, d), dtype=torch.float32, device=dev),
         "z_total": torch.empty((B, H, d), dtype=torch.float32, device=dev),
     }
-    ws = workspace if workspace is not None else workspace_for(k)
+    ws = workspace if workspace is not None else workspace_for(k, "linear_precompute")
     st = lib().sla2_linear_precompute(ctypes.byref(shp), _ptr(k), _ptr(v), _ptr(out["k_colmean"]),
                                       _ptr(out["h"]), _ptr(out["z"]), _ptr(out["h_total"]),
                                       _ptr(out["z_total"]), _ptr(ws), ws.numel(), _stream(dev))
@@ -255,9 +275,10 @@ def _make_taps(q, want, events=None):
 
 
 def sla2_forward(q, k, v, proj_q, proj_k, alpha, keep_frac, taps=False, out=None,
-                 workspace=None, events=None):
+                 workspace=None, events=None, quant="i8_fp8"):
     """O [B,H,N,d] fp32; with taps=True (or a collection of tap names) also a dict of taps.
 
+    quant: "i8_fp8" (the low-bit sparse branch) or "none" (fp32 operands).
     `events`: optional list of 10 torch.cuda.Event(enable_timing=True); the library records
     them before the first and after every kernel on the current stream."""
     _contig(q, k, v, proj_q, proj_k, alpha, out)
@@ -265,9 +286,9 @@ def sla2_forward(q, k, v, proj_q, proj_k, alpha, keep_frac, taps=False, out=None
     dev = q.device
     o = out if out is not None else torch.empty(q.shape, dtype=torch.float32, device=dev)
     ctaps, tdict = _make_taps(q, taps, events)
-    ws = workspace if workspace is not None else workspace_for(q)
+    ws = workspace if workspace is not None else workspace_for(q, "forward", keep_frac)
     st = lib().sla2_forward(ctypes.byref(shp), _ptr(q), _ptr(k), _ptr(v), _ptr(proj_q),
-                            _ptr(proj_k), _ptr(alpha), float(keep_frac), SLA2_QUANT_I8_FP8,
+                            _ptr(proj_k), _ptr(alpha), float(keep_frac), QUANT[quant],
                             _ptr(o), ctypes.byref(ctaps) if ctaps else None, _ptr(ws),
                             ws.numel(), _stream(dev))
     _check(st, "sla2_forward")
@@ -275,7 +296,7 @@ def sla2_forward(q, k, v, proj_q, proj_k, alpha, keep_frac, taps=False, out=None
 
 
 def sla2_forward_sla1(q, k, v, proj_o, keep_frac, out=None, o_l=None, workspace=None,
-                      events=None):
+                      events=None, quant="i8_fp8"):
     """The earlier SLA mix (comparison workload): returns (O, O_l) fp32 [B,H,N,d].
 
     `events`: optional list of 10 torch.cuda.Event(enable_timing=True), recorded before the
@@ -285,26 +306,26 @@ def sla2_forward_sla1(q, k, v, proj_o, keep_frac, out=None, o_l=None, workspace=
     dev = q.device
     o = out if out is not None else torch.empty(q.shape, dtype=torch.float32, device=dev)
     ol = o_l if o_l is not None else torch.empty(q.shape, dtype=torch.float32, device=dev)
-    ws = workspace if workspace is not None else workspace_for(q)
+    ws = workspace if workspace is not None else workspace_for(q, "forward_sla1", keep_frac)
     evs = event_array(events) if events is not None else None
     st = lib().sla2_forward_sla1(ctypes.byref(shp), _ptr(q), _ptr(k), _ptr(v), _ptr(proj_o),
-                                 float(keep_frac), SLA2_QUANT_I8_FP8, _ptr(o), _ptr(ol), evs,
+                                 float(keep_frac), QUANT[quant], _ptr(o), _ptr(ol), evs,
                                  _ptr(ws), ws.numel(), _stream(dev))
     _check(st, "sla2_forward_sla1")
     return o, ol
 
 
 def sla2_forward_with_mask(q, k, v, mask, alpha, taps=False, out=None, workspace=None,
-                           events=None):
+                           events=None, quant="i8_fp8"):
     """O [B,H,N,d] fp32 from a caller block mask [B,H,N/128,N/64] uint8."""
     _contig(q, k, v, mask, alpha, out)
     shp = shape_of(q)
     dev = q.device
     o = out if out is not None else torch.empty(q.shape, dtype=torch.float32, device=dev)
     ctaps, tdict = _make_taps(q, taps, events)
-    ws = workspace if workspace is not None else workspace_for(q)
+    ws = workspace if workspace is not None else workspace_for(q, "forward_with_mask")
     st = lib().sla2_forward_with_mask(ctypes.byref(shp), _ptr(q), _ptr(k), _ptr(v), _ptr(mask),
-                                      _ptr(alpha), SLA2_QUANT_I8_FP8, _ptr(o),
+                                      _ptr(alpha), QUANT[quant], _ptr(o),
                                       ctypes.byref(ctaps) if ctaps else None, _ptr(ws),
                                       ws.numel(), _stream(dev))
     _check(st, "sla2_forward_with_mask")
@@ -332,7 +353,7 @@ def sla2_backward(q, k, v, mask, alpha, grad_out, out=None, workspace=None, even
                torch.empty(q.shape, dtype=torch.float32, device=dev),
                torch.empty((B, H, N // 128), dtype=torch.float32, device=dev))
     _contig(*out)
-    ws = workspace if workspace is not None else workspace_for(q)
+    ws = workspace if workspace is not None else workspace_for(q, "backward")
     evs = event_array(events, BACKWARD_STAGES + 1) if events is not None else None
     st = lib().sla2_backward(ctypes.byref(shp), _ptr(q), _ptr(k), _ptr(v), _ptr(mask),
                              _ptr(alpha), _ptr(grad_out), _ptr(out[0]), _ptr(out[1]),

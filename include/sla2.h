@@ -31,19 +31,23 @@
  *              (SLA2_ERR_MISALIGNED otherwise). The library allocates no device
  *              memory and keeps no pointer after a call returns; buffers must stay alive
  *              until the stream has executed the work.
- *   Workspace  Caller-provided device scratch of sla2_workspace_bytes(...) bytes.
- *   Streams    `stream` is a hipStream_t (NULL = the default stream). All work is
- *              ordered on it; no call synchronises or copies device -> host.
- *              sla2_forward (without stage_events) runs the router's projection
- *              and scoring on a helper stream that the library creates once per
- *              device (default priority, with two events): forked from `stream`
- *              after the column mean, joined back before the attention kernel.
+ *   Workspace  Caller-provided device scratch of sla2_workspace_bytes(shape, entry,
+ *              keep_frac) bytes for the entry point it is passed to (each entry
+ *              point asks only for what its kernels use).
+ *   Streams    `stream` is a hipStream_t (NULL = the default stream). Every kernel
+ *              of a call is enqueued on it, in order; no call creates streams or
+ *              events, synchronises or copies device -> host (except
+ *              sla2_workspace_status, which says so).
  *   Errors     Arguments are validated on the host before anything is enqueued;
  *              on error nothing is written. A failed launch returns SLA2_ERR_HIP.
- *              No C++ exception crosses this interface. Calls are re-entrant;
- *              concurrent calls must use distinct workspaces.
+ *              No C++ exception crosses this interface. Calls are re-entrant and
+ *              hold no state between calls (the library caches only the device's
+ *              architecture check); concurrent calls must use distinct workspaces.
+ *              The attention kernel synchronises its wavefronts with bounded
+ *              waits; if one ever gives up, it sets an error word in the workspace
+ *              (read by sla2_workspace_status) instead of hanging.
  *   Debug      Environment SLA2_DEBUG_SYNC=1 synchronises and checks after every
- *              kernel (slow; for debugging only).
+ *              kernel, including the workspace's error word (slow; for debugging).
  */
 #ifndef SLA2_H
 #define SLA2_H
@@ -64,15 +68,32 @@ typedef enum {
     SLA2_ERR_BAD_ARGUMENT = 5,
     SLA2_ERR_WORKSPACE_TOO_SMALL = 6,
     SLA2_ERR_UNSUPPORTED_DEVICE = 7,
-    SLA2_ERR_HIP = 8
+    SLA2_ERR_HIP = 8,
+    SLA2_ERR_WAIT_TIMEOUT = 9
 } sla2_status;
 
 /* element type of Q, K, V */
 typedef enum { SLA2_FP32 = 0, SLA2_BF16 = 1 } sla2_dtype;
 
-/* operand precision of the sparse branch (step 2). Only the low-bit form the
- * pages describe is built: INT8 Q, K per block, OCP E4M3 P, V. */
-typedef enum { SLA2_QUANT_I8_FP8 = 1 } sla2_quant;
+/* operand precision of the sparse branch (step 2 of the summary page's computation
+ * flow quantises Q, K and P, V before the products; Eq. 9 and Eq. 11 of §4 of the
+ * second page hold exactly only without quantisation):
+ *   SLA2_QUANT_NONE    the unquantised branch: S = Q K_s^T / sqrt(d) and P V with
+ *                      fp32 operands (fp32 MFMA, fp32 softmax); the reference form, not
+ *                      the fast one. The code and scale taps are not written.
+ *   SLA2_QUANT_I8_FP8  the low-bit branch: INT8 Q, K per block, OCP E4M3 P, V. */
+typedef enum { SLA2_QUANT_NONE = 0, SLA2_QUANT_I8_FP8 = 1 } sla2_quant;
+
+/* the entry point a workspace is sized for (sla2_workspace_bytes) */
+typedef enum {
+    SLA2_ENTRY_ROUTER = 0,
+    SLA2_ENTRY_ROUTER_SOFT = 1,
+    SLA2_ENTRY_LINEAR_PRECOMPUTE = 2,
+    SLA2_ENTRY_FORWARD = 3,
+    SLA2_ENTRY_FORWARD_WITH_MASK = 4,
+    SLA2_ENTRY_FORWARD_SLA1 = 5,
+    SLA2_ENTRY_BACKWARD = 6
+} sla2_entry;
 
 typedef struct {
     int32_t B, H, N, d;
@@ -108,9 +129,22 @@ typedef struct {
  * n_key_blocks < 1 or keep_frac is not in (0, 1]. */
 int32_t sla2_blocks_kept(int32_t n_key_blocks, float keep_frac);
 
-/* Device workspace, in bytes, that any entry point needs for this shape; the same
- * size serves every call with this shape. Returns 0 for an invalid shape. */
-size_t sla2_workspace_bytes(const sla2_shape *shape);
+/* Device workspace, in bytes, that `entry` needs for this shape. keep_frac matters
+ * only for SLA2_ENTRY_FORWARD and SLA2_ENTRY_FORWARD_SLA1 (their block lists hold
+ * kb = sla2_blocks_kept(N/64, keep_frac) entries per row); other entries ignore it.
+ * Returns 0 for an invalid shape, entry or keep_frac. A workspace sized for one entry
+ * serves any call of that entry with the same shape and a kept count no larger. */
+size_t sla2_workspace_bytes(const sla2_shape *shape, sla2_entry entry, float keep_frac);
+
+/* Error word of a workspace after the work enqueued on `stream` so far: SYNCHRONISES
+ * `stream` and copies 4 bytes device -> host. SLA2_ERR_WAIT_TIMEOUT if a bounded wait
+ * inside the attention kernel of the last forward call that used this workspace gave up
+ * (its output is then unreliable), SLA2_OK otherwise. Meaningful only after a call of
+ * sla2_forward, sla2_forward_with_mask or sla2_forward_sla1 on this workspace (each clears
+ * the word before its attention kernel); the word is the workspace's first 4 bytes.
+ * SLA2_ERR_NULL_POINTER, SLA2_ERR_MISALIGNED or SLA2_ERR_WORKSPACE_TOO_SMALL (< 256 bytes)
+ * for a bad workspace, SLA2_ERR_HIP if the copy fails. */
+sla2_status sla2_workspace_status(const void *workspace, size_t workspace_bytes, void *stream);
 
 /* Static English text for a status code. */
 const char *sla2_status_string(sla2_status status);
