@@ -147,21 +147,36 @@ sla2_status check_workspace(const Plan& p, const void* ws, size_t bytes) {
   return SLA2_OK;
 }
 
-// The one piece of state the library keeps: per device, whether it is a gfx950 (checked, and
-// the scoring kernel's LDS limit raised, on the first call on that device).
+// Scratch of sla2_router_noalloc: a file-scope device array, one copy per GPU, held until the
+// process ends. In host code `scratch` names a host-side stand-in, not device memory: its
+// device address is taken once per device, at that device's set-up (hipGetSymbolAddress with
+// the device current), kept in g_scratch[dev], and only that pointer is ever handed to
+// kernels.
+static __device__ __align__(256) uint8_t scratch[SLA2_NOALLOC_SCRATCH_BYTES];
+
+// The state the library keeps, per device, from its set-up (the first call on that device or
+// sla2_init_device): whether it is a gfx950 (and the scoring kernel's LDS limit raised), and the
+// device address of `scratch`.
 std::atomic<int> g_dev_ok[64];  // 0 unknown, 1 gfx950, 2 other
+std::atomic<void*> g_scratch[64];
 
 sla2_status check_device() {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return SLA2_ERR_HIP;
   if (dev < 0 || dev >= 64) return SLA2_ERR_UNSUPPORTED_DEVICE;
-  int st = g_dev_ok[dev].load(std::memory_order_relaxed);
+  int st = g_dev_ok[dev].load(std::memory_order_acquire);
   if (st == 0) {
     hipDeviceProp_t prop;
     if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return SLA2_ERR_HIP;
     st = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
-    if (st == 1 && configure_router() != hipSuccess) return SLA2_ERR_HIP;
-    g_dev_ok[dev].store(st, std::memory_order_relaxed);
+    if (st == 1) {
+      if (configure_router() != hipSuccess) return SLA2_ERR_HIP;
+      void* ptr = nullptr;
+      if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr)
+        return SLA2_ERR_HIP;
+      g_scratch[dev].store(ptr, std::memory_order_release);
+    }
+    g_dev_ok[dev].store(st, std::memory_order_release);
   }
   return st == 1 ? SLA2_OK : SLA2_ERR_UNSUPPORTED_DEVICE;
 }
@@ -249,7 +264,8 @@ const char* sla2_status_string(sla2_status s) {
       return "bad argument (keep_frac must lie in (0, 1]; quant must be SLA2_QUANT_NONE or "
              "SLA2_QUANT_I8_FP8; tau finite and > 0)";
     case SLA2_ERR_WORKSPACE_TOO_SMALL:
-      return "workspace smaller than sla2_workspace_bytes() for this entry point";
+      return "workspace smaller than sla2_workspace_bytes() for this entry point (for "
+             "sla2_router_noalloc: the shape needs more than SLA2_NOALLOC_SCRATCH_BYTES)";
     case SLA2_ERR_UNSUPPORTED_DEVICE: return "the current HIP device is not gfx950 (MI355X)";
     case SLA2_ERR_HIP: return "a HIP call or kernel launch failed";
     case SLA2_ERR_WAIT_TIMEOUT:
@@ -258,24 +274,29 @@ const char* sla2_status_string(sla2_status s) {
   return "unknown status";
 }
 
-sla2_status sla2_router(const sla2_shape* shape, const void* Q, const void* K,
-                        const float* proj_q, const float* proj_k, float keep_frac,
-                        uint8_t* mask, int32_t* blocks, float* scores, void* workspace,
-                        size_t workspace_bytes, void* stream_) {
-  Geom g;
-  sla2_status st = check_shape(shape, &g);
+sla2_status sla2_init_device(void) { return check_device(); }
+
+namespace {
+
+// Checks of the router's arguments other than the workspace (both router entry points).
+sla2_status check_router_args(const sla2_shape* shape, const void* Q, const void* K,
+                              const float* proj_q, const float* proj_k, float keep_frac,
+                              const uint8_t* mask, const int32_t* blocks, const float* scores,
+                              Geom* g) {
+  sla2_status st = check_shape(shape, g);
   if (st != SLA2_OK) return st;
   PtrCheck pc;
   pc.req(Q); pc.req(K); pc.req(proj_q); pc.req(proj_k); pc.req(blocks);
   pc.opt(mask); pc.opt(scores);
   if (pc.st != SLA2_OK) return pc.st;
   if (!keep_ok(keep_frac)) return SLA2_ERR_BAD_ARGUMENT;
-  const int kb = sla2_blocks_kept(g.nkb, keep_frac);
-  const Plan p = make_plan(g, SLA2_ENTRY_ROUTER, kb);
-  if ((st = check_workspace(p, workspace, workspace_bytes)) != SLA2_OK) return st;
-  if ((st = check_device()) != SLA2_OK) return st;
-  hipStream_t stream = static_cast<hipStream_t>(stream_);
-  const int dt = shape->dtype == SLA2_FP32 ? 0 : 1;
+  return SLA2_OK;
+}
+
+// pool -> colmean -> project -> score_topk with the router's workspace regions at `workspace`.
+sla2_status run_router(const Geom& g, int dt, const void* Q, const void* K, const float* proj_q,
+                       const float* proj_k, int kb, uint8_t* mask, int32_t* blocks,
+                       float* scores, void* workspace, const Plan& p, hipStream_t stream) {
   Rec rec(static_cast<void**>(nullptr));
   SLA2_LAUNCH(launch_pool(g, dt, Q, K, at<double>(workspace, p.qsum), at<double>(workspace, p.ksum),
                           nullptr, nullptr, nullptr, stream));
@@ -287,6 +308,43 @@ sla2_status sla2_router(const sla2_shape* shape, const void* Q, const void* K,
   SLA2_LAUNCH(launch_score_topk(g, at<double>(workspace, p.A), at<double>(workspace, p.Bt), kb,
                                 mask, blocks, kb, nullptr, scores, stream));
   return SLA2_OK;
+}
+
+}  // namespace
+
+sla2_status sla2_router(const sla2_shape* shape, const void* Q, const void* K,
+                        const float* proj_q, const float* proj_k, float keep_frac,
+                        uint8_t* mask, int32_t* blocks, float* scores, void* workspace,
+                        size_t workspace_bytes, void* stream_) {
+  Geom g;
+  sla2_status st = check_router_args(shape, Q, K, proj_q, proj_k, keep_frac, mask, blocks,
+                                     scores, &g);
+  if (st != SLA2_OK) return st;
+  const int kb = sla2_blocks_kept(g.nkb, keep_frac);
+  const Plan p = make_plan(g, SLA2_ENTRY_ROUTER, kb);
+  if ((st = check_workspace(p, workspace, workspace_bytes)) != SLA2_OK) return st;
+  if ((st = check_device()) != SLA2_OK) return st;
+  return run_router(g, shape->dtype == SLA2_FP32 ? 0 : 1, Q, K, proj_q, proj_k, kb, mask,
+                    blocks, scores, workspace, p, static_cast<hipStream_t>(stream_));
+}
+
+sla2_status sla2_router_noalloc(const sla2_shape* shape, const void* Q, const void* K,
+                                const float* proj_q, const float* proj_k, float keep_frac,
+                                uint8_t* mask, int32_t* blocks, float* scores, void* stream_) {
+  Geom g;
+  sla2_status st = check_router_args(shape, Q, K, proj_q, proj_k, keep_frac, mask, blocks,
+                                     scores, &g);
+  if (st != SLA2_OK) return st;
+  const int kb = sla2_blocks_kept(g.nkb, keep_frac);
+  const Plan p = make_plan(g, SLA2_ENTRY_ROUTER, kb);
+  if (p.total > SLA2_NOALLOC_SCRATCH_BYTES) return SLA2_ERR_WORKSPACE_TOO_SMALL;
+  if ((st = check_device()) != SLA2_OK) return st;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return SLA2_ERR_HIP;
+  void* ws = g_scratch[dev].load(std::memory_order_acquire);   // set by check_device
+  if (ws == nullptr) return SLA2_ERR_HIP;
+  return run_router(g, shape->dtype == SLA2_FP32 ? 0 : 1, Q, K, proj_q, proj_k, kb, mask,
+                    blocks, scores, ws, p, static_cast<hipStream_t>(stream_));
 }
 
 sla2_status sla2_router_soft(const sla2_shape* shape, const void* Q, const void* K,

@@ -97,9 +97,12 @@ def lib():
         L.sla2_backward.argtypes = [ctypes.POINTER(Shape), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                     ctypes.POINTER(vp), vp, sz, vp]
         L.sla2_fit_alpha.argtypes = [ctypes.POINTER(Shape), vp, vp, vp, vp, vp]
+        L.sla2_init_device.argtypes = []
+        L.sla2_router_noalloc.argtypes = [ctypes.POINTER(Shape), vp, vp, vp, vp, f32, vp, vp, vp,
+                                          vp]
         for name in ("sla2_router", "sla2_router_soft", "sla2_linear_precompute", "sla2_forward",
                      "sla2_forward_sla1", "sla2_forward_with_mask", "sla2_backward",
-                     "sla2_fit_alpha"):
+                     "sla2_fit_alpha", "sla2_init_device", "sla2_router_noalloc"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -191,6 +194,26 @@ def sla2_router(q, k, proj_q, proj_k, keep_frac, want_mask=True, want_scores=Fal
                            ws.numel(), _stream(dev))
     _check(st, "sla2_router")
     return blocks, mask, scores
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20   # SLA2_NOALLOC_SCRATCH_BYTES
+
+
+def sla2_init_device():
+    """One-time set-up of the current device (done by the first call of any entry point)."""
+    _check(lib().sla2_init_device(), "sla2_init_device")
+
+
+def sla2_router_noalloc(q, k, proj_q, proj_k, keep_frac, blocks, mask=None, scores=None):
+    """sla2_router without a workspace (the library's static per-GPU scratch); the caller
+    passes every output: blocks [B,H,N/128,kb] int32, mask and scores optional. Returns blocks."""
+    _contig(q, k, proj_q, proj_k, blocks, mask, scores)
+    shp = shape_of(q)
+    st = lib().sla2_router_noalloc(ctypes.byref(shp), _ptr(q), _ptr(k), _ptr(proj_q),
+                                   _ptr(proj_k), float(keep_frac), _ptr(mask), _ptr(blocks),
+                                   _ptr(scores), _stream(q.device))
+    _check(st, "sla2_router_noalloc")
+    return blocks
 
 
 def sla2_router_soft(q, k, proj_q, proj_k, keep_frac, tau=0.1, want_lambda=True,

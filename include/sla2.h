@@ -191,6 +191,33 @@ sla2_status sla2_linear_precompute(const sla2_shape *shape, const void *K, const
                                    float *h_total, float *z_total,
                                    void *workspace, size_t workspace_bytes, void *stream);
 
+/* Sets up the current device for the library: checks that it is a gfx950, raises the
+ * scoring kernel's LDS limit, and takes the device address of the static scratch of
+ * sla2_router_noalloc. The first call of any entry point on a device does this by itself;
+ * call it once per device beforehand where that first call must not load code or take
+ * addresses (graph capture, allocation-free loops). SLA2_ERR_UNSUPPORTED_DEVICE on another
+ * GPU, SLA2_ERR_HIP if a HIP call fails. */
+sla2_status sla2_init_device(void);
+
+/* Bytes of the static device scratch of sla2_router_noalloc (one copy per GPU, held until
+ * the process ends): enough for the router at B*H = 12, N = 32768 (19 MB). */
+#define SLA2_NOALLOC_SCRATCH_BYTES (32u << 20)
+
+/* sla2_router for callers that cannot allocate device memory or pass a workspace (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation): the same kernels
+ * and results as sla2_router, with the workspace in a file-scope device array of
+ * SLA2_NOALLOC_SCRATCH_BYTES per GPU instead of caller memory. No allocation of any kind, no
+ * copy. Shapes whose router workspace (sla2_workspace_bytes(shape, SLA2_ENTRY_ROUTER, ...))
+ * exceeds the scratch return SLA2_ERR_WORKSPACE_TOO_SMALL before anything is enqueued; other
+ * arguments and errors as sla2_router. Every call on one GPU shares that GPU's scratch, which
+ * keeps the last call's contents (each call overwrites every region it reads before reading
+ * it): calls that overlap on one GPU (different streams or threads, or an earlier call's work
+ * still pending on another stream) race. Call sla2_init_device first where even the device's
+ * one-time set-up must happen beforehand. */
+sla2_status sla2_router_noalloc(const sla2_shape *shape, const void *Q, const void *K,
+                                const float *proj_q, const float *proj_k, float keep_frac,
+                                uint8_t *mask, int32_t *blocks, float *scores, void *stream);
+
 /* The whole forward: router, sparse branch, linear branch and combine.
  *   O [B,H,N,d] fp32 (required); taps optional (NULL). */
 sla2_status sla2_forward(const sla2_shape *shape, const void *Q, const void *K, const void *V,

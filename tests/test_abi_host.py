@@ -28,6 +28,7 @@ def test_library_exports_every_declared_symbol():
     L = sla2.lib()
     names = declared_functions()
     assert set(names) == {"sla2_blocks_kept", "sla2_workspace_bytes", "sla2_workspace_status",
+                          "sla2_init_device", "sla2_router_noalloc",
                           "sla2_status_string", "sla2_router", "sla2_router_soft",
                           "sla2_linear_precompute", "sla2_forward", "sla2_forward_sla1",
                           "sla2_forward_with_mask", "sla2_backward", "sla2_fit_alpha"}
@@ -209,3 +210,18 @@ def test_workspace_status_validates_before_touching_the_device():
     assert L.sla2_workspace_status(MIS, 1024, None) == MISAL
     assert L.sla2_workspace_status(A, 255, None) == WS
     assert "bounded wait" in sla2.sla2_status_string(TIMEOUT)
+
+
+def test_noalloc_router_validates_on_the_host():
+    L = sla2.lib()
+    s = shape()
+    f = L.sla2_router_noalloc
+    assert f(ctypes.byref(s), A, A, A, A, 0.25, None, None, None, None) == NULL   # blocks required
+    assert f(ctypes.byref(s), A, A, A, A, 0.0, None, A, None, None) == ARG
+    assert f(ctypes.byref(s), A, A, A, MIS, 0.25, None, A, None, None) == MISAL
+    assert f(ctypes.byref(shape(N=100)), A, A, A, A, 0.25, None, A, None, None) == SHAPE
+    # the router at B*H = 12, N = 32768 fits the static scratch; at H = 40, N = 75648 it does not
+    assert need(shape(1, 12, 32768), "router") <= sla2.NOALLOC_SCRATCH_BYTES
+    big = shape(1, 40, 75648)
+    assert need(big, "router") > sla2.NOALLOC_SCRATCH_BYTES
+    assert f(ctypes.byref(big), A, A, A, A, 0.05, None, A, None, None) == WS
