@@ -199,9 +199,9 @@ def run_router_soft(args, w, q, k, wq, wk, keep):
         log(args, f"[bench]   {n:11s} {t * 1e3:9.1f} us  {kernels[n]}")
     dom = names[int(np.argmax(per))]
     t_dom = float(np.max(per)) * 1e-3
-    if acc.kernel_bound(dom) == "mfma_fp64":
+    if acc.kernel_bound(dom) == "mfma_fp32":
         achieved = acc.kernel_flops(prob, dom) / t_dom / 1e12
-        peak, unit, bound = acc.MI355X_PEAK["fp64_tflops"], "TFLOP/s", "mfma"
+        peak, unit, bound = acc.MI355X_PEAK["mfma_fp32_tflops"], "TFLOP/s", "mfma"
     else:
         achieved = acc.kernel_bytes(prob, dom) / t_dom / 1e9
         peak, unit, bound = acc.MI355X_PEAK["hbm_gbs"], "GB/s", "hbm"
@@ -211,7 +211,7 @@ def run_router_soft(args, w, q, k, wq, wk, keep):
         "value": round(rows / (ms * 1e-3), 1),
         "unit": "query-block rows/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f64+f32",
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d,
                    "input_dtype": w.dtype, "keep_frac": keep, "kb": kb, "tau": args.tau},

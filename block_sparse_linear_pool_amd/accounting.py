@@ -19,6 +19,7 @@ MI355X_PEAK = {
     "mfma_i8_fp8_tflops": 5000.0,  # dense INT8 / FP8 MFMA
     "mfma_bf16_tflops": 2500.0,
     "fp64_tflops": 78.6,
+    "mfma_fp32_tflops": 157.3,  # dense fp32 MFMA
 }
 
 KERNELS_FORWARD = ("pool", "colmean", "project", "score_topk", "kv_prep", "linear_total", "attn")
@@ -122,8 +123,15 @@ def kernel_bytes(p: Problem, name: str) -> float:
         # Q, K read; fp64 block sums written
         return 2 * E * p.in_bytes + BH * (p.nqb + p.nkb) * d * 8
     if name == "score_soft":
-        # A, B^T (fp64) read; the fp32 soft mask and lambda written
-        return BH * (p.nqb + p.nkb) * d * 8 + BH * p.nqb * p.nkb * 4 + BH * p.nqb * 4
+        # fp64 Q block sums and fp32 B read; the fp32 soft mask and lambda written
+        return BH * p.nqb * d * 8 + BH * p.nkb * d * 4 + BH * p.nqb * p.nkb * 4 + BH * p.nqb * 4
+    if name == "score_topk":
+        # fp64 Q block sums and fp32 B read; mask, lists and counts written
+        return (BH * p.nqb * d * 8 + BH * p.nkb * d * 4 + BH * p.nqb * p.nkb
+                + BH * p.nqb * (p.kb + 1) * 4)
+    if name == "project":
+        # fp64 key-block sums read, fp32 B written
+        return BH * p.nkb * d * (8 + 4)
     if name == "sla1_mix":
         # O_l and O read, O written
         return 3 * E * 4
@@ -146,9 +154,10 @@ def kernel_flops(p: Problem, name: str) -> float:
         # (4 N d^2 per head) is reported separately by linear_flops()
         return sparse_flops(p)
     if name in ("score_topk", "score_soft"):
-        return 2.0 * p.BH * p.nqb * p.nkb * p.d
+        # A = Qbar Wq and the logits A B^T
+        return 2.0 * p.BH * p.nqb * p.d * p.d + 2.0 * p.BH * p.nqb * p.nkb * p.d
     if name == "project":
-        return 2.0 * p.BH * (p.nqb + p.nkb) * p.d * p.d
+        return 2.0 * p.BH * p.nkb * p.d * p.d
     if name in ("kv_prep", "sla1_mix"):
         return 2.0 * p.BH * p.N * p.d * p.d
     if name == "bwd_lin_q":
@@ -168,12 +177,12 @@ def kernel_flops(p: Problem, name: str) -> float:
 
 def kernel_bound(name: str) -> str:
     """Roofline a kernel is priced against: attn on the INT8/FP8 matrix peak, the backward's
-    matrix kernels on the bf16 matrix peak, the fp64 logits kernels on the fp64 matrix peak,
-    everything else on HBM bandwidth."""
+    matrix kernels on the bf16 matrix peak, the router's fp32 projections and logits on the
+    fp32 matrix peak, everything else on HBM bandwidth."""
     if name == "attn":
         return "mfma"
     if name in ("bwd_q", "bwd_kv", "bwd_kv_extra", "bwd_lin_q"):
         return "mfma_bf16"
     if name in ("score_topk", "score_soft", "project"):
-        return "mfma_fp64"
+        return "mfma_fp32"
     return "hbm"

@@ -9,12 +9,13 @@
 //               the forward) the INT8 codes of Q for the sparse branch.
 //   colmean     mu = colmean(K) from the key-block sums (all blocks have 64 rows), the
 //               K smoothing of §7 note 1 of the second page.
-//   project     A = Qbar Wq, B = (Kbar - mu) Wk in fp64 (Kbar - mu is the mean of K_s); with
-//               no weights the identity (the heuristic router of the earlier SLA).
-//   score_topk  G = A B^T / sqrt(d) in fp64 into LDS, then one wavefront per query
-//               block selects the kb largest logits exactly (ties to the lower index)
-//               and writes the mask and the ascending block list; in its soft mode the
-//               SoftTop-k mask sigma(P_c / tau + lambda_i) of the training-time router.
+//   project     B = (Kbar - mu) Wk in fp32 (Kbar - mu is the mean of K_s); with no weights
+//               the identity (the heuristic router of the earlier SLA).
+//   score_topk  per 16 query blocks: A = Qbar Wq, G = A B^T / sqrt(d) in fp32 (MFMA) into
+//               LDS, then one wavefront per query block selects the kb largest logits
+//               exactly (ties to the lower index) and writes the mask and the ascending
+//               block list; in its soft mode the SoftTop-k mask sigma(P_c / tau + lambda_i)
+//               of the training-time router.
 //   fill        a constant into a float array (alpha = 1 for the earlier SLA mix).
 // Ranking by the logit G is ranking by P_c = softmax(G): softmax is monotone per row.
 #include "sla2_common.h"
@@ -175,86 +176,67 @@ hipError_t launch_colmean(const Geom& g, const double* ksum, double* mu64, float
   return hipGetLastError();
 }
 
-// fp64 MFMA 16x16x4 operand/result layout (gfx950): lane l supplies A[l % 16][l / 16] and
-// B[l / 16][l % 16]; result register i of lane l is D[l / 16 + 4 i][l % 16].
-__device__ inline f64x4 mfma_f64(double a, double b, f64x4 c) {
-  return __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, c, 0, 0, 0);
+// fp32 MFMA 16x16x4 operand/result layout (gfx950): lane l supplies A[l % 16][k] and
+// B[k][l % 16] for the K slot k = l / 16; result register i of lane l is D[4 (l / 16) + i][l % 16].
+// K step s of a 128-long dot product pairs slot k with element 32 k + s, so a lane's 32 operand
+// values of one row are contiguous in memory.
+__device__ inline f32x4 mfma_f32(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
-// ---------------------------------------------------------------- project
-// grid (ceil(nqb/16) + ceil(nkb/16), BH), 256 threads. A workgroup takes 16 rows of either
-// Qbar (W = proj_q) or Kbar - mu (W = proj_k); wavefront w the 16x16 fp64 MFMA output tiles
-// of columns 32 w .. 32 w + 31, the two K = 128 chains interleaved, all W values of both
-// tiles loaded up front.
-constexpr int kXPad = kD + 1;
-__global__ __launch_bounds__(256) void project_kernel(
-    const double* __restrict__ qsum, const double* __restrict__ ksum,
-    const double* __restrict__ mu64, const float* __restrict__ wq, const float* __restrict__ wk,
-    double* __restrict__ A, double* __restrict__ Bt, int nqb, int nkb, int H, int identity) {
-  __shared__ double xs[16][kXPad];
+// ---------------------------------------------------------------- project (key side)
+// B = (Kbar - mu) Wk, fp32 [BH][nkb][d] row-major (Kbar - mu is the mean of K_s; no weights:
+// the identity, the heuristic router of the earlier SLA). grid (ceil(nkb / 16), BH), 256
+// threads: 16 key blocks per workgroup, wavefront w the output columns 32 w .. 32 w + 31 (two
+// 16 x 16 tiles, K = 128 in 32 fp32 MFMA steps each).
+constexpr int kXPad = kD + 4;
+__global__ __launch_bounds__(256) void project_kernel(const double* __restrict__ ksum,
+                                                      const double* __restrict__ mu64,
+                                                      const float* __restrict__ wk,
+                                                      float* __restrict__ B, int nkb, int H) {
+  __shared__ float xs[16][kXPad];
   const int bh = blockIdx.y, h = bh % H, t = threadIdx.x;
-  const int lane = t & 63, w = t >> 6;
-  const int qwg = (nqb + 15) / 16;
-  const bool is_q = static_cast<int>(blockIdx.x) < qwg;
-  const int r0 = 16 * (is_q ? blockIdx.x : blockIdx.x - qwg);
-  const int nrows = is_q ? nqb : nkb;
-  const double* src = is_q ? qsum + static_cast<size_t>(bh) * nqb * kD
-                           : ksum + static_cast<size_t>(bh) * nkb * kD;
-  const double scale = is_q ? 1.0 / kBQ : 1.0 / kBK;
+  const int lane = t & 63, w = t >> 6, ra = lane & 15, kq = lane >> 4;
+  const int r0 = 16 * blockIdx.x;
+  const double* src = ksum + static_cast<size_t>(bh) * nkb * kD;
   for (int e = t; e < 16 * kD; e += 256) {
     const int r = e >> 7, c = e & 127;
-    double v = 0.0;
-    if (r0 + r < nrows) {
-      v = src[static_cast<size_t>(r0 + r) * kD + c] * scale;
-      if (!is_q) v -= mu64[bh * kD + c];
-    }
-    xs[r][c] = v;
+    xs[r][c] = r0 + r < nkb
+                   ? static_cast<float>(src[static_cast<size_t>(r0 + r) * kD + c] * (1.0 / kBK) -
+                                        mu64[bh * kD + c])
+                   : 0.f;
   }
-  if (identity) {
-    // proj_q = proj_k = I (the heuristic router of the earlier SLA): A = Qbar, B = Kbar - mu
-    __syncthreads();
+  __syncthreads();
+  float* out = B + static_cast<size_t>(bh) * nkb * kD;
+  if (wk == nullptr) {
     for (int e = t; e < 16 * kD; e += 256) {
       const int r = e >> 7, c = e & 127;
-      if (r0 + r >= nrows) continue;
-      if (is_q) A[(static_cast<size_t>(bh) * nqb + r0 + r) * kD + c] = xs[r][c];
-      else Bt[(static_cast<size_t>(bh) * kD + c) * nkb + r0 + r] = xs[r][c];
+      if (r0 + r < nkb) out[static_cast<size_t>(r0 + r) * kD + c] = xs[r][c];
     }
     return;
   }
-  const float* W = (is_q ? wq : wk) + static_cast<size_t>(h) * kD * kD;
-  const int ra = lane & 15, kq = lane >> 4;
-  float wv[2][32];
+  const float* W = wk + static_cast<size_t>(h) * kD * kD;
+  f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll 8
+  for (int s = 0; s < 32; ++s) {
+    const int k = 32 * kq + s;
+    const float x = xs[ra][k];
+    acc[0] = mfma_f32(x, W[k * kD + 32 * w + ra], acc[0]);
+    acc[1] = mfma_f32(x, W[k * kD + 32 * w + 16 + ra], acc[1]);
+  }
 #pragma unroll
   for (int u = 0; u < 2; ++u)
 #pragma unroll
-    for (int s = 0; s < 32; ++s) wv[u][s] = W[(4 * s + kq) * kD + 32 * w + 16 * u + ra];
-  __syncthreads();
-  f64x4 acc[2] = {f64x4{0.0, 0.0, 0.0, 0.0}, f64x4{0.0, 0.0, 0.0, 0.0}};
-#pragma unroll
-  for (int s = 0; s < 32; ++s) {
-    const double x = xs[ra][4 * s + kq];
-    acc[0] = mfma_f64(x, static_cast<double>(wv[0][s]), acc[0]);
-    acc[1] = mfma_f64(x, static_cast<double>(wv[1][s]), acc[1]);
-  }
-#pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int col = 32 * w + 16 * u + ra;
-#pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int r = r0 + kq + 4 * i;
-      if (r >= nrows) continue;
-      if (is_q) A[(static_cast<size_t>(bh) * nqb + r) * kD + col] = acc[u][i];
-      else Bt[(static_cast<size_t>(bh) * kD + col) * nkb + r] = acc[u][i];
+      const int r = r0 + 4 * kq + i;
+      if (r < nkb) out[static_cast<size_t>(r) * kD + 32 * w + 16 * u + ra] = acc[u][i];
     }
-  }
 }
 
-hipError_t launch_project(const Geom& g, const double* qsum, const double* ksum,
-                          const double* mu64, const float* wq, const float* wk, double* A,
-                          double* Bt, hipStream_t s) {
-  dim3 grid((g.nqb + 15) / 16 + (g.nkb + 15) / 16, g.BH);
-  hipLaunchKernelGGL(project_kernel, grid, dim3(256), 0, s, qsum, ksum, mu64, wq, wk, A, Bt,
-                     g.nqb, g.nkb, g.H, wq == nullptr ? 1 : 0);
+hipError_t launch_project(const Geom& g, const double* ksum, const double* mu64, const float* wk,
+                          float* B, hipStream_t s) {
+  hipLaunchKernelGGL(project_kernel, dim3((g.nkb + 15) / 16, g.BH), dim3(256), 0, s, ksum, mu64,
+                     wk, B, g.nkb, g.H);
   return hipGetLastError();
 }
 
@@ -270,10 +252,10 @@ hipError_t launch_fill(float* p, int n, float v, hipStream_t s) {
 }
 
 // ---------------------------------------------------------------- score + top-k
-__device__ inline uint64_t order_key(double g) {
-  // monotone map from finite doubles to unsigned integers (larger g -> larger key)
-  const uint64_t b = static_cast<uint64_t>(__double_as_longlong(g));
-  return (b >> 63) ? ~b : (b | (1ull << 63));
+__device__ inline uint32_t order_key(float g) {
+  // monotone map from finite floats to unsigned integers (larger g -> larger key)
+  const uint32_t b = __float_as_uint(g);
+  return (b >> 31) ? ~b : (b | 0x80000000u);
 }
 
 __device__ inline int count_below_lane(uint64_t m) {
@@ -281,10 +263,10 @@ __device__ inline int count_below_lane(uint64_t m) {
                                    __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0));
 }
 
-// Rows of logits one workgroup keeps in LDS (fp64), by key-block count.
-// Eight rows (two per wavefront in the selection) keep enough workgroups in flight; the logit
-// tiles are 16 rows tall, the other 8 zero.
-__host__ __device__ inline int score_rows(int nkb) { return nkb <= 2048 ? 8 : 4; }
+// Query-block rows one scoring workgroup handles (its logits stay in LDS as fp32, at most
+// 128 KB): 16 (one full MFMA tile) up to 2048 key blocks, else 8.
+__host__ __device__ inline int score_rows(int nkb) { return nkb <= 2048 ? 16 : 8; }
+constexpr int kScoreThreads = 1024;   // 16 wavefronts: one row each in the selection
 
 // Kept set of one row, exact (ties to the lower index), by one wavefront. The row's keys
 // sit in registers, E per lane (key j = lane + 64 e). T is built bit by bit from the top as
@@ -292,18 +274,18 @@ __host__ __device__ inline int score_rows(int nkb) { return nkb <= 2048 ? 8 : 4;
 // popcounts, stopping early once #{key >= T} is exactly kb. Then every key > T is kept, plus
 // the lowest-index keys equal to T up to kb.
 template <int E>
-__device__ void select_row(const double* g, int nkb, int kb, int lane, size_t row,
+__device__ void select_row(const float* g, int nkb, int kb, int lane, size_t row,
                            int32_t* __restrict__ list, int list_stride,
                            uint8_t* __restrict__ mask) {
-  uint64_t key[E];
+  uint32_t key[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) {
     const int j = lane + 64 * e;
-    key[e] = j < nkb ? order_key(g[j]) : 0ull;   // finite keys are >= 1
+    key[e] = j < nkb ? order_key(g[j]) : 0u;   // finite keys are >= 1
   }
-  uint64_t T = 0;
-  for (int bit = 63; bit >= 0; --bit) {
-    const uint64_t cand = T | (1ull << bit);
+  uint32_t T = 0;
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t cand = T | (1u << bit);
     int c = 0;
 #pragma unroll
     for (int e = 0; e < E; ++e) c += __popcll(__ballot(key[e] >= cand));
@@ -335,212 +317,190 @@ __device__ void select_row(const double* g, int nkb, int kb, int lane, size_t ro
   }
 }
 
-// SoftTop-k of rows (training-time router, §4 Eq. 17 of the second page), two rows per
-// wavefront at once (their reductions overlap): P_c = softmax(g) in fp64, x = P_c / tau in
-// fp32, then lambda with f(lambda) = sum_j sigma(x_j + lambda) = kb. The root lies in the
-// bracket [L - max x, L - min x], L = log(kb / (nkb - kb)) (every term is at most, resp. at
-// least, kb / nkb at its ends). Safeguarded Newton in fp32, 16 steps from the uniform-row
-// root L - 1 / (tau nkb): each step evaluates f and f' = sum sigma (1 - sigma), narrows the
-// bracket at the current point, and takes the Newton step, or the bracket midpoint when that
-// step leaves the bracket. Row sums are butterfly reductions (every lane holds the same
-// value, fixed order: deterministic). kb = nkb gives ones and lambda = +inf. Writes
-// soft[row][j] = sigma(x_j + lambda) and lam[row]; `valid[q]` false skips row q's writes.
+// SoftTop-k of one row (training-time router, §4 Eq. 17 of the second page): P_c = softmax(g)
+// in fp64, x = P_c / tau in fp32, then lambda with f(lambda) = sum_j sigma(x_j + lambda) = kb.
+// The root lies in the bracket [L - max x, L - min x], L = log(kb / (nkb - kb)) (every term is
+// at most, resp. at least, kb / nkb at its ends). Safeguarded Newton in fp32, 16 steps from
+// the uniform-row root L - 1 / (tau nkb): each step evaluates f and f' = sum sigma (1 - sigma),
+// narrows the bracket at the current point, and takes the Newton step, or the bracket midpoint
+// when that step leaves the bracket. Row sums are butterfly reductions (every lane holds the
+// same value, fixed order: deterministic). kb = nkb gives ones and lambda = +inf. Writes
+// soft[row][j] = sigma(x_j + lambda) and lam[row].
 template <int E>
-__device__ void soft_rows(const double* const (&g)[2], const bool (&valid)[2], int nkb, int kb,
-                          float inv_tau, int lane, const size_t (&row)[2],
-                          float* __restrict__ soft, float* __restrict__ lam) {
-  float x[2][E];
-#pragma unroll
-  for (int q = 0; q < 2; ++q) {
+__device__ void soft_row(const float* g, int nkb, int kb, float inv_tau, int lane, size_t row,
+                         float* __restrict__ soft, float* __restrict__ lam) {
+  float x[E];
+  {
     double ex[E];
     double mx = -1.0e300;
 #pragma unroll
     for (int e = 0; e < E; ++e) {
       const int j = lane + 64 * e;
-      if (j < nkb) mx = fmax(mx, g[q][j]);
+      if (j < nkb) mx = fmax(mx, static_cast<double>(g[j]));
     }
     for (int o = 32; o >= 1; o >>= 1) mx = fmax(mx, __shfl_xor(mx, o));
     double sum = 0.0;
 #pragma unroll
     for (int e = 0; e < E; ++e) {
       const int j = lane + 64 * e;
-      ex[e] = j < nkb ? exp(g[q][min(j, nkb - 1)] - mx) : 0.0;
+      ex[e] = j < nkb ? exp(static_cast<double>(g[min(j, nkb - 1)]) - mx) : 0.0;
       sum += ex[e];
     }
     for (int o = 32; o >= 1; o >>= 1) sum += __shfl_xor(sum, o);
 #pragma unroll
-    for (int e = 0; e < E; ++e)
-      x[q][e] = static_cast<float>(ex[e] / sum * static_cast<double>(inv_tau));
+    for (int e = 0; e < E; ++e) x[e] = static_cast<float>(ex[e] / sum * static_cast<double>(inv_tau));
   }
-  float lv[2] = {INFINITY, INFINITY};
+  float lv = INFINITY;
   if (kb < nkb) {
-    float lo[2], hi[2];
     const float L = logf(static_cast<float>(kb) / static_cast<float>(nkb - kb));
+    float xmax = -INFINITY, xmin = INFINITY;
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      float xmax = -INFINITY, xmin = INFINITY;
+    for (int e = 0; e < E; ++e)
+      if (lane + 64 * e < nkb) {
+        xmax = fmaxf(xmax, x[e]);
+        xmin = fminf(xmin, x[e]);
+      }
+    for (int o = 32; o >= 1; o >>= 1) {
+      xmax = fmaxf(xmax, __shfl_xor(xmax, o));
+      xmin = fminf(xmin, __shfl_xor(xmin, o));
+    }
+    float lo = L - xmax, hi = L - xmin;
+    lv = fminf(fmaxf(L - inv_tau / static_cast<float>(nkb), lo), hi);
+    const float kbf = static_cast<float>(kb);
+    for (int it = 0; it < 16; ++it) {
+      float f = 0.f, df = 0.f;
 #pragma unroll
       for (int e = 0; e < E; ++e)
         if (lane + 64 * e < nkb) {
-          xmax = fmaxf(xmax, x[q][e]);
-          xmin = fminf(xmin, x[q][e]);
+          const float sg = 1.0f / (1.0f + __expf(-(x[e] + lv)));
+          f += sg;
+          df = fmaf(sg, 1.0f - sg, df);
         }
       for (int o = 32; o >= 1; o >>= 1) {
-        xmax = fmaxf(xmax, __shfl_xor(xmax, o));
-        xmin = fminf(xmin, __shfl_xor(xmin, o));
+        f += __shfl_xor(f, o);
+        df += __shfl_xor(df, o);
       }
-      lo[q] = L - xmax;
-      hi[q] = L - xmin;
-      lv[q] = fminf(fmaxf(L - inv_tau / static_cast<float>(nkb), lo[q]), hi[q]);
-    }
-    const float kbf = static_cast<float>(kb);
-    for (int it = 0; it < 16; ++it) {
-      float f[2], df[2];
-#pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        f[q] = 0.f;
-        df[q] = 0.f;
-#pragma unroll
-        for (int e = 0; e < E; ++e)
-          if (lane + 64 * e < nkb) {
-            const float sg = 1.0f / (1.0f + __expf(-(x[q][e] + lv[q])));
-            f[q] += sg;
-            df[q] = fmaf(sg, 1.0f - sg, df[q]);
-          }
-      }
-      for (int o = 32; o >= 1; o >>= 1) {
-#pragma unroll
-        for (int q = 0; q < 2; ++q) {
-          f[q] += __shfl_xor(f[q], o);
-          df[q] += __shfl_xor(df[q], o);
-        }
-      }
-#pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        const float fq = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(f[q])));
-        const float dq = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(df[q])));
-        if (fq < kbf) lo[q] = lv[q];
-        else hi[q] = lv[q];
-        const float nt = lv[q] - (fq - kbf) / dq;
-        lv[q] = (nt > lo[q] && nt < hi[q]) ? nt : 0.5f * (lo[q] + hi[q]);
-      }
+      const float fq = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(f)));
+      const float dq = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(df)));
+      if (fq < kbf) lo = lv;
+      else hi = lv;
+      const float nt = lv - (fq - kbf) / dq;
+      lv = (nt > lo && nt < hi) ? nt : 0.5f * (lo + hi);
     }
   }
 #pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    if (!valid[q]) continue;
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-      const int j = lane + 64 * e;
-      if (j < nkb)
-        soft[row[q] * nkb + j] = kb < nkb ? 1.0f / (1.0f + __expf(-(x[q][e] + lv[q]))) : 1.0f;
-    }
-    if (lane == 0 && lam) lam[row[q]] = lv[q];
+  for (int e = 0; e < E; ++e) {
+    const int j = lane + 64 * e;
+    if (j < nkb) soft[row * nkb + j] = kb < nkb ? 1.0f / (1.0f + __expf(-(x[e] + lv))) : 1.0f;
   }
+  if (lane == 0 && lam) lam[row] = lv;
 }
 
-// grid (ceil(nqb / RT), BH), 256 threads, RT = score_rows(nkb); dynamic LDS RT * nkb doubles.
-// E = keys per lane held in registers (nkb <= 64 E). kSoft: the SoftTop-k mask and lambda
-// (soft, lam, inv_tau) instead of the hard selection.
+// grid (ceil(nqb / RT), BH), kScoreThreads threads, RT = score_rows(nkb); dynamic LDS RT * nkb
+// floats. Per workgroup: the RT query-block rows' A = Qbar Wq (fp32 MFMA; no weights: the
+// identity), then the logits G = A B^T / sqrt(d) of every key block (fp32 MFMA, 16 x 16 tiles
+// dealt to the 16 wavefronts; a lane's B operand is 32 contiguous floats of one key block's
+// row), then one row per wavefront: the exact hard Top-k (kSoft = false: mask, ascending list,
+// count and the optional fp32 P_c) or the SoftTop-k mask and lambda (kSoft). E = keys per lane
+// held in registers (nkb <= 64 E).
 template <int E, bool kSoft>
-__global__ __launch_bounds__(256) void score_topk_kernel(
-    const double* __restrict__ A, const double* __restrict__ Bt, int nqb, int nkb, int kb,
-    uint8_t* __restrict__ mask, int32_t* __restrict__ list, int list_stride,
-    int32_t* __restrict__ cnt, float* __restrict__ scores, float inv_tau,
+__global__ __launch_bounds__(kScoreThreads) void score_topk_kernel(
+    const double* __restrict__ qsum, const float* __restrict__ wq, const float* __restrict__ B,
+    int nqb, int nkb, int H, int kb, uint8_t* __restrict__ mask, int32_t* __restrict__ list,
+    int list_stride, int32_t* __restrict__ cnt, float* __restrict__ scores, float inv_tau,
     float* __restrict__ soft, float* __restrict__ lam) {
-  extern __shared__ double G[];                 // [RT][nkb]
-  __shared__ double as[16][kXPad];
+  extern __shared__ float G[];                 // [RT][nkb]
+  __shared__ float xs[16][kXPad];              // Qbar rows
+  __shared__ float as[16][kXPad];              // A rows
   const int RT = score_rows(nkb);
-  const int bh = blockIdx.y, t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int bh = blockIdx.y, h = bh % H, t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int ra = lane & 15, kq = lane >> 4;
   const int i0 = blockIdx.x * RT;
-  for (int e = t; e < 16 * kD; e += 256) {
-    const int r = e >> 7, k = e & 127;
+  for (int e = t; e < 16 * kD; e += kScoreThreads) {
+    const int r = e >> 7, c = e & 127;
     const int i = i0 + r;
-    as[r][k] = (r < RT && i < nqb) ? A[(static_cast<size_t>(bh) * nqb + i) * kD + k] : 0.0;
+    xs[r][c] = (r < RT && i < nqb)
+                   ? static_cast<float>(qsum[(static_cast<size_t>(bh) * nqb + i) * kD + c] *
+                                        (1.0 / kBQ))
+                   : 0.f;
   }
   __syncthreads();
-  // logits: 16-column fp64 MFMA tiles, round-robin over the wavefronts
-  const double inv_sqrt_d = 0.088388347648318440550;  // 1/sqrt(128)
-  const double* bt = Bt + static_cast<size_t>(bh) * kD * nkb;
-  const int ntile = (nkb + 15) >> 4, ra = lane & 15, kq = lane >> 4;
-  // This wavefront's column tiles ct = w, w + 4, ...; step q = tile q / 2, k half q % 2. The B
-  // values of step q + 1 load while step q multiplies (two register buffers); loads are
-  // unconditional at clamped addresses and masked in the product.
-  const int nsteps = 2 * ((ntile - w + 3) / 4);
-  auto bload = [&](double (&dst)[16], int q) {
-    const int qc = min(q, nsteps - 1);
-    const int col = min(16 * (w + 4 * (qc >> 1)) + ra, nkb - 1);
-    const double* bc = bt + col + static_cast<size_t>(64 * (qc & 1) + kq) * nkb;
+  if (wq == nullptr) {
+    for (int e = t; e < 16 * kD; e += kScoreThreads) as[e >> 7][e & 127] = xs[e >> 7][e & 127];
+  } else if (w < 8) {
+    // output columns 16 w .. 16 w + 15
+    const float* W = wq + static_cast<size_t>(h) * kD * kD;
+    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 8
+    for (int s = 0; s < 32; ++s) {
+      const int k = 32 * kq + s;
+      acc = mfma_f32(xs[ra][k], W[k * kD + 16 * w + ra], acc);
+    }
 #pragma unroll
-    for (int s = 0; s < 16; ++s) dst[s] = bc[static_cast<size_t>(4 * s) * nkb];
-  };
-  if (nsteps > 0) {
-    double bb[2][16];
-    bload(bb[0], 0);
-    f64x4 acc = f64x4{0.0, 0.0, 0.0, 0.0};
-    for (int q0 = 0; q0 < nsteps; q0 += 2) {
+    for (int i = 0; i < 4; ++i) as[4 * kq + i][16 * w + ra] = acc[i];
+  }
+  __syncthreads();
+  {
+    // this lane's A operand: row ra, elements 32 kq .. 32 kq + 31
+    float a_op[32];
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {   // u = k half of step q0 + u
-        bload(bb[u ^ 1], q0 + u + 1);
-        const int col = 16 * (w + 4 * (q0 >> 1)) + ra;
-        const bool ok = col < nkb;
-        if (u == 0) acc = f64x4{0.0, 0.0, 0.0, 0.0};
+    for (int s = 0; s < 32; ++s) a_op[s] = as[ra][32 * kq + s];
+    const float inv_sqrt_d = 0.088388347648318440f;   // 1/sqrt(128)
+    const float* Bh = B + static_cast<size_t>(bh) * nkb * kD;
+    const int ntile = (nkb + 15) >> 4;
+    for (int ct = w; ct < ntile; ct += kScoreThreads / 64) {
+      const int col = 16 * ct + ra;
+      const f32x4* bp = reinterpret_cast<const f32x4*>(Bh + static_cast<size_t>(min(col, nkb - 1)) * kD + 32 * kq);
+      f32x4 bv[8];
 #pragma unroll
-        for (int s = 0; s < 16; ++s)
-          acc = mfma_f64(as[ra][4 * (16 * u + s) + kq], ok ? bb[u][s] : 0.0, acc);
-        if (u == 1) {
+      for (int u = 0; u < 8; ++u) bv[u] = bp[u];
+      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int r = kq + 4 * i;
-            if (ok && r < RT) G[r * nkb + col] = acc[i] * inv_sqrt_d + 0.0;  // +0.0: no -0
-          }
+      for (int s = 0; s < 32; ++s) acc = mfma_f32(a_op[s], bv[s >> 2][s & 3], acc);
+      if (col < nkb) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = 4 * kq + i;
+          if (r < RT) G[r * nkb + col] = acc[i] * inv_sqrt_d + 0.0f;   // +0: no -0
         }
       }
     }
   }
   __syncthreads();
-  const int nE = (nkb + 63) >> 6;
-  for (int r = w; r < RT; r += 4) {
-    const int i = i0 + r;
-    if (i >= nqb) break;
-    const double* g = G + r * nkb;
-    const size_t row = static_cast<size_t>(bh) * nqb + i;
-    if constexpr (kSoft) {
-      // rows r and r + 4 together (the second only when it exists)
-      const int r2 = r + 4;
-      const bool v2 = r2 < RT && i0 + r2 < nqb;
-      const double* const gq[2] = {g, G + (v2 ? r2 : r) * nkb};
-      const bool vq[2] = {true, v2};
-      const size_t rq[2] = {row, row + (v2 ? 4 : 0)};
-      soft_rows<E>(gq, vq, nkb, kb, inv_tau, lane, rq, soft, lam);
-      if (RT > 4) break;   // this wavefront's rows are done (RT <= 8)
-      continue;
+  const int r = w;
+  const int i = i0 + r;
+  if (r >= RT || i >= nqb) return;
+  const float* g = G + r * nkb;
+  const size_t row = static_cast<size_t>(bh) * nqb + i;
+  if constexpr (kSoft) {
+    soft_row<E>(g, nkb, kb, inv_tau, lane, row, soft, lam);
+    return;
+  }
+  select_row<E>(g, nkb, kb, lane, row, list, list_stride, mask);
+  if (lane == 0 && cnt) cnt[row] = kb;
+  if (scores) {
+    const int nE = (nkb + 63) >> 6;
+    double mx = -1.0e300;
+    for (int e = 0; e < nE; ++e) {
+      const int j = lane + 64 * e;
+      if (j < nkb) mx = fmax(mx, static_cast<double>(g[j]));
     }
-    select_row<E>(g, nkb, kb, lane, row, list, list_stride, mask);
-    if (lane == 0 && cnt) cnt[row] = kb;
-    if (scores) {
-      double mx = -1.0e300;
-      for (int e = 0; e < nE; ++e) {
-        const int j = lane + 64 * e;
-        if (j < nkb) mx = fmax(mx, g[j]);
-      }
-      for (int o = 32; o >= 1; o >>= 1) mx = fmax(mx, __shfl_xor(mx, o));
-      double sum = 0.0;
-      for (int e = 0; e < nE; ++e) {
-        const int j = lane + 64 * e;
-        if (j < nkb) sum += exp(g[j] - mx);
-      }
-      for (int o = 32; o >= 1; o >>= 1) sum += __shfl_xor(sum, o);
-      for (int e = 0; e < nE; ++e) {
-        const int j = lane + 64 * e;
-        if (j < nkb) scores[row * nkb + j] = static_cast<float>(exp(g[j] - mx) / sum);
-      }
+    for (int o = 32; o >= 1; o >>= 1) mx = fmax(mx, __shfl_xor(mx, o));
+    double sum = 0.0;
+    for (int e = 0; e < nE; ++e) {
+      const int j = lane + 64 * e;
+      if (j < nkb) sum += exp(static_cast<double>(g[j]) - mx);
+    }
+    for (int o = 32; o >= 1; o >>= 1) sum += __shfl_xor(sum, o);
+    for (int e = 0; e < nE; ++e) {
+      const int j = lane + 64 * e;
+      if (j < nkb) scores[row * nkb + j] = static_cast<float>(exp(static_cast<double>(g[j]) - mx) / sum);
     }
   }
 }
 
 hipError_t configure_router() {
-  // largest dynamic LDS: RT * nkb doubles = 128 KB at the top of every RT class
+  // largest dynamic LDS: RT * nkb floats = 128 KB at the top of every RT class
   const void* fns[] = {reinterpret_cast<const void*>(&score_topk_kernel<8, false>),
                        reinterpret_cast<const void*>(&score_topk_kernel<16, false>),
                        reinterpret_cast<const void*>(&score_topk_kernel<32, false>),
@@ -551,46 +511,43 @@ hipError_t configure_router() {
                        reinterpret_cast<const void*>(&score_topk_kernel<64, true>)};
   for (const void* f : fns) {
     const hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                             16 * 1024 * 8);
+                                             32 * 1024 * 4);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
 }
 
 template <bool kSoft>
-static void launch_score_t(const Geom& g, const double* A, const double* Bt, int kb, uint8_t* mask,
-                           int32_t* list, int list_stride, int32_t* cnt, float* scores,
-                           float inv_tau, float* soft, float* lam, hipStream_t s) {
+static void launch_score_t(const Geom& g, const double* qsum, const float* wq, const float* B,
+                           int kb, uint8_t* mask, int32_t* list, int list_stride, int32_t* cnt,
+                           float* scores, float inv_tau, float* soft, float* lam, hipStream_t s) {
   const int RT = score_rows(g.nkb);
   dim3 grid((g.nqb + RT - 1) / RT, g.BH);
-  const size_t lds = static_cast<size_t>(RT) * g.nkb * sizeof(double);
+  const size_t lds = static_cast<size_t>(RT) * g.nkb * sizeof(float);
   const int E = (g.nkb + 63) / 64;
-  if (E <= 8)
-    hipLaunchKernelGGL((score_topk_kernel<8, kSoft>), grid, dim3(256), lds, s, A, Bt, g.nqb, g.nkb,
-                       kb, mask, list, list_stride, cnt, scores, inv_tau, soft, lam);
-  else if (E <= 16)
-    hipLaunchKernelGGL((score_topk_kernel<16, kSoft>), grid, dim3(256), lds, s, A, Bt, g.nqb,
-                       g.nkb, kb, mask, list, list_stride, cnt, scores, inv_tau, soft, lam);
-  else if (E <= 32)
-    hipLaunchKernelGGL((score_topk_kernel<32, kSoft>), grid, dim3(256), lds, s, A, Bt, g.nqb,
-                       g.nkb, kb, mask, list, list_stride, cnt, scores, inv_tau, soft, lam);
-  else
-    hipLaunchKernelGGL((score_topk_kernel<64, kSoft>), grid, dim3(256), lds, s, A, Bt, g.nqb,
-                       g.nkb, kb, mask, list, list_stride, cnt, scores, inv_tau, soft, lam);
+#define SLA2_SCORE(EE)                                                                          \
+  hipLaunchKernelGGL((score_topk_kernel<EE, kSoft>), grid, dim3(kScoreThreads), lds, s, qsum, wq, \
+                     B, g.nqb, g.nkb, g.H, kb, mask, list, list_stride, cnt, scores, inv_tau,    \
+                     soft, lam)
+  if (E <= 8) SLA2_SCORE(8);
+  else if (E <= 16) SLA2_SCORE(16);
+  else if (E <= 32) SLA2_SCORE(32);
+  else SLA2_SCORE(64);
+#undef SLA2_SCORE
 }
 
-hipError_t launch_score_topk(const Geom& g, const double* A, const double* Bt, int kb,
-                             uint8_t* mask, int32_t* list, int list_stride, int32_t* cnt,
+hipError_t launch_score_topk(const Geom& g, const double* qsum, const float* wq, const float* B,
+                             int kb, uint8_t* mask, int32_t* list, int list_stride, int32_t* cnt,
                              float* scores, hipStream_t s) {
-  launch_score_t<false>(g, A, Bt, kb, mask, list, list_stride, cnt, scores, 0.f, nullptr,
+  launch_score_t<false>(g, qsum, wq, B, kb, mask, list, list_stride, cnt, scores, 0.f, nullptr,
                         nullptr, s);
   return hipGetLastError();
 }
 
-hipError_t launch_score_soft(const Geom& g, const double* A, const double* Bt, int kb,
-                             float inv_tau, float* soft, float* lam, hipStream_t s) {
-  launch_score_t<true>(g, A, Bt, kb, nullptr, nullptr, 0, nullptr, nullptr, inv_tau, soft, lam,
-                       s);
+hipError_t launch_score_soft(const Geom& g, const double* qsum, const float* wq, const float* B,
+                             int kb, float inv_tau, float* soft, float* lam, hipStream_t s) {
+  launch_score_t<true>(g, qsum, wq, B, kb, nullptr, nullptr, 0, nullptr, nullptr, inv_tau, soft,
+                       lam, s);
   return hipGetLastError();
 }
 

@@ -153,7 +153,8 @@ const char *sla2_status_string(sla2_status status);
  *   mask   [B,H,N/128,N/64] uint8 M_c, or NULL
  *   blocks [B,H,N/128,kb] int32 kept key-block indices, ascending (required)
  *   scores [B,H,N/128,N/64] fp32 P_c, or NULL
- * Ranking is by the logit in fp64; equal logits go to the lower block index. */
+ * The projections and logits are fp32 (MFMA; fp64 block sums and colmean); ranking is by
+ * the fp32 logit, exact, equal logits to the lower block index. */
 sla2_status sla2_router(const sla2_shape *shape, const void *Q, const void *K,
                         const float *proj_q, const float *proj_k, float keep_frac,
                         uint8_t *mask, int32_t *blocks, float *scores,
@@ -166,7 +167,7 @@ sla2_status sla2_router(const sla2_shape *shape, const void *Q, const void *K,
  *   stage_events  NULL, or 5 caller-created hipEvent_t handles recorded on the stream
  *             before the first kernel and after each of pool, colmean, project and
  *             score_soft (the SoftTop-k pass), so consecutive pairs time each kernel
- * P_c as in sla2_router (fp64 logits and softmax). lambda_i makes every row sum to kb =
+ * P_c as in sla2_router (fp32 logits, fp64 softmax). lambda_i makes every row sum to kb =
  * sla2_blocks_kept(N/64, keep_frac), so the mask tends to the hard Top-k mask as tau -> 0;
  * it is found in fp32 by 16 safeguarded Newton steps inside the bracket [L - max x,
  * L - min x], x = P_c / tau, L = log(kb / (N/64 - kb)) (the pages' binary search, with
@@ -200,7 +201,7 @@ sla2_status sla2_linear_precompute(const sla2_shape *shape, const void *K, const
 sla2_status sla2_init_device(void);
 
 /* Bytes of the static device scratch of sla2_router_noalloc (one copy per GPU, held until
- * the process ends): enough for the router at B*H = 12, N = 32768 (19 MB). */
+ * the process ends): enough for the router at B*H = 12, N = 32768 (13 MB). */
 #define SLA2_NOALLOC_SCRATCH_BYTES (32u << 20)
 
 /* sla2_router for callers that cannot allocate device memory or pass a workspace (code under
