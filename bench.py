@@ -607,7 +607,9 @@ def main():
     traffic = stored_traffic(args, dom, w, keep)
     roofline = {"kernel": dom, "bound": acc.kernel_bound(dom), "achieved": round(achieved, 2),
                 "peak": peak, "unit": unit, "frac": round(achieved / peak, 4),
-                "traffic": traffic, "avg_launch_ms": round(t_dom * 1e3, 5)}
+                "traffic": traffic, "avg_launch_ms": round(t_dom * 1e3, 5),
+                "whole_call_frac": round(acc.whole_call_frac(prob, ms * 1e-3), 4),
+                "whole_call_min_bytes": round(acc.call_min_bytes(prob))}
 
     full = acc.full_attention_flops(prob)
     result = {

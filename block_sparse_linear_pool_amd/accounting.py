@@ -84,6 +84,22 @@ def linear_flops(p: Problem) -> float:
     return 2.0 * p.BH * p.N * p.d * p.d + 2.0 * p.BH * p.N * p.d * p.d
 
 
+def call_min_bytes(p: Problem) -> float:
+    """Algorithmic-minimum HBM bytes of one forward call: Q, K, V read once, K read a second
+    time for its column mean, O written in fp32, and the per-key-block h_j^T (bf16) and z_j
+    (fp32) written once and read once."""
+    return (3 * p.E * p.in_bytes + p.E * p.in_bytes + p.E * 4
+            + 2 * p.BH * p.nkb * (p.d * p.d * 2 + p.d * 4))
+
+
+def whole_call_frac(p: Problem, seconds: float) -> float:
+    """Whole-call roofline fraction: the larger of the sparse branch's matrix time at the
+    dense INT8/FP8 peak and the minimum bytes' time at the HBM peak, over the call's time."""
+    t_mfma = sparse_flops(p) / (MI355X_PEAK["mfma_i8_fp8_tflops"] * 1e12)
+    t_hbm = call_min_bytes(p) / (MI355X_PEAK["hbm_gbs"] * 1e9)
+    return max(t_mfma, t_hbm) / seconds
+
+
 def full_attention_backward_flops(p: Problem) -> float:
     """Dense attention backward: five N x N x d products (S, dP, dV, dK, dQ), 10 B H N^2 d."""
     return 10.0 * p.BH * p.N * p.N * p.d
