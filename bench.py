@@ -42,14 +42,16 @@ def parse():
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run plain device copies of a known size (the calibration "
                          "workload for the FETCH_SIZE / WRITE_SIZE counters), then exit")
-    ap.add_argument("--op", choices=("forward", "router_soft", "sla1", "backward", "fit_alpha"),
+    ap.add_argument("--op", choices=("forward", "router_soft", "sla1", "backward", "fit_alpha",
+                                     "router_grad"),
                     default="forward",
                     help="forward (default): the inference forward; router_soft: the SoftTop-k "
                          "router (training-time step 1); sla1: the earlier SLA mix O = O_s + "
                          "O_l Wo with the heuristic router (comparison workload); backward: "
                          "the gradients dQ, dK, dV, dalpha for the router's mask; fit_alpha: "
-                         "the stage-1 alpha fit against full attention; each prints its own "
-                         "JSON line")
+                         "the stage-1 alpha fit against full attention; router_grad: the "
+                         "stage-1 router gradient (straight-through SoftTop-k) against full "
+                         "attention; each prints its own JSON line")
     ap.add_argument("--tau", type=float, default=0.1, help="SoftTop-k temperature (router_soft)")
     ap.add_argument("--quiet", action="store_true")
     return ap.parse_args()
@@ -508,6 +510,54 @@ def run_fit_alpha(args, w, q, k, v, wq, wk, keep):
     print(json.dumps(result), flush=True)
 
 
+def run_router_grad(args, w, gq, gk, gv, gwq, gwk, ga, keep):
+    """Times sla2_router_grad (the whole call: router, unquantised forward, the dense pass over
+    every block pair, the router's chain) against O_full = the library's unquantised forward
+    with every block kept (dense softmax attention), computed once before the timed region."""
+    import torch
+
+    from block_sparse_linear_pool_amd import accounting as acc
+    from block_sparse_linear_pool_amd import sla2
+
+    dev = gq.device
+    eye = torch.eye(w.d, device=dev).expand(w.H, w.d, w.d).contiguous()
+    ones = torch.ones((w.H, w.n_qb), device=dev)
+    o_full = sla2.sla2_forward(gq, gk, gv, eye, eye, ones, 1.0, quant="none")
+    ws = sla2.workspace_for(gq, "router_grad", keep)
+    for _ in range(args.warmup):
+        res = sla2.sla2_router_grad(gq, gk, gv, gwq, gwk, ga, keep, o_full, tau=args.tau,
+                                    workspace=ws)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        res = sla2.sla2_router_grad(gq, gk, gv, gwq, gwk, ga, keep, o_full, tau=args.tau,
+                                    workspace=ws)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    kb = sla2.sla2_blocks_kept(w.n_kb, keep)
+    prob = acc.Problem(w.B, w.H, w.N, kb, in_bytes=2 if w.dtype == "bf16" else 4)
+    fl = acc.kernel_flops(prob, "mask_grad")
+    tf = fl / (ms * 1e-3) / 1e12
+    loss = res[0].cpu().numpy()
+    result = {
+        "metric": "SLA2 stage-1 router gradient ms/call, N=32768 H=12 d=128 @97%",
+        "value": round(ms, 4), "unit": "ms per call", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": False,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f16+fp32", "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d,
+                   "input_dtype": w.dtype, "keep_frac": keep, "kb": kb, "tau": args.tau,
+                   "dense_pass_tflop_per_call": round(fl / 1e12, 3),
+                   "loss_mean_per_head": float(loss.mean())},
+        "roofline": {"kernel": "whole call (dense pass FLOPs)", "bound": "mfma_f16",
+                     "achieved": round(tf, 2), "peak": acc.MI355X_PEAK["mfma_bf16_tflops"],
+                     "unit": "TFLOP/s", "frac": round(tf / acc.MI355X_PEAK["mfma_bf16_tflops"], 4),
+                     "traffic": None, "avg_launch_ms": round(ms, 5)},
+    }
+    print(json.dumps(result), flush=True)
+
+
 def main():
     args = parse()
     if args.copy_probe:
@@ -559,6 +609,10 @@ def main():
     if args.op == "fit_alpha":
         del gq, gk, gv, out, ws
         run_fit_alpha(args, w, q, k, v, wq, wk, keep)
+        return
+    if args.op == "router_grad":
+        del out, ws
+        run_router_grad(args, w, gq, gk, gv, gwq, gwk, ga, keep)
         return
 
     def step(events=None):

@@ -165,6 +165,9 @@ def kernel_bytes(p: Problem, name: str) -> float:
 
 
 def kernel_flops(p: Problem, name: str) -> float:
+    if name == "mask_grad":
+        # stage-1 router gradient: S, delta V^T and phi(Q) phi(K_s)^T for every block pair
+        return 3 * 2.0 * 128 * 64 * p.d * p.BH * p.nqb * p.nkb
     if name == "attn":
         # INT8/FP8 sparse-branch work only: the linear branch's bf16 phi(Q) H product
         # (4 N d^2 per head) is reported separately by linear_flops()

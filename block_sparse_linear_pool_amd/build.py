@@ -15,7 +15,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libsla2.so")
-SOURCES = ["router.hip", "linear.hip", "sparse.hip", "exact.hip", "backward.hip", "fit.hip", "abi.cpp"]
+SOURCES = ["router.hip", "linear.hip", "sparse.hip", "exact.hip", "backward.hip", "fit.hip", "grad.hip", "abi.cpp"]
 
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",

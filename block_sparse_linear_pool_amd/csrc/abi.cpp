@@ -8,6 +8,7 @@
 #include "../../include/sla2.h"
 #include "sla2_common.h"
 #include "sla2_fit.h"
+#include "sla2_grad.h"
 
 using namespace sla2;
 
@@ -22,7 +23,9 @@ struct Plan {
       hpart, zpart, htot, ztot, ones;
   // backward only
   size_t tcnt, tlist, lse2, Dd, dht, dz, dhtot, dztot, kcol, kmean, qbf, vbf, ksb, dos, kplan,
-      xoff, items, xpart, total;
+      xoff, items, xpart;
+  // stage-1 router gradient only
+  size_t soft, lam, gO, gOs, gOl, ks16, v16, pk16, gmask, lossp, Arow, dA, dG, dB, total;
   int cap;
 };
 
@@ -38,10 +41,11 @@ Plan make_plan(const Geom& g, sla2_entry e, int kb) {
   };
   const size_t BH = static_cast<size_t>(g.BH), N = g.N, nqb = g.nqb, nkb = g.nkb;
   const size_t np = (nkb + kKpPerWg - 1) / kKpPerWg;
+  const bool grad = e == SLA2_ENTRY_ROUTER_GRAD;
   const bool router = e == SLA2_ENTRY_ROUTER || e == SLA2_ENTRY_ROUTER_SOFT ||
-                      e == SLA2_ENTRY_FORWARD || e == SLA2_ENTRY_FORWARD_SLA1;
+                      e == SLA2_ENTRY_FORWARD || e == SLA2_ENTRY_FORWARD_SLA1 || grad;
   const bool fwd = e == SLA2_ENTRY_FORWARD || e == SLA2_ENTRY_FORWARD_WITH_MASK ||
-                   e == SLA2_ENTRY_FORWARD_SLA1;
+                   e == SLA2_ENTRY_FORWARD_SLA1 || grad;
   const bool bwd = e == SLA2_ENTRY_BACKWARD;
   p.err = take(4);                     // offset 0: the attention kernel's error word
   p.qsum = take(BH * nqb * kD * 8);    // the pool pass always writes both block sums
@@ -50,7 +54,8 @@ Plan make_plan(const Geom& g, sla2_entry e, int kb) {
   p.mu32 = take(BH * kD * 4);
   if (router) p.Bt = take(BH * nkb * kD * 4);   // B = (Kbar - mu) Wk, fp32
   if (fwd || bwd) {
-    const size_t stride = e == SLA2_ENTRY_FORWARD || e == SLA2_ENTRY_FORWARD_SLA1 ? kb : nkb;
+    const size_t stride =
+        e == SLA2_ENTRY_FORWARD || e == SLA2_ENTRY_FORWARD_SLA1 || grad ? kb : nkb;
     p.mask = take(BH * nqb * nkb);
     p.list = take(BH * nqb * stride * 4);
     p.cnt = take(BH * nqb * 4);
@@ -93,11 +98,27 @@ Plan make_plan(const Geom& g, sla2_entry e, int kb) {
     p.items = take(BH * static_cast<size_t>(p.cap) * 4);
     p.xpart = take(BH * static_cast<size_t>(p.cap) * kSlot * 4);
   }
+  if (grad) {
+    p.soft = take(BH * nqb * nkb * 4);
+    p.lam = take(BH * nqb * 4);
+    p.gO = take(BH * N * kD * 4);
+    p.gOs = take(BH * N * kD * 4);
+    p.gOl = take(BH * N * kD * 4);
+    p.ks16 = take(BH * N * kD * 2);
+    p.v16 = take(BH * N * kD * 2);
+    p.pk16 = take(BH * N * kD * 2);
+    p.gmask = take(BH * nqb * nkb * 4);
+    p.lossp = take(BH * nqb * 4);
+    p.Arow = take(BH * nqb * kD * 4);
+    p.dA = take(BH * nqb * kD * 4);
+    p.dG = take(BH * nqb * nkb * 4);
+    p.dB = take(BH * nkb * kD * 4);
+  }
   p.total = o;
   return p;
 }
 
-bool entry_ok(int e) { return e >= SLA2_ENTRY_ROUTER && e <= SLA2_ENTRY_BACKWARD; }
+bool entry_ok(int e) { return e >= SLA2_ENTRY_ROUTER && e <= SLA2_ENTRY_ROUTER_GRAD; }
 
 template <typename T>
 T* at(void* ws, size_t off) {
@@ -234,7 +255,8 @@ size_t sla2_workspace_bytes(const sla2_shape* shape, sla2_entry entry, float kee
   Geom g;
   if (check_shape(shape, &g) != SLA2_OK || !entry_ok(entry)) return 0;
   int kb = g.nkb;
-  if (entry == SLA2_ENTRY_FORWARD || entry == SLA2_ENTRY_FORWARD_SLA1) {
+  if (entry == SLA2_ENTRY_FORWARD || entry == SLA2_ENTRY_FORWARD_SLA1 ||
+      entry == SLA2_ENTRY_ROUTER_GRAD) {
     if (!keep_ok(keep_frac)) return 0;
     kb = sla2_blocks_kept(g.nkb, keep_frac);
   }
@@ -711,6 +733,80 @@ sla2_status sla2_fit_alpha(const sla2_shape* shape, const float* O_full, const f
   if (launch_fit_alpha(g.B, g.H, g.N, O_full, O_s, O_l, alpha, stream) != hipSuccess)
     return SLA2_ERR_HIP;
   if (debug_sync() && hipStreamSynchronize(stream) != hipSuccess) return SLA2_ERR_HIP;
+  return SLA2_OK;
+}
+
+sla2_status sla2_router_grad(const sla2_shape* shape, const void* Q, const void* K, const void* V,
+                             const float* proj_q, const float* proj_k, const float* alpha,
+                             float keep_frac, float tau, const float* O_full, float* dproj_q,
+                             float* dproj_k, double* loss, float* mask_grad, void* workspace,
+                             size_t workspace_bytes, void* stream_) {
+  Geom g;
+  sla2_status st = check_shape(shape, &g);
+  if (st != SLA2_OK) return st;
+  PtrCheck pc;
+  pc.req(Q); pc.req(K); pc.req(V); pc.req(proj_q); pc.req(proj_k); pc.req(alpha);
+  pc.req(O_full); pc.req(dproj_q); pc.req(dproj_k); pc.req(loss);
+  pc.opt(mask_grad);
+  if (pc.st != SLA2_OK) return pc.st;
+  if (!keep_ok(keep_frac) || !std::isfinite(tau) || !(tau > 0.f) || !std::isfinite(1.0f / tau))
+    return SLA2_ERR_BAD_ARGUMENT;
+  const int kb = sla2_blocks_kept(g.nkb, keep_frac);
+  const Plan p = make_plan(g, SLA2_ENTRY_ROUTER_GRAD, kb);
+  if ((st = check_workspace(p, workspace, workspace_bytes)) != SLA2_OK) return st;
+  if ((st = check_device()) != SLA2_OK) return st;
+  hipStream_t stream = static_cast<hipStream_t>(stream_);
+  const int dt = shape->dtype == SLA2_FP32 ? 0 : 1;
+  void* ws = workspace;
+  Rec rec(static_cast<void**>(nullptr));
+  // the router: hard Top-k (mask and lists) and SoftTop-k (soft mask) from the same logits
+  SLA2_LAUNCH(launch_pool(g, dt, Q, K, at<double>(ws, p.qsum), at<double>(ws, p.ksum), nullptr,
+                          at<float>(ws, p.sq), nullptr, stream));
+  SLA2_LAUNCH(launch_colmean(g, at<double>(ws, p.ksum), at<double>(ws, p.mu64), at<float>(ws, p.mu32),
+                             nullptr, at<uint32_t>(ws, p.err), stream));
+  SLA2_LAUNCH(launch_project(g, at<double>(ws, p.ksum), at<double>(ws, p.mu64), proj_k,
+                             at<float>(ws, p.Bt), stream));
+  SLA2_LAUNCH(launch_score_topk(g, at<double>(ws, p.qsum), proj_q, at<float>(ws, p.Bt), kb,
+                                at<uint8_t>(ws, p.mask), at<int32_t>(ws, p.list), kb,
+                                at<int32_t>(ws, p.cnt), nullptr, stream));
+  SLA2_LAUNCH(launch_score_soft(g, at<double>(ws, p.qsum), proj_q, at<float>(ws, p.Bt), kb,
+                                1.0f / tau, at<float>(ws, p.soft), at<float>(ws, p.lam), stream));
+  // the unquantised forward with its branch outputs kept
+  sla2_taps tp{};
+  tp.O_s = at<float>(ws, p.gOs);
+  tp.O_l = at<float>(ws, p.gOl);
+  if ((st = run_branches(g, dt, SLA2_QUANT_NONE, Q, K, V, alpha, at<float>(ws, p.gO), &tp, ws, p,
+                         kb, rec, stream)) != SLA2_OK)
+    return st;
+  // dL/dM over every block pair, then the router's chain
+  GradArgs x{};
+  x.mu32 = at<float>(ws, p.mu32);
+  x.ks16 = at<uint32_t>(ws, p.ks16);
+  x.v16 = at<uint32_t>(ws, p.v16);
+  x.pk16 = at<uint32_t>(ws, p.pk16);
+  x.O = at<float>(ws, p.gO);
+  x.O_full = O_full;
+  x.O_s = tp.O_s;
+  x.O_l = tp.O_l;
+  x.z = at<float>(ws, p.z);
+  x.ztot = at<float>(ws, p.ztot);
+  x.mask = at<uint8_t>(ws, p.mask);
+  x.list = at<int32_t>(ws, p.list);
+  x.list_stride = kb;
+  x.cnt = at<int32_t>(ws, p.cnt);
+  x.alpha = alpha;
+  x.g = mask_grad ? mask_grad : at<float>(ws, p.gmask);
+  x.lossp = at<float>(ws, p.lossp);
+  x.Arow = at<float>(ws, p.Arow);
+  x.dA = at<float>(ws, p.dA);
+  x.dG = at<float>(ws, p.dG);
+  x.dB = at<float>(ws, p.dB);
+  SLA2_LAUNCH(launch_grad_prep(g, dt, K, V, x, stream));
+  SLA2_LAUNCH(launch_mask_grad(g, dt, Q, x, stream));
+  SLA2_LAUNCH(launch_router_vjp(g, at<double>(ws, p.qsum), at<double>(ws, p.ksum),
+                                at<double>(ws, p.mu64), proj_q, at<float>(ws, p.Bt),
+                                at<float>(ws, p.soft), x, 1.0f / tau, dproj_q, dproj_k, loss,
+                                stream));
   return SLA2_OK;
 }
 

@@ -24,7 +24,7 @@ SLA2_QUANT_NONE, SLA2_QUANT_I8_FP8 = 0, 1
 QUANT = {"none": SLA2_QUANT_NONE, "i8_fp8": SLA2_QUANT_I8_FP8}
 # sla2_entry: the entry point a workspace is sized for
 ENTRY = {"router": 0, "router_soft": 1, "linear_precompute": 2, "forward": 3,
-         "forward_with_mask": 4, "forward_sla1": 5, "backward": 6}
+         "forward_with_mask": 4, "forward_sla1": 5, "backward": 6, "router_grad": 7}
 D = 128
 
 STATUS = {
@@ -97,12 +97,15 @@ def lib():
         L.sla2_backward.argtypes = [ctypes.POINTER(Shape), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                     ctypes.POINTER(vp), vp, sz, vp]
         L.sla2_fit_alpha.argtypes = [ctypes.POINTER(Shape), vp, vp, vp, vp, vp]
+        L.sla2_router_grad.argtypes = [ctypes.POINTER(Shape), vp, vp, vp, vp, vp, vp, f32, f32,
+                                       vp, vp, vp, vp, vp, vp, sz, vp]
         L.sla2_init_device.argtypes = []
         L.sla2_router_noalloc.argtypes = [ctypes.POINTER(Shape), vp, vp, vp, vp, f32, vp, vp, vp,
                                           vp]
         for name in ("sla2_router", "sla2_router_soft", "sla2_linear_precompute", "sla2_forward",
                      "sla2_forward_sla1", "sla2_forward_with_mask", "sla2_backward",
-                     "sla2_fit_alpha", "sla2_init_device", "sla2_router_noalloc"):
+                     "sla2_fit_alpha", "sla2_init_device", "sla2_router_noalloc",
+                     "sla2_router_grad"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -397,3 +400,26 @@ def sla2_fit_alpha(o_full, o_s, o_l, out=None):
                               _stream(o_s.device))
     _check(st, "sla2_fit_alpha")
     return a
+
+
+def sla2_router_grad(q, k, v, proj_q, proj_k, alpha, keep_frac, o_full, tau=0.1,
+                     want_mask_grad=False, workspace=None):
+    """Stage-1 router gradient: returns (loss [H] fp64, dproj_q [H,d,d], dproj_k [H,d,d],
+    mask_grad [B,H,N/128,N/64] fp32 or None) for L = sum (O - O_full)^2 with the hard mask in
+    the unquantised forward and its gradient passed straight through to SoftTop-k."""
+    _contig(q, k, v, proj_q, proj_k, alpha, o_full)
+    shp = shape_of(q)
+    B, H, N, d = q.shape
+    dev = q.device
+    loss = torch.empty(H, dtype=torch.float64, device=dev)
+    dwq = torch.empty((H, d, d), dtype=torch.float32, device=dev)
+    dwk = torch.empty((H, d, d), dtype=torch.float32, device=dev)
+    mg = (torch.empty((B, H, N // 128, N // 64), dtype=torch.float32, device=dev)
+          if want_mask_grad else None)
+    ws = workspace if workspace is not None else workspace_for(q, "router_grad", keep_frac)
+    st = lib().sla2_router_grad(ctypes.byref(shp), _ptr(q), _ptr(k), _ptr(v), _ptr(proj_q),
+                                _ptr(proj_k), _ptr(alpha), float(keep_frac), float(tau),
+                                _ptr(o_full), _ptr(dwq), _ptr(dwk), _ptr(loss), _ptr(mg), _ptr(ws),
+                                ws.numel(), _stream(dev))
+    _check(st, "sla2_router_grad")
+    return loss, dwq, dwk, mg

@@ -92,7 +92,8 @@ typedef enum {
     SLA2_ENTRY_FORWARD = 3,
     SLA2_ENTRY_FORWARD_WITH_MASK = 4,
     SLA2_ENTRY_FORWARD_SLA1 = 5,
-    SLA2_ENTRY_BACKWARD = 6
+    SLA2_ENTRY_BACKWARD = 6,
+    SLA2_ENTRY_ROUTER_GRAD = 7
 } sla2_entry;
 
 typedef struct {
@@ -130,7 +131,7 @@ typedef struct {
 int32_t sla2_blocks_kept(int32_t n_key_blocks, float keep_frac);
 
 /* Device workspace, in bytes, that `entry` needs for this shape. keep_frac matters
- * only for SLA2_ENTRY_FORWARD and SLA2_ENTRY_FORWARD_SLA1 (their block lists hold
+ * only for SLA2_ENTRY_FORWARD, SLA2_ENTRY_FORWARD_SLA1 and SLA2_ENTRY_ROUTER_GRAD (their block lists hold
  * kb = sla2_blocks_kept(N/64, keep_frac) entries per row); other entries ignore it.
  * Returns 0 for an invalid shape, entry or keep_frac. A workspace sized for one entry
  * serves any call of that entry with the same shape and a kept count no larger. */
@@ -291,9 +292,37 @@ sla2_status sla2_backward(const sla2_shape *shape, const void *Q, const void *K,
  *   O_s, O_l [B,H,N,d] fp32, the branch outputs under the mask (sla2_taps.O_s, O_l)
  *   alpha  [H,N/128] fp32 output
  * shape->dtype is not used (all four arrays are fp32). fp64 accumulation, fixed order
- * (deterministic). No workspace. The router part of stage 1 is not provided. */
+ * (deterministic). No workspace. The router part of stage 1 is sla2_router_grad. */
 sla2_status sla2_fit_alpha(const sla2_shape *shape, const float *O_full, const float *O_s,
                            const float *O_l, float *alpha, void *stream);
+
+/* Stage-1 router gradient: the router part of the first training stage ("SLA2: Sparse-Linear
+ * Attention with Learnable Routing and QAT", summary page, novelty paragraph: router and alpha
+ * are first fitted against full attention, and SoftTop-k replaces Top-k in training so that
+ * the router gets gradients; "SLA2: Sparse-Linear Attention v2 for Diffusion Transformers",
+ * §4 Eq. 17 (SoftTop-k), §5 training table, stage 1). For
+ *   L = sum over b, h, rows, columns of (O - O_full)^2
+ * it returns L per head and dL/dproj_q, dL/dproj_k under these readings (the pages leave
+ * them open): the forward is the UNQUANTISED forward with the hard Top-k mask (stage 1 comes
+ * before the quantisation-aware stage); the mask enters through the relaxation that weights
+ * key block j's exponentials in the sparse branch by M_ij and its h_j, z_j in the linear
+ * branch by 1 - M_ij (the forward itself at a 0/1 mask); dL/dM at the hard mask is passed
+ * straight through to the SoftTop-k mask sigma(P_c / tau + lambda_i) (kept count kb, lambda_i
+ * held to the row-sum constraint), then through P_c = softmax((Qbar Wq)(Kbar_s Wk)^T / sqrt(d)).
+ *   O_full  [B,H,N,d] fp32, the full-attention target
+ *   keep_frac, tau  as in sla2_router_soft (kb = sla2_blocks_kept(N/64, keep_frac))
+ *   dproj_q, dproj_k  [H,d,d] fp32 outputs (summed over the batch; overwritten)
+ *   loss    [H] fp64 output (summed over the batch)
+ *   mask_grad  NULL, or [B,H,N/128,N/64] fp32 output: dL/dM_ij at the hard mask
+ * Cost: a dense pass over every (query block, key block) pair, three 128 x 64 x 128 products
+ * each (S, delta V^T and phi(Q) phi(K_s)^T) with f16 operands (delta = 2 (O - O_full) scaled by
+ * a power of two per row) and fp32 accumulation; the router part in fp32 with fp64 sums for
+ * dproj_q, dproj_k and the loss. Deterministic. Workspace: SLA2_ENTRY_ROUTER_GRAD. */
+sla2_status sla2_router_grad(const sla2_shape *shape, const void *Q, const void *K, const void *V,
+                             const float *proj_q, const float *proj_k, const float *alpha,
+                             float keep_frac, float tau, const float *O_full, float *dproj_q,
+                             float *dproj_k, double *loss, float *mask_grad, void *workspace,
+                             size_t workspace_bytes, void *stream);
 
 #ifdef __cplusplus
 }

@@ -31,7 +31,8 @@ def test_library_exports_every_declared_symbol():
                           "sla2_init_device", "sla2_router_noalloc",
                           "sla2_status_string", "sla2_router", "sla2_router_soft",
                           "sla2_linear_precompute", "sla2_forward", "sla2_forward_sla1",
-                          "sla2_forward_with_mask", "sla2_backward", "sla2_fit_alpha"}
+                          "sla2_forward_with_mask", "sla2_backward", "sla2_fit_alpha",
+                          "sla2_router_grad"}
     for n in names:
         assert hasattr(L, n), n
 
@@ -57,11 +58,12 @@ def test_workspace_bytes():
     assert sla2.sla2_workspace_bytes(1, 1, 128, d=64) == 0
     assert sla2.sla2_workspace_bytes(1, 1, 262144 + 128) == 0
     assert sla2.sla2_workspace_bytes(256, 256, 128) == 0        # B*H > 65535
-    assert sla2.sla2_workspace_bytes(1, 1, 1024, entry=7) == 0  # no such entry
+    assert sla2.sla2_workspace_bytes(1, 1, 1024, entry=8) == 0  # no such entry
     assert sla2.sla2_workspace_bytes(1, 1, 1024, entry=-1) == 0
-    for bad in (0.0, 1.5, float("nan")):                          # keep_frac matters for these two
+    for bad in (0.0, 1.5, float("nan")):                          # keep_frac matters for these
         assert sla2.sla2_workspace_bytes(1, 1, 1024, entry="forward", keep_frac=bad) == 0
         assert sla2.sla2_workspace_bytes(1, 1, 1024, entry="forward_sla1", keep_frac=bad) == 0
+        assert sla2.sla2_workspace_bytes(1, 1, 1024, entry="router_grad", keep_frac=bad) == 0
         assert sla2.sla2_workspace_bytes(1, 1, 1024, entry="router", keep_frac=bad) > 0
     for s in range(10):
         assert isinstance(sla2.sla2_status_string(s), str) and sla2.sla2_status_string(s)
@@ -102,6 +104,14 @@ def test_workspace_bytes_per_entry_point():
     f5 = sla2.sla2_workspace_bytes(1, 40, 75648, entry="forward", keep_frac=0.05)
     assert 3.2e9 < f5 < 3.6e9
     assert sla2.sla2_workspace_bytes(1, 40, 75648, entry="backward") > 2.5 * f5
+    # the router gradient: the forward's regions, the soft mask, O, O_s, O_l (fp32), f16 copies
+    # of K_s, V, phi(K_s), the mask gradient and the router part
+    up = lambda x: -(-x // 256) * 256
+    BH, nqb, nkb, d, E_ = B * H, N // 128, N // 64, 128, B * H * N * 128
+    extra = [BH * nqb * nkb * 4, BH * nqb * 4, E_ * 4, E_ * 4, E_ * 4, E_ * 2, E_ * 2, E_ * 2,
+             BH * nqb * nkb * 4, BH * nqb * 4, BH * nqb * d * 4, BH * nqb * d * 4,
+             BH * nqb * nkb * 4, BH * nkb * d * 4]
+    assert size["router_grad"] == size["forward"] + sum(up(r) for r in extra)
 
 
 def shape(B=1, H=2, N=1024, d=128, dtype=1):
@@ -225,3 +235,32 @@ def test_noalloc_router_validates_on_the_host():
     big = shape(1, 40, 75648)
     assert need(big, "router") > sla2.NOALLOC_SCRATCH_BYTES
     assert f(ctypes.byref(big), A, A, A, A, 0.05, None, A, None, None) == WS
+
+
+def test_router_grad_validates_on_the_host():
+    L = sla2.lib()
+    s = shape()
+    n = need(s, "router_grad")
+    f = L.sla2_router_grad
+
+    def call(q=A, k=A, v=A, wq=A, wk=A, al=A, keep=0.25, tau=0.1, of=A, dq=A, dk=A, loss=A,
+             mg=None, ws=A, wsb=n, shp=s):
+        return f(ctypes.byref(shp), q, k, v, wq, wk, al, keep, tau, of, dq, dk, loss, mg, ws, wsb,
+                 None)
+    assert call(of=None) == NULL                     # the target is required
+    assert call(dq=None) == NULL
+    assert call(loss=None) == NULL
+    assert call(v=None) == NULL
+    assert call(mg=MIS) == MISAL                     # optional, but aligned when given
+    assert call(dk=MIS) == MISAL
+    assert call(tau=0.0) == ARG
+    assert call(tau=float("inf")) == ARG
+    assert call(keep=0.0) == ARG
+    assert call(keep=1.5) == ARG
+    assert call(wsb=n - 1) == WS
+    assert call(wsb=need(s, "forward")) == WS        # sized for another entry
+    assert call(ws=None) == NULL
+    assert call(shp=shape(N=100)) == SHAPE
+    import torch
+    if not torch.cuda.is_available():
+        assert call() in (HIP, DEV)                  # valid arguments reach the device check

@@ -1,0 +1,124 @@
+"""GPU parity of sla2_router_grad (the stage-1 router gradient) against the oracle's
+straight-through chain (oracle/sla2_fit.py router_grad_head), through the C ABI.
+
+Cases: the i.i.d. workload's shape (fp32, 2 heads, N = 2048, keep 25 %); a batch of two (the
+gradients are summed over it); two heads of the 8x32x32 grid workload (bf16, N = 8192, keep
+10 %); keep 100 % (every block kept: the soft mask is 1 and the gradient 0, with no NaN). The
+router weights are the generators' N(0, 1/d) draws scaled up so that P_c is not flat: every
+row's kb-th and (kb + 1)-th largest P_c then differ by far more than the router's 1e-5 band, a
+precondition checked on the oracle's P_c, so the GPU's hard mask is the oracle's (checked
+through sla2_router).
+
+Tolerances. The dense pass takes Q, K_s, V, phi(Q), phi(K_s) and the scaled delta as f16
+(unit roundoff 2^-11 = 4.9e-4) with fp32 accumulation: each of the three products per block
+pair carries a relative error of a few 2^-11, e^S inherits S's absolute error (|S| ~ 1, so
+~1e-3 relative), and g_ij is a difference of two such sums of similar size (the factors c_q,
+c'_q centre them), so its error is a few 1e-3 of the larger term. The router part is fp32 with
+fp64 sums. Bounds: mask gradient and dproj relative L2 <= 2e-2; loss (fp32 forward against
+the fp64 one, on differences O - O_full of ~10 % of O) relative <= 1e-4.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from block_sparse_linear_pool_amd import sla2
+from block_sparse_linear_pool_amd import workloads as W
+from oracle import sla2 as F
+from oracle import sla2_fit as S
+from tests.gpu_helpers import dev, host, rel_l2
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+TAU = 0.1
+GRAD_TOL = 2e-2
+LOSS_TOL = 1e-4
+GAP = 1e-4     # smallest relative gap between the kb-th and (kb + 1)-th largest P_c
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def oracle_case(q, k, v, wq, wk, alpha, keep):
+    B, H, N, _ = q.shape
+    O_full = np.zeros(q.shape)
+    refs = {}
+    for b in range(B):
+        for h in range(H):
+            O_full[b, h] = S.full_attention_head(q[b, h], k[b, h], v[b, h])
+            r = S.router_grad_head(q[b, h], k[b, h], v[b, h], wq[h], wk[h], alpha[h], keep, TAU,
+                                   O_full[b, h])
+            kb = r["kb"]
+            if kb < N // 64:
+                s = -np.sort(-r["P_c"], axis=1)
+                gap = ((s[:, kb - 1] - s[:, kb]) / s[:, kb - 1]).min()
+                assert gap > GAP, f"near tie in the router of b{b} h{h}: {gap:.2e}"
+            refs[(b, h)] = r
+    return O_full, refs
+
+
+def run_and_compare(q, k, v, wq, wk, alpha, keep, tdt):
+    B, H = q.shape[:2]
+    O_full, refs = oracle_case(q, k, v, wq, wk, alpha, keep)
+    g = [dev(q, tdt), dev(k, tdt), dev(v, tdt), dev(wq), dev(wk), dev(alpha)]
+    loss, dwq, dwk, mg = sla2.sla2_router_grad(*g, keep, dev(O_full.astype(np.float32)), tau=TAU,
+                                               want_mask_grad=True)
+    _, mask, _ = sla2.sla2_router(g[0], g[1], g[3], g[4], keep)
+    torch.cuda.synchronize()
+    loss, dwq, dwk, mg, mask = host(loss), host(dwq), host(dwk), host(mg), host(mask)
+    for (b, h), r in refs.items():
+        assert (mask[b, h] == r["mask"]).all(), (b, h)
+        e = rel_l2(mg[b, h], r["mask_grad"])
+        say(f"  b{b} h{h}: mask grad relL2 {e:.2e} (|g| max {np.abs(r['mask_grad']).max():.2e})")
+        assert e <= GRAD_TOL
+    for h in range(H):
+        ref_loss = sum(refs[(b, h)]["loss"] for b in range(B))
+        ref_q = sum(refs[(b, h)]["dWq"] for b in range(B))
+        ref_k = sum(refs[(b, h)]["dWk"] for b in range(B))
+        el = abs(loss[h] - ref_loss) / ref_loss
+        eq, ek = rel_l2(dwq[h], ref_q), rel_l2(dwk[h], ref_k)
+        say(f"  h{h}: loss {loss[h]:.6e} rel {el:.2e}; dproj_q relL2 {eq:.2e}; dproj_k relL2 {ek:.2e}")
+        assert el <= LOSS_TOL
+        assert np.isfinite(dwq[h]).all() and np.isfinite(dwk[h]).all()
+        if np.abs(ref_q).max() > 0:
+            assert eq <= GRAD_TOL and ek <= GRAD_TOL
+        else:
+            assert not dwq[h].any() and not dwk[h].any()
+    return refs
+
+
+def test_router_grad_iid_fp32():
+    q, k, v = W.random_qkv(21, 1, 2, 2048)
+    wq, wk, alpha = W.random_weights(21, 2, 16, alpha_lo=0.2)
+    say("router grad: i.i.d. fp32, 2 heads, N 2048, keep 0.25")
+    run_and_compare(q, k, v, wq * 10, wk * 10, alpha, 0.25, torch.float32)
+
+
+def test_router_grad_batch_of_two():
+    q, k, v = W.random_qkv(23, 2, 2, 1024)
+    wq, wk, alpha = W.random_weights(23, 2, 8, alpha_lo=0.2)
+    say("router grad: batch of two, fp32, N 1024, keep 0.25")
+    run_and_compare(q, k, v, wq * 10, wk * 10, alpha, 0.25, torch.float32)
+
+
+@pytest.mark.timeout(600)
+def test_router_grad_grid_bf16():
+    w = W.WORKLOADS["grid_8x32x32_N8192"]
+    heads = [4, 10]
+    q, k, v = W.generate(w, heads=heads)
+    wq, wk, alpha = W.weights(w)
+    say("router grad: grid workload bf16, heads", heads, "N 8192, keep 0.1")
+    run_and_compare(q, k, v, wq[heads] * 8, wk[heads] * 8, alpha[heads], 0.1, torch.bfloat16)
+
+
+def test_router_grad_everything_kept():
+    q, k, v = W.random_qkv(25, 1, 2, 1024)
+    wq, wk, alpha = W.random_weights(25, 2, 8, alpha_lo=0.2)
+    say("router grad: keep 1.0")
+    refs = run_and_compare(q, k, v, wq * 10, wk * 10, alpha, 1.0, torch.float32)
+    for r in refs.values():
+        assert not r["dWq"].any() and not r["dWk"].any()
