@@ -86,7 +86,7 @@ def expected_forward_bytes(B, H, N, kb):
 
 def test_workspace_bytes_per_entry_point():
     """Each entry point asks only for what its kernels use: at the 12-head N = 32768 shape with
-    3 % kept the forward needs 0.42 GB, the backward 3.7 GB (its bf16 operand copies, dH_i^T and
+    3 % kept the forward needs 0.42 GB, the backward 1.29 GB (its bf16 operand copies, dH_i^T and
     the work-item partials), the router 13 MB."""
     B, H, N = 1, 12, 32768
     kb = sla2.sla2_blocks_kept(N // 64, 0.03)

@@ -10,12 +10,13 @@ precondition checked on the oracle's P_c, so the GPU's hard mask is the oracle's
 through sla2_router).
 
 Tolerances. The dense pass takes Q, K_s, V, phi(Q), phi(K_s) and the scaled delta as f16
-(unit roundoff 2^-11 = 4.9e-4) with fp32 accumulation: each of the three products per block
-pair carries a relative error of a few 2^-11, e^S inherits S's absolute error (|S| ~ 1, so
-~1e-3 relative), and g_ij is a difference of two such sums of similar size (the factors c_q,
-c'_q centre them), so its error is a few 1e-3 of the larger term. The router part is fp32 with
-fp64 sums. Bounds: mask gradient and dproj relative L2 <= 2e-2; loss (fp32 forward against
-the fp64 one, on differences O - O_full of ~10 % of O) relative <= 1e-4.
+(each element rounded with relative error at most 2^-12 = 2.4e-4) with fp32 accumulation; a
+block pair's number sums 8192 products whose rounding errors are independent, so its relative
+error is of order 2^-12 times the ratio of the terms' magnitudes to the sum's, a few 1e-4
+where delta V^T - c cancels; the router part is fp32 with fp64 sums and adds little. Bound:
+2e-3 relative L2 on the mask gradient and on dproj_q, dproj_k (measured 3e-5 to 3e-4); the
+loss (fp32 forward against the fp64 one, on differences O - O_full of ~10 % of O): 1e-4
+relative (measured <= 1.6e-5).
 """
 import sys
 
@@ -33,7 +34,7 @@ pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
 
 TAU = 0.1
-GRAD_TOL = 2e-2
+GRAD_TOL = 2e-3
 LOSS_TOL = 1e-4
 GAP = 1e-4     # smallest relative gap between the kb-th and (kb + 1)-th largest P_c
 
