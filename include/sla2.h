@@ -59,7 +59,12 @@
 extern "C" {
 #endif
 
-typedef enum {
+/* The status, dtype, quantisation and entry types are plain 32-bit integers with named values
+ * (not C enum types), so that any value a caller passes is well defined on the C++ side: an
+ * out-of-range value is rejected with SLA2_ERR_BAD_DTYPE / SLA2_ERR_BAD_ARGUMENT, or gives 0 from
+ * sla2_workspace_bytes and "unknown status" from sla2_status_string. */
+typedef int32_t sla2_status;
+enum {
     SLA2_OK = 0,
     SLA2_ERR_NULL_POINTER = 1,
     SLA2_ERR_BAD_SHAPE = 2,
@@ -70,10 +75,11 @@ typedef enum {
     SLA2_ERR_UNSUPPORTED_DEVICE = 7,
     SLA2_ERR_HIP = 8,
     SLA2_ERR_WAIT_TIMEOUT = 9
-} sla2_status;
+};
 
 /* element type of Q, K, V */
-typedef enum { SLA2_FP32 = 0, SLA2_BF16 = 1 } sla2_dtype;
+typedef int32_t sla2_dtype;
+enum { SLA2_FP32 = 0, SLA2_BF16 = 1 };
 
 /* operand precision of the sparse branch (step 2 of the summary page's computation
  * flow quantises Q, K and P, V before the products; Eq. 9 and Eq. 11 of §4 of the
@@ -82,10 +88,12 @@ typedef enum { SLA2_FP32 = 0, SLA2_BF16 = 1 } sla2_dtype;
  *                      fp32 operands (fp32 MFMA, fp32 softmax); the reference form, not
  *                      the fast one. The code and scale taps are not written.
  *   SLA2_QUANT_I8_FP8  the low-bit branch: INT8 Q, K per block, OCP E4M3 P, V. */
-typedef enum { SLA2_QUANT_NONE = 0, SLA2_QUANT_I8_FP8 = 1 } sla2_quant;
+typedef int32_t sla2_quant;
+enum { SLA2_QUANT_NONE = 0, SLA2_QUANT_I8_FP8 = 1 };
 
 /* the entry point a workspace is sized for (sla2_workspace_bytes) */
-typedef enum {
+typedef int32_t sla2_entry;
+enum {
     SLA2_ENTRY_ROUTER = 0,
     SLA2_ENTRY_ROUTER_SOFT = 1,
     SLA2_ENTRY_LINEAR_PRECOMPUTE = 2,
@@ -94,7 +102,7 @@ typedef enum {
     SLA2_ENTRY_FORWARD_SLA1 = 5,
     SLA2_ENTRY_BACKWARD = 6,
     SLA2_ENTRY_ROUTER_GRAD = 7
-} sla2_entry;
+};
 
 typedef struct {
     int32_t B, H, N, d;

@@ -180,3 +180,80 @@ def backward(Q, K, V, mask, alpha_row, dO):
     dalpha = (dO * (O_s - O_l)).reshape(n_qb, BQ * d).sum(axis=1)
     return dict(dQ=dQ, dK=dK, dV=dV, dalpha=dalpha, O_s=O_s, O_l=O_l, lse=lse, D=D,
                 dH=dH, dZ=dZ)
+
+
+def backward_spot(Q, K, V, mask, alpha_row, dO, qblocks, kblocks):
+    """Some of backward()'s outputs at sizes where the full function is too slow: dQ and dalpha
+    of the query blocks `qblocks`, dV of the key blocks `kblocks`. The same steps as backward(),
+    restricted to what those outputs need, with the sums over a row's dropped blocks taken as the
+    total minus the kept blocks (H_i = H_tot - sum_{j kept} h_j, Z_i likewise: the same sums, in
+    another order). dV_j still needs dH_i of every query block that drops j, so the linear
+    branch runs per query block over all of them; the sparse branch runs only for the query
+    blocks in `qblocks` and those that keep a block in `kblocks`.
+
+    Returns dict dQ {i: [128, d]}, dalpha {i: float}, dV {j: [64, d]}."""
+    Q, K, V, mask, alpha_row = _check(Q, K, V, mask, alpha_row)
+    dO = np.asarray(dO, np.float64)
+    N, d = Q.shape
+    n_qb, n_kb = N // BQ, N // BK
+    c = 1.0 / math.sqrt(d)
+    Ks = K - K.mean(axis=0)
+    lists = mask_to_lists(mask)
+    pk = phi(Ks).reshape(n_kb, BK, d)
+    Vb = V.reshape(n_kb, BK, d)
+    h = np.matmul(pk.transpose(0, 2, 1), Vb)            # h_j = phi(K_s,j)^T V_j
+    z = pk.sum(axis=1)
+    h_tot, z_tot = h.sum(axis=0), z.sum(axis=0)
+    want_q = set(int(i) for i in qblocks)
+    want_k = set(int(j) for j in kblocks)
+    dQ = {i: np.zeros((BQ, d)) for i in want_q}
+    dV = {j: np.zeros((BK, d)) for j in want_k}
+    O_s, O_l = {}, {}
+    # sparse branch
+    for i, L in enumerate(lists):
+        if len(L) == 0 or not (i in want_q or want_k.intersection(int(j) for j in L)):
+            continue
+        rows = slice(i * BQ, (i + 1) * BQ)
+        cols = _key_cols(L)
+        S = Q[rows] @ Ks[cols].T * c
+        m = S.max(axis=1, keepdims=True)
+        P = np.exp(S - m)
+        P /= P.sum(axis=1, keepdims=True)
+        Os = P @ V[cols]
+        dOs = alpha_row[i] * dO[rows]
+        if i in want_q:
+            O_s[i] = Os
+            D = (dOs * Os).sum(axis=1)
+            dS = P * (dOs @ V[cols].T - D[:, None])
+            dQ[i] += dS @ Ks[cols] * c
+        for t, j in enumerate(L):
+            if int(j) in want_k:
+                dV[int(j)] += P[:, t * BK:(t + 1) * BK].T @ dOs
+    # linear branch: every query block with a dropped set (dh_j needs all of them)
+    pq = phi(Q)
+    dH = np.zeros((n_qb, d, d))
+    for i, L in enumerate(lists):
+        if len(L) == n_kb:
+            continue
+        rows = slice(i * BQ, (i + 1) * BQ)
+        H = h_tot - h[L].sum(axis=0)
+        Z = z_tot - z[L].sum(axis=0)
+        a = pq[rows]
+        den = a @ Z
+        Ol = (a @ H) / den[:, None]
+        dOl = (1.0 - alpha_row[i]) * dO[rows]
+        dnum = dOl / den[:, None]
+        dH[i] = a.T @ dnum
+        if i in want_q:
+            O_l[i] = Ol
+            dden = -(dOl * Ol).sum(axis=1) / den
+            da = dnum @ H.T + dden[:, None] * Z[None, :]
+            dQ[i] += _softmax_vjp(a, da)
+    for j in want_k:
+        drop_j = np.flatnonzero(mask[:, j] == 0)
+        dV[j] += pk[j] @ dH[drop_j].sum(axis=0)
+    dalpha = {}
+    for i in want_q:
+        rows = slice(i * BQ, (i + 1) * BQ)
+        dalpha[i] = float((dO[rows] * (O_s.get(i, 0.0) - O_l.get(i, 0.0))).sum())
+    return dict(dQ=dQ, dalpha=dalpha, dV=dV)

@@ -153,6 +153,59 @@ def mask_grad(Q, Ks, V, M, alpha_row, O_full):
     return g
 
 
+def mask_grad_rows(Q, Ks, V, M, alpha_row, O_full_rows):
+    """Rows of mask_grad at sizes where the whole is too slow: O_full_rows maps query block i to
+    the target's rows [128, d] of that block; returns {i: dL/dM[i, :]}. The same steps as
+    mask_grad (relaxed forward, delta, the two parts), for those query blocks only: a row of the
+    derivative depends only on its own block's outputs and mask row and on the per-key-block
+    h_j, z_j."""
+    Q = np.asarray(Q, np.float64)
+    Ks = np.asarray(Ks, np.float64)
+    V = np.asarray(V, np.float64)
+    M = np.asarray(M, np.float64)
+    N, d = Q.shape
+    h, z = _f.linear_precompute(Ks, V)
+    out = {}
+    for i, target in O_full_rows.items():
+        rows = slice(i * BQ, (i + 1) * BQ)
+        a = float(alpha_row[i])
+        S = Q[rows] @ Ks.T / np.sqrt(d)
+        E = np.exp(S - S.max(axis=1, keepdims=True))
+        W = E * np.repeat(M[i], _f.BK)[None, :]
+        l = W.sum(axis=1)
+        O_s = (W @ V) / l[:, None] if (l > 0).all() else np.zeros((BQ, d))
+        U = 1.0 - M[i]
+        p = _f.phi(Q[rows])
+        O_l = np.zeros((BQ, d))
+        if U.any():
+            H = np.einsum("j,jab->ab", U, h)
+            Z = U @ z
+            den = p @ Z
+            O_l = (p @ H) / den[:, None]
+        dl = 2.0 * (a * O_s + (1.0 - a) * O_l - np.asarray(target, np.float64))
+        g = np.zeros(M.shape[1])
+        if (l > 0).all():
+            c = (dl * O_s).sum(axis=1)
+            T = E * (dl @ V.T - c[:, None]) / l[:, None]
+            g += a * T.reshape(BQ, M.shape[1], _f.BK).sum(axis=(0, 2))
+        if U.any():
+            c2 = (dl * O_l).sum(axis=1)
+            g -= (1.0 - a) * _linear_part(p, den, dl, c2, h, z)
+        out[i] = g
+    return out
+
+
+def full_attention_rows(Q, K, V, blocks):
+    """Rows of full_attention_head for the query blocks in `blocks`: {i: [128, d]}."""
+    Q = np.asarray(Q, np.float64)
+    K = np.asarray(K, np.float64)
+    out = {}
+    for i in blocks:
+        S = Q[i * BQ:(i + 1) * BQ] @ K.T / np.sqrt(Q.shape[1])
+        out[i] = _f.softmax_rows(S) @ np.asarray(V, np.float64)
+    return out
+
+
 def _linear_part(p, den, dl, c2, h, z):
     """sum_q [delta_q . (phi(q) h_j) - c'_q (phi(q) . z_j)] / den_q for every block j."""
     first = np.einsum("qa,jab,qb->j", p / den[:, None], h, dl)

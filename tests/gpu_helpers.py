@@ -42,6 +42,22 @@ def oracle_heads(q, k, v, wq, wk, alpha, keep, heads=None, mask=None, quant=True
     return out
 
 
+def rows_agreeing(gpu_mask, oracle_mask):
+    """Query blocks whose GPU kept set is the oracle's own. A row block of O depends only on its
+    own mask row (its kept list in the sparse branch, its dropped set in the linear one), so
+    there the oracle's rows, computed with its own router, are the expected values. Rows whose
+    sets differ are held to the near-tie band (check_mask_band); their outputs are not compared,
+    since the oracle takes no input from the GPU."""
+    return ((np.asarray(gpu_mask) != 0) == (np.asarray(oracle_mask) != 0)).all(axis=-1)
+
+
+def row_errors(got, ref, rows):
+    """rel L2 and max-abs of got against ref over the 128-row blocks selected by `rows`."""
+    sel = np.repeat(np.asarray(rows, bool), 128)
+    return rel_l2(np.asarray(got)[sel], np.asarray(ref)[sel]), max_abs(np.asarray(got)[sel],
+                                                                        np.asarray(ref)[sel])
+
+
 def check_mask_band(P, kb, gpu_mask):
     """Router contract: the GPU kept set has kb members per row, holds every block whose
     P_c exceeds the oracle's kb-th largest T by more than 1e-5 relative and no block below

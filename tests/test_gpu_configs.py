@@ -3,7 +3,8 @@
 Each test runs sla2_forward on the whole workload, every batch and head in one call (the
 library's normal launch for that shape), and compares sampled (batch, head) slices with the
 oracle: the kept sets must agree outside the 1e-5 near-tie band of P_c, and O must be within
-rel L2 3e-3 / max-abs 2e-2 of the oracle run with the GPU's mask. The oracle takes tens of
+rel L2 3e-3 / max-abs 2e-2 of the oracle's own forward on the query blocks whose kept sets
+agree (at least 90 % of them; a row block's output depends only on its own mask row). The oracle takes tens of
 seconds per slice at these sizes, hence the longer per-test timeouts.
 """
 import sys
@@ -15,7 +16,8 @@ import torch
 from block_sparse_linear_pool_amd import sla2
 from block_sparse_linear_pool_amd import workloads as W
 from oracle import sla2 as oracle
-from tests.gpu_helpers import MAX_ABS_TOL, REL_L2_TOL, check_mask_band, dev, host, max_abs, rel_l2
+from tests.gpu_helpers import (MAX_ABS_TOL, REL_L2_TOL, check_mask_band, dev, host, row_errors,
+                               rows_agreeing)
 
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
@@ -42,13 +44,12 @@ def run_and_check(w, plan):
         assert np.isfinite(O).all()
         for b, h in samples:
             r = oracle.forward_head(q[b, h], k[b, h], v[b, h], wq[h], wk[h], alpha[h], keep)
-            if not np.array_equal(mask[b, h], r["mask"]):
-                differ = check_mask_band(r["P_c"], r["kb"], mask[b, h])
-                say(f"  keep {keep} b{b} h{h}: {differ} rows differ inside the band")
-                r = oracle.forward_head(q[b, h], k[b, h], v[b, h], wq[h], wk[h], alpha[h], keep,
-                                        mask=mask[b, h])
-            e, m = rel_l2(O[b, h], r["O"]), max_abs(O[b, h], r["O"])
-            say(f"  keep {keep} (kb {r['kb']}) b{b} h{h}: O relL2 {e:.2e} maxabs {m:.2e}")
+            differ = check_mask_band(r["P_c"], r["kb"], mask[b, h])
+            rows = rows_agreeing(mask[b, h], r["mask"])
+            e, m = row_errors(O[b, h], r["O"], rows)
+            say(f"  keep {keep} (kb {r['kb']}) b{b} h{h}: O relL2 {e:.2e} maxabs {m:.2e} "
+                f"({differ} rows differ inside the band)")
+            assert rows.mean() >= 0.9
             assert e <= REL_L2_TOL and m <= MAX_ABS_TOL
 
 

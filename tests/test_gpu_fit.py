@@ -18,7 +18,7 @@ from block_sparse_linear_pool_amd import sla2
 from block_sparse_linear_pool_amd import workloads as W
 from oracle import sla2 as oracle
 from oracle import sla2_fit as fit
-from tests.gpu_helpers import dev, host
+from tests.gpu_helpers import check_mask_band, dev, host, rows_agreeing
 
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
@@ -60,19 +60,23 @@ def test_fit_end_to_end_and_backward_at_the_minimum():
     _, mask, _ = sla2.sla2_router(g[0], g[1], dev(wq), dev(wk), keep)
     torch.cuda.synchronize()
     mask_h = host(mask)
-    # the oracle's pipeline on the GPU's mask (near-tie router choices are not this test's subject)
+    # the oracle's own pipeline; alpha of a query block depends only on that block's mask row,
+    # so it is compared where the GPU's kept set is the oracle's (near-tie rows aside)
     Of, Os, Ol = (np.empty((B, H, N, D)) for _ in range(3))
+    agree = np.zeros((H, N // 128), bool)
     for h in range(H):
         r1 = oracle.forward_head(q[0, h], k[0, h], v[0, h], np.eye(D), np.eye(D), np.ones(N // 128),
                                  1.0)
-        r = oracle.forward_head(q[0, h], k[0, h], v[0, h], wq[h], wk[h], np.ones(N // 128), keep,
-                                mask=mask_h[0, h])
+        r = oracle.forward_head(q[0, h], k[0, h], v[0, h], wq[h], wk[h], np.ones(N // 128), keep)
+        check_mask_band(r["P_c"], r["kb"], mask_h[0, h])
+        agree[h] = rows_agreeing(mask_h[0, h], r["mask"])
         Of[0, h], Os[0, h], Ol[0, h] = r1["O"], r["O_s"], r["O_l"]
     a_ref = fit.fit_alpha(Of, Os, Ol)
     a = host(a_gpu)
     say("alpha gpu", np.round(a, 3).tolist())
     say("alpha ref", np.round(a_ref, 3).tolist())
-    assert np.abs(a - a_ref).max() <= 2e-2
+    assert agree.mean() >= 0.9
+    assert np.abs(a - a_ref)[agree].max() <= 2e-2
     # reported, not asserted (the pages only say "close to"): the kept row mass P_1 1 per
     # query block, from the oracle's exact softmax over all keys
     mass = np.zeros((H, N // 128))

@@ -3,7 +3,8 @@ straight-through chain (oracle/sla2_fit.py router_grad_head), through the C ABI.
 
 Cases: the i.i.d. workload's shape (fp32, 2 heads, N = 2048, keep 25 %); a batch of two (the
 gradients are summed over it); two heads of the 8x32x32 grid workload (bf16, N = 8192, keep
-10 %); keep 100 % (every block kept: the soft mask is 1 and the gradient 0, with no NaN). The
+10 %); keep 100 % (every block kept: the soft mask is 1 and the gradient 0, with no NaN); and
+the bench's 12-head N = 32768 workload in one call, sampled rows of the mask gradient. The
 router weights are the generators' N(0, 1/d) draws scaled up so that P_c is not flat: every
 row's kb-th and (kb + 1)-th largest P_c then differ by far more than the router's 1e-5 band, a
 precondition checked on the oracle's P_c, so the GPU's hard mask is the oracle's (checked
@@ -28,7 +29,7 @@ from block_sparse_linear_pool_amd import sla2
 from block_sparse_linear_pool_amd import workloads as W
 from oracle import sla2 as F
 from oracle import sla2_fit as S
-from tests.gpu_helpers import dev, host, rel_l2
+from tests.gpu_helpers import check_mask_band, dev, host, rel_l2, rows_agreeing
 
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
@@ -123,3 +124,42 @@ def test_router_grad_everything_kept():
     refs = run_and_compare(q, k, v, wq * 10, wk * 10, alpha, 1.0, torch.float32)
     for r in refs.values():
         assert not r["dWq"].any() and not r["dWk"].any()
+
+
+@pytest.mark.timeout(600)
+def test_router_grad_bench_size_sampled_rows():
+    """The 12-head N = 32768 workload as bench.py runs it (all heads in one call, 3 % kept, the
+    target from the library's unquantised forward at keep 1): rows of the mask gradient of
+    heads 0 and 7 against the oracle's row-restricted derivative (its own router, its own
+    full-attention rows), on query blocks whose GPU kept set is the oracle's."""
+    w = W.WORKLOADS["wan13b_480p_N32768"]
+    keep = w.keep_frac[-1]
+    q, k, v = W.generate(w)
+    wq, wk, alpha = W.weights(w)
+    t = torch.bfloat16
+    g = [dev(q, t), dev(k, t), dev(v, t), dev(wq), dev(wk), dev(alpha)]
+    eye = dev(np.broadcast_to(np.eye(128, dtype=np.float32), (w.H, 128, 128)).copy())
+    ones = dev(np.ones((w.H, w.n_qb), np.float32))
+    say("router grad at the bench size: GPU")
+    o_full = sla2.sla2_forward(g[0], g[1], g[2], eye, eye, ones, 1.0, quant="none")
+    loss, dwq, dwk, mg = sla2.sla2_router_grad(*g, keep, o_full, tau=TAU, want_mask_grad=True)
+    _, mask, _ = sla2.sla2_router(g[0], g[1], g[3], g[4], keep)
+    torch.cuda.synchronize()
+    mg, mask, loss = host(mg), host(mask), host(loss)
+    assert np.isfinite(mg).all() and np.isfinite(host(dwq)).all() and np.isfinite(host(dwk)).all()
+    assert (loss > 0).all()
+    checked = 0
+    for h in (0, 7):
+        r = F.forward_head(q[0, h], k[0, h], v[0, h], wq[h], wk[h], alpha[h], keep, quant=False)
+        check_mask_band(r["P_c"], r["kb"], mask[0, h])
+        agree = rows_agreeing(mask[0, h], r["mask"])
+        rows = [i for i in (0, 100, 255) if agree[i]]
+        targets = S.full_attention_rows(q[0, h], k[0, h], v[0, h], rows)
+        ref = S.mask_grad_rows(q[0, h], r["Ks"], v[0, h], r["mask"].astype(np.float64), alpha[h],
+                               targets)
+        for i in rows:
+            e = rel_l2(mg[0, h, i], ref[i])
+            say(f"  h{h} query block {i}: mask grad relL2 {e:.2e} (|g| max {np.abs(ref[i]).max():.2e})")
+            assert e <= GRAD_TOL
+            checked += 1
+    assert checked >= 3

@@ -142,3 +142,31 @@ def test_branch_switches():
     g0 = bw.backward(Q, K, V, mask, np.zeros(3), dO)
     assert np.all(g0["dQ"][128:256] == 0)           # block 1 drops nothing
     assert np.all(np.isneginf(g0["lse"][256:384]))
+
+
+def test_backward_spot_equals_the_full_backward():
+    """backward_spot (selected query and key blocks, dropped sums as total minus kept) against
+    backward() at a size where both run: a random mask with an all-kept and an all-dropped
+    query block and a key block kept by every query block."""
+    rng = np.random.default_rng(61)
+    N, d = 1024, 16
+    Q = rng.standard_normal((N, d))
+    K = rng.standard_normal((N, d)) + rng.standard_normal(d)
+    V = rng.standard_normal((N, d))
+    dO = rng.standard_normal((N, d))
+    mask = (rng.random((N // 128, N // 64)) < 0.3).astype(np.uint8)
+    mask[2, :] = 1
+    mask[3, :] = 0
+    mask[:, 5] = 1
+    mask[3, 5] = 0
+    alpha = rng.uniform(0.1, 0.9, N // 128)
+    full = bw.backward(Q, K, V, mask, alpha, dO)
+    qb, kb = [0, 2, 3, 7], [0, 5, 9, 15]
+    spot = bw.backward_spot(Q, K, V, mask, alpha, dO, qb, kb)
+    for i in qb:
+        ref = full["dQ"][i * 128:(i + 1) * 128]
+        assert np.abs(spot["dQ"][i] - ref).max() <= 1e-10 * np.abs(ref).max()
+        assert abs(spot["dalpha"][i] - full["dalpha"][i]) <= 1e-10 * abs(full["dalpha"]).max()
+    for j in kb:
+        ref = full["dV"][j * 64:(j + 1) * 64]
+        assert np.abs(spot["dV"][j] - ref).max() <= 1e-10 * np.abs(ref).max()

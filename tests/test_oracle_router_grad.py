@@ -242,3 +242,21 @@ def test_planted_mistakes_fail_the_pins(monkeypatch):
     right = S.soft_topk_vjp(soft, TAU, g)[i, j]
     assert abs(right - fd_ij) <= 1e-5 * abs(fd_ij) + 1e-9
     assert abs(wrong[i, j] - fd_ij) > 1e-3 * abs(fd_ij)
+
+
+def test_mask_grad_rows_equals_mask_grad():
+    """The row-restricted derivative (for sampled rows at large sizes) against the whole one,
+    and the row-restricted full-attention target against the whole target."""
+    Q, K, V, Wq, Wk, alpha, O_full = problem(18)
+    Ks = smoothed(K)
+    M = (np.random.default_rng(19).random((N // 128, N // 64)) < 0.3).astype(float)
+    M[0, :] = 1.0                                   # a row with no dropped block
+    M[1, :] = 0.0
+    M[1, 2] = 1.0
+    whole = S.mask_grad(Q, Ks, V, M, alpha, O_full)
+    rows = S.full_attention_rows(Q, K, V, [0, 1, 3])
+    for i, r in rows.items():
+        assert np.abs(r - O_full[128 * i:128 * (i + 1)]).max() <= 1e-12
+    part = S.mask_grad_rows(Q, Ks, V, M, alpha, rows)
+    for i, g in part.items():
+        assert np.abs(g - whole[i]).max() <= 1e-10 * np.abs(whole[i]).max()
