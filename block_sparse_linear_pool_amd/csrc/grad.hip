@@ -93,13 +93,16 @@ __global__ __launch_bounds__(256) void grad_prep_kernel(const T* __restrict__ K,
 // registers (Q, delta scaled by a power of two, phi(Q), all f16); register r of the
 // accumulator is key 8 (r / 4) + 4 g + r % 4 of the tile, query lane % 32.
 //
-// Key tiles (K_s, V, phi(K_s): 64 rows x 256 B each) come in through global_load_lds, double
-// buffered; 16-byte chunk c of row r is stored at position c ^ (r % 16) of the row, so the
-// 16 lanes of one LDS read phase touch 16 different bank groups.
+// Key tiles come in through global_load_lds, 32 keys at a time (K_s, V, phi(K_s): 32 rows x
+// 256 B each), double buffered: 48 KB, so two workgroups share a CU and each SIMD holds two
+// wavefronts (one waits on its loads or its dependent exponentials while the other issues).
+// 16-byte chunk c of row r is stored at position c ^ (r % 16) of the row, so the 16 lanes of
+// one LDS read phase touch 16 different bank groups.
 constexpr int kGThreads = 256;
-constexpr int kGTile = kBK * kD * 2;                 // 16 KB: one f16 64 x 128 tile
-constexpr int kGBuf = 3 * kGTile;                    // K_s, V, phi(K_s)
-constexpr int kGLds = 2 * kGBuf;                     // double buffered
+constexpr int kGTile = kBK * kD * 2;                 // 16 KB: one f16 64 x 128 tile (pass 1)
+constexpr int kGHalf = 32 * kD * 2;                  // 8 KB: 32 key rows of one operand
+constexpr int kGBuf = 3 * kGHalf;                    // K_s, V, phi(K_s) of 32 keys
+constexpr int kGLds = 2 * kGBuf;                     // double buffered (pass 1 uses 16 KB)
 
 // this wavefront's quarter of a key block's three tiles into LDS buffer `buf`
 __device__ inline void g_issue(int8_t* buf, const uint32_t* ks, const uint32_t* vv,
@@ -124,6 +127,25 @@ __device__ inline void g_issue(int8_t* buf, const uint32_t* ks, const uint32_t* 
     }
   }
 }
+// this wavefront's quarter of 32 keys' three 8 KB tiles (rows 4 u .. 4 u + 3 for u = w, 4 + w)
+__device__ inline void g_issue_half(int8_t* buf, const uint32_t* ks, const uint32_t* vv,
+                                    const uint32_t* pk, size_t row0, int w, int lane) {
+#pragma unroll
+  for (int t = 0; t < 3; ++t) {
+    const uint32_t* src = t == 0 ? ks : (t == 1 ? vv : pk);
+#pragma unroll
+    for (int u2 = 0; u2 < 2; ++u2) {
+      const int u = 4 * u2 + w;
+      const int row = 4 * u + (lane >> 4);
+      const int c = (lane & 15) ^ (row & 15);
+      const uint32_t* s = src + (row0 + row) * (kD / 2) + 4 * c;
+      int8_t* d = buf + t * kGHalf + 1024 * u;
+      __builtin_amdgcn_global_load_lds(
+          s, reinterpret_cast<__attribute__((address_space(3))) void*>(reinterpret_cast<uintptr_t>(d)),
+          16, 0, 0);
+    }
+  }
+}
 // A fragment: key row `row` (0..63) of a tile, K step s (d = 16 s + 8 g .. +7)
 __device__ inline f16x8 g_frag(const int8_t* tile, int row, int s, int g) {
   const int c = 2 * s + g;
@@ -131,7 +153,7 @@ __device__ inline f16x8 g_frag(const int8_t* tile, int row, int s, int g) {
 }
 
 template <typename T>
-__global__ __launch_bounds__(kGThreads) void mask_grad_kernel(const T* __restrict__ Q,
+__global__ __launch_bounds__(kGThreads, 2) void mask_grad_kernel(const T* __restrict__ Q,
                                                               const GradArgs x, int N, int H) {
   __shared__ __attribute__((aligned(16))) int8_t smem[kGLds];
   __shared__ float zrow[kD];
@@ -228,7 +250,8 @@ __global__ __launch_bounds__(kGThreads) void mask_grad_kernel(const T* __restric
 #pragma unroll
   for (int s = 0; s < 8; ++s)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) den = fmaf(ph[8 * s + e] * pinv, zrow[16 * s + 8 * g + e], den);
+    for (int e = 0; e < 8; ++e)
+      den = fmaf(static_cast<float>(pB[s][e]), zrow[16 * s + 8 * g + e], den);   // f16 phi(q)
   den += __shfl_xor(den, 32);
 
   const float c2 = kGLog2e * kGInvSqrtD;
@@ -275,46 +298,47 @@ __global__ __launch_bounds__(kGThreads) void mask_grad_kernel(const T* __restric
   const float kl = (nuns > 0 && den != 0.f) ? (1.f - a) / den : 0.f;
   const float undo = 1.0f / dsc;
 
-  // ---- pass 2: every key block
+  // ---- pass 2: every key block, 32 keys per step (two steps a block)
   float* gout = x.g + row * nkb;
-  g_issue(smem, x.ks16, x.v16, x.pk16, tile0, w, lane, false);
+  const int nh = 2 * nkb;
+  g_issue_half(smem, x.ks16, x.v16, x.pk16, tile0, w, lane);
   __builtin_amdgcn_s_waitcnt(0x0F70);
   __syncthreads();
-  for (int j = 0; j < nkb; ++j) {
-    int8_t* cur = smem + (j & 1) * kGBuf;
-    if (j + 1 < nkb)
-      g_issue(smem + ((j + 1) & 1) * kGBuf, x.ks16, x.v16, x.pk16,
-              tile0 + static_cast<size_t>(j + 1) * kBK, w, lane, false);
-    if (t == 0 && j > 0)   // block j - 1's sum (its parts were written before the barrier)
-      gout[j - 1] = (red[(j - 1) & 1][0] + red[(j - 1) & 1][1]) +
-                    (red[(j - 1) & 1][2] + red[(j - 1) & 1][3]);
-    float a1 = 0.f, a2 = 0.f, a3 = 0.f, a4 = 0.f;
-#pragma unroll
-    for (int kt2 = 0; kt2 < 2; ++kt2) {
-      const int kr = 32 * kt2 + l32;
-      f32x16 sv = f32x16{}, dp = f32x16{}, sp = f32x16{};
-#pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        sv = __builtin_amdgcn_mfma_f32_32x32x16_f16(g_frag(cur, kr, s, g), qB[s], sv, 0, 0, 0);
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_f16(g_frag(cur + kGTile, kr, s, g), dB[s], dp,
-                                                    0, 0, 0);
-        sp = __builtin_amdgcn_mfma_f32_32x32x16_f16(g_frag(cur + 2 * kGTile, kr, s, g), pB[s],
-                                                    sp, 0, 0, 0);
-      }
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float e = __builtin_amdgcn_exp2f(fmaf(sv[r], c2, -m2));
-        a1 = fmaf(e, dp[r], a1);
-        a2 += e;
-        a3 = fmaf(sp[r], dp[r], a3);
-        a4 += sp[r];
-      }
+  float a1 = 0.f, a2 = 0.f, a3 = 0.f, a4 = 0.f;
+  for (int hb = 0; hb < nh; ++hb) {
+    const int8_t* cur = smem + (hb & 1) * kGBuf;
+    if (hb + 1 < nh)
+      g_issue_half(smem + ((hb + 1) & 1) * kGBuf, x.ks16, x.v16, x.pk16,
+                   tile0 + static_cast<size_t>(hb + 1) * 32, w, lane);
+    if (t == 0 && (hb & 1) == 0 && hb > 0) {   // block hb / 2 - 1 (its parts are visible)
+      const int jb = (hb >> 1) - 1;
+      gout[jb] = (red[jb & 1][0] + red[jb & 1][1]) + (red[jb & 1][2] + red[jb & 1][3]);
     }
-    const float gl = ka * fmaf(a1, undo, -c_s * a2) - kl * fmaf(a3, undo, -c_l * a4);
-    const float ws = wave_sum(gl);
-    if (lane == 0) red[j & 1][w] = ws;
-    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): block j + 1's tiles landed
-    __syncthreads();                      // ... for every wavefront; block j's parts visible
+    f32x16 sv = f32x16{}, dp = f32x16{}, sp = f32x16{};
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      sv = __builtin_amdgcn_mfma_f32_32x32x16_f16(g_frag(cur, l32, s, g), qB[s], sv, 0, 0, 0);
+      dp = __builtin_amdgcn_mfma_f32_32x32x16_f16(g_frag(cur + kGHalf, l32, s, g), dB[s], dp, 0,
+                                                  0, 0);
+      sp = __builtin_amdgcn_mfma_f32_32x32x16_f16(g_frag(cur + 2 * kGHalf, l32, s, g), pB[s], sp,
+                                                  0, 0, 0);
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float e = __builtin_amdgcn_exp2f(fmaf(sv[r], c2, -m2));
+      a1 = fmaf(e, dp[r], a1);
+      a2 += e;
+      a3 = fmaf(sp[r], dp[r], a3);
+      a4 += sp[r];
+    }
+    if (hb & 1) {   // the block's second half: its number
+      const float gl = ka * fmaf(a1, undo, -c_s * a2) - kl * fmaf(a3, undo, -c_l * a4);
+      const float ws = wave_sum(gl);
+      if (lane == 0) red[(hb >> 1) & 1][w] = ws;
+      a1 = a2 = a3 = a4 = 0.f;
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): the next 32 keys' tiles landed
+    __syncthreads();                      // ... for every wavefront; this step's parts visible
   }
   if (t == 0)
     gout[nkb - 1] = (red[(nkb - 1) & 1][0] + red[(nkb - 1) & 1][1]) +
