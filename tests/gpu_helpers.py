@@ -42,6 +42,22 @@ def oracle_heads(q, k, v, wq, wk, alpha, keep, heads=None, mask=None, quant=True
     return out
 
 
+def oracle_router_masks(q, k, wq, wk, keep):
+    """The oracle router's hard Top-k masks [B, H, N/128, N/64] (uint8): the input mask of the
+    backward tests, given to the GPU and to the oracle alike."""
+    B, H, N, _ = q.shape
+    kb = oracle.kept_blocks(N // 64, keep)
+    out = np.zeros((B, H, N // 128, N // 64), np.uint8)
+    for b in range(B):
+        for h in range(H):
+            _, mu32 = oracle.colmean(k[b, h])
+            ks = oracle.smooth_k(k[b, h], mu32)
+            _, P = oracle.router_scores(oracle.block_mean(np.asarray(q[b, h], np.float64), 128),
+                                        oracle.block_mean(ks, 64), wq[h], wk[h])
+            out[b, h] = oracle.topk_blocks(P, kb)[0]
+    return out
+
+
 def rows_agreeing(gpu_mask, oracle_mask):
     """Query blocks whose GPU kept set is the oracle's own. A row block of O depends only on its
     own mask row (its kept list in the sparse branch, its dropped set in the linear one), so

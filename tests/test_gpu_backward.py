@@ -16,7 +16,7 @@ import torch
 from block_sparse_linear_pool_amd import sla2
 from block_sparse_linear_pool_amd import workloads as W
 from oracle import sla2_backward as bw
-from tests.gpu_helpers import dev, host, rel_l2
+from tests.gpu_helpers import dev, host, oracle_router_masks, rel_l2
 
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
@@ -137,9 +137,7 @@ def test_backward_router_masks(name, heads):
     wq, wk, alpha = W.weights(w)
     if heads is not None:
         wq, wk, alpha = wq[heads], wk[heads], alpha[heads]
-    t = TDT[w.dtype]
-    _, mask, _ = sla2.sla2_router(dev(q, t), dev(k, t), dev(wq), dev(wk), w.keep_frac[0])
-    mask = host(mask)
+    mask = oracle_router_masks(q, k, wq, wk, w.keep_frac[0])
     dO = W.grad_out(w.seed, q.shape)
     say("backward router mask", name, q.shape)
     B, H = q.shape[:2]
@@ -155,16 +153,15 @@ def test_backward_benchmark_size_and_determinism():
     wq, wk, alpha = W.weights(w)
     t = TDT[w.dtype]
     g = [dev(q, t), dev(k, t), dev(v, t)]
-    _, mask, _ = sla2.sla2_router(g[0], g[1], dev(wq), dev(wk), w.keep_frac[-1])
+    mask = oracle_router_masks(q, k, wq, wk, w.keep_frac[-1])
     dO = W.grad_out(w.seed, q.shape)
-    ga, gd = dev(alpha), dev(dO)
-    first = sla2.sla2_backward(*g, mask, ga, gd)
-    second = sla2.sla2_backward(*g, mask, ga, gd)
+    ga, gd, gm = dev(alpha), dev(dO), dev(mask, torch.uint8)
+    first = sla2.sla2_backward(*g, gm, ga, gd)
+    second = sla2.sla2_backward(*g, gm, ga, gd)
     torch.cuda.synchronize()
     for x, y in zip(first, second):
         assert torch.equal(x, y)
     got = [host(x) for x in first]
-    mask = host(mask)
     say("backward bench size")
     for b, h in [(0, 3), (0, 10)]:
         r = bw.backward(q[b, h], k[b, h], v[b, h], mask[b, h], alpha[h], dO[b, h])
@@ -176,18 +173,17 @@ def test_backward_benchmark_size_and_determinism():
 @pytest.mark.timeout(900)
 def test_backward_wan14b_full_size():
     """The largest shape: B = 1, H = 40, N = 75648 (591 query blocks, 1182 key blocks), 5 %
-    kept, the router's mask; every head in one call, one head against the oracle."""
+    kept, the (oracle) router's mask; every head in one call, one head against the oracle."""
     w = W.WORKLOADS["wan14b_720p_N75648"]
     q, k, v = W.generate(w)
     wq, wk, alpha = W.weights(w)
     t = TDT[w.dtype]
     g = [dev(q, t), dev(k, t), dev(v, t)]
-    _, mask, _ = sla2.sla2_router(g[0], g[1], dev(wq), dev(wk), w.keep_frac[0])
+    mask = oracle_router_masks(q, k, wq, wk, w.keep_frac[0])
     dO = W.grad_out(w.seed, q.shape)
-    got = [host(x) for x in sla2.sla2_backward(*g, mask, dev(alpha), dev(dO))]
+    got = [host(x) for x in sla2.sla2_backward(*g, dev(mask, torch.uint8), dev(alpha), dev(dO))]
     for x in got:
         assert np.isfinite(x).all()
-    mask = host(mask)
     b, h = 0, 27
     say("backward wan14b: oracle on one head")
     r = bw.backward(q[b, h], k[b, h], v[b, h], mask[b, h], alpha[h], dO[b, h])
