@@ -8,6 +8,7 @@
   block indices and scales come from memory), rows 60-90 % kept (the linear branch then sums
   the dropped blocks directly instead of total minus kept), a full and an empty row.
 - sla2_forward at keep 0.75 (the router's kept count above half of the row).
+- The unquantised forward at the 12-head N = 32768 workload, all heads in one call.
 - The workspace's error word: clear after every forward, reported when set.
 """
 import sys
@@ -186,3 +187,31 @@ def test_workspace_error_word():
     assert sla2.sla2_workspace_status(ws) == 9
     sla2.sla2_forward(*g, keep, workspace=ws)
     assert sla2.sla2_workspace_status(ws) == 0
+
+
+@pytest.mark.timeout(600)
+def test_unquantised_bench_size():
+    """sla2_forward with quant = none on the 12-head N = 32768 workload in one call: heads 2
+    and 11 against the unquantised oracle's own forward (rows whose kept sets agree)."""
+    w = W.WORKLOADS["wan13b_480p_N32768"]
+    keep = w.keep_frac[-1]
+    q, k, v = W.generate(w)
+    wq, wk, alpha = W.weights(w)
+    t = torch.bfloat16
+    g = [dev(q, t), dev(k, t), dev(v, t), dev(wq), dev(wk), dev(alpha)]
+    say("unquantised at the bench size")
+    O, taps = sla2.sla2_forward(*g, keep, taps=("O_s",), quant="none")
+    _, mask, _ = sla2.sla2_router(g[0], g[1], g[3], g[4], keep)
+    torch.cuda.synchronize()
+    O, Os, mask = host(O), host(taps["O_s"]), host(mask)
+    for h in (2, 11):
+        r = oracle.forward_head(q[0, h], k[0, h], v[0, h], wq[h], wk[h], alpha[h], keep,
+                                quant=False)
+        check_mask_band(r["P_c"], r["kb"], mask[0, h])
+        rows = rows_agreeing(mask[0, h], r["mask"])
+        assert rows.mean() >= 0.9
+        e_s, _ = row_errors(Os[0, h], r["O_s"], rows)
+        e, m = row_errors(O[0, h], r["O"], rows)
+        say(f"  h{h}: O_s relL2 {e_s:.2e}; O relL2 {e:.2e} maxabs {m:.2e}")
+        assert e_s <= EXACT_OS_TOL
+        assert e <= REL_L2_TOL and m <= MAX_ABS_TOL
