@@ -19,7 +19,7 @@ constexpr size_t kAlign = 256;
 size_t up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 struct Plan {
-  size_t err, qsum, ksum, mu64, mu32, Bt, mask, list, cnt, qc, kc, vc, sq, sk, sv, hbf, z,
+  size_t err, qsum, ksum, mu64, mu32, Bt, At, mask, list, cnt, qc, kc, vc, sq, sk, sv, hbf, z,
       hpart, zpart, htot, ztot, ones;
   // backward only
   size_t tcnt, tlist, lse2, Dd, dht, dz, dhtot, dztot, kcol, kmean, qbf, vbf, ksb, dos, kplan,
@@ -52,7 +52,10 @@ Plan make_plan(const Geom& g, sla2_entry e, int kb) {
   p.ksum = take(BH * nkb * kD * 8);
   p.mu64 = take(BH * kD * 8);
   p.mu32 = take(BH * kD * 4);
-  if (router) p.Bt = take(BH * nkb * kD * 4);   // B = (Kbar - mu) Wk, fp32
+  if (router) {
+    p.Bt = take(BH * nkb * kD * 4);   // B = (Kbar - mu) Wk, fp32
+    p.At = take(BH * nqb * kD * 4);   // A = Qbar Wq, fp32
+  }
   if (fwd || bwd) {
     const size_t stride =
         e == SLA2_ENTRY_FORWARD || e == SLA2_ENTRY_FORWARD_SLA1 || grad ? kb : nkb;
@@ -322,10 +325,10 @@ sla2_status run_router(const Geom& g, int dt, const void* Q, const void* K, cons
   SLA2_LAUNCH(launch_colmean(g, at<double>(workspace, p.ksum), at<double>(workspace, p.mu64),
                              at<float>(workspace, p.mu32), nullptr, nullptr, stream));
   SLA2_LAUNCH(launch_project(g, at<double>(workspace, p.ksum), at<double>(workspace, p.mu64),
-                             proj_k, at<float>(workspace, p.Bt), stream));
-  SLA2_LAUNCH(launch_score_topk(g, at<double>(workspace, p.qsum), proj_q,
-                                at<float>(workspace, p.Bt), kb, mask, blocks, kb, nullptr, scores,
-                                stream));
+                             proj_k, at<float>(workspace, p.Bt), at<double>(workspace, p.qsum),
+                             proj_q, at<float>(workspace, p.At), stream));
+  SLA2_LAUNCH(launch_score_topk(g, at<float>(workspace, p.At), at<float>(workspace, p.Bt), kb,
+                                mask, blocks, kb, nullptr, scores, stream));
   return SLA2_OK;
 }
 
@@ -392,10 +395,10 @@ sla2_status sla2_router_soft(const sla2_shape* shape, const void* Q, const void*
   SLA2_LAUNCH(launch_colmean(g, at<double>(workspace, p.ksum), at<double>(workspace, p.mu64),
                              at<float>(workspace, p.mu32), nullptr, nullptr, stream));
   SLA2_LAUNCH(launch_project(g, at<double>(workspace, p.ksum), at<double>(workspace, p.mu64),
-                             proj_k, at<float>(workspace, p.Bt), stream));
-  SLA2_LAUNCH(launch_score_soft(g, at<double>(workspace, p.qsum), proj_q,
-                                at<float>(workspace, p.Bt), kb, 1.0f / tau, soft_mask, lambda,
-                                stream));
+                             proj_k, at<float>(workspace, p.Bt), at<double>(workspace, p.qsum),
+                             proj_q, at<float>(workspace, p.At), stream));
+  SLA2_LAUNCH(launch_score_soft(g, at<float>(workspace, p.At), at<float>(workspace, p.Bt), kb,
+                                1.0f / tau, soft_mask, lambda, stream));
   return SLA2_OK;
 }
 
@@ -541,8 +544,9 @@ sla2_status sla2_forward(const sla2_shape* shape, const void* Q, const void* K, 
   SLA2_LAUNCH(launch_colmean(g, at<double>(ws, p.ksum), at<double>(ws, p.mu64), at<float>(ws, p.mu32),
                              taps ? taps->k_colmean : nullptr, at<uint32_t>(ws, p.err), stream));
   SLA2_LAUNCH(launch_project(g, at<double>(ws, p.ksum), at<double>(ws, p.mu64), proj_k,
-                             at<float>(ws, p.Bt), stream));
-  SLA2_LAUNCH(launch_score_topk(g, at<double>(ws, p.qsum), proj_q, at<float>(ws, p.Bt), kb,
+                             at<float>(ws, p.Bt), at<double>(ws, p.qsum), proj_q,
+                             at<float>(ws, p.At), stream));
+  SLA2_LAUNCH(launch_score_topk(g, at<float>(ws, p.At), at<float>(ws, p.Bt), kb,
                                 at<uint8_t>(ws, p.mask), at<int32_t>(ws, p.list), kb,
                                 at<int32_t>(ws, p.cnt), nullptr, stream));
   return run_branches(g, dt, quant, Q, K, V, alpha, O, taps, ws, p, kb, rec, stream);
@@ -576,8 +580,9 @@ sla2_status sla2_forward_sla1(const sla2_shape* shape, const void* Q, const void
                              nullptr, at<uint32_t>(ws, p.err), stream));
   // the heuristic router: proj_q = proj_k = I (null weights select the identity mode)
   SLA2_LAUNCH(launch_project(g, at<double>(ws, p.ksum), at<double>(ws, p.mu64), nullptr,
-                             at<float>(ws, p.Bt), stream));
-  SLA2_LAUNCH(launch_score_topk(g, at<double>(ws, p.qsum), nullptr, at<float>(ws, p.Bt), kb,
+                             at<float>(ws, p.Bt), at<double>(ws, p.qsum), nullptr,
+                             at<float>(ws, p.At), stream));
+  SLA2_LAUNCH(launch_score_topk(g, at<float>(ws, p.At), at<float>(ws, p.Bt), kb,
                                 at<uint8_t>(ws, p.mask), at<int32_t>(ws, p.list), kb,
                                 at<int32_t>(ws, p.cnt), nullptr, stream));
   // both branches with alpha = 1 and the O_l tap: O receives O_s, O_l the linear branch
@@ -765,11 +770,12 @@ sla2_status sla2_router_grad(const sla2_shape* shape, const void* Q, const void*
   SLA2_LAUNCH(launch_colmean(g, at<double>(ws, p.ksum), at<double>(ws, p.mu64), at<float>(ws, p.mu32),
                              nullptr, at<uint32_t>(ws, p.err), stream));
   SLA2_LAUNCH(launch_project(g, at<double>(ws, p.ksum), at<double>(ws, p.mu64), proj_k,
-                             at<float>(ws, p.Bt), stream));
-  SLA2_LAUNCH(launch_score_topk(g, at<double>(ws, p.qsum), proj_q, at<float>(ws, p.Bt), kb,
+                             at<float>(ws, p.Bt), at<double>(ws, p.qsum), proj_q,
+                             at<float>(ws, p.At), stream));
+  SLA2_LAUNCH(launch_score_topk(g, at<float>(ws, p.At), at<float>(ws, p.Bt), kb,
                                 at<uint8_t>(ws, p.mask), at<int32_t>(ws, p.list), kb,
                                 at<int32_t>(ws, p.cnt), nullptr, stream));
-  SLA2_LAUNCH(launch_score_soft(g, at<double>(ws, p.qsum), proj_q, at<float>(ws, p.Bt), kb,
+  SLA2_LAUNCH(launch_score_soft(g, at<float>(ws, p.At), at<float>(ws, p.Bt), kb,
                                 1.0f / tau, at<float>(ws, p.soft), at<float>(ws, p.lam), stream));
   // the unquantised forward with its branch outputs kept
   sla2_taps tp{};

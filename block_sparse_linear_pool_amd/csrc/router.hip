@@ -9,9 +9,9 @@
 //               the forward) the INT8 codes of Q for the sparse branch.
 //   colmean     mu = colmean(K) from the key-block sums (all blocks have 64 rows), the
 //               K smoothing of §7 note 1 of the second page.
-//   project     B = (Kbar - mu) Wk in fp32 (Kbar - mu is the mean of K_s); with no weights
-//               the identity (the heuristic router of the earlier SLA).
-//   score_topk  per 16 query blocks: A = Qbar Wq, G = A B^T / sqrt(d) in fp32 (MFMA) into
+//   project     B = (Kbar - mu) Wk and A = Qbar Wq in fp32 (Kbar - mu is the mean of K_s);
+//               with no weights the identity (the heuristic router of the earlier SLA).
+//   score_topk  per 16 query blocks: G = A B^T / sqrt(d) in fp32 (MFMA) into
 //               LDS, then one wavefront per query block selects the kb largest logits
 //               exactly (ties to the lower index) and writes the mask and the ascending
 //               block list; in its soft mode the SoftTop-k mask sigma(P_c / tau + lambda_i)
@@ -135,34 +135,39 @@ hipError_t launch_pool(const Geom& g, int dtype, const void* Q, const void* K, d
 }
 
 // ---------------------------------------------------------------- colmean
-// grid (8, BH), 256 threads: workgroup x takes columns 16 x .. 16 x + 15 of head bh; thread t
-// sums column 16 x + t % 16 over key blocks t / 16, t / 16 + 16, ... with four accumulators
-// (four loads in flight); the 16 partial sums are combined in a fixed order (deterministic).
-__global__ __launch_bounds__(256) void colmean_kernel(const double* __restrict__ ksum,
-                                                      double* __restrict__ mu64,
-                                                      float* __restrict__ mu32,
-                                                      float* __restrict__ mu32_tap,
-                                                      uint32_t* __restrict__ err, int nkb,
-                                                      int N) {
-  __shared__ double part[16][17];
+// grid (8, BH), 1024 threads: workgroup x takes columns 16 x .. 16 x + 15 of head bh; thread t
+// sums column 16 x + t % 16 over key blocks t / 16 + 64 m (eight loads in flight per round, so
+// one round covers 512 key blocks); the 64 partial sums of a column are combined by a fixed
+// pairwise tree in LDS (deterministic).
+constexpr int kColThreads = 1024;
+__global__ __launch_bounds__(kColThreads) void colmean_kernel(const double* __restrict__ ksum,
+                                                              double* __restrict__ mu64,
+                                                              float* __restrict__ mu32,
+                                                              float* __restrict__ mu32_tap,
+                                                              uint32_t* __restrict__ err, int nkb,
+                                                              int N) {
+  __shared__ double part[64][17];
   const int bh = blockIdx.y, t = threadIdx.x, c = 16 * blockIdx.x + (t & 15), sl = t >> 4;
   if (err != nullptr && blockIdx.x == 0 && blockIdx.y == 0 && t == 0) *err = 0u;
   const double* p = ksum + static_cast<size_t>(bh) * nkb * kD + c;
-  double a0 = 0.0, a1 = 0.0, a2 = 0.0, a3 = 0.0;
-  int j = sl;
-  for (; j + 48 < nkb; j += 64) {
-    a0 += p[static_cast<size_t>(j) * kD];
-    a1 += p[static_cast<size_t>(j + 16) * kD];
-    a2 += p[static_cast<size_t>(j + 32) * kD];
-    a3 += p[static_cast<size_t>(j + 48) * kD];
+  double a = 0.0;
+  for (int j0 = sl; j0 < nkb; j0 += 512) {
+    double v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      v[u] = j0 + 64 * u < nkb ? p[static_cast<size_t>(j0 + 64 * u) * kD] : 0.0;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) a += v[u];
   }
-  for (; j < nkb; j += 16) a0 += p[static_cast<size_t>(j) * kD];
-  part[sl][t & 15] = (a0 + a1) + (a2 + a3);
+  part[sl][t & 15] = a;
   __syncthreads();
+#pragma unroll
+  for (int h = 32; h >= 1; h >>= 1) {
+    if (sl < h) part[sl][t & 15] += part[sl + h][t & 15];
+    __syncthreads();
+  }
   if (t < 16) {
-    double s = 0.0;
-    for (int q = 0; q < 16; ++q) s += part[q][t];
-    const double mu = s / static_cast<double>(N);
+    const double mu = part[0][t] / static_cast<double>(N);
     mu64[bh * kD + c] = mu;
     mu32[bh * kD + c] = static_cast<float>(mu);
     if (mu32_tap) mu32_tap[bh * kD + c] = static_cast<float>(mu);
@@ -171,8 +176,8 @@ __global__ __launch_bounds__(256) void colmean_kernel(const double* __restrict__
 
 hipError_t launch_colmean(const Geom& g, const double* ksum, double* mu64, float* mu32,
                           float* mu32_tap, uint32_t* err, hipStream_t s) {
-  hipLaunchKernelGGL(colmean_kernel, dim3(kD / 16, g.BH), dim3(256), 0, s, ksum, mu64, mu32,
-                     mu32_tap, err, g.nkb, g.N);
+  hipLaunchKernelGGL(colmean_kernel, dim3(kD / 16, g.BH), dim3(kColThreads), 0, s, ksum, mu64,
+                     mu32, mu32_tap, err, g.nkb, g.N);
   return hipGetLastError();
 }
 
@@ -184,59 +189,96 @@ __device__ inline f32x4 mfma_f32(float a, float b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
-// ---------------------------------------------------------------- project (key side)
-// B = (Kbar - mu) Wk, fp32 [BH][nkb][d] row-major (Kbar - mu is the mean of K_s; no weights:
-// the identity, the heuristic router of the earlier SLA). grid (ceil(nkb / 16), BH), 256
-// threads: 16 key blocks per workgroup, wavefront w the output columns 32 w .. 32 w + 31 (two
-// 16 x 16 tiles, K = 128 in 32 fp32 MFMA steps each).
+// ---------------------------------------------------------------- project (both sides)
+// B = (Kbar - mu) Wk and A = Qbar Wq, fp32 [BH][rows][d] row-major (Kbar - mu is the mean of
+// K_s; no weights: the identity, the heuristic router of the earlier SLA). grid
+// (ceil(nkb / R) + ceil(nqb / R), BH), R = kProjRows, 256 threads: R key blocks (the first
+// ceil(nkb / R) workgroups) or R query blocks per workgroup, wavefront w the output columns
+// 32 w .. 32 w + 31 (R / 16 x 2 tiles of 16 x 16, K = 128 in 32 fp32 MFMA steps each); a
+// lane's 64 weights stay in registers for all its tiles. Every load of a thread (block sums,
+// means, weights) is issued before the first is used. (R = 32 halves the weight reads but
+// measured no faster at 12 heads, N = 32768.)
 constexpr int kXPad = kD + 4;
+constexpr int kProjRows = 16;
 __global__ __launch_bounds__(256) void project_kernel(const double* __restrict__ ksum,
                                                       const double* __restrict__ mu64,
                                                       const float* __restrict__ wk,
-                                                      float* __restrict__ B, int nkb, int H) {
-  __shared__ float xs[16][kXPad];
+                                                      float* __restrict__ B,
+                                                      const double* __restrict__ qsum,
+                                                      const float* __restrict__ wq,
+                                                      float* __restrict__ A, int nkb, int nqb,
+                                                      int H) {
+  __shared__ float xs[kProjRows][kXPad];
   const int bh = blockIdx.y, h = bh % H, t = threadIdx.x;
   const int lane = t & 63, w = t >> 6, ra = lane & 15, kq = lane >> 4;
-  const int r0 = 16 * blockIdx.x;
-  const double* src = ksum + static_cast<size_t>(bh) * nkb * kD;
-  for (int e = t; e < 16 * kD; e += 256) {
-    const int r = e >> 7, c = e & 127;
-    xs[r][c] = r0 + r < nkb
-                   ? static_cast<float>(src[static_cast<size_t>(r0 + r) * kD + c] * (1.0 / kBK) -
-                                        mu64[bh * kD + c])
-                   : 0.f;
+  const int nkt = (nkb + kProjRows - 1) / kProjRows;
+  const bool key_side = static_cast<int>(blockIdx.x) < nkt;
+  const int r0 = kProjRows * (key_side ? blockIdx.x : blockIdx.x - nkt);
+  const int nrow = key_side ? nkb : nqb;
+  const double* src = key_side ? ksum + static_cast<size_t>(bh) * nkb * kD
+                               : qsum + static_cast<size_t>(bh) * nqb * kD;
+  const float* W = key_side ? wk : wq;
+  float* out = key_side ? B + static_cast<size_t>(bh) * nkb * kD
+                        : A + static_cast<size_t>(bh) * nqb * kD;
+  float wv[2][32];
+  if (W != nullptr) {
+    const float* Wh = W + static_cast<size_t>(h) * kD * kD;
+#pragma unroll
+    for (int s = 0; s < 32; ++s) {
+      const int k = 32 * kq + s;
+      wv[0][s] = Wh[k * kD + 32 * w + ra];
+      wv[1][s] = Wh[k * kD + 32 * w + 16 + ra];
+    }
+  }
+  constexpr int kPer = kProjRows * kD / 256;
+  double xv[kPer];
+  const double mu = key_side ? mu64[bh * kD + (t & 127)] : 0.0;   // column t % 128 throughout
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    const int r = (t + 256 * u) >> 7;
+    xv[u] = r0 + r < nrow ? src[static_cast<size_t>(r0 + r) * kD + (t & 127)] : 0.0;
+  }
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    const int r = (t + 256 * u) >> 7;
+    xs[r][t & 127] = r0 + r >= nrow ? 0.f
+                     : key_side     ? static_cast<float>(xv[u] * (1.0 / kBK) - mu)
+                                    : static_cast<float>(xv[u] * (1.0 / kBQ));
   }
   __syncthreads();
-  float* out = B + static_cast<size_t>(bh) * nkb * kD;
-  if (wk == nullptr) {
-    for (int e = t; e < 16 * kD; e += 256) {
+  if (W == nullptr) {
+    for (int e = t; e < kProjRows * kD; e += 256) {
       const int r = e >> 7, c = e & 127;
-      if (r0 + r < nkb) out[static_cast<size_t>(r0 + r) * kD + c] = xs[r][c];
+      if (r0 + r < nrow) out[static_cast<size_t>(r0 + r) * kD + c] = xs[r][c];
     }
     return;
   }
-  const float* W = wk + static_cast<size_t>(h) * kD * kD;
-  f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-#pragma unroll 8
-  for (int s = 0; s < 32; ++s) {
-    const int k = 32 * kq + s;
-    const float x = xs[ra][k];
-    acc[0] = mfma_f32(x, W[k * kD + 32 * w + ra], acc[0]);
-    acc[1] = mfma_f32(x, W[k * kD + 32 * w + 16 + ra], acc[1]);
-  }
 #pragma unroll
-  for (int u = 0; u < 2; ++u)
+  for (int rt = 0; rt < kProjRows / 16; ++rt) {
+    f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = r0 + 4 * kq + i;
-      if (r < nkb) out[static_cast<size_t>(r) * kD + 32 * w + 16 * u + ra] = acc[u][i];
+    for (int s = 0; s < 32; ++s) {
+      const float x = xs[16 * rt + ra][32 * kq + s];
+      acc[0] = mfma_f32(x, wv[0][s], acc[0]);
+      acc[1] = mfma_f32(x, wv[1][s], acc[1]);
     }
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = r0 + 16 * rt + 4 * kq + i;
+        if (r < nrow) out[static_cast<size_t>(r) * kD + 32 * w + 16 * u + ra] = acc[u][i];
+      }
+  }
 }
 
 hipError_t launch_project(const Geom& g, const double* ksum, const double* mu64, const float* wk,
-                          float* B, hipStream_t s) {
-  hipLaunchKernelGGL(project_kernel, dim3((g.nkb + 15) / 16, g.BH), dim3(256), 0, s, ksum, mu64,
-                     wk, B, g.nkb, g.H);
+                          float* B, const double* qsum, const float* wq, float* A,
+                          hipStream_t s) {
+  const int tiles = (g.nkb + kProjRows - 1) / kProjRows +
+                    (A != nullptr ? (g.nqb + kProjRows - 1) / kProjRows : 0);
+  hipLaunchKernelGGL(project_kernel, dim3(tiles, g.BH), dim3(256), 0, s, ksum, mu64, wk, B,
+                     qsum, wq, A, g.nkb, g.nqb, g.H);
   return hipGetLastError();
 }
 
@@ -268,15 +310,41 @@ __device__ inline int count_below_lane(uint64_t m) {
 __host__ __device__ inline int score_rows(int nkb) { return nkb <= 2048 ? 16 : 8; }
 constexpr int kScoreThreads = 1024;   // 16 wavefronts: one row each in the selection
 
+// The largest T with #{key >= T} >= kb, built bit by bit from the top (each count a sum of
+// ballot popcounts over the wavefront's N keys per lane), stopping early once #{key >= T} is
+// exactly kb. Either way #{key >= T} >= kb and no key above T is left out of the kb largest.
+template <int N>
+__device__ inline uint32_t kth_key(const uint32_t (&key)[N], int kb) {
+  uint32_t T = 0;
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t cand = T | (1u << bit);
+    int c = 0;
+#pragma unroll
+    for (int e = 0; e < N; ++e) c += __popcll(__ballot(key[e] >= cand));
+    if (c >= kb) {
+      T = cand;
+      // exactly kb keys >= T: they are the kept set (no key equal to the boundary is left
+      // out), and the selection below keeps exactly the keys >= T
+      if (c == kb) break;
+    }
+  }
+  return T;
+}
+
+constexpr int kCand = 256;   // candidate keys one wavefront compacts before its threshold search
+
 // Kept set of one row, exact (ties to the lower index), by one wavefront. The row's keys
-// sit in registers, E per lane (key j = lane + 64 e). T is built bit by bit from the top as
-// the largest T with #{key >= T} >= kb (the kb-th largest key), each count a sum of ballot
-// popcounts, stopping early once #{key >= T} is exactly kb. Then every key > T is kept, plus
-// the lowest-index keys equal to T up to kb.
+// sit in registers, E per lane (key j = lane + 64 e). T is a threshold from kth_key; every key
+// > T is kept, plus the lowest-index keys equal to T up to kb.
+// Candidate filter (kb <= 64, more than 256 keys): the kb-th largest of the 64 lane maxima,
+// T0, is at most the kb-th largest key (those kb maxima are kb distinct keys >= T0), so every
+// key that can be kept is >= T0. When at most kCand keys are, they are compacted into `cand`
+// (this wavefront's LDS) and searched 4 per lane instead of E; a search result below T0 (an
+// early stop with exactly kb candidates) is raised to T0, where #{key >= T0} is also kb.
 template <int E>
 __device__ void select_row(const float* g, int nkb, int kb, int lane, size_t row,
                            int32_t* __restrict__ list, int list_stride,
-                           uint8_t* __restrict__ mask) {
+                           uint8_t* __restrict__ mask, uint32_t* cand) {
   uint32_t key[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) {
@@ -284,22 +352,39 @@ __device__ void select_row(const float* g, int nkb, int kb, int lane, size_t row
     key[e] = j < nkb ? order_key(g[j]) : 0u;   // finite keys are >= 1
   }
   uint32_t T = 0;
-  for (int bit = 31; bit >= 0; --bit) {
-    const uint32_t cand = T | (1u << bit);
-    int c = 0;
+  bool found = false;
+  if (kb <= 64 && nkb > 256) {
+    uint32_t mx[1] = {key[0]};
 #pragma unroll
-    for (int e = 0; e < E; ++e) c += __popcll(__ballot(key[e] >= cand));
-    if (c >= kb) {
-      T = cand;
-      // exactly kb keys >= T: they are the kept set (no key equal to the boundary is left
-      // out), and the code below keeps exactly the keys >= T
-      if (c == kb) break;
+    for (int e = 1; e < E; ++e) mx[0] = max(mx[0], key[e]);
+    const uint32_t T0 = kth_key<1>(mx, kb);
+    int C = 0;
+#pragma unroll
+    for (int e = 0; e < E; ++e) C += __popcll(__ballot(key[e] >= T0));
+    if (C <= kCand) {
+      int at = 0;
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const bool in = key[e] >= T0;
+        const uint64_t m = __ballot(in);
+        if (in) cand[at + count_below_lane(m)] = key[e];
+        at += __popcll(m);
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      uint32_t ck[kCand / 64];
+#pragma unroll
+      for (int u = 0; u < kCand / 64; ++u) ck[u] = lane + 64 * u < C ? cand[lane + 64 * u] : 0u;
+      T = max(kth_key<kCand / 64>(ck, kb), T0);
+      found = true;
     }
   }
+  if (!found) T = kth_key<E>(key, kb);
   int gt = 0;
 #pragma unroll
   for (int e = 0; e < E; ++e) gt += __popcll(__ballot(key[e] > T));
-  const int need = kb - gt;   // >= 1: equal keys to keep, lowest indices first
+  const int need = kb - gt;   // >= 0: equal keys to keep, lowest indices first
   int eq_before = 0, sel_before = 0;
 #pragma unroll
   for (int e = 0; e < E; ++e) {
@@ -397,66 +482,52 @@ __device__ void soft_row(const float* g, int nkb, int kb, float inv_tau, int lan
 }
 
 // grid (ceil(nqb / RT), BH), kScoreThreads threads, RT = score_rows(nkb); dynamic LDS RT * nkb
-// floats. Per workgroup: the RT query-block rows' A = Qbar Wq (fp32 MFMA; no weights: the
-// identity), then the logits G = A B^T / sqrt(d) of every key block (fp32 MFMA, 16 x 16 tiles
-// dealt to the 16 wavefronts; a lane's B operand is 32 contiguous floats of one key block's
-// row), then one row per wavefront: the exact hard Top-k (kSoft = false: mask, ascending list,
-// count and the optional fp32 P_c) or the SoftTop-k mask and lambda (kSoft). E = keys per lane
-// held in registers (nkb <= 64 E).
+// floats. Per workgroup: the logits G = A B^T / sqrt(d) of its RT query-block rows against
+// every key block (fp32 MFMA, 16 x 16 tiles dealt to the 16 wavefronts, the next tile's B
+// operands loaded during the current tile's products; a lane's A and B operands are 32
+// contiguous floats of one row) into LDS, then one row per wavefront: the exact hard Top-k
+// (kSoft = false: mask, ascending list, count and the optional fp32 P_c) or the SoftTop-k mask
+// and lambda (kSoft). E = keys per lane held in registers (nkb <= 64 E).
 template <int E, bool kSoft>
 __global__ __launch_bounds__(kScoreThreads) void score_topk_kernel(
-    const double* __restrict__ qsum, const float* __restrict__ wq, const float* __restrict__ B,
-    int nqb, int nkb, int H, int kb, uint8_t* __restrict__ mask, int32_t* __restrict__ list,
-    int list_stride, int32_t* __restrict__ cnt, float* __restrict__ scores, float inv_tau,
+    const float* __restrict__ A, const float* __restrict__ B, int nqb, int nkb, int kb,
+    uint8_t* __restrict__ mask, int32_t* __restrict__ list, int list_stride,
+    int32_t* __restrict__ cnt, float* __restrict__ scores, float inv_tau,
     float* __restrict__ soft, float* __restrict__ lam) {
-  extern __shared__ float G[];                 // [RT][nkb]
-  __shared__ float xs[16][kXPad];              // Qbar rows
-  __shared__ float as[16][kXPad];              // A rows
+  extern __shared__ float G[];                        // [RT][nkb]
+  __shared__ uint32_t cand[kScoreThreads / 64][kCand];
   const int RT = score_rows(nkb);
-  const int bh = blockIdx.y, h = bh % H, t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int bh = blockIdx.y, t = threadIdx.x, lane = t & 63, w = t >> 6;
   const int ra = lane & 15, kq = lane >> 4;
   const int i0 = blockIdx.x * RT;
-  for (int e = t; e < 16 * kD; e += kScoreThreads) {
-    const int r = e >> 7, c = e & 127;
-    const int i = i0 + r;
-    xs[r][c] = (r < RT && i < nqb)
-                   ? static_cast<float>(qsum[(static_cast<size_t>(bh) * nqb + i) * kD + c] *
-                                        (1.0 / kBQ))
-                   : 0.f;
-  }
-  __syncthreads();
-  if (wq == nullptr) {
-    for (int e = t; e < 16 * kD; e += kScoreThreads) as[e >> 7][e & 127] = xs[e >> 7][e & 127];
-  } else if (w < 8) {
-    // output columns 16 w .. 16 w + 15
-    const float* W = wq + static_cast<size_t>(h) * kD * kD;
-    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll 8
-    for (int s = 0; s < 32; ++s) {
-      const int k = 32 * kq + s;
-      acc = mfma_f32(xs[ra][k], W[k * kD + 16 * w + ra], acc);
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) as[4 * kq + i][16 * w + ra] = acc[i];
-  }
-  __syncthreads();
   {
-    // this lane's A operand: row ra, elements 32 kq .. 32 kq + 31
-    float a_op[32];
-#pragma unroll
-    for (int s = 0; s < 32; ++s) a_op[s] = as[ra][32 * kq + s];
     const float inv_sqrt_d = 0.088388347648318440f;   // 1/sqrt(128)
     const float* Bh = B + static_cast<size_t>(bh) * nkb * kD;
     const int ntile = (nkb + 15) >> 4;
-    for (int ct = w; ct < ntile; ct += kScoreThreads / 64) {
-      const int col = 16 * ct + ra;
-      const f32x4* bp = reinterpret_cast<const f32x4*>(Bh + static_cast<size_t>(min(col, nkb - 1)) * kD + 32 * kq);
-      f32x4 bv[8];
+    f32x4 bv[8], bn[8], av[8];
+    auto load_tile = [&](f32x4(&dst)[8], int ct) {
+      const int col = min(16 * ct + ra, nkb - 1);
+      const f32x4* bp = reinterpret_cast<const f32x4*>(Bh + static_cast<size_t>(col) * kD + 32 * kq);
 #pragma unroll
-      for (int u = 0; u < 8; ++u) bv[u] = bp[u];
+      for (int u = 0; u < 8; ++u) dst[u] = bp[u];
+    };
+    if (w < ntile) load_tile(bv, w);
+    // this lane's A operand: row i0 + ra (zero past RT or nqb), elements 32 kq .. 32 kq + 31
+    const int ia = i0 + ra;
+    if (ra < RT && ia < nqb) {
+      const f32x4* ap = reinterpret_cast<const f32x4*>(A + (static_cast<size_t>(bh) * nqb + ia) * kD + 32 * kq);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) av[u] = ap[u];
+    } else {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) av[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    for (int ct = w; ct < ntile; ct += kScoreThreads / 64) {
+      if (ct + kScoreThreads / 64 < ntile) load_tile(bn, ct + kScoreThreads / 64);
       f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int s = 0; s < 32; ++s) acc = mfma_f32(a_op[s], bv[s >> 2][s & 3], acc);
+      for (int s = 0; s < 32; ++s) acc = mfma_f32(av[s >> 2][s & 3], bv[s >> 2][s & 3], acc);
+      const int col = 16 * ct + ra;
       if (col < nkb) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -464,6 +535,8 @@ __global__ __launch_bounds__(kScoreThreads) void score_topk_kernel(
           if (r < RT) G[r * nkb + col] = acc[i] * inv_sqrt_d + 0.0f;   // +0: no -0
         }
       }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) bv[u] = bn[u];
     }
   }
   __syncthreads();
@@ -476,7 +549,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_topk_kernel(
     soft_row<E>(g, nkb, kb, inv_tau, lane, row, soft, lam);
     return;
   }
-  select_row<E>(g, nkb, kb, lane, row, list, list_stride, mask);
+  select_row<E>(g, nkb, kb, lane, row, list, list_stride, mask, cand[w]);
   if (lane == 0 && cnt) cnt[row] = kb;
   if (scores) {
     const int nE = (nkb + 63) >> 6;
@@ -518,17 +591,17 @@ hipError_t configure_router() {
 }
 
 template <bool kSoft>
-static void launch_score_t(const Geom& g, const double* qsum, const float* wq, const float* B,
-                           int kb, uint8_t* mask, int32_t* list, int list_stride, int32_t* cnt,
-                           float* scores, float inv_tau, float* soft, float* lam, hipStream_t s) {
+static void launch_score_t(const Geom& g, const float* A, const float* B, int kb, uint8_t* mask,
+                           int32_t* list, int list_stride, int32_t* cnt, float* scores,
+                           float inv_tau, float* soft, float* lam, hipStream_t s) {
   const int RT = score_rows(g.nkb);
   dim3 grid((g.nqb + RT - 1) / RT, g.BH);
   const size_t lds = static_cast<size_t>(RT) * g.nkb * sizeof(float);
   const int E = (g.nkb + 63) / 64;
-#define SLA2_SCORE(EE)                                                                          \
-  hipLaunchKernelGGL((score_topk_kernel<EE, kSoft>), grid, dim3(kScoreThreads), lds, s, qsum, wq, \
-                     B, g.nqb, g.nkb, g.H, kb, mask, list, list_stride, cnt, scores, inv_tau,    \
-                     soft, lam)
+#define SLA2_SCORE(EE)                                                                        \
+  hipLaunchKernelGGL((score_topk_kernel<EE, kSoft>), grid, dim3(kScoreThreads), lds, s, A, B, \
+                     g.nqb, g.nkb, kb, mask, list, list_stride, cnt, scores, inv_tau, soft,   \
+                     lam)
   if (E <= 8) SLA2_SCORE(8);
   else if (E <= 16) SLA2_SCORE(16);
   else if (E <= 32) SLA2_SCORE(32);
@@ -536,18 +609,17 @@ static void launch_score_t(const Geom& g, const double* qsum, const float* wq, c
 #undef SLA2_SCORE
 }
 
-hipError_t launch_score_topk(const Geom& g, const double* qsum, const float* wq, const float* B,
-                             int kb, uint8_t* mask, int32_t* list, int list_stride, int32_t* cnt,
+hipError_t launch_score_topk(const Geom& g, const float* A, const float* B, int kb,
+                             uint8_t* mask, int32_t* list, int list_stride, int32_t* cnt,
                              float* scores, hipStream_t s) {
-  launch_score_t<false>(g, qsum, wq, B, kb, mask, list, list_stride, cnt, scores, 0.f, nullptr,
-                        nullptr, s);
+  launch_score_t<false>(g, A, B, kb, mask, list, list_stride, cnt, scores, 0.f, nullptr, nullptr,
+                        s);
   return hipGetLastError();
 }
 
-hipError_t launch_score_soft(const Geom& g, const double* qsum, const float* wq, const float* B,
-                             int kb, float inv_tau, float* soft, float* lam, hipStream_t s) {
-  launch_score_t<true>(g, qsum, wq, B, kb, nullptr, nullptr, 0, nullptr, nullptr, inv_tau, soft,
-                       lam, s);
+hipError_t launch_score_soft(const Geom& g, const float* A, const float* B, int kb,
+                             float inv_tau, float* soft, float* lam, hipStream_t s) {
+  launch_score_t<true>(g, A, B, kb, nullptr, nullptr, 0, nullptr, nullptr, inv_tau, soft, lam, s);
   return hipGetLastError();
 }
 

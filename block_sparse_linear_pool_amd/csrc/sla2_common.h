@@ -240,12 +240,14 @@ hipError_t configure_router();
 // err (optional): the attention kernel's error word, cleared here (one launch before it)
 hipError_t launch_colmean(const Geom& g, const double* ksum, double* mu64, float* mu32,
                           float* mu32_tap, uint32_t* err, hipStream_t s);
-// B = (Kbar - mu) Wk, fp32 [BH][nkb][d] (wk null: the identity)
+// B = (Kbar - mu) Wk, fp32 [BH][nkb][d], and (A non-null) A = Qbar Wq, fp32 [BH][nqb][d]
+// (wk, wq null: the identity)
 hipError_t launch_project(const Geom& g, const double* ksum, const double* mu64, const float* wk,
-                          float* B, hipStream_t s);
-// A = Qbar Wq (wq null: the identity), G = A B^T / sqrt(d), exact Top-k per row
-hipError_t launch_score_topk(const Geom& g, const double* qsum, const float* wq, const float* B,
-                             int kb, uint8_t* mask, int32_t* list, int list_stride, int32_t* cnt,
+                          float* B, const double* qsum, const float* wq, float* A,
+                          hipStream_t s);
+// G = A B^T / sqrt(d), exact Top-k per row
+hipError_t launch_score_topk(const Geom& g, const float* A, const float* B, int kb,
+                             uint8_t* mask, int32_t* list, int list_stride, int32_t* cnt,
                              float* scores, hipStream_t s);
 // p[0 .. n) = v (a kernel: no memset node in a captured graph)
 hipError_t launch_fill(float* p, int n, float v, hipStream_t s);
@@ -253,8 +255,8 @@ hipError_t launch_fill(float* p, int n, float v, hipStream_t s);
 hipError_t launch_sla1_mix(const Geom& g, const float* Ol, const float* Wo, float* O,
                            hipStream_t s);
 // SoftTop-k (training-time router): soft [BH, nqb, nkb] fp32, lam [BH, nqb] fp32 (or null)
-hipError_t launch_score_soft(const Geom& g, const double* qsum, const float* wq, const float* B,
-                             int kb, float inv_tau, float* soft, float* lam, hipStream_t s);
+hipError_t launch_score_soft(const Geom& g, const float* A, const float* B, int kb,
+                             float inv_tau, float* soft, float* lam, hipStream_t s);
 hipError_t launch_mask_to_list(const Geom& g, const uint8_t* mask_in, uint8_t* mask_out,
                                int32_t* list, int32_t* cnt, hipStream_t s);
 // Fragment order of the d x d linear-branch matrices read by the attention kernel. Its

@@ -210,7 +210,7 @@ sla2_status sla2_linear_precompute(const sla2_shape *shape, const void *K, const
 sla2_status sla2_init_device(void);
 
 /* Bytes of the static device scratch of sla2_router_noalloc (one copy per GPU, held until
- * the process ends): enough for the router at B*H = 12, N = 32768 (13 MB). */
+ * the process ends): enough for the router at B*H = 12, N = 32768 (14 MB). */
 #define SLA2_NOALLOC_SCRATCH_BYTES (32u << 20)
 
 /* sla2_router for callers that cannot allocate device memory or pass a workspace (code under

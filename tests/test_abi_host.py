@@ -75,7 +75,7 @@ def expected_forward_bytes(B, H, N, kb):
     BH, nqb, nkb, d = B * H, N // 128, N // 64, 128
     np_ = -(-nkb // 8)
     regions = [4, BH * nqb * d * 8, BH * nkb * d * 8, BH * d * 8, BH * d * 4,   # err, sums, mu
-               BH * nkb * d * 4,                                               # B = Kbar_s Wk
+               BH * nkb * d * 4, BH * nqb * d * 4,                             # B, A (fp32)
                BH * nqb * nkb, BH * nqb * kb * 4, BH * nqb * 4,                # mask, lists, counts
                BH * N * d, BH * N * d, BH * nkb * 4, BH * nkb * 4,             # K, V codes, scales
                BH * nkb * d * d * 2, BH * d * d * 4, BH * d * 4,               # h_j^T bf16, totals
@@ -87,13 +87,13 @@ def expected_forward_bytes(B, H, N, kb):
 def test_workspace_bytes_per_entry_point():
     """Each entry point asks only for what its kernels use: at the 12-head N = 32768 shape with
     3 % kept the forward needs 0.42 GB, the backward 1.29 GB (its bf16 operand copies, dH_i^T and
-    the work-item partials), the router 13 MB."""
+    the work-item partials), the router 14 MB."""
     B, H, N = 1, 12, 32768
     kb = sla2.sla2_blocks_kept(N // 64, 0.03)
     size = {e: sla2.sla2_workspace_bytes(B, H, N, entry=e, keep_frac=0.03) for e in E}
     assert size["forward"] == expected_forward_bytes(B, H, N, kb)
     assert 0.41e9 < size["forward"] < 0.43e9
-    assert size["router"] == size["router_soft"] < 14e6
+    assert size["router"] == size["router_soft"] < 15e6
     assert size["linear_precompute"] < size["forward"]
     assert size["forward_with_mask"] < size["forward"] + 4 * B * H * (N // 128) * (N // 64)
     assert size["forward_sla1"] > size["forward"]               # plus the alpha = 1 row

@@ -1,7 +1,7 @@
 """The allocation-free router entry point, sla2_router_noalloc, against sla2_router (GPU,
 through the C ABI). Both run the same kernels on the same inputs, so block lists, masks and
 scores must be identical (index work: bit for bit). Two calls in a row share the GPU's static
-scratch: the first at the 12-head N = 32768 workload (13 MB of the 32 MiB scratch), the second
+scratch: the first at the 12-head N = 32768 workload (14 MB of the 32 MiB scratch), the second
 smaller (the 2-head N = 2048 workload), which must not see the first call's leftovers."""
 import sys
 
