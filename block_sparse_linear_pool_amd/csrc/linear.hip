@@ -330,39 +330,51 @@ hipError_t launch_kv_prep(const Geom& g, int dtype, const void* K, const void* V
 }
 
 // ---------------------------------------------------------------- linear_total
-// grid (kD * kD / 64 + 2, BH), 256 threads. Workgroup x < 256 reduces elements 64 x .. 64 x + 63
-// of H_tot^T (partials are transposed; written in fragment order, or with `standard` set as
-// H_tot, [d_phi][d_v]); workgroups 256, 257 reduce Z_tot columns 0-63, 64-127. Wavefront w sums
-// partials w, w + 4, ... (four accumulators, all loads in flight); the four wavefront sums
-// are combined in a fixed order (deterministic).
+// grid (kD * kD / 256 + 1, BH), 256 threads. Workgroup x < 64 reduces elements 256 x .. 256 x +
+// 255 of H_tot^T (partials are transposed; written in fragment order, or with `standard` set as
+// H_tot, [d_phi][d_v]), lane l the four elements 256 x + 4 l .. + 3 (one 16-byte load, a
+// wavefront's load one contiguous 1 KB run); workgroup 64 reduces Z_tot (lanes 0-31). Wavefront
+// w sums partials w, w + 4, ... in rounds of 16 (all sixteen loads in flight, one round for up
+// to 512 key blocks); the four wavefront sums are combined in a fixed order (deterministic).
 __global__ __launch_bounds__(256) void linear_total_kernel(const float* __restrict__ hpart,
                                                            const float* __restrict__ zpart,
                                                            float* __restrict__ htot,
                                                            float* __restrict__ ztot, int np,
                                                            int standard) {
-  __shared__ float red[4][64];
+  __shared__ f32x4 red[4][64];
   const int bh = blockIdx.y, t = threadIdx.x, lane = t & 63, w = t >> 6;
-  const bool is_z = blockIdx.x >= kD * kD / 64;
-  const int e = is_z ? 64 * (blockIdx.x - kD * kD / 64) + lane : 64 * blockIdx.x + lane;
+  const bool is_z = blockIdx.x >= kD * kD / 256;
+  const bool live = !is_z || lane < kD / 4;   // Z_tot has 128 elements: lanes 0-31
+  const int e = is_z ? 4 * (lane & 31) : 256 * blockIdx.x + 4 * lane;
   const int stride = is_z ? kD : kD * kD;
   const float* src = (is_z ? zpart : hpart) + static_cast<size_t>(bh) * np * stride + e;
-  float a[4] = {0.f, 0.f, 0.f, 0.f};
-  int p = w;
-  for (; p + 12 < np; p += 16) {
+  f32x4 a = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int p = w; p < np; p += 64) {
+    f32x4 v[16];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) a[k] += src[static_cast<size_t>(p + 4 * k) * stride];
+    for (int k = 0; k < 16; ++k)
+      v[k] = live && p + 4 * k < np
+                 ? *reinterpret_cast<const f32x4*>(src + static_cast<size_t>(p + 4 * k) * stride)
+                 : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k = 0; k < 16; ++k) a += v[k];
   }
-  for (; p < np; p += 4) a[0] += src[static_cast<size_t>(p) * stride];
-  red[w][lane] = (a[0] + a[1]) + (a[2] + a[3]);
+  red[w][lane] = a;
   __syncthreads();
-  if (w == 0) {
-    const float v = (red[0][lane] + red[1][lane]) + (red[2][lane] + red[3][lane]);
+  if (w == 0 && live) {
+    const f32x4 v = (red[0][lane] + red[1][lane]) + (red[2][lane] + red[3][lane]);
     if (is_z) {
-      ztot[static_cast<size_t>(bh) * kD + e] = v;
+      *reinterpret_cast<f32x4*>(ztot + static_cast<size_t>(bh) * kD + e) = v;
     } else {
-      const int dv = e >> 7, dphi = e & (kD - 1);
-      const int out = standard ? dphi * kD + dv : htot_frag_index(dv, dphi);
-      htot[static_cast<size_t>(bh) * (kD * kD) + out] = v;
+      const int dv = e >> 7, dphi = e & (kD - 1);   // dphi a multiple of 4
+      float* hb = htot + static_cast<size_t>(bh) * (kD * kD);
+      if (standard) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) hb[(dphi + c) * kD + dv] = v[c];
+      } else {
+        // fragment order keeps dphi .. dphi + 3 of one dv together
+        *reinterpret_cast<f32x4*>(hb + htot_frag_index(dv, dphi)) = v;
+      }
     }
   }
 }
@@ -370,7 +382,7 @@ __global__ __launch_bounds__(256) void linear_total_kernel(const float* __restri
 hipError_t launch_linear_total(const Geom& g, const float* hpart, const float* zpart,
                                float* htot, float* ztot, int standard, hipStream_t s) {
   const int np = (g.nkb + kKpPerWg - 1) / kKpPerWg;
-  hipLaunchKernelGGL(linear_total_kernel, dim3(kD * kD / 64 + 2, g.BH), dim3(256), 0, s, hpart,
+  hipLaunchKernelGGL(linear_total_kernel, dim3(kD * kD / 256 + 1, g.BH), dim3(256), 0, s, hpart,
                      zpart, htot, ztot, np, standard);
   return hipGetLastError();
 }
