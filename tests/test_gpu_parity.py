@@ -96,6 +96,48 @@ def test_router_constant_rows_all_ties():
     assert np.array_equal(host(blocks)[0, 0], np.tile(np.arange(4), (4, 1)))
 
 
+@pytest.mark.parametrize("keep", [0.03, 0.125, 0.13])
+def test_router_ties_with_many_key_blocks(keep):
+    """512 key blocks (N = 32768), where the selection first narrows the search to the keys at or
+    above the kb-th largest lane maximum when kb <= 64 (keep 3 % and 12.5 %; 13 % gives kb = 66,
+    the plain search). Head 0: 49 key blocks hold the same rows (eight of them in one lane,
+    indices 7 + 64 m), far above the others under the identity projections, so every row's
+    boundary falls inside or just past that tie group: the lowest-index copies must be kept.
+    Head 1: all-zero Q, every logit 0 (all 512 keys are candidates): blocks 0 .. kb - 1."""
+    N, nkb = 32768, 512
+    q, k, v = W.random_qkv(37, 1, 2, N)
+    q[0, 0] += 1.0
+    dups = sorted(set([7 + 64 * m for m in range(8)]) | set(range(100, 142)))
+    assert len(dups) == 49
+    for j in dups:
+        k[0, 0, 64 * j:64 * j + 64] = 2.0
+    q[0, 1] = 0.0
+    eye = np.broadcast_to(np.eye(128, dtype=np.float32), (2, 128, 128)).copy()
+    kb = oracle.kept_blocks(nkb, keep)
+    blocks, mask, _ = sla2.sla2_router(dev(q), dev(k), dev(eye), dev(eye), keep)
+    blocks, mask = host(blocks), host(mask)
+    exact_rows = 0
+    for h in range(2):
+        _, mu32 = oracle.colmean(k[0, h])
+        Ks = oracle.smooth_k(k[0, h], mu32)
+        _, P = oracle.router_scores(oracle.block_mean(q[0, h], 128), oracle.block_mean(Ks, 64),
+                                    eye[h], eye[h])
+        ref_mask, ref_lists = oracle.topk_blocks(P, kb)
+        check_mask_band(P, kb, mask[0, h])
+        for i in range(N // 128):
+            assert np.array_equal(blocks[0, h, i], np.flatnonzero(mask[0, h, i]))
+            s = np.sort(P[i])[::-1]
+            if s[kb - 1] == s[kb] or s[kb - 1] - s[kb] > 1e-5 * s[kb - 1]:
+                assert np.array_equal(mask[0, h, i], ref_mask[i]), (h, i)
+                exact_rows += 1
+        if h == 0 and kb <= 49:
+            assert (ref_lists == np.array(dups[:kb])).all()
+        if h == 1:
+            assert (blocks[0, 1] == np.arange(kb)).all()
+    say(f"router ties, keep {keep} (kb {kb}): {exact_rows} of 512 rows compared exactly")
+    assert exact_rows >= 256
+
+
 # ------------------------------------------------------------------ quantisation + precompute
 @pytest.mark.parametrize("name,heads", [("tiny_iid_N2048", None), ("grid_8x32x32_N8192", [3])])
 def test_codes_and_scales_bit_exact(name, heads):
