@@ -173,10 +173,11 @@ def kernel_flops(p: Problem, name: str) -> float:
         # (4 N d^2 per head) is reported separately by linear_flops()
         return sparse_flops(p)
     if name in ("score_topk", "score_soft"):
-        # A = Qbar Wq and the logits A B^T
-        return 2.0 * p.BH * p.nqb * p.d * p.d + 2.0 * p.BH * p.nqb * p.nkb * p.d
+        # the logits A B^T
+        return 2.0 * p.BH * p.nqb * p.nkb * p.d
     if name == "project":
-        return 2.0 * p.BH * p.nkb * p.d * p.d
+        # B = Kbar_s Wk and A = Qbar Wq
+        return 2.0 * p.BH * (p.nkb + p.nqb) * p.d * p.d
     if name in ("kv_prep", "sla1_mix"):
         return 2.0 * p.BH * p.N * p.d * p.d
     if name == "bwd_lin_q":
