@@ -139,15 +139,15 @@ def kernel_bytes(p: Problem, name: str) -> float:
         # Q, K read; fp64 block sums written
         return 2 * E * p.in_bytes + BH * (p.nqb + p.nkb) * d * 8
     if name == "score_soft":
-        # fp64 Q block sums and fp32 B read; the fp32 soft mask and lambda written
-        return BH * p.nqb * d * 8 + BH * p.nkb * d * 4 + BH * p.nqb * p.nkb * 4 + BH * p.nqb * 4
+        # fp32 A and B read; the fp32 soft mask and lambda written
+        return BH * p.nqb * d * 4 + BH * p.nkb * d * 4 + BH * p.nqb * p.nkb * 4 + BH * p.nqb * 4
     if name == "score_topk":
-        # fp64 Q block sums and fp32 B read; mask, lists and counts written
-        return (BH * p.nqb * d * 8 + BH * p.nkb * d * 4 + BH * p.nqb * p.nkb
+        # fp32 A and B read; mask, lists and counts written
+        return (BH * p.nqb * d * 4 + BH * p.nkb * d * 4 + BH * p.nqb * p.nkb
                 + BH * p.nqb * (p.kb + 1) * 4)
     if name == "project":
-        # fp64 key-block sums read, fp32 B written
-        return BH * p.nkb * d * (8 + 4)
+        # fp64 block sums read (keys and queries), fp32 B and A written
+        return BH * (p.nkb + p.nqb) * d * (8 + 4)
     if name == "sla1_mix":
         # O_l and O read, O written
         return 3 * E * 4
