@@ -405,10 +405,11 @@ __device__ void select_row(const float* g, int nkb, int kb, int lane, size_t row
 // SoftTop-k of one row (training-time router, §4 Eq. 17 of the second page): P_c = softmax(g)
 // in fp64, x = P_c / tau in fp32, then lambda with f(lambda) = sum_j sigma(x_j + lambda) = kb.
 // The root lies in the bracket [L - max x, L - min x], L = log(kb / (nkb - kb)) (every term is
-// at most, resp. at least, kb / nkb at its ends). Safeguarded Newton in fp32, 16 steps from
+// at most, resp. at least, kb / nkb at its ends). Safeguarded Newton in fp32, at most 16 steps from
 // the uniform-row root L - 1 / (tau nkb): each step evaluates f and f' = sum sigma (1 - sigma),
 // narrows the bracket at the current point, and takes the Newton step, or the bracket midpoint
-// when that step leaves the bracket. Row sums are butterfly reductions (every lane holds the
+// when that step leaves the bracket; it stops early once a step moves lambda by at most 1e-7
+// relative (converged in fp32). Row sums are butterfly reductions (every lane holds the
 // same value, fixed order: deterministic). kb = nkb gives ones and lambda = +inf. Writes
 // soft[row][j] = sigma(x_j + lambda) and lam[row].
 template <int E>
@@ -470,7 +471,11 @@ __device__ void soft_row(const float* g, int nkb, int kb, float inv_tau, int lan
       if (fq < kbf) lo = lv;
       else hi = lv;
       const float nt = lv - (fq - kbf) / dq;
-      lv = (nt > lo && nt < hi) ? nt : 0.5f * (lo + hi);
+      const float nv = (nt > lo && nt < hi) ? nt : 0.5f * (lo + hi);
+      // every lane holds the same lambda: the exit is uniform
+      const bool done = fabsf(nv - lv) <= 1e-7f * fmaxf(1.0f, fabsf(lv));
+      lv = nv;
+      if (done) break;
     }
   }
 #pragma unroll
