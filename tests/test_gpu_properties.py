@@ -1,4 +1,4 @@
-"""Properties the forward must have exactly, checked on every row of the 12-head N = 32768
+"""Properties the forward and backward must have exactly, checked on every row of the 12-head N = 32768
 workload through the C ABI (the oracle's per-head cost limits its own checks there to sampled
 heads and rows).
 
@@ -7,6 +7,7 @@ heads and rows).
   doubles with the block's absolute maximum; h_j, H_tot, the accumulator's units and N_l
   double; the softmax weights, phi and the normaliser do not depend on V), quantised and
   unquantised.
+- The backward is linear in the upstream gradient: 2 dO gives twice every gradient, bit for bit.
 - Relabelling the heads (Q, K, V, the projections and alpha together) relabels the outputs bit
   for bit: every (batch, head) slice is computed on its own, whatever workgroup takes it.
 """
@@ -61,3 +62,22 @@ def test_head_relabelling_relabels_outputs_exactly():
     torch.cuda.synchronize()
     assert np.array_equal(host(m2), host(m1)[:, perm])
     assert np.array_equal(host(o2), host(o1)[:, perm])
+
+
+@pytest.mark.timeout(600)
+def test_backward_is_linear_in_the_upstream_gradient_exactly():
+    """dQ, dK, dV and dalpha of 2 dO are twice those of dO bit for bit (the bf16 copy of
+    alpha dO, every product, D, the centring of dK and the linear branch's terms all commute
+    with the exact scale), for the router's own mask on the full workload."""
+    w, q, k, v, wq, wk, alpha = inputs()
+    keep = w.keep_frac[-1]
+    t = torch.bfloat16
+    g = [dev(q, t), dev(k, t), dev(v, t)]
+    _, mask, _ = sla2.sla2_router(g[0], g[1], dev(wq), dev(wk), keep)
+    do = dev(W.grad_out(w.seed, q.shape))
+    a = dev(alpha)
+    r1 = [host(x) for x in sla2.sla2_backward(*g, mask, a, do)]
+    r2 = [host(x) for x in sla2.sla2_backward(*g, mask, a, do * 2)]
+    for x1, x2 in zip(r1, r2):
+        assert np.isfinite(x1).all() and np.abs(x1).max() > 0
+        assert np.array_equal(x2, 2 * x1)
