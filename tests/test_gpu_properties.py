@@ -1,6 +1,6 @@
-"""Properties the forward and backward must have exactly, checked on every row of the 12-head N = 32768
-workload through the C ABI (the oracle's per-head cost limits its own checks there to sampled
-heads and rows).
+"""Properties the forward and backward must have exactly, checked on every row of the 12-head
+N = 32768 workload through the C ABI (the oracle's per-head cost limits its own checks there to
+sampled heads and rows).
 
 - Scaling V by 2 scales O by 2 bit for bit: every step that touches V commutes with an exact
   power-of-two scale (bf16 inputs; the E4M3 codes of V are unchanged because the block scale
