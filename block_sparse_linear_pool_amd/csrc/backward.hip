@@ -63,36 +63,6 @@ __device__ inline uint2 ld_tr4(const uint16_t* p) {
       reinterpret_cast<__attribute__((address_space(3))) v4i16*>(reinterpret_cast<uintptr_t>(p)));
   return __builtin_bit_cast(uint2, v);
 }
-// Operand rows of a 32-column tile starting at column c0 of a [rows][kLd] tile: lane
-// (g, l) gets column c0 + l, rows k0 + 8 g .. +7 (natural order).
-__device__ inline bf16x8 ld_col8(const uint16_t* base, int c0, int k0, int g, int lane) {
-  const int s = lane & 15;
-  const uint16_t* p = base + (k0 + 8 * g + (s >> 2)) * kLd + c0 + 16 * ((lane >> 4) & 1) + 4 * (s & 3);
-  const uint2 a = ld_tr4(p), b = ld_tr4(p + 4 * kLd);
-  const i32x4 v = {static_cast<int>(a.x), static_cast<int>(a.y), static_cast<int>(b.x),
-                   static_cast<int>(b.y)};
-  return __builtin_bit_cast(bf16x8, v);
-}
-// The same with rows k0 + 4 g .. +3 and k0 + 8 + 4 g .. +3 (accumulator register order).
-__device__ inline bf16x8 ld_col8_acc(const uint16_t* base, int c0, int k0, int g, int lane) {
-  const int s = lane & 15;
-  const uint16_t* p = base + (k0 + 4 * g + (s >> 2)) * kLd + c0 + 16 * ((lane >> 4) & 1) + 4 * (s & 3);
-  const uint2 a = ld_tr4(p), b = ld_tr4(p + 8 * kLd);
-  const i32x4 v = {static_cast<int>(a.x), static_cast<int>(a.y), static_cast<int>(b.x),
-                   static_cast<int>(b.y)};
-  return __builtin_bit_cast(bf16x8, v);
-}
-// accumulator registers 8 h .. 8 h + 7 as a bf16 operand
-__device__ inline bf16x8 acc_op(const f32x16& c, int h) {
-  const i32x4 v = {static_cast<int>(pack_bf16x2(c[8 * h], c[8 * h + 1])),
-                   static_cast<int>(pack_bf16x2(c[8 * h + 2], c[8 * h + 3])),
-                   static_cast<int>(pack_bf16x2(c[8 * h + 4], c[8 * h + 5])),
-                   static_cast<int>(pack_bf16x2(c[8 * h + 6], c[8 * h + 7]))};
-  return __builtin_bit_cast(bf16x8, v);
-}
-__device__ inline f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-}
 __device__ inline void st_bf16x8(uint16_t* p, const float* v) {
   const i32x4 w = {static_cast<int>(pack_bf16x2(v[0], v[1])), static_cast<int>(pack_bf16x2(v[2], v[3])),
                    static_cast<int>(pack_bf16x2(v[4], v[5])), static_cast<int>(pack_bf16x2(v[6], v[7]))};
