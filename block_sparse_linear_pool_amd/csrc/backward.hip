@@ -82,41 +82,6 @@ __device__ inline int lanes_below(uint64_t m) {
                                    __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0));
 }
 
-// acc[u][k] += element 8 (t + 256 u) + k of the bf16 d x d tiles src + idx(n) d^2 for n in
-// [n0, n1), added in n order; kF tiles' loads are issued together.
-template <int kF = 2, typename Idx>
-__device__ inline void sum_tiles(float (&acc)[8][8], const uint16_t* src, Idx idx, int n0, int n1,
-                                 int t) {
-  int n = n0;
-  for (; n + kF - 1 < n1; n += kF) {
-    i32x4 v[kF][8];
-#pragma unroll
-    for (int f = 0; f < kF; ++f) {
-      const uint16_t* a = src + static_cast<size_t>(idx(n + f)) * (kD * kD);
-#pragma unroll
-      for (int u = 0; u < 8; ++u) v[f][u] = *reinterpret_cast<const i32x4*>(a + 8 * (t + 256 * u));
-    }
-#pragma unroll
-    for (int f = 0; f < kF; ++f)
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        float fa[8];
-        unpack_bf16x8(v[f][u], fa);
-#pragma unroll
-        for (int k = 0; k < 8; ++k) acc[u][k] += fa[k];
-      }
-  }
-  for (; n < n1; ++n) {
-    const uint16_t* a = src + static_cast<size_t>(idx(n)) * (kD * kD);
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      float fa[8];
-      unpack_bf16x8(*reinterpret_cast<const i32x4*>(a + 8 * (t + 256 * u)), fa);
-#pragma unroll
-      for (int k = 0; k < 8; ++k) acc[u][k] += fa[k];
-    }
-  }
-}
 // sum of src[idx(n) * kD + col] over n in [n0, n1), in n order, four loads in flight
 template <typename Idx>
 __device__ inline float sum_rows(const float* src, Idx idx, int n0, int n1, int col) {
